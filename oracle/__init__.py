@@ -1,0 +1,191 @@
+"""CPU reference ("oracle") of one SMC-SD round, in double precision.
+
+TEST INFRASTRUCTURE ONLY: the test suite, the smoke check and the CPU-baseline leg of the
+benchmark call it to check the GPU library; the library itself never imports it. The
+arithmetic lives in ``smcsd_oracle.c`` (plain C, fp64, one loop per definition); this module
+only builds that file with gcc and marshals numpy arrays to it.
+
+bf16 arrays are passed as their raw 16-bit patterns (numpy ``uint16``), fp32 as ``float32``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+import threading
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "smcsd_oracle.c")
+_SO = os.path.join(_HERE, "libsmcsd_oracle.so")
+
+F32, BF16 = 0, 1
+ALWAYS, ESS, NEVER = 0, 1, 2
+MODES = {"always": ALWAYS, "ess": ESS, "never": NEVER}
+
+_lock = threading.Lock()
+_lib = None
+
+
+def build(force: bool = True) -> str:
+    """Compile the oracle with gcc (OpenMP over independent rows, strict IEEE double)."""
+    if not force and os.path.exists(_SO):
+        return _SO
+    tmp = _SO + ".tmp%d" % os.getpid()
+    cmd = ["gcc", "-O2", "-std=c11", "-fopenmp", "-ffp-contract=off", "-fno-fast-math",
+           "-shared", "-fPIC", "-o", tmp, _SRC, "-lm"]
+    subprocess.run(cmd, check=True)
+    os.replace(tmp, _SO)
+    return _SO
+
+
+def lib() -> ctypes.CDLL:
+    global _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(_SO):
+                build()
+            L = ctypes.CDLL(_SO)
+            p, i32, i64, f64, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
+                                     ctypes.c_double, ctypes.c_float)
+            L.orc_row_logsumexp.restype = f64
+            L.orc_row_logsumexp.argtypes = [p, i32, i64, f64]
+            L.orc_row_tv.restype = f64
+            L.orc_row_tv.argtypes = [p, p, i32, i64, f64]
+            L.orc_row_gumbel_argmax.restype = i32
+            L.orc_row_gumbel_argmax.argtypes = [p, i32, p, i64, f32, p]
+            L.orc_resample_request.restype = i32
+            L.orc_resample_request.argtypes = [i32, p, p, f64, i32, f64, p, p, p, p, p]
+            L.orc_remap_request.restype = i32
+            L.orc_remap_request.argtypes = [i32, i32, p, p, p, p, i32]
+            L.orc_round.restype = i32
+            L.orc_round.argtypes = [i32, i32, i32, i64, i64, i32, p, p, p, p, p, p, i32, f32, p,
+                                    p, p, p, p, p, p, p, p, p, i32, i32, p, p, p, p, p]
+            L.orc_num_threads.restype = i32
+            L.orc_num_threads.argtypes = []
+            _lib = L
+    return _lib
+
+
+def _ptr(a: np.ndarray | None):
+    return None if a is None else a.ctypes.data_as(ctypes.c_void_p)
+
+
+def _logits(z: np.ndarray):
+    z = np.ascontiguousarray(z)
+    if z.dtype == np.float32:
+        return z, F32
+    if z.dtype == np.uint16:
+        return z, BF16
+    raise TypeError("logits must be float32 or raw bf16 bits (uint16), got %s" % z.dtype)
+
+
+def num_threads() -> int:
+    return int(lib().orc_num_threads())
+
+
+def row_logsumexp(z: np.ndarray, T: float) -> float:
+    """log sum_v exp(z_v / T) of one row (fp32 or bf16 bits)."""
+    z, dt = _logits(z.reshape(-1))
+    return float(lib().orc_row_logsumexp(_ptr(z), dt, z.size, float(T)))
+
+
+def row_tv(zp: np.ndarray, zq: np.ndarray, T: float) -> float:
+    """1/2 sum |p - q| of the temperature-scaled softmaxes of two rows."""
+    zp, dt = _logits(zp.reshape(-1))
+    zq, dt2 = _logits(zq.reshape(-1))
+    assert dt == dt2 and zp.size == zq.size
+    return float(lib().orc_row_tv(_ptr(zp), _ptr(zq), dt, zp.size, float(T)))
+
+
+def row_gumbel_argmax(z: np.ndarray, g: np.ndarray, T: float) -> tuple[int, float]:
+    """(argmax_v fma(z_v, 1/T, g_v) in binary32, top-2 key gap)."""
+    z, dt = _logits(z.reshape(-1))
+    g = np.ascontiguousarray(g.reshape(-1), dtype=np.float32)
+    assert g.size == z.size
+    gap = np.zeros(1, np.float64)
+    idx = lib().orc_row_gumbel_argmax(_ptr(z), dt, _ptr(g), z.size, float(T), _ptr(gap))
+    return int(idx), float(gap[0])
+
+
+def resample_request(lw, logw_prev, u: float, mode="always", ess_frac: float = 0.5):
+    """Normalise + ESS + systematic resampling of one request. Returns a dict."""
+    lw = np.ascontiguousarray(lw, dtype=np.float64)
+    prev = np.ascontiguousarray(logw_prev, dtype=np.float64)
+    N = lw.size
+    logZ = np.zeros(1)
+    ess = np.zeros(1)
+    anc = np.zeros(N, np.int32)
+    new = np.zeros(N)
+    gap = np.zeros(N)
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    rs = lib().orc_resample_request(N, _ptr(lw), _ptr(prev), float(u), m, float(ess_frac),
+                                    _ptr(logZ), _ptr(ess), _ptr(anc), _ptr(new), _ptr(gap))
+    return dict(resampled=int(rs), log_norm=float(logZ[0]), ess=float(ess[0]), ancestors=anc,
+                log_weights=new, anc_gap=gap)
+
+
+def remap_request(anc, page_table, refcount):
+    """Page-table remap of one request. Returns (new table, new refcount, status)."""
+    anc = np.ascontiguousarray(anc, dtype=np.int32)
+    pt = np.ascontiguousarray(page_table, dtype=np.int32)
+    N, P = pt.shape
+    out = np.zeros_like(pt)
+    rc = np.array(refcount, dtype=np.int32, copy=True)
+    st = lib().orc_remap_request(N, P, _ptr(anc), _ptr(pt), _ptr(out), _ptr(rc), rc.size)
+    return out, rc, int(st)
+
+
+def round(inputs: dict, *, V: int | None = None, mode="always", ess_frac: float = 0.5,
+          tv: bool = False, with_pages: bool = True) -> dict:
+    """One full SMC-SD round on host arrays.
+
+    ``inputs`` holds numpy arrays: target [R,N,K+1,ld], draft [R,N,K,ld] (float32 or bf16
+    bits as uint16), tokens [R,N,K] int32, temperature [R], gumbel [R,N,ld], uniform [R],
+    log_weights [R,N] float32 and optionally page_table [R,N,P] int32 + refcount
+    [num_pages] int32. ``V`` defaults to ld.
+    """
+    tgt, dt = _logits(inputs["target"])
+    dft, dt2 = _logits(inputs["draft"])
+    if dt != dt2:
+        raise TypeError("target and draft dtypes differ")
+    R, N, K1, ld = tgt.shape
+    K = K1 - 1
+    if dft.shape != (R, N, K, ld):
+        raise ValueError("draft shape %s != %s" % (dft.shape, (R, N, K, ld)))
+    V = ld if V is None else int(V)
+    tok = np.ascontiguousarray(inputs["tokens"], dtype=np.int32)
+    temp = np.ascontiguousarray(inputs["temperature"], dtype=np.float32)
+    gum = np.ascontiguousarray(inputs["gumbel"], dtype=np.float32)
+    uni = np.ascontiguousarray(inputs["uniform"], dtype=np.float32)
+    lwin = np.ascontiguousarray(inputs["log_weights"], dtype=np.float32)
+    assert tok.shape == (R, N, K) and temp.shape == (R,) and gum.shape == (R, N, ld)
+    assert uni.shape == (R,) and lwin.shape == (R, N)
+    out = dict(
+        log_w_incr=np.zeros((R, N)), log_weights=np.zeros((R, N)), log_norm=np.zeros(R),
+        ess=np.zeros(R), resampled=np.zeros(R, np.int32), ancestors=np.zeros((R, N), np.int32),
+        bonus=np.zeros((R, N), np.int32), out_tokens=np.zeros((R, N, K + 1), np.int32),
+        anc_gap=np.zeros((R, N)), bonus_gap=np.zeros((R, N)),
+    )
+    out["tv"] = np.zeros((R, N, K)) if tv else None
+    pt = rc = pt_out = None
+    P = num_pages = 0
+    if with_pages and inputs.get("page_table") is not None:
+        pt = np.ascontiguousarray(inputs["page_table"], dtype=np.int32)
+        P = pt.shape[2]
+        rc = np.array(inputs["refcount"], dtype=np.int32, copy=True)
+        num_pages = rc.size
+        pt_out = np.zeros_like(pt)
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    st = lib().orc_round(R, N, K, V, ld, dt, _ptr(tgt), _ptr(dft), _ptr(tok), _ptr(temp),
+                         _ptr(gum), _ptr(uni), m, float(ess_frac), _ptr(lwin),
+                         _ptr(out["log_w_incr"]), _ptr(out["log_weights"]), _ptr(out["log_norm"]),
+                         _ptr(out["ess"]), _ptr(out["resampled"]), _ptr(out["ancestors"]),
+                         _ptr(out["bonus"]), _ptr(out["out_tokens"]), _ptr(out["tv"]),
+                         P, num_pages, _ptr(pt), _ptr(pt_out), _ptr(rc), _ptr(out["anc_gap"]),
+                         _ptr(out["bonus_gap"]))
+    out["status"] = int(st)
+    out["page_table"] = pt_out
+    out["refcount"] = rc
+    return out

@@ -1,0 +1,351 @@
+/*
+ * smcsd_oracle.c -- plain, slow CPU reference of one SMC-SD round, in double precision.
+ *
+ * TEST INFRASTRUCTURE ONLY. It exists to check the GPU library, not to run in its place:
+ * only the test suite, the smoke check and the CPU-baseline leg of the benchmark load it.
+ * It shares no code, header, table or helper with the GPU library.
+ *
+ * What one round computes is taken from "Faster LLM Inference via Sequential Monte Carlo"
+ * (SMC-SD), section 2 "Methodology":
+ *   - a request keeps N particles, each a partially generated string;
+ *   - the draft model extends every particle by K tokens;
+ *   - the target model scores all extended particles in one batched pass;
+ *   - no token is rejected; each particle instead receives an importance weight;
+ *   - low-weight particles are evicted and high-weight ones duplicated, giving N again,
+ *     as in sequential Monte Carlo;
+ *   - every round also yields one bonus token from the target, so K+1 tokens per round;
+ *   - a duplicated particle shares KV pages with its source by copying page metadata and
+ *     exchanging pointers, never by copying KV tensors.
+ * The per-position total-variation distance is the block-divergence signal of the METASD
+ * page (section 2, "alignment feedback as reward"). Bonus noise is precomputed Gumbel noise
+ * as in the STAND page (method item 2, Gumbel-Top-K with cached noise), used here with k=1.
+ *
+ * The pages print no formulas. Where they are silent this file takes the plainest reading:
+ *   R1 weight: log w_i = sum_k [log p(x_k) - log q(x_k)] over the K drafted tokens; the bonus
+ *      token is drawn from p itself, so its ratio is 1 and it adds nothing.
+ *   R2 temperature: one T per request divides both target and draft logits.
+ *   R3 carried weights: l_i = logW_prev_i + log w_i; logZ = LSE_i l_i; after resampling every
+ *      log-weight becomes -log N, otherwise l_i - logZ is carried (normalised).
+ *   R4 resampling scheme: systematic, U_j = (j+u)/N, ancestor = min{i : U_j < C_i} with C the
+ *      inclusive prefix sum of the normalised weights, clamped to N-1.
+ *   R5 ESS = 1 / sum W_i^2; mode ESS resamples iff ESS < ess_frac * N (strict).
+ *   R6 bonus: drawn per original particle from its row K and inherited through the ancestor.
+ *   R7 the bonus decision is taken in binary32, key_v = fma(z_v, fl(1/T), G_v) rounded once,
+ *      lowest index on ties -- the precision the GPU kernel decides in.
+ *   R8 page table: [N][P] int32 per request, negative = unused; a refcount counts table
+ *      entries that reference a page.
+ * Summation order: over v ascending within a row, over k ascending, over i ascending.
+ */
+#include <math.h>
+#include <stddef.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+enum { ORC_F32 = 0, ORC_BF16 = 1 };
+enum { ORC_ALWAYS = 0, ORC_ESS = 1, ORC_NEVER = 2 };
+
+/* A bf16 value is the upper 16 bits of an IEEE-754 binary32, so widening is exact. */
+static float elem_f32(const void *row, int dtype, int64_t v)
+{
+    if (dtype == ORC_F32)
+        return ((const float *)row)[v];
+    uint32_t bits = (uint32_t)((const uint16_t *)row)[v] << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return f;
+}
+
+static double elem(const void *row, int dtype, int64_t v)
+{
+    return (double)elem_f32(row, dtype, v);
+}
+
+static size_t esize(int dtype) { return dtype == ORC_F32 ? 4u : 2u; }
+
+/*
+ * Temperature-scaled log-softmax normaliser of one logits row:
+ *   LSE(z/T) = m + log sum_v exp(z_v/T - m),  m = max_v z_v/T.
+ * log p(v) = z_v/T - LSE. (SMC-SD page, section 2: the weights need normalised target and
+ * draft probabilities at the drafted tokens; reading R2 for T.)
+ */
+double orc_row_logsumexp(const void *row, int dtype, int64_t V, double T)
+{
+    double m = -INFINITY;
+    for (int64_t v = 0; v < V; ++v) {
+        double a = elem(row, dtype, v) / T;
+        if (a > m)
+            m = a;
+    }
+    double s = 0.0;
+    for (int64_t v = 0; v < V; ++v)
+        s += exp(elem(row, dtype, v) / T - m);
+    return m + log(s);
+}
+
+/*
+ * Total-variation distance between the target and draft distributions of one position:
+ *   TV = 1/2 sum_v |exp(zp_v/T - A) - exp(zq_v/T - B)|
+ * with A, B the normalisers above (METASD page, section 2: block divergence is built on the
+ * total-variation distance between drafter and target distributions).
+ */
+static double tv_given_norms(const void *zp, const void *zq, int dtype, int64_t V, double T,
+                             double A, double B)
+{
+    double s = 0.0;
+    for (int64_t v = 0; v < V; ++v)
+        s += fabs(exp(elem(zp, dtype, v) / T - A) - exp(elem(zq, dtype, v) / T - B));
+    return 0.5 * s;
+}
+
+double orc_row_tv(const void *zp, const void *zq, int dtype, int64_t V, double T)
+{
+    double A = orc_row_logsumexp(zp, dtype, V, T);
+    double B = orc_row_logsumexp(zq, dtype, V, T);
+    return tv_given_norms(zp, zq, dtype, V, T, A, B);
+}
+
+/*
+ * Bonus token by Gumbel-max: argmax_v (z_v/T + G_v) with G precomputed standard Gumbel
+ * noise. Adding the row's normaliser to every key changes nothing, so this is argmax of
+ * log p(v) + G_v, i.e. one draw from p (STAND page, method item 2: Gumbel noise added to
+ * log-probabilities, top-k of the sum, noise precomputed and cached; here k = 1).
+ * Decision precision per reading R7. *gap receives key(best) - key(second best).
+ */
+int32_t orc_row_gumbel_argmax(const void *row, int dtype, const float *g, int64_t V, float T,
+                              double *gap)
+{
+    float invT = 1.0f / T;
+    float k1 = -INFINITY, k2 = -INFINITY;
+    int32_t best = 0;
+    for (int64_t v = 0; v < V; ++v) {
+        float key = fmaf(elem_f32(row, dtype, v), invT, g[v]);
+        if (key > k1) {
+            k2 = k1;
+            k1 = key;
+            best = (int32_t)v;
+        } else if (key > k2) {
+            k2 = key;
+        }
+    }
+    if (gap)
+        *gap = (double)k1 - (double)k2;
+    return best;
+}
+
+/*
+ * Normalise, ESS, resample decision and systematic resampling for one request
+ * (SMC-SD page, section 2: evict low-weight particles, duplicate high-weight ones, keep N;
+ * readings R3, R4, R5).
+ *   l_i = logw_prev_i + lw_i
+ *   e_i = exp(l_i - max l),  W_i = e_i / sum e,  logZ = max l + log sum e,  ESS = 1/sum W_i^2
+ * Resampled: anc_j = min{i : (j+u)/N < C_i} (clamped to N-1), logw_new_i = -log N.
+ * Otherwise: anc_j = j, logw_new_i = l_i - logZ.
+ * gap[j] = min_i |U_j - C_i| (infinity when not resampled): how close ancestor j is to a tie.
+ * Returns 1 if the request was resampled.
+ */
+int32_t orc_resample_request(int32_t N, const double *lw, const double *logw_prev, double u,
+                             int32_t mode, double ess_frac, double *logZ, double *ess,
+                             int32_t *anc, double *logw_new, double *gap)
+{
+    double *l = malloc(sizeof(double) * (size_t)N * 3);
+    double *W = l + N, *C = l + 2 * (size_t)N;
+    double m = -INFINITY;
+    for (int32_t i = 0; i < N; ++i) {
+        l[i] = logw_prev[i] + lw[i];
+        if (l[i] > m)
+            m = l[i];
+    }
+    double se = 0.0;
+    for (int32_t i = 0; i < N; ++i) {
+        W[i] = exp(l[i] - m);
+        se += W[i];
+    }
+    double s2 = 0.0;
+    for (int32_t i = 0; i < N; ++i) {
+        W[i] = W[i] / se;
+        s2 += W[i] * W[i];
+    }
+    *logZ = m + log(se);
+    *ess = 1.0 / s2;
+    int32_t rs = mode == ORC_ALWAYS || (mode == ORC_ESS && *ess < ess_frac * (double)N);
+    if (rs) {
+        double c = 0.0;
+        for (int32_t i = 0; i < N; ++i) {
+            c += W[i];
+            C[i] = c;
+        }
+        for (int32_t j = 0; j < N; ++j) {
+            double U = ((double)j + u) / (double)N;
+            int32_t i = 0;
+            while (i < N - 1 && !(U < C[i]))
+                ++i;
+            anc[j] = i;
+            double g = INFINITY;
+            for (int32_t t = 0; t < N; ++t)
+                g = fmin(g, fabs(U - C[t]));
+            gap[j] = g;
+        }
+        for (int32_t i = 0; i < N; ++i)
+            logw_new[i] = -log((double)N);
+    } else {
+        for (int32_t j = 0; j < N; ++j) {
+            anc[j] = j;
+            gap[j] = INFINITY;
+        }
+        for (int32_t i = 0; i < N; ++i)
+            logw_new[i] = l[i] - *logZ;
+    }
+    free(l);
+    return rs;
+}
+
+/*
+ * Page-table remap by pointer exchange for one request (SMC-SD page, section 2: a
+ * duplicated particle gets a copy of its source's page metadata and shares the KV pages
+ * through pointers; KV tensors are never copied; reading R8).
+ *   pt_out[j][c] = pt_in[anc_j][c]
+ *   o_i = #{j : anc_j = i};  for each valid pt_in[i][c]: refcount[page] += o_i - 1
+ * Returns 0, or -1 if an ancestor or page id is out of range or a refcount ends negative.
+ */
+int32_t orc_remap_request(int32_t N, int32_t P, const int32_t *anc, const int32_t *pt_in,
+                          int32_t *pt_out, int32_t *refcount, int32_t num_pages)
+{
+    int32_t err = 0;
+    int32_t *o = calloc((size_t)N, sizeof(int32_t));
+    for (int32_t j = 0; j < N; ++j) {
+        if (anc[j] < 0 || anc[j] >= N) {
+            free(o);
+            return -1;
+        }
+        o[anc[j]] += 1;
+    }
+    for (int32_t j = 0; j < N; ++j)
+        for (int32_t c = 0; c < P; ++c)
+            pt_out[(size_t)j * P + c] = pt_in[(size_t)anc[j] * P + c];
+    for (int32_t i = 0; i < N; ++i)
+        for (int32_t c = 0; c < P; ++c) {
+            int32_t page = pt_in[(size_t)i * P + c];
+            if (page < 0)
+                continue;
+            if (page >= num_pages) {
+                err = -1;
+                continue;
+            }
+            refcount[page] += o[i] - 1;
+        }
+    for (int32_t i = 0; i < N; ++i)
+        for (int32_t c = 0; c < P; ++c) {
+            int32_t page = pt_in[(size_t)i * P + c];
+            if (page >= 0 && page < num_pages && refcount[page] < 0)
+                err = -1;
+        }
+    free(o);
+    return err;
+}
+
+/*
+ * One whole round over R requests (SMC-SD page, section 2, in the order propose -> weight
+ * -> resample -> remap; reading R6 for the bonus).
+ *
+ * Layouts (row stride ld elements, ld >= V; element type per dtype):
+ *   target [R][N][K+1][ld]  rows 0..K-1 score the drafted tokens, row K is the bonus position
+ *   draft  [R][N][K][ld]    row k is the distribution x_k was drawn from
+ *   tokens [R][N][K] int32, temperature [R], gumbel [R][N][ld] fp32, uniform [R] in [0,1),
+ *   logw_in [R][N] fp32 (normalised), page tables [R][N][P] int32, refcount [num_pages].
+ * Outputs in double where the value is real: lw [R][N], logw_out [R][N], log_norm [R],
+ * ess [R], tv [R][N][K] (NULL skips TV), anc_gap [R][N], bonus_gap [R][N]; int32 elsewhere.
+ * out_tokens [R][N][K+1] may be NULL; pt_in == NULL skips the remap.
+ * Returns 0, or a negative code on an out-of-range token (-1) or remap error (-2).
+ */
+int32_t orc_round(int32_t R, int32_t N, int32_t K, int64_t V, int64_t ld, int32_t dtype,
+                  const void *target, const void *draft, const int32_t *tokens,
+                  const float *temperature, const float *gumbel, const float *uniform,
+                  int32_t mode, float ess_frac, const float *logw_in,
+                  double *lw, double *logw_out, double *log_norm, double *ess,
+                  int32_t *resampled, int32_t *anc, int32_t *bonus, int32_t *out_tokens,
+                  double *tv, int32_t P, int32_t num_pages, const int32_t *pt_in,
+                  int32_t *pt_out, int32_t *refcount, double *anc_gap, double *bonus_gap)
+{
+    const size_t es = esize(dtype);
+    const int64_t rows = (int64_t)R * N * K;
+    double *d = malloc(sizeof(double) * (size_t)(rows > 0 ? rows : 1));
+    int32_t bad_token = 0;
+
+    /* Per drafted position: log p(x_k) - log q(x_k), and the TV of that position. */
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad_token)
+    for (int64_t row = 0; row < rows; ++row) {
+        int64_t r = row / ((int64_t)N * K);
+        int64_t ik = row % ((int64_t)N * K);
+        int64_t i = ik / K, k = ik % K;
+        const char *zp = (const char *)target + (size_t)(((r * N + i) * (K + 1) + k) * ld) * es;
+        const char *zq = (const char *)draft + (size_t)(((r * N + i) * K + k) * ld) * es;
+        double T = (double)temperature[r];
+        double A = orc_row_logsumexp(zp, dtype, V, T);
+        double B = orc_row_logsumexp(zq, dtype, V, T);
+        int32_t x = tokens[row];
+        if (x < 0 || x >= V) {
+            bad_token = 1;
+            d[row] = 0.0;
+        } else {
+            d[row] = (elem(zp, dtype, x) / T - A) - (elem(zq, dtype, x) / T - B);
+        }
+        if (tv)
+            tv[row] = tv_given_norms(zp, zq, dtype, V, T, A, B);
+    }
+
+    /* Bonus token of every original particle. */
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t ri = 0; ri < (int64_t)R * N; ++ri) {
+        int64_t r = ri / N;
+        const char *zb = (const char *)target + (size_t)((ri * (K + 1) + K) * ld) * es;
+        bonus[ri] = orc_row_gumbel_argmax(zb, dtype, gumbel + (size_t)ri * ld, V, temperature[r],
+                                          bonus_gap ? &bonus_gap[ri] : NULL);
+    }
+
+    int32_t err = bad_token ? -1 : 0;
+    double *prev = malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    double *gap_tmp = malloc(sizeof(double) * (size_t)(N > 0 ? N : 1));
+    for (int32_t r = 0; r < R; ++r) {
+        for (int32_t i = 0; i < N; ++i) {
+            double s = 0.0;
+            for (int32_t k = 0; k < K; ++k)
+                s += d[((size_t)r * N + i) * K + k];
+            lw[(size_t)r * N + i] = s;
+            prev[i] = (double)logw_in[(size_t)r * N + i];
+        }
+        resampled[r] = orc_resample_request(N, lw + (size_t)r * N, prev, (double)uniform[r], mode,
+                                            (double)ess_frac, &log_norm[r], &ess[r],
+                                            anc + (size_t)r * N, logw_out + (size_t)r * N,
+                                            anc_gap ? anc_gap + (size_t)r * N : gap_tmp);
+        if (out_tokens) {
+            for (int32_t j = 0; j < N; ++j) {
+                int32_t a = anc[(size_t)r * N + j];
+                int32_t *dst = out_tokens + ((size_t)r * N + j) * (K + 1);
+                for (int32_t k = 0; k < K; ++k)
+                    dst[k] = tokens[((size_t)r * N + a) * K + k];
+                dst[K] = bonus[(size_t)r * N + a];
+            }
+        }
+        if (pt_in) {
+            if (orc_remap_request(N, P, anc + (size_t)r * N, pt_in + (size_t)r * N * P,
+                                  pt_out + (size_t)r * N * P, refcount, num_pages) != 0)
+                err = err ? err : -2;
+        }
+    }
+    free(gap_tmp);
+    free(prev);
+    free(d);
+    return err;
+}
+
+/* Threads OpenMP would use for the parallel loops above (1 when built without OpenMP). */
+int32_t orc_num_threads(void)
+{
+#ifdef _OPENMP
+    extern int omp_get_max_threads(void);
+    return (int32_t)omp_get_max_threads();
+#else
+    return 1;
+#endif
+}
