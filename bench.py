@@ -1,0 +1,221 @@
+#!/usr/bin/env python3
+"""Throughput of the SMC-SD round on one MI355X.
+
+One step = one full round (logits pass, finalize, page-table remap) over all R requests of
+the workload, inputs resident in HBM. The log-weights and refcounts carry over from round
+to round, and the two page-table buffers swap after each round (pointer exchange), so no
+state is reset inside the timed region.
+
+Prints one JSON line with:
+  * value: rounds/s;
+  * roofline of the dominant kernel (the logits pass): algorithmic bytes per launch, divided
+    by its mean duration from HIP events the library records around that launch on the
+    round's stream;
+  * cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_HBM_GBPS = 8000.0
+PROFILES = os.path.join(ROOT, "profiles")
+KERNEL_SOURCES = ["smc_particle_resampling_amd/csrc/k_logits.hip",
+                  "smc_particle_resampling_amd/csrc/smcsd_internal.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+class HipEvents:
+    """hipEvent_t handles for timing kernels on a given stream (plumbing over libamdhip64)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        e = ctypes.c_void_p()
+        if self.hip.hipEventCreate(ctypes.byref(e)) != 0:
+            raise RuntimeError("hipEventCreate failed")
+        return e.value
+
+    def elapsed_ms(self, a, b) -> float:
+        self.hip.hipEventSynchronize(b)
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return float(ms.value)
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(e)
+
+
+def read_roofline(smcsd, torch, dev, gib=4):
+    """Attainable HBM read GB/s: plain streaming read of `gib` GiB (best of 3)."""
+    n = gib << 30
+    buf = torch.empty(n, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.empty(2048 * 256, dtype=torch.int32, device=dev)
+    best = 0.0
+    for _ in range(4):
+        torch.cuda.synchronize()
+        t = time.perf_counter()
+        smcsd.smcsd_bench_stream_read(buf, sink, 2048)
+        torch.cuda.synchronize()
+        best = max(best, n / (time.perf_counter() - t) / 1e9)
+    del buf
+    return best
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on
+    the current kernel source (else None)."""
+    p = os.path.join(PROFILES, "traffic_k_logits_%s.json" % workload)
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(w, target_s=12.0):
+    """The oracle (as it is) on a bounded sample of the workload: one whole request (all N
+    particles, K positions, V logits), timed with a wall clock around oracle.round and
+    repeated until ~target_s; rounds/s = 1 / (R * seconds per request)."""
+    import oracle
+    from smc_particle_resampling_amd import synth
+    host = synth.to_host(synth.make_inputs(w.scaled(R=1), 11, device="cpu"))
+    times = []
+    while not times or (sum(times) < target_s and len(times) < 50):
+        t = time.perf_counter()
+        oracle.round(host, V=w.V, mode=w.mode, ess_frac=w.ess_frac, tv=w.tv)
+        times.append(time.perf_counter() - t)
+    per_request = sum(times) / len(times)
+    return {"value": 1.0 / (w.R * per_request), "unit": "rounds/s", "cores": oracle.num_threads(),
+            "kind": "oracle",
+            "sample": "1 of %d requests (N=%d, K=%d, V=%d, TV %s), fp64 oracle round repeated "
+                      "%d times, %.3f s each; rounds/s = 1/(%d * that)" % (
+                          w.R, w.N, w.K, w.V, "on" if w.tv else "off", len(times), per_request,
+                          w.R)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-roofline", action="store_true")
+    ap.add_argument("--copy-calibration", type=int, default=0,
+                    help="also run N launches of a plain 1 GiB copy (for counter scaling)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: the round shards by request with no "
+              "communication, so N GPUs run N independent copies of this line.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from smc_particle_resampling_amd import smcsd, synth
+
+    name = args.workload or synth.HEADLINE
+    w = synth.WORKLOADS[name]
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print("# building inputs for %s" % name, file=sys.stderr, flush=True)
+    inp = synth.make_inputs(w, 0, device=dev)
+    torch.cuda.synchronize()
+    out = smcsd.alloc_outputs(w.R, w.N, w.K, dev, tv=w.tv, V=w.V,
+                              dtype=smcsd.BF16 if w.dtype == "bf16" else smcsd.F32)
+    tables = [inp["page_table"], torch.empty_like(inp["page_table"])]
+    ev = HipEvents()
+    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+
+    def step(t, timing=None):
+        out["page_table_out"] = tables[(t + 1) % 2]
+        inp["page_table"] = tables[t % 2]
+        smcsd.run_round(inp, mode=w.mode, ess_frac=w.ess_frac, tv=w.tv, outputs=out,
+                        timing_events=timing)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    print("# warmup done", file=sys.stderr, flush=True)
+    t0 = time.perf_counter()
+    for t in range(args.steps):
+        step(args.warmup + t, timing=pairs[t])
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    flags = int(out["error_flags"].item())
+    if flags:
+        raise SystemExit("device error flags %d" % flags)
+    kms = [ev.elapsed_ms(a, b) for a, b in pairs]
+    for a, b in pairs:
+        ev.destroy(a)
+        ev.destroy(b)
+    k_mean_ms = sum(kms) / len(kms)
+    ms_per_step = elapsed * 1e3 / args.steps
+    alg = w.algorithmic_bytes()
+    logits_bytes = alg["target"] + alg["draft"] + alg["noise"]
+    achieved = logits_bytes / (k_mean_ms * 1e-3) / 1e9
+    print("# round %.3f ms, logits kernel %.3f ms (min %.3f max %.3f)" % (
+        ms_per_step, k_mean_ms, min(kms), max(kms)), file=sys.stderr, flush=True)
+
+    for _ in range(args.copy_calibration):
+        src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        smcsd.smcsd_bench_copy(src, dst)
+        torch.cuda.synchronize()
+        del src, dst
+
+    rr = None if args.no_read_roofline else read_roofline(smcsd, torch, dev)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    line = {
+        "metric": "SMC-SD rounds/s and achieved HBM GB/s (% of peak), N=32 K=8 V=128256 bf16",
+        "value": args.steps / elapsed,
+        "unit": "rounds/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms_per_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic",
+        "config": {"workload": name, "R": w.R, "N": w.N, "K": w.K, "V": w.V,
+                   "tv": w.tv, "resample": w.mode, "pages_per_particle": w.P,
+                   "round_GBps": (logits_bytes + alg["table"]) / (ms_per_step * 1e-3) / 1e9},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": achieved / PEAK_HBM_GBPS, "traffic": stored_traffic(name),
+                     "kernel": "k_logits", "kernel_ms": k_mean_ms,
+                     "algorithmic_bytes_per_launch": logits_bytes,
+                     "attainable_read_GBps": rr},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,192 @@
+/*
+ * smcsd.h -- C ABI of libsmcsd.so: one round of Sequential Monte Carlo speculative decoding
+ * (SMC-SD) on AMD Instinct MI355X (gfx950).
+ *
+ * The round follows "Faster LLM Inference via Sequential Monte Carlo", section 2
+ * (Methodology). A request keeps N particles. The draft model has extended each particle by
+ * K tokens, and one batched target pass has scored every position. This library takes those
+ * logits. It weights every particle by importance instead of rejecting tokens, then evicts
+ * low-weight particles and duplicates high-weight ones back to N. It draws the round's bonus
+ * token from the target and shares the KV pages of duplicated particles by exchanging page
+ * ids, never by copying KV tensors. Two by-products come from the same pass:
+ *   - the per-position total-variation distance that the METASD page (section 2) uses as
+ *     its block-divergence signal;
+ *   - the bonus token itself, drawn with precomputed Gumbel noise as in the STAND page
+ *     (method item 2: Gumbel-Top-K with cached noise, here k = 1).
+ *
+ * Conventions for every entry point:
+ *  - Pointers are device memory owned by the caller (hipMalloc or a torch tensor) unless
+ *    stated otherwise. The library allocates nothing, frees nothing and keeps no pointer
+ *    after a call returns; all scratch lives in the caller's workspace.
+ *  - Work is enqueued asynchronously on `stream` (NULL = the default stream). Results are
+ *    valid once that stream has been synchronised. Calls on different streams with disjoint
+ *    buffers may run concurrently. Two calls that share a workspace must not overlap.
+ *  - Argument errors are found on the host, before any HIP call, and are returned
+ *    synchronously; nothing is enqueued then. A failed launch returns SMCSD_ERR_DEVICE.
+ *  - Device-side preconditions cannot be checked on the host: finite logits and noise,
+ *    T > 0, u in [0,1), tokens in [0,V), page ids < num_pages, a consistent refcount.
+ *    Kernels guard every index they use. They OR the bits below into *error_flags (when
+ *    non-NULL, zeroed by the caller) instead of reading or writing out of bounds.
+ *  - All results are deterministic: no floating-point atomics, fixed reduction orders.
+ */
+#ifndef SMCSD_H
+#define SMCSD_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* hipStream_t / hipEvent_t handles, declared without the HIP headers. */
+typedef struct ihipStream_t *smcsd_stream;
+typedef struct ihipEvent_t *smcsd_event;
+
+typedef enum smcsd_status {
+    SMCSD_OK = 0,
+    SMCSD_ERR_ARG = 1,         /* null, out-of-range or inconsistent argument */
+    SMCSD_ERR_UNSUPPORTED = 2, /* valid request beyond this build's limits (see below) */
+    SMCSD_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than smcsd_workspace_size() */
+    SMCSD_ERR_DEVICE = 4       /* a HIP launch or runtime call failed */
+} smcsd_status;
+
+typedef enum smcsd_dtype { SMCSD_F32 = 0, SMCSD_BF16 = 1 } smcsd_dtype;
+
+/* When to resample. ESS: iff ESS < ess_frac * N (strict). */
+typedef enum smcsd_resample_mode {
+    SMCSD_RESAMPLE_ALWAYS = 0,
+    SMCSD_RESAMPLE_ESS = 1,
+    SMCSD_RESAMPLE_NEVER = 2
+} smcsd_resample_mode;
+
+/* Device-side error bits OR-ed into *error_flags. */
+#define SMCSD_DEVERR_TOKEN 1u     /* drafted token outside [0,V); its log-ratio counts as 0 */
+#define SMCSD_DEVERR_ANCESTOR 2u  /* ancestor outside [0,N) given to remap; its row is skipped */
+#define SMCSD_DEVERR_PAGE 4u      /* page id >= num_pages; its refcount update is skipped */
+#define SMCSD_DEVERR_REFCOUNT 8u  /* a refcount went below zero (inconsistent input table) */
+#define SMCSD_DEVERR_EXCHANGE 16u /* a TV slice exchange exceeded its time limit (results void) */
+
+/* Build limits. */
+#define SMCSD_MAX_N 1024 /* particles per request */
+#define SMCSD_MAX_K 256  /* drafted tokens per particle */
+
+/*
+ * Arguments of smcsd_round. Sizes first, then device pointers.
+ * Row layout: every logits row and noise row is `ld` elements long, contiguous in v, and
+ * only the first V elements are read. `ld` must be >= V and a multiple of 8 (bf16) or
+ * 4 (f32), and the base pointers must be 16-byte aligned, so every row starts on a 16-byte
+ * boundary. (Vocabularies that are not a multiple of 8 pad their rows; padding is ignored.)
+ */
+typedef struct smcsd_round_args {
+    int32_t R;          /* requests in the batch (0 = nothing to do) */
+    int32_t N;          /* particles per request, 1..SMCSD_MAX_N */
+    int32_t K;          /* drafted tokens per particle, 1..SMCSD_MAX_K */
+    int32_t V;          /* vocabulary size, >= 1 */
+    int64_t ld;         /* row stride in elements of logits and noise rows */
+    int32_t dtype;      /* smcsd_dtype of target_logits and draft_logits */
+    int32_t mode;       /* smcsd_resample_mode */
+    float ess_frac;     /* threshold for SMCSD_RESAMPLE_ESS, in (0, 1] */
+    int32_t P;          /* page-table columns per particle (ignored if page_table_in NULL) */
+    int32_t num_pages;  /* length of refcount */
+    int32_t reserved0;  /* must be 0 */
+
+    /* inputs */
+    const void *target_logits;   /* [R][N][K+1][ld]: rows 0..K-1 score x_0..x_{K-1}, row K is
+                                    the bonus position */
+    const void *draft_logits;    /* [R][N][K][ld]: row k is the distribution x_k came from */
+    const int32_t *draft_tokens; /* [R][N][K] drafted tokens x_k */
+    const float *temperature;    /* [R] T_r > 0, divides target and draft logits */
+    const float *gumbel;         /* [R][N][ld] f32 standard Gumbel noise for the bonus */
+    const float *uniform;        /* [R] u_r in [0,1) for systematic resampling */
+
+    /* in/out */
+    float *log_weights;          /* [R][N] normalised log-weights (LSE over N = 0);
+                                    first round: -log N. Replaced by the new weights. */
+
+    /* outputs */
+    float *log_w_incr;           /* [R][N] sum_k log p(x_k) - log q(x_k), original particles */
+    float *log_norm;             /* [R] logZ = LSE_i(log_weights_in + log_w_incr) */
+    float *ess;                  /* [R] 1 / sum_i W_i^2 */
+    int32_t *resampled;          /* [R] 1 if the request was resampled this round */
+    int32_t *ancestors;          /* [R][N] source particle of each new slot (identity if not
+                                    resampled) */
+    int32_t *bonus;              /* [R][N] bonus token of each ORIGINAL particle */
+    int32_t *out_tokens;         /* [R][N][K+1] tokens of each NEW slot: its ancestor's K
+                                    drafted tokens and bonus; may be NULL */
+    float *tv;                   /* [R][N][K] TV(p_k, q_k) per original particle; NULL = off */
+    const int32_t *page_table_in;/* [R][N][P] page ids, negative = unused; NULL = no remap */
+    int32_t *page_table_out;     /* [R][N][P] rows gathered through ancestors; must not alias
+                                    page_table_in (swap the two buffers between rounds) */
+    int32_t *refcount;           /* [num_pages] references from table entries; updated */
+    int32_t *error_flags;        /* optional device int32, SMCSD_DEVERR_* bits OR-ed in */
+
+    void *workspace;             /* device scratch, >= smcsd_workspace_size() bytes,
+                                    256-byte aligned; contents need no initialisation */
+    size_t workspace_bytes;
+
+    smcsd_event timing_begin;    /* optional: recorded on `stream` right before and after */
+    smcsd_event timing_end;      /* the logits-pass kernel (for roofline timing) */
+} smcsd_round_args;
+
+/*
+ * One SMC-SD round for R independent requests ("Faster LLM Inference via Sequential Monte
+ * Carlo", section 2: weight -> resample -> keep K+1 tokens -> share pages).
+ * Per request r, particle i, position k < K, with a = target/T_r and b = draft/T_r:
+ *   A_ik = LSE_v a[k,v],  B_ik = LSE_v b[k,v]                 (log-softmax normalisers)
+ *   log_w_incr_i = sum_k (a[k,x_k] - A_ik) - (b[k,x_k] - B_ik) (importance weight p/q)
+ *   tv_ik = 1/2 sum_v |exp(a[k,v]-A_ik) - exp(b[k,v]-B_ik)|    (METASD block divergence)
+ *   bonus_i = argmax_v fl32(fma(target[K,v], fl32(1/T_r), gumbel[v])), lowest v on ties
+ *   l_i = log_weights_i + log_w_incr_i, logZ = LSE_i l_i, W_i = exp(l_i - logZ),
+ *   ESS = 1/sum W_i^2; resample per `mode`.
+ *   Resampled: C = inclusive prefix sum of W (double), U_j = (j+u_r)/N,
+ *              ancestors_j = min{i : U_j < C_i} clamped to N-1; log_weights_i = -log N.
+ *   Otherwise: ancestors_j = j; log_weights_i = l_i - logZ.
+ *   page_table_out[j] = page_table_in[ancestors_j]; for each valid entry page of old row i
+ *   with o_i = #{j : ancestors_j = i} != 1: refcount[page] += o_i - 1 (integer atomics).
+ * Precision: logits widened exactly to f32, f32 accumulation over v, per-request weight
+ * arithmetic and the prefix sum in f64.
+ */
+smcsd_status smcsd_round(const smcsd_round_args *args, smcsd_stream stream);
+
+/*
+ * Normalise, ESS, resample decision and systematic resampling alone, from given per-particle
+ * log-weight increments (same definitions as in smcsd_round; "Faster LLM Inference via
+ * Sequential Monte Carlo", section 2: evict and duplicate back to N).
+ * log_w_incr [R][N] in; log_weights [R][N] in/out; uniform [R] in; log_norm, ess [R] out;
+ * resampled [R] out; ancestors [R][N] out. No workspace is needed.
+ */
+smcsd_status smcsd_resample(int32_t R, int32_t N, const float *log_w_incr, float *log_weights,
+                            const float *uniform, int32_t mode, float ess_frac,
+                            float *log_norm, float *ess, int32_t *resampled,
+                            int32_t *ancestors, smcsd_stream stream);
+
+/*
+ * Page-table remap by pointer exchange alone ("Faster LLM Inference via Sequential Monte
+ * Carlo", section 2, KV-cache management: duplicated particles get a copy of the page
+ * metadata and share the pages; KV tensors are untouched).
+ * ancestors [R][N] in; page_table_in [R][N][P] in; page_table_out [R][N][P] out (must not
+ * alias the input); refcount [num_pages] in/out; error_flags optional.
+ * Definitions as in smcsd_round. Out-of-range ancestors skip their row, out-of-range page
+ * ids skip their update, and both set a bit in *error_flags.
+ */
+smcsd_status smcsd_remap_pages(int32_t R, int32_t N, int32_t P, const int32_t *ancestors,
+                               const int32_t *page_table_in, int32_t *page_table_out,
+                               int32_t *refcount, int32_t num_pages, int32_t *error_flags,
+                               smcsd_stream stream);
+
+/* Workspace bytes smcsd_round needs for these sizes (0 if the sizes are invalid). */
+size_t smcsd_workspace_size(int32_t R, int32_t N, int32_t K, int32_t V, int32_t dtype,
+                            int32_t tv_enabled);
+
+/* Static, human-readable name of a status code. */
+const char *smcsd_status_string(smcsd_status status);
+
+/* sizeof(smcsd_round_args) as compiled into the library (for bindings to check layout). */
+size_t smcsd_round_args_size(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SMCSD_H */

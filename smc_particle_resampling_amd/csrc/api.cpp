@@ -1,0 +1,281 @@
+// api.cpp -- the C ABI of libsmcsd.so (include/smcsd.h): argument validation, the launch
+// plan, workspace layout and the launch sequence of one SMC-SD round.
+//
+// Validation is plain host code and makes no HIP call, so argument errors come back
+// synchronously, before anything is enqueued, on any machine.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstring>
+
+#include "smcsd.h"
+#include "smcsd_bench.h"
+#include "smcsd_internal.h"
+
+namespace smcsd {
+
+static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+bool make_plan(int32_t R, int32_t N, int32_t K, int32_t V, int64_t ld, int32_t dtype, bool tv,
+               Plan* p) {
+    if (R < 0 || N < 1 || N > SMCSD_MAX_N || K < 1 || K > SMCSD_MAX_K || V < 1) return false;
+    if (dtype != SMCSD_F32 && dtype != SMCSD_BF16) return false;
+    Plan q;
+    q.R = R;
+    q.N = N;
+    q.K = K;
+    q.V = V;
+    q.ld = ld;
+    q.dtype = dtype;
+    q.tv = tv;
+    q.epc = dtype == SMCSD_F32 ? 4 : 8;
+    q.chunks = (int32_t)(((int64_t)V + q.epc - 1) / q.epc);
+    const int32_t s0 = (q.chunks + kMaxSliceChunks - 1) / kMaxSliceChunks;
+    q.cps = (q.chunks + s0 - 1) / s0;
+    q.S = (q.chunks + q.cps - 1) / q.cps;   // no empty slice
+    q.pairs = (int64_t)R * N * K;
+    q.bonus_rows = (int64_t)R * N;
+    q.pair_wgs = q.pairs * q.S;
+    q.total_wgs = (q.pairs + q.bonus_rows) * q.S;
+    if (q.total_wgs >= (int64_t)INT32_MAX) return false;     // grid range
+    if (tv && q.S > kMaxTvSlices) return false;               // V > 524288 (bf16) with TV
+    size_t off = 0;
+    q.off_ctrl = off;
+    off = align256(off + sizeof(Ctrl));
+    q.off_pp = off;
+    off = align256(off + sizeof(PairPart) * (size_t)q.pair_wgs);
+    q.off_tvp = off;
+    off = align256(off + (tv ? sizeof(float) * (size_t)q.pair_wgs : 0));
+    q.off_bp = off;
+    off = align256(off + sizeof(BonusPart) * (size_t)(q.bonus_rows * q.S));
+    q.bytes = off;
+    *p = q;
+    return true;
+}
+
+static bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + nb && y < x + na;
+}
+
+static smcsd_status check_round(const smcsd_round_args* a, Plan* plan) {
+    if (!a) return SMCSD_ERR_ARG;
+    if (a->R < 0 || a->N < 1 || a->K < 1 || a->V < 1 || a->reserved0 != 0) return SMCSD_ERR_ARG;
+    if (a->dtype != SMCSD_F32 && a->dtype != SMCSD_BF16) return SMCSD_ERR_ARG;
+    if (a->mode < SMCSD_RESAMPLE_ALWAYS || a->mode > SMCSD_RESAMPLE_NEVER) return SMCSD_ERR_ARG;
+    if (a->mode == SMCSD_RESAMPLE_ESS && !(a->ess_frac > 0.0f && a->ess_frac <= 1.0f))
+        return SMCSD_ERR_ARG;
+    const int64_t epc = a->dtype == SMCSD_F32 ? 4 : 8;
+    if (a->ld < a->V || a->ld % epc != 0) return SMCSD_ERR_ARG;
+    if (a->N > SMCSD_MAX_N || a->K > SMCSD_MAX_K) return SMCSD_ERR_UNSUPPORTED;
+    if (a->R == 0) return SMCSD_OK;
+    if (!a->target_logits || !a->draft_logits || !a->draft_tokens || !a->temperature ||
+        !a->gumbel || !a->uniform || !a->log_weights || !a->log_w_incr || !a->log_norm ||
+        !a->ess || !a->resampled || !a->ancestors || !a->bonus)
+        return SMCSD_ERR_ARG;
+    if (!aligned16(a->target_logits) || !aligned16(a->draft_logits) || !aligned16(a->gumbel))
+        return SMCSD_ERR_ARG;
+    if (a->page_table_in) {
+        if (a->P < 1 || a->num_pages < 1 || !a->page_table_out || !a->refcount)
+            return SMCSD_ERR_ARG;
+        const size_t tb = sizeof(int32_t) * (size_t)a->R * a->N * a->P;
+        if (overlap(a->page_table_in, tb, a->page_table_out, tb)) return SMCSD_ERR_ARG;
+    }
+    if (!make_plan(a->R, a->N, a->K, a->V, a->ld, a->dtype, a->tv != nullptr, plan))
+        return SMCSD_ERR_UNSUPPORTED;
+    if (!a->workspace || a->workspace_bytes < plan->bytes) return SMCSD_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(a->workspace) & 255u) return SMCSD_ERR_WORKSPACE;
+    return SMCSD_OK;
+}
+
+}  // namespace smcsd
+
+using namespace smcsd;
+
+extern "C" {
+
+size_t smcsd_round_args_size(void) { return sizeof(smcsd_round_args); }
+
+const char* smcsd_status_string(smcsd_status s) {
+    switch (s) {
+    case SMCSD_OK: return "ok";
+    case SMCSD_ERR_ARG: return "invalid argument";
+    case SMCSD_ERR_UNSUPPORTED: return "unsupported size";
+    case SMCSD_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
+    case SMCSD_ERR_DEVICE: return "HIP launch or runtime error";
+    }
+    return "unknown status";
+}
+
+size_t smcsd_workspace_size(int32_t R, int32_t N, int32_t K, int32_t V, int32_t dtype,
+                            int32_t tv_enabled) {
+    Plan p;
+    const int64_t epc = dtype == SMCSD_F32 ? 4 : 8;
+    if (!make_plan(R, N, K, V, ((int64_t)V + epc - 1) / epc * epc, dtype, tv_enabled != 0, &p))
+        return 0;
+    return p.bytes;
+}
+
+smcsd_status smcsd_round(const smcsd_round_args* args, smcsd_stream stream) {
+    Plan plan;
+    const smcsd_status st = check_round(args, &plan);
+    if (st != SMCSD_OK || args->R == 0) return st;
+    const smcsd_round_args& a = *args;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(a.workspace);
+
+    LogitsArgs la{};
+    la.target = a.target_logits;
+    la.draft = a.draft_logits;
+    la.temperature = a.temperature;
+    la.gumbel = a.gumbel;
+    la.ctrl = reinterpret_cast<Ctrl*>(ws + plan.off_ctrl);
+    la.pp = reinterpret_cast<PairPart*>(ws + plan.off_pp);
+    la.tvp = reinterpret_cast<float*>(ws + plan.off_tvp);
+    la.bp = reinterpret_cast<BonusPart*>(ws + plan.off_bp);
+    la.error_flags = a.error_flags;
+    la.ld = a.ld;
+    la.pairs = plan.pairs;
+    la.pair_wgs = plan.pair_wgs;
+    la.total_wgs = plan.total_wgs;
+    la.N = a.N;
+    la.K = a.K;
+    la.V = a.V;
+    la.chunks = plan.chunks;
+    la.S = plan.S;
+    la.cps = plan.cps;
+
+    hipError_t e = hipSuccess;
+    if (plan.tv) {
+        // the abort flag starts at 0 and every exchange word at the all-ones "empty" pattern
+        // (fill kernels, not memset nodes, so the sequence can be captured in a graph)
+        e = launch_fill_words(reinterpret_cast<uint32_t*>(ws + plan.off_ctrl),
+                              (int64_t)sizeof(Ctrl) / 4, 0u, s);
+        if (e == hipSuccess)
+            e = launch_fill_words(reinterpret_cast<uint32_t*>(la.pp),
+                                  (int64_t)(plan.pair_wgs * sizeof(PairPart) / 4), ~0u, s);
+        if (e != hipSuccess) return SMCSD_ERR_DEVICE;
+    }
+    if (a.timing_begin && hipEventRecord(reinterpret_cast<hipEvent_t>(a.timing_begin), s) != hipSuccess)
+        return SMCSD_ERR_DEVICE;
+    e = launch_logits(plan, la, s);
+    if (e != hipSuccess) return SMCSD_ERR_DEVICE;
+    if (a.timing_end && hipEventRecord(reinterpret_cast<hipEvent_t>(a.timing_end), s) != hipSuccess)
+        return SMCSD_ERR_DEVICE;
+
+    FinalizeArgs fa{};
+    fa.target = a.target_logits;
+    fa.draft = a.draft_logits;
+    fa.tokens = a.draft_tokens;
+    fa.temperature = a.temperature;
+    fa.pp = la.pp;
+    fa.tvp = plan.tv ? la.tvp : nullptr;
+    fa.bp = la.bp;
+    fa.log_w_incr = a.log_w_incr;
+    fa.log_weights = a.log_weights;
+    fa.uniform = a.uniform;
+    fa.log_norm = a.log_norm;
+    fa.ess = a.ess;
+    fa.resampled = a.resampled;
+    fa.ancestors = a.ancestors;
+    fa.bonus = a.bonus;
+    fa.out_tokens = a.out_tokens;
+    fa.tv = a.tv;
+    fa.error_flags = a.error_flags;
+    fa.ld = a.ld;
+    fa.N = a.N;
+    fa.K = a.K;
+    fa.V = a.V;
+    fa.S = plan.S;
+    fa.mode = a.mode;
+    fa.ess_frac = a.ess_frac;
+    e = launch_finalize(a.R, true, a.dtype, fa, s);
+    if (e != hipSuccess) return SMCSD_ERR_DEVICE;
+
+    if (a.page_table_in) {
+        RemapArgs ra{};
+        ra.ancestors = a.ancestors;
+        ra.pt_in = a.page_table_in;
+        ra.pt_out = a.page_table_out;
+        ra.refcount = a.refcount;
+        ra.error_flags = a.error_flags;
+        ra.N = a.N;
+        ra.P = a.P;
+        ra.num_pages = a.num_pages;
+        ra.blocks_per_request = (int32_t)std::max<int64_t>(1, ((int64_t)a.N * a.P + 2047) / 2048);
+        e = launch_remap(a.R, ra, s);
+        if (e != hipSuccess) return SMCSD_ERR_DEVICE;
+    }
+    return SMCSD_OK;
+}
+
+smcsd_status smcsd_resample(int32_t R, int32_t N, const float* log_w_incr, float* log_weights,
+                            const float* uniform, int32_t mode, float ess_frac,
+                            float* log_norm, float* ess, int32_t* resampled,
+                            int32_t* ancestors, smcsd_stream stream) {
+    if (R < 0 || N < 1) return SMCSD_ERR_ARG;
+    if (mode < SMCSD_RESAMPLE_ALWAYS || mode > SMCSD_RESAMPLE_NEVER) return SMCSD_ERR_ARG;
+    if (mode == SMCSD_RESAMPLE_ESS && !(ess_frac > 0.0f && ess_frac <= 1.0f)) return SMCSD_ERR_ARG;
+    if (N > SMCSD_MAX_N) return SMCSD_ERR_UNSUPPORTED;
+    if (R == 0) return SMCSD_OK;
+    if (!log_w_incr || !log_weights || !uniform || !log_norm || !ess || !resampled || !ancestors)
+        return SMCSD_ERR_ARG;
+    FinalizeArgs fa{};
+    fa.log_w_incr = const_cast<float*>(log_w_incr);
+    fa.log_weights = log_weights;
+    fa.uniform = uniform;
+    fa.log_norm = log_norm;
+    fa.ess = ess;
+    fa.resampled = resampled;
+    fa.ancestors = ancestors;
+    fa.N = N;
+    fa.K = 0;
+    fa.mode = mode;
+    fa.ess_frac = ess_frac;
+    const hipError_t e = launch_finalize(R, false, SMCSD_F32, fa, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SMCSD_OK : SMCSD_ERR_DEVICE;
+}
+
+smcsd_status smcsd_remap_pages(int32_t R, int32_t N, int32_t P, const int32_t* ancestors,
+                               const int32_t* page_table_in, int32_t* page_table_out,
+                               int32_t* refcount, int32_t num_pages, int32_t* error_flags,
+                               smcsd_stream stream) {
+    if (R < 0 || N < 1 || P < 1 || num_pages < 1) return SMCSD_ERR_ARG;
+    if (N > SMCSD_MAX_N) return SMCSD_ERR_UNSUPPORTED;
+    if (R == 0) return SMCSD_OK;
+    if (!ancestors || !page_table_in || !page_table_out || !refcount) return SMCSD_ERR_ARG;
+    const size_t tb = sizeof(int32_t) * (size_t)R * N * P;
+    if (overlap(page_table_in, tb, page_table_out, tb)) return SMCSD_ERR_ARG;
+    if ((int64_t)R * (((int64_t)N * P + 2047) / 2048) >= (int64_t)INT32_MAX) return SMCSD_ERR_UNSUPPORTED;
+    RemapArgs ra{};
+    ra.ancestors = ancestors;
+    ra.pt_in = page_table_in;
+    ra.pt_out = page_table_out;
+    ra.refcount = refcount;
+    ra.error_flags = error_flags;
+    ra.N = N;
+    ra.P = P;
+    ra.num_pages = num_pages;
+    ra.blocks_per_request = (int32_t)std::max<int64_t>(1, ((int64_t)N * P + 2047) / 2048);
+    const hipError_t e = launch_remap(R, ra, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SMCSD_OK : SMCSD_ERR_DEVICE;
+}
+
+smcsd_status smcsd_bench_stream_read(const void* src, size_t bytes, uint32_t* sink,
+                                     int32_t grid, smcsd_stream stream) {
+    if (!src || !sink || grid < 1 || bytes % 16 != 0 || !aligned16(src)) return SMCSD_ERR_ARG;
+    const hipError_t e = launch_bench_read(src, bytes, sink, grid, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SMCSD_OK : SMCSD_ERR_DEVICE;
+}
+
+smcsd_status smcsd_bench_copy(const void* src, void* dst, size_t bytes, smcsd_stream stream) {
+    if (!src || !dst || bytes % 16 != 0 || !aligned16(src) || !aligned16(dst)) return SMCSD_ERR_ARG;
+    if (overlap(src, bytes, dst, bytes)) return SMCSD_ERR_ARG;
+    const hipError_t e = launch_bench_copy(src, dst, bytes, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SMCSD_OK : SMCSD_ERR_DEVICE;
+}
+
+}  // extern "C"

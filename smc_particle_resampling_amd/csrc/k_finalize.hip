@@ -1,0 +1,172 @@
+// k_finalize.hip -- per-request end of an SMC-SD round: importance weights, normalisation,
+// ESS, the resample decision, systematic resampling and the tokens each new slot keeps.
+//
+// "Faster LLM Inference via Sequential Monte Carlo", section 2: every particle gets an
+// importance weight instead of accept/reject; low-weight particles are evicted and
+// high-weight ones duplicated back to N; each round keeps K drafted tokens plus one bonus
+// token. One workgroup handles one request. The slice partials of the logits pass are
+// combined in fixed slice order, and everything per request runs in double precision: the
+// log-weights, logsumexp, ESS and the inclusive prefix sum of the weights. A boundary tie
+// U_j == C_i therefore resolves the same way on every run.
+#include "smcsd_internal.h"
+
+namespace smcsd {
+namespace {
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+template <int DT>
+__device__ __forceinline__ double logit_at(const void* base, int64_t row, int64_t ld, int32_t v) {
+    if constexpr (DT == SMCSD_F32) {
+        return (double)static_cast<const float*>(base)[row * ld + v];
+    } else {
+        const uint16_t bits = static_cast<const uint16_t*>(base)[row * ld + v];
+        return (double)__uint_as_float((uint32_t)bits << 16);
+    }
+}
+
+template <int DT, bool FROM_PARTIALS>
+__global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
+    __shared__ double s_l[SMCSD_MAX_N];    // l_i = log_weights_i + log_w_incr_i
+    __shared__ double s_c[SMCSD_MAX_N];    // W_i, then C_i
+    __shared__ int32_t s_bonus[SMCSD_MAX_N];
+    __shared__ double s_logZ;
+    __shared__ int32_t s_rs;
+    const int tid = threadIdx.x;
+    const int64_t r = blockIdx.x;
+    const int32_t N = a.N, K = a.K;
+
+    if constexpr (FROM_PARTIALS) {
+        const float T = a.temperature[r];
+        const float c32 = kLog2e / T;          // the scale the logits pass used
+        const double c = (double)c32;
+        const double invT = 1.0 / (double)T;
+        for (int32_t i = tid; i < N; i += kThreads) {
+            const int64_t ri = r * N + i;
+            double lw = 0.0;
+            for (int32_t k = 0; k < K; ++k) {
+                const int64_t u = ri * K + k;
+                const PairPart* part = a.pp + u * a.S;
+                float Mp = -INFINITY, Mq = -INFINITY;
+                for (int t = 0; t < a.S; ++t) {
+                    Mp = fmaxf(Mp, part[t].mp);
+                    Mq = fmaxf(Mq, part[t].mq);
+                }
+                double Sp = 0.0, Sq = 0.0;
+                for (int t = 0; t < a.S; ++t) {
+                    Sp += (double)part[t].sp * exp2(((double)part[t].mp - (double)Mp) * c);
+                    Sq += (double)part[t].sq * exp2(((double)part[t].mq - (double)Mq) * c);
+                }
+                const int32_t x = a.tokens[u];
+                if (x < 0 || x >= a.V) {
+                    flag_error(a.error_flags, SMCSD_DEVERR_TOKEN);
+                } else {
+                    // (zp[x] - Mp)/T - log Sp  -  ((zq[x] - Mq)/T - log Sq)
+                    const double zp = logit_at<DT>(a.target, ri * (K + 1) + k, a.ld, x);
+                    const double zq = logit_at<DT>(a.draft, u, a.ld, x);
+                    lw += ((zp - (double)Mp) - (zq - (double)Mq)) * invT - (log(Sp) - log(Sq));
+                }
+                if (a.tv) {
+                    double s = 0.0;
+                    for (int t = 0; t < a.S; ++t) s += (double)a.tvp[u * a.S + t];
+                    a.tv[u] = (float)fmin(fmax(0.5 * s, 0.0), 1.0);
+                }
+            }
+            a.log_w_incr[ri] = (float)lw;
+            s_l[i] = (double)a.log_weights[ri] + lw;
+            // bonus token of original particle i: best (key, index) over the slices
+            const BonusPart* bpart = a.bp + ri * a.S;
+            float best = bpart[0].key;
+            int32_t besti = bpart[0].idx;
+            for (int t = 1; t < a.S; ++t)
+                if (better(bpart[t].key, bpart[t].idx, best, besti)) {
+                    best = bpart[t].key;
+                    besti = bpart[t].idx;
+                }
+            if (besti < 0 || besti >= a.V) besti = 0;   // only if every key was NaN
+            a.bonus[ri] = besti;
+            s_bonus[i] = besti;
+        }
+    } else {
+        for (int32_t i = tid; i < N; i += kThreads)
+            s_l[i] = (double)a.log_weights[r * N + i] + (double)a.log_w_incr[r * N + i];
+    }
+    __syncthreads();
+
+    if (tid == 0) {
+        double m = -INFINITY;
+        for (int32_t i = 0; i < N; ++i) m = fmax(m, s_l[i]);
+        double se = 0.0;
+        for (int32_t i = 0; i < N; ++i) {
+            s_c[i] = exp(s_l[i] - m);
+            se += s_c[i];
+        }
+        double s2 = 0.0;
+        for (int32_t i = 0; i < N; ++i) {
+            s_c[i] = s_c[i] / se;
+            s2 += s_c[i] * s_c[i];
+        }
+        const double logZ = m + log(se);
+        const double ess = 1.0 / s2;
+        const int32_t rs = a.mode == SMCSD_RESAMPLE_ALWAYS ||
+                           (a.mode == SMCSD_RESAMPLE_ESS && ess < (double)a.ess_frac * (double)N);
+        if (rs) {
+            double acc = 0.0;
+            for (int32_t i = 0; i < N; ++i) {
+                acc += s_c[i];
+                s_c[i] = acc;
+            }
+        }
+        a.log_norm[r] = (float)logZ;
+        a.ess[r] = (float)ess;
+        a.resampled[r] = rs;
+        s_logZ = logZ;
+        s_rs = rs;
+    }
+    __syncthreads();
+
+    const int32_t rs = s_rs;
+    const double logZ = s_logZ;
+    const double u = (double)a.uniform[r];
+    for (int32_t j = tid; j < N; j += kThreads) {
+        int32_t anc = j;
+        if (rs) {
+            // min{i : U_j < C_i}, the last index standing in for "none" (clamp to N-1)
+            const double U = ((double)j + u) / (double)N;
+            int32_t lo = 0, hi = N - 1;
+            while (lo < hi) {
+                const int32_t mid = (lo + hi) >> 1;
+                if (U < s_c[mid]) hi = mid;
+                else lo = mid + 1;
+            }
+            anc = lo;
+        }
+        a.ancestors[r * N + j] = anc;
+        a.log_weights[r * N + j] = rs ? (float)(-log((double)N)) : (float)(s_l[j] - logZ);
+        if constexpr (FROM_PARTIALS) {
+            if (a.out_tokens) {
+                int32_t* dst = a.out_tokens + (r * N + j) * (K + 1);
+                const int32_t* src = a.tokens + (r * N + anc) * K;
+                for (int32_t k = 0; k < K; ++k) dst[k] = src[k];
+                dst[K] = s_bonus[anc];
+            }
+        }
+    }
+}
+
+}  // namespace
+
+hipError_t launch_finalize(int32_t R, bool from_partials, int32_t dtype, const FinalizeArgs& a,
+                           hipStream_t s) {
+    const dim3 grid((unsigned)R), block(kThreads);
+    if (!from_partials) {
+        k_finalize<SMCSD_F32, false><<<grid, block, 0, s>>>(a);
+    } else if (dtype == SMCSD_BF16) {
+        k_finalize<SMCSD_BF16, true><<<grid, block, 0, s>>>(a);
+    } else {
+        k_finalize<SMCSD_F32, true><<<grid, block, 0, s>>>(a);
+    }
+    return hipGetLastError();
+}
+
+}  // namespace smcsd

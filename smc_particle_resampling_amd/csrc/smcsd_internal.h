@@ -1,0 +1,187 @@
+// smcsd_internal.h -- launch plan, workspace layout and device helpers shared by the
+// kernels of libsmcsd.so. Not installed; the public contract is include/smcsd.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "smcsd.h"
+
+namespace smcsd {
+
+constexpr int kThreads = 256;        // workgroup size of every kernel (4 wave64)
+constexpr int kWaves = kThreads / 64;
+constexpr int kChunksPerLane = 8;    // 16-byte chunks each lane holds per row of a slice
+constexpr int kMaxSliceChunks = kThreads * kChunksPerLane;
+constexpr int kMaxTvSlices = 32;     // TV exchange: wave 0 reads the 2*S partial words
+
+// How one logits row is cut into 16-byte chunks and the chunks into slices, one workgroup
+// per slice. Every slice is non-empty and every chunk has at least one element < V.
+struct Plan {
+    int32_t R = 0, N = 0, K = 0, V = 0;
+    int64_t ld = 0;
+    int32_t dtype = 0;
+    int32_t epc = 0;         // elements per 16-byte chunk: 8 (bf16) or 4 (f32)
+    int32_t chunks = 0;      // chunks per row: ceil(V / epc)
+    int32_t S = 0;           // slices per row
+    int32_t cps = 0;         // chunks per slice (the last slice may hold fewer)
+    int64_t pairs = 0;       // R*N*K (target, draft) row pairs
+    int64_t bonus_rows = 0;  // R*N bonus rows
+    int64_t pair_wgs = 0;    // pairs * S
+    int64_t total_wgs = 0;   // (pairs + bonus_rows) * S
+    bool tv = false;
+    // workspace offsets in bytes
+    size_t off_ctrl = 0, off_pp = 0, off_tvp = 0, off_bp = 0, bytes = 0;
+};
+
+// Control block at the start of the workspace (zeroed before each TV launch).
+struct Ctrl {
+    uint32_t abort;   // set when a slice exchange timed out; later waits return at once
+    uint32_t pad;
+};
+
+// Per (row pair, slice): max and sum of exp2((z - max) * log2e/T) of target and draft.
+// As two 64-bit words (mp, sp) and (mq, sq) it is also the unit of the TV slice exchange.
+struct PairPart {
+    float mp, sp, mq, sq;
+};
+
+// Per (bonus row, slice): best fp32 key and its vocabulary index.
+struct BonusPart {
+    float key;
+    int32_t idx;
+};
+
+bool make_plan(int32_t R, int32_t N, int32_t K, int32_t V, int64_t ld, int32_t dtype, bool tv,
+               Plan* p);
+
+// Arguments of the logits pass, passed by value.
+struct LogitsArgs {
+    const void* target;
+    const void* draft;
+    const float* temperature;
+    const float* gumbel;
+    Ctrl* ctrl;
+    PairPart* pp;
+    float* tvp;
+    BonusPart* bp;
+    int32_t* error_flags;
+    int64_t ld;
+    int64_t pairs, pair_wgs, total_wgs;
+    int32_t N, K, V;
+    int32_t chunks, S, cps;
+};
+
+struct FinalizeArgs {
+    // from the logits pass (nullptr when log_w_incr is an input)
+    const void* target;
+    const void* draft;
+    const int32_t* tokens;
+    const float* temperature;
+    const PairPart* pp;
+    const float* tvp;
+    const BonusPart* bp;
+    // weights
+    float* log_w_incr;        // out (from partials) or in
+    float* log_weights;       // in/out
+    const float* uniform;
+    float* log_norm;
+    float* ess;
+    int32_t* resampled;
+    int32_t* ancestors;
+    int32_t* bonus;
+    int32_t* out_tokens;
+    float* tv;
+    int32_t* error_flags;
+    int64_t ld;
+    int32_t N, K, V, S;
+    int32_t mode;
+    float ess_frac;
+};
+
+struct RemapArgs {
+    const int32_t* ancestors;
+    const int32_t* pt_in;
+    int32_t* pt_out;
+    int32_t* refcount;
+    int32_t* error_flags;
+    int32_t N, P, num_pages, blocks_per_request;
+};
+
+// Host launchers (defined next to their kernels). Return hipSuccess or the launch error.
+hipError_t launch_fill_words(uint32_t* p, int64_t n, uint32_t value, hipStream_t s);
+hipError_t launch_logits(const Plan& plan, const LogitsArgs& a, hipStream_t s);
+hipError_t launch_finalize(int32_t R, bool from_partials, int32_t dtype, const FinalizeArgs& a,
+                           hipStream_t s);
+hipError_t launch_remap(int32_t R, const RemapArgs& a, hipStream_t s);
+hipError_t launch_bench_read(const void* src, size_t bytes, uint32_t* sink, int32_t grid,
+                             hipStream_t s);
+hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
+// ------------------------------------------------------------------ device helpers
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+
+// Element e (0..epc-1) of a 16-byte chunk as f32 (exact widening for bf16).
+template <int DT>
+__device__ __forceinline__ float chunk_elem(const u32x4& c, int e) {
+    if constexpr (DT == SMCSD_F32) {
+        return __uint_as_float(c[e]);
+    } else {
+        const uint32_t w = c[e >> 1];
+        return (e & 1) ? bf16_hi(w) : bf16_lo(w);
+    }
+}
+
+__device__ __forceinline__ void flag_error(int32_t* flags, uint32_t bit) {
+    if (flags) atomicOr(reinterpret_cast<unsigned int*>(flags), bit);
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+    return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+    return v;
+}
+
+// Block-wide reductions in a fixed order (lanes by xor tree, then waves 0..3), so results
+// are bit-identical from run to run. `lds` needs kWaves floats. All threads get the result.
+__device__ __forceinline__ float block_max(float v, float* lds) {
+    v = wave_max(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) lds[w] = v;
+    __syncthreads();
+    float r = lds[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) r = fmaxf(r, lds[i]);
+    __syncthreads();
+    return r;
+}
+
+__device__ __forceinline__ float block_sum(float v, float* lds) {
+    v = wave_sum(v);
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) lds[w] = v;
+    __syncthreads();
+    float r = lds[0];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) r += lds[i];
+    __syncthreads();
+    return r;
+}
+
+// (key, index) argmax: the larger key wins, the lower index wins on equal keys.
+__device__ __forceinline__ bool better(float k1, int32_t i1, float k2, int32_t i2) {
+    return k1 > k2 || (k1 == k2 && i1 < i2);
+}
+
+}  // namespace smcsd

@@ -1,0 +1,285 @@
+"""ctypes binding of libsmcsd.so (include/smcsd.h), with the same names as the C entry points.
+
+Argument marshalling only: torch tensors are checked for device, dtype, shape and
+contiguity, then their device pointers and the current HIP stream go to the C ABI. Every
+step of the round runs in the library's HIP kernels. There is no fallback: importing this
+module raises if the library has not been built (``python -m
+smc_particle_resampling_amd.build``).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsmcsd.so")
+if not os.path.exists(_LIB_PATH):
+    raise ImportError("libsmcsd.so is not built (expected at %s); run "
+                      "`python -m smc_particle_resampling_amd.build`" % _LIB_PATH)
+_lib = ctypes.CDLL(_LIB_PATH)
+
+OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE = 0, 1, 2, 3, 4
+F32, BF16 = 0, 1
+RESAMPLE_ALWAYS, RESAMPLE_ESS, RESAMPLE_NEVER = 0, 1, 2
+MODES = {"always": RESAMPLE_ALWAYS, "ess": RESAMPLE_ESS, "never": RESAMPLE_NEVER}
+DEVERR_TOKEN, DEVERR_ANCESTOR, DEVERR_PAGE, DEVERR_REFCOUNT, DEVERR_EXCHANGE = 1, 2, 4, 8, 16
+MAX_N, MAX_K = 1024, 256
+
+_i32, _i64, _f32, _p, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
+
+
+class RoundArgs(ctypes.Structure):
+    """Mirror of smcsd_round_args."""
+    _fields_ = [
+        ("R", _i32), ("N", _i32), ("K", _i32), ("V", _i32), ("ld", _i64), ("dtype", _i32),
+        ("mode", _i32), ("ess_frac", _f32), ("P", _i32), ("num_pages", _i32), ("reserved0", _i32),
+        ("target_logits", _p), ("draft_logits", _p), ("draft_tokens", _p), ("temperature", _p),
+        ("gumbel", _p), ("uniform", _p), ("log_weights", _p), ("log_w_incr", _p),
+        ("log_norm", _p), ("ess", _p), ("resampled", _p), ("ancestors", _p), ("bonus", _p),
+        ("out_tokens", _p), ("tv", _p), ("page_table_in", _p), ("page_table_out", _p),
+        ("refcount", _p), ("error_flags", _p), ("workspace", _p), ("workspace_bytes", _sz),
+        ("timing_begin", _p), ("timing_end", _p),
+    ]
+
+
+_lib.smcsd_round.restype = _i32
+_lib.smcsd_round.argtypes = [ctypes.POINTER(RoundArgs), _p]
+_lib.smcsd_resample.restype = _i32
+_lib.smcsd_resample.argtypes = [_i32, _i32, _p, _p, _p, _i32, _f32, _p, _p, _p, _p, _p]
+_lib.smcsd_remap_pages.restype = _i32
+_lib.smcsd_remap_pages.argtypes = [_i32, _i32, _i32, _p, _p, _p, _p, _i32, _p, _p]
+_lib.smcsd_workspace_size.restype = _sz
+_lib.smcsd_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32, _i32]
+_lib.smcsd_status_string.restype = ctypes.c_char_p
+_lib.smcsd_status_string.argtypes = [_i32]
+_lib.smcsd_round_args_size.restype = _sz
+_lib.smcsd_round_args_size.argtypes = []
+_lib.smcsd_bench_stream_read.restype = _i32
+_lib.smcsd_bench_stream_read.argtypes = [_p, _sz, _p, _i32, _p]
+_lib.smcsd_bench_copy.restype = _i32
+_lib.smcsd_bench_copy.argtypes = [_p, _p, _sz, _p]
+
+
+class SmcsdError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__("%s: %s (status %d)" % (where, smcsd_status_string(status), status))
+        self.status = status
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def raw_library() -> ctypes.CDLL:
+    return _lib
+
+
+def smcsd_status_string(status: int) -> str:
+    return _lib.smcsd_status_string(int(status)).decode()
+
+
+def smcsd_round_args_size() -> int:
+    return int(_lib.smcsd_round_args_size())
+
+
+def smcsd_workspace_size(R: int, N: int, K: int, V: int, dtype: int, tv_enabled: bool) -> int:
+    return int(_lib.smcsd_workspace_size(R, N, K, V, dtype, int(bool(tv_enabled))))
+
+
+# ------------------------------------------------------------------ marshalling helpers
+def _ptr(t: torch.Tensor | None):
+    return None if t is None else t.data_ptr()
+
+
+def _check(t, name, dtype, shape, device):
+    if t is None:
+        raise ValueError("%s is required" % name)
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError("%s has dtype %s, expected %s" % (name, t.dtype, dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s has shape %s, expected %s" % (name, tuple(t.shape), tuple(shape)))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+    return t
+
+
+def _stream(device, stream):
+    if stream is not None:
+        return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def smcsd_round(*, target_logits, draft_logits, draft_tokens, temperature, gumbel, uniform,
+                log_weights, log_w_incr, log_norm, ess, resampled, ancestors, bonus,
+                workspace, out_tokens=None, tv=None, page_table_in=None, page_table_out=None,
+                refcount=None, error_flags=None, V: int | None = None, mode="always",
+                ess_frac: float = 0.5, timing_events=None, stream=None) -> None:
+    """Enqueue one SMC-SD round (smcsd_round). Shapes: target [R,N,K+1,ld], draft
+    [R,N,K,ld] (both float32 or bfloat16), draft_tokens [R,N,K] int32, temperature [R],
+    gumbel [R,N,ld], uniform [R], per-request/per-particle outputs as in include/smcsd.h."""
+    dev = target_logits.device
+    if target_logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("logits must be float32 or bfloat16")
+    if target_logits.dim() != 4:
+        raise ValueError("target_logits must be [R, N, K+1, ld]")
+    R, N, K1, ld = target_logits.shape
+    K = K1 - 1
+    V = ld if V is None else int(V)
+    f32, i32 = torch.float32, torch.int32
+    _check(target_logits, "target_logits", None, None, dev)
+    _check(draft_logits, "draft_logits", target_logits.dtype, (R, N, K, ld), dev)
+    _check(draft_tokens, "draft_tokens", i32, (R, N, K), dev)
+    _check(temperature, "temperature", f32, (R,), dev)
+    _check(gumbel, "gumbel", f32, (R, N, ld), dev)
+    _check(uniform, "uniform", f32, (R,), dev)
+    _check(log_weights, "log_weights", f32, (R, N), dev)
+    _check(log_w_incr, "log_w_incr", f32, (R, N), dev)
+    _check(log_norm, "log_norm", f32, (R,), dev)
+    _check(ess, "ess", f32, (R,), dev)
+    _check(resampled, "resampled", i32, (R,), dev)
+    _check(ancestors, "ancestors", i32, (R, N), dev)
+    _check(bonus, "bonus", i32, (R, N), dev)
+    _check(workspace, "workspace", torch.uint8, None, dev)
+    if out_tokens is not None:
+        _check(out_tokens, "out_tokens", i32, (R, N, K + 1), dev)
+    if tv is not None:
+        _check(tv, "tv", f32, (R, N, K), dev)
+    P = num_pages = 0
+    if page_table_in is not None:
+        P = page_table_in.shape[-1]
+        _check(page_table_in, "page_table_in", i32, (R, N, P), dev)
+        _check(page_table_out, "page_table_out", i32, (R, N, P), dev)
+        _check(refcount, "refcount", i32, None, dev)
+        num_pages = refcount.numel()
+    if error_flags is not None:
+        _check(error_flags, "error_flags", i32, None, dev)
+    a = RoundArgs()
+    a.R, a.N, a.K, a.V, a.ld = R, N, K, V, ld
+    a.dtype = BF16 if target_logits.dtype == torch.bfloat16 else F32
+    a.mode = MODES[mode] if isinstance(mode, str) else int(mode)
+    a.ess_frac = float(ess_frac)
+    a.P, a.num_pages, a.reserved0 = P, num_pages, 0
+    a.target_logits, a.draft_logits = _ptr(target_logits), _ptr(draft_logits)
+    a.draft_tokens, a.temperature = _ptr(draft_tokens), _ptr(temperature)
+    a.gumbel, a.uniform, a.log_weights = _ptr(gumbel), _ptr(uniform), _ptr(log_weights)
+    a.log_w_incr, a.log_norm, a.ess = _ptr(log_w_incr), _ptr(log_norm), _ptr(ess)
+    a.resampled, a.ancestors, a.bonus = _ptr(resampled), _ptr(ancestors), _ptr(bonus)
+    a.out_tokens, a.tv = _ptr(out_tokens), _ptr(tv)
+    a.page_table_in, a.page_table_out = _ptr(page_table_in), _ptr(page_table_out)
+    a.refcount, a.error_flags = _ptr(refcount), _ptr(error_flags)
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    if timing_events is not None:
+        a.timing_begin, a.timing_end = timing_events
+    st = _lib.smcsd_round(ctypes.byref(a), _stream(dev, stream))
+    if st != OK:
+        raise SmcsdError(st, "smcsd_round")
+
+
+def smcsd_resample(*, log_w_incr, log_weights, uniform, log_norm, ess, resampled, ancestors,
+                   mode="always", ess_frac: float = 0.5, stream=None) -> None:
+    """Enqueue normalise + ESS + systematic resampling from given log-weight increments."""
+    dev = log_w_incr.device
+    R, N = log_w_incr.shape
+    f32, i32 = torch.float32, torch.int32
+    _check(log_w_incr, "log_w_incr", f32, (R, N), dev)
+    _check(log_weights, "log_weights", f32, (R, N), dev)
+    _check(uniform, "uniform", f32, (R,), dev)
+    _check(log_norm, "log_norm", f32, (R,), dev)
+    _check(ess, "ess", f32, (R,), dev)
+    _check(resampled, "resampled", i32, (R,), dev)
+    _check(ancestors, "ancestors", i32, (R, N), dev)
+    m = MODES[mode] if isinstance(mode, str) else int(mode)
+    st = _lib.smcsd_resample(R, N, _ptr(log_w_incr), _ptr(log_weights), _ptr(uniform), m,
+                             float(ess_frac), _ptr(log_norm), _ptr(ess), _ptr(resampled),
+                             _ptr(ancestors), _stream(dev, stream))
+    if st != OK:
+        raise SmcsdError(st, "smcsd_resample")
+
+
+def smcsd_remap_pages(*, ancestors, page_table_in, page_table_out, refcount, error_flags=None,
+                      stream=None) -> None:
+    """Enqueue the page-table remap by pointer exchange."""
+    dev = ancestors.device
+    R, N, P = page_table_in.shape
+    i32 = torch.int32
+    _check(ancestors, "ancestors", i32, (R, N), dev)
+    _check(page_table_in, "page_table_in", i32, (R, N, P), dev)
+    _check(page_table_out, "page_table_out", i32, (R, N, P), dev)
+    _check(refcount, "refcount", i32, None, dev)
+    if error_flags is not None:
+        _check(error_flags, "error_flags", i32, None, dev)
+    st = _lib.smcsd_remap_pages(R, N, P, _ptr(ancestors), _ptr(page_table_in),
+                                _ptr(page_table_out), _ptr(refcount), refcount.numel(),
+                                _ptr(error_flags), _stream(dev, stream))
+    if st != OK:
+        raise SmcsdError(st, "smcsd_remap_pages")
+
+
+def smcsd_bench_stream_read(src: torch.Tensor, sink: torch.Tensor, grid: int, stream=None) -> None:
+    st = _lib.smcsd_bench_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                      int(grid), _stream(src.device, stream))
+    if st != OK:
+        raise SmcsdError(st, "smcsd_bench_stream_read")
+
+
+def smcsd_bench_copy(src: torch.Tensor, dst: torch.Tensor, stream=None) -> None:
+    st = _lib.smcsd_bench_copy(_ptr(src), _ptr(dst), src.numel() * src.element_size(),
+                               _stream(src.device, stream))
+    if st != OK:
+        raise SmcsdError(st, "smcsd_bench_copy")
+
+
+# ------------------------------------------------------------------ allocation conveniences
+def alloc_outputs(R: int, N: int, K: int, device, tv: bool = False, out_tokens: bool = True,
+                  V: int = 1, dtype: int = BF16) -> dict:
+    """Output tensors and a workspace for smcsd_round (torch allocates; nothing is computed)."""
+    f32, i32 = torch.float32, torch.int32
+    ws = smcsd_workspace_size(R, N, K, V, dtype, tv)
+    if ws == 0 and R > 0:
+        raise ValueError("sizes unsupported: R=%d N=%d K=%d V=%d" % (R, N, K, V))
+    return dict(
+        log_w_incr=torch.empty((R, N), dtype=f32, device=device),
+        log_norm=torch.empty((R,), dtype=f32, device=device),
+        ess=torch.empty((R,), dtype=f32, device=device),
+        resampled=torch.empty((R,), dtype=i32, device=device),
+        ancestors=torch.empty((R, N), dtype=i32, device=device),
+        bonus=torch.empty((R, N), dtype=i32, device=device),
+        out_tokens=torch.empty((R, N, K + 1), dtype=i32, device=device) if out_tokens else None,
+        tv=torch.empty((R, N, K), dtype=f32, device=device) if tv else None,
+        error_flags=torch.zeros((1,), dtype=i32, device=device),
+        workspace=torch.empty((max(ws, 256),), dtype=torch.uint8, device=device),
+    )
+
+
+def run_round(inputs: dict, *, mode="always", ess_frac=0.5, tv=False, pages=True, outputs=None,
+              timing_events=None, stream=None) -> dict:
+    """smcsd_round on a dict from ``synth.make_inputs`` (log_weights, page tables and refcount
+    are updated in place / swapped like a caller would). Returns the output tensors."""
+    tgt = inputs["target"]
+    R, N, K1, ld = tgt.shape
+    K = K1 - 1
+    dt = BF16 if tgt.dtype == torch.bfloat16 else F32
+    out = outputs or alloc_outputs(R, N, K, tgt.device, tv=tv, V=inputs["V"], dtype=dt)
+    pt_in = inputs.get("page_table") if pages else None
+    if pt_in is not None and "page_table_out" not in out:
+        out["page_table_out"] = torch.empty_like(pt_in)
+    smcsd_round(target_logits=tgt, draft_logits=inputs["draft"], draft_tokens=inputs["tokens"],
+                temperature=inputs["temperature"], gumbel=inputs["gumbel"],
+                uniform=inputs["uniform"], log_weights=inputs["log_weights"],
+                log_w_incr=out["log_w_incr"], log_norm=out["log_norm"], ess=out["ess"],
+                resampled=out["resampled"], ancestors=out["ancestors"], bonus=out["bonus"],
+                out_tokens=out.get("out_tokens"), tv=out.get("tv"), page_table_in=pt_in,
+                page_table_out=out.get("page_table_out") if pt_in is not None else None,
+                refcount=inputs.get("refcount") if pt_in is not None else None,
+                error_flags=out["error_flags"], workspace=out["workspace"], V=inputs["V"],
+                mode=mode, ess_frac=ess_frac, timing_events=timing_events, stream=stream)
+    return out
+
+
+__all__ = [n for n in dir() if n.startswith("smcsd_")] + [
+    "RoundArgs", "SmcsdError", "alloc_outputs", "run_round", "library_path", "MODES"]

@@ -1,0 +1,144 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function include/*.h
+declares, the binding's struct layout matches, and host-side argument validation returns
+the documented status codes before any HIP call."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from smc_particle_resampling_amd import smcsd as S
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared_functions():
+    names = set()
+    for h in ("smcsd.h", "smcsd_bench.h"):
+        src = open(os.path.join(ROOT, "include", h)).read()
+        src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+        for m in re.finditer(r"^\s*(?:const\s+)?[A-Za-z_][A-Za-z0-9_]*\s*\**\s*(smcsd_[A-Za-z0-9_]+)\s*\(",
+                             src, flags=re.M):
+            names.add(m.group(1))
+    return names
+
+
+def test_every_declared_symbol_is_exported():
+    names = _declared_functions()
+    assert {"smcsd_round", "smcsd_resample", "smcsd_remap_pages", "smcsd_workspace_size",
+            "smcsd_status_string", "smcsd_round_args_size", "smcsd_bench_stream_read",
+            "smcsd_bench_copy"} <= names
+    lib = ctypes.CDLL(S.library_path())
+    for n in sorted(names):
+        assert hasattr(lib, n), n
+
+
+def test_struct_layout_matches():
+    assert S.smcsd_round_args_size() == ctypes.sizeof(S.RoundArgs)
+    assert S.RoundArgs.ld.offset == 16
+    assert S.RoundArgs.target_logits.offset == 48
+
+
+def test_status_strings():
+    for st in range(5):
+        assert S.smcsd_status_string(st) not in ("", "unknown status")
+    assert S.smcsd_status_string(99) == "unknown status"
+
+
+def test_workspace_size():
+    a = S.smcsd_workspace_size(64, 32, 8, 128256, S.BF16, True)
+    b = S.smcsd_workspace_size(64, 32, 8, 128256, S.BF16, False)
+    assert a > b > 0 and a % 256 == 0
+    assert S.smcsd_workspace_size(1, 0, 4, 100, S.BF16, False) == 0          # N = 0
+    assert S.smcsd_workspace_size(1, 8, 0, 100, S.BF16, False) == 0          # K = 0
+    assert S.smcsd_workspace_size(1, 8, 4, 100, 7, False) == 0               # dtype
+    assert S.smcsd_workspace_size(1, S.MAX_N + 1, 4, 100, S.BF16, False) == 0
+
+
+# A syntactically valid argument block with fake, aligned, non-null device pointers. The
+# calls below must fail validation before touching them.
+def _args(**kw):
+    a = S.RoundArgs()
+    a.R, a.N, a.K, a.V, a.ld = 2, 8, 4, 1000, 1000
+    a.dtype, a.mode, a.ess_frac = S.BF16, S.RESAMPLE_ALWAYS, 0.5
+    base = 0x10000000
+    for i, (name, _) in enumerate(S.RoundArgs._fields_[11:30]):
+        setattr(a, name, base + 0x100000 * i)
+    a.page_table_in = None
+    a.workspace = base + 0x8000000
+    a.workspace_bytes = 1 << 30
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _round(a):
+    return S.raw_library().smcsd_round(ctypes.byref(a), None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("N", 0, S.ERR_ARG), ("K", 0, S.ERR_ARG), ("V", 0, S.ERR_ARG), ("R", -1, S.ERR_ARG),
+    ("ld", 999, S.ERR_ARG), ("ld", 1004, S.ERR_ARG), ("dtype", 2, S.ERR_ARG),
+    ("mode", 3, S.ERR_ARG), ("reserved0", 1, S.ERR_ARG),
+    ("N", S.MAX_N + 1, S.ERR_UNSUPPORTED), ("K", S.MAX_K + 1, S.ERR_UNSUPPORTED),
+    ("target_logits", None, S.ERR_ARG), ("draft_logits", None, S.ERR_ARG),
+    ("draft_tokens", None, S.ERR_ARG), ("gumbel", None, S.ERR_ARG), ("uniform", None, S.ERR_ARG),
+    ("log_weights", None, S.ERR_ARG), ("ancestors", None, S.ERR_ARG), ("bonus", None, S.ERR_ARG),
+    ("target_logits", 0x10000008, S.ERR_ARG),                # not 16-byte aligned
+    ("workspace", None, S.ERR_WORKSPACE), ("workspace_bytes", 100, S.ERR_WORKSPACE),
+    ("workspace", 0x18000010, S.ERR_WORKSPACE),              # not 256-byte aligned
+])
+def test_round_validation(field, value, status):
+    assert _round(_args(**{field: value})) == status
+
+
+def test_round_validation_ess_and_pages():
+    assert _round(_args(mode=S.RESAMPLE_ESS, ess_frac=0.0)) == S.ERR_ARG
+    assert _round(_args(mode=S.RESAMPLE_ESS, ess_frac=1.5)) == S.ERR_ARG
+    pt = 0x30000000
+    assert _round(_args(page_table_in=pt, page_table_out=pt, P=4, num_pages=10)) == S.ERR_ARG
+    assert _round(_args(page_table_in=pt, page_table_out=pt + 64, P=4, num_pages=10)) == S.ERR_ARG
+    assert _round(_args(page_table_in=pt, page_table_out=None, P=4, num_pages=10)) == S.ERR_ARG
+    assert _round(_args(page_table_in=pt, page_table_out=pt + (1 << 20), P=0, num_pages=10)) == S.ERR_ARG
+    # TV exchanges 2 words per slice within one wave: at most 32 slices (V <= 524288 bf16)
+    assert _round(_args(V=524288 + 8, ld=524288 + 8)) == S.ERR_UNSUPPORTED
+    assert _round(_args(V=524288 + 8, ld=524288 + 8, tv=None, workspace_bytes=100)) == S.ERR_WORKSPACE
+    # fp32 rows need ld % 4 == 0 only
+    assert _round(_args(dtype=S.F32, ld=1004, workspace_bytes=100)) == S.ERR_WORKSPACE
+
+
+def test_empty_batch_is_a_no_op():
+    assert _round(_args(R=0)) == S.OK
+    assert _round(_args(R=0, target_logits=None)) == S.OK
+
+
+def test_resample_and_remap_validation():
+    lib = S.raw_library()
+    p = 0x10000000
+    assert lib.smcsd_resample(1, 0, p, p, p, 0, 0.5, p, p, p, p, None) == S.ERR_ARG
+    assert lib.smcsd_resample(1, 4, None, p, p, 0, 0.5, p, p, p, p, None) == S.ERR_ARG
+    assert lib.smcsd_resample(1, 4, p, p, p, 5, 0.5, p, p, p, p, None) == S.ERR_ARG
+    assert lib.smcsd_resample(1, 4, p, p, p, 1, 0.0, p, p, p, p, None) == S.ERR_ARG
+    assert lib.smcsd_resample(1, S.MAX_N + 1, p, p, p, 0, 0.5, p, p, p, p, None) == S.ERR_UNSUPPORTED
+    assert lib.smcsd_resample(0, 4, None, None, None, 0, 0.5, None, None, None, None, None) == S.OK
+    assert lib.smcsd_remap_pages(1, 4, 0, p, p, p + 4096, p, 10, None, None) == S.ERR_ARG
+    assert lib.smcsd_remap_pages(1, 4, 4, p, p, p, p, 10, None, None) == S.ERR_ARG     # alias
+    assert lib.smcsd_remap_pages(1, 4, 4, None, p, p + 4096, p, 10, None, None) == S.ERR_ARG
+    assert lib.smcsd_remap_pages(0, 4, 4, None, None, None, None, 10, None, None) == S.OK
+    assert lib.smcsd_bench_copy(p, p, 64, None) == S.ERR_ARG
+    assert lib.smcsd_bench_stream_read(p + 4, 64, p, 1, None) == S.ERR_ARG
+
+
+def test_binding_rejects_bad_tensors_before_the_library():
+    import torch
+    t = torch.zeros(1, 2, 3, 8)
+    with pytest.raises(ValueError):
+        S.smcsd_round(target_logits=t.to(torch.float16), draft_logits=None, draft_tokens=None,
+                      temperature=None, gumbel=None, uniform=None, log_weights=None,
+                      log_w_incr=None, log_norm=None, ess=None, resampled=None, ancestors=None,
+                      bonus=None, workspace=None)
+    with pytest.raises(ValueError):
+        S.smcsd_round(target_logits=t, draft_logits=torch.zeros(1, 2, 3, 8), draft_tokens=None,
+                      temperature=None, gumbel=None, uniform=None, log_weights=None,
+                      log_w_incr=None, log_norm=None, ess=None, resampled=None, ancestors=None,
+                      bonus=None, workspace=None)

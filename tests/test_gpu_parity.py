@@ -1,0 +1,236 @@
+"""GPU parity: the HIP round (through the C ABI) against the CPU oracle on the same seeded
+inputs, element by element, to the bar in tests/parity.py.
+
+Sizes: every workload scaled down so the oracle finishes in seconds while still spanning
+several slices per row and a ragged last chunk; the full-size workloads, with the oracle
+on sampled requests where a full oracle round would take minutes; and the edge cases
+(V = 1, V not a multiple of 8, N = 1, N at its maximum, K = 1, empty batch, p == q,
+every resample mode, out-of-range ids).
+"""
+import math
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import parity
+from smc_particle_resampling_amd import smcsd, synth
+
+pytestmark = pytest.mark.gpu
+W = synth.WORKLOADS
+
+
+@pytest.fixture(scope="module")
+def dev():
+    assert torch.cuda.is_available(), "GPU tests need a HIP device"
+    return torch.device("cuda:0")
+
+
+def _say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run_and_compare(w: synth.Workload, dev, seed=0, requests=None, pages=True, ragged=False,
+                    inputs=None, modify=None):
+    _say("case", w.name, "R N K V", w.R, w.N, w.K, w.V, "ld", w.row_stride, "seed", seed,
+         "requests", requests)
+    inp = inputs or synth.make_inputs(w, seed, device=dev, ragged_pages=ragged)
+    if modify:
+        modify(inp)
+    host = synth.to_host(inp, requests)
+    rc_before = inp["refcount"].cpu().numpy().copy() if pages else None
+    out = smcsd.run_round(inp, mode=w.mode, ess_frac=w.ess_frac, tv=w.tv, pages=pages)
+    torch.cuda.synchronize()
+    assert int(out["error_flags"].item()) == 0, "device error flags %d" % int(out["error_flags"].item())
+    gpu = parity.to_numpy(out, requests)
+    lw = inp["log_weights"].cpu()
+    gpu["log_weights"] = (lw if requests is None else lw[list(requests)]).numpy()
+    rc_after = inp["refcount"].cpu().numpy() if pages else None
+    ora = oracle.round(host, V=w.V, mode=w.mode, ess_frac=w.ess_frac, tv=w.tv, with_pages=pages)
+    assert ora["status"] == 0
+    stats = parity.check_round(host, ora, gpu, N=w.N, mode=w.mode, ess_frac=w.ess_frac,
+                               tv=w.tv, pages=pages, rc_before=rc_before, rc_after=rc_after)
+    _say("  ok", stats)
+    return inp, out, ora, gpu
+
+
+# ---------------------------------------------------------------- scaled-down workloads
+SMALL = [
+    W["r1-n8-k4-v32000-f32"].scaled(R=2),
+    W["r16-n16-k4-v128256-bf16"].scaled(R=3, V=40000, ctx=256),
+    W["r64-n32-k8-v128256-bf16-tv"].scaled(R=2, V=20000, ctx=256),
+    W["r8-n16-k4-v152064-bf16-zipf-ess"].scaled(R=3, V=30000, ctx=1024),
+    W["r32-n32-k8-v256000-bf16-tv-mixT"].scaled(R=4, V=36000, ctx=256),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_scaled_workloads(w, dev):
+    run_and_compare(w, dev, seed=1)
+
+
+@pytest.mark.parametrize("V,dtype,tv", [(1, "bf16", True), (7, "f32", True), (8, "bf16", False),
+                                        (9, "bf16", True), (33, "f32", False),
+                                        (5001, "bf16", True), (16385, "bf16", True),
+                                        (16384 * 3 + 8, "bf16", True), (8191, "f32", True),
+                                        (524288, "bf16", True), (524281, "bf16", True)])
+def test_ragged_and_tiny_vocabularies(V, dtype, tv, dev):
+    w = W["r16-n16-k4-v128256-bf16"].scaled(name="ragged", R=2, N=8, K=3, V=V, dtype=dtype,
+                                            tv=tv, ctx=128)
+    run_and_compare(w, dev, seed=2, ragged=True)
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (1, 4), (3, 1), (1024, 2), (40, 17)])
+def test_particle_and_position_extremes(N, K, dev):
+    w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="extreme", R=2, N=N, K=K, V=3000, ctx=64)
+    run_and_compare(w, dev, seed=3)
+
+
+@pytest.mark.parametrize("mode,frac", [("never", 0.5), ("ess", 0.5), ("ess", 1.0), ("always", 0.5)])
+def test_resample_modes(mode, frac, dev):
+    w = W["r8-n16-k4-v152064-bf16-zipf-ess"].scaled(name="modes", R=6, V=12000, ctx=256,
+                                                    mode=mode, ess_frac=frac)
+    run_and_compare(w, dev, seed=4)
+
+
+def test_identical_target_and_draft(dev):
+    w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="p-equals-q", R=3, V=20000, ctx=128)
+
+    def same(inp):
+        K = w.K
+        inp["draft"].copy_(inp["target"][:, :, :K])
+        inp["uniform"].copy_(torch.tensor([0.0, 0.5, 1.0 - 2.0 ** -24], device=dev))
+
+    inp, out, ora, gpu = run_and_compare(w, dev, seed=5, modify=same)
+    assert np.all(gpu["log_w_incr"] == 0.0)
+    assert np.all(gpu["tv"] == 0.0)
+    assert np.all(gpu["ess"] == w.N)
+    assert np.all(gpu["ancestors"] == np.arange(w.N))
+
+
+def test_empty_batch(dev):
+    w = W["r16-n16-k4-v128256-bf16"].scaled(name="empty", R=0, V=1000, ctx=64)
+    inp = synth.make_inputs(w, 0, device=dev, pages=False)
+    out = smcsd.run_round(inp, pages=False)
+    torch.cuda.synchronize()
+    assert out["ancestors"].numel() == 0
+
+
+# ---------------------------------------------------------------- full-size workloads
+@pytest.mark.parametrize("name", ["r1-n8-k4-v32000-f32", "r16-n16-k4-v128256-bf16",
+                                  "r8-n16-k4-v152064-bf16-zipf-ess"])
+def test_full_size_workloads(name, dev):
+    run_and_compare(W[name], dev, seed=0)
+
+
+@pytest.mark.parametrize("name,requests", [("r64-n32-k8-v128256-bf16-tv", [0, 37, 63]),
+                                           ("r32-n32-k8-v256000-bf16-tv-mixT", [0, 13, 31])])
+def test_full_size_sampled_requests(name, requests, dev):
+    _, _, ora, gpu = run_and_compare(W[name], dev, seed=0, requests=requests)
+    assert gpu["tv"].min() >= 0 and gpu["tv"].max() <= 1
+
+
+# ---------------------------------------------------------------- determinism
+def test_bitwise_deterministic(dev):
+    w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="determinism", R=8, V=40000, ctx=256)
+    inp = synth.make_inputs(w, 6, device=dev)
+    lw0 = inp["log_weights"].clone()
+    rc0 = inp["refcount"].clone()
+    outs = []
+    for _ in range(2):
+        inp["log_weights"].copy_(lw0)
+        inp["refcount"].copy_(rc0)
+        o = smcsd.run_round(inp, tv=True)
+        torch.cuda.synchronize()
+        outs.append({k: v.clone() for k, v in o.items() if k != "workspace" and v is not None})
+        outs[-1]["log_weights"] = inp["log_weights"].clone()
+        outs[-1]["refcount"] = inp["refcount"].clone()
+    for k in outs[0]:
+        assert torch.equal(outs[0][k], outs[1][k]), k
+
+
+# ---------------------------------------------------------------- multi-round state
+def test_three_rounds_with_carried_state(dev):
+    w = W["r16-n16-k4-v128256-bf16"].scaled(name="three-rounds", R=4, V=9000, ctx=256,
+                                            tv=True)
+    inp = synth.make_inputs(w, 7, device=dev)
+    for t in range(3):
+        _say("round", t)
+        inp2 = synth.make_inputs(w, 100 + t, device=dev, pages=False)   # fresh logits
+        for k in ("target", "draft", "tokens", "gumbel", "uniform"):
+            inp[k] = inp2[k]
+        _, out, _, _ = run_and_compare(w, dev, inputs=inp)
+        # pointer exchange between rounds: the output table becomes the next input
+        inp["page_table"], out["page_table_out"] = out["page_table_out"], inp["page_table"]
+
+
+# ---------------------------------------------------------------- standalone entry points
+@pytest.mark.parametrize("N,mode", [(1, "always"), (7, "always"), (32, "ess"), (1000, "always"),
+                                    (64, "never")])
+def test_smcsd_resample(N, mode, dev):
+    R = 5
+    g = torch.Generator().manual_seed(N)
+    lw = (torch.randn(R, N, generator=g) * 2).float()
+    prev = torch.log_softmax(torch.randn(R, N, generator=g).double(), 1).float()
+    u = torch.rand(R, generator=g).float()
+    d = dict(log_w_incr=lw.to(dev), log_weights=prev.to(dev), uniform=u.to(dev),
+             log_norm=torch.empty(R, device=dev), ess=torch.empty(R, device=dev),
+             resampled=torch.empty(R, dtype=torch.int32, device=dev),
+             ancestors=torch.empty(R, N, dtype=torch.int32, device=dev))
+    smcsd.smcsd_resample(**d, mode=mode, ess_frac=0.5)
+    torch.cuda.synchronize()
+    for r in range(R):
+        ref = oracle.resample_request(lw[r].double().numpy(), prev[r].double().numpy(),
+                                      float(u[r]), mode, 0.5)
+        assert int(d["resampled"][r]) == ref["resampled"]
+        assert float(d["log_norm"][r]) == pytest.approx(ref["log_norm"], rel=1e-6, abs=1e-6)
+        assert float(d["ess"][r]) == pytest.approx(ref["ess"], rel=1e-6)
+        safe = ref["anc_gap"] >= 1e-9
+        assert np.array_equal(d["ancestors"][r].cpu().numpy()[safe], ref["ancestors"][safe])
+        np.testing.assert_allclose(d["log_weights"][r].cpu().numpy(), ref["log_weights"],
+                                   rtol=1e-6, atol=1e-6)
+
+
+def test_smcsd_remap_pages_and_error_flags(dev):
+    R, N, P = 3, 16, 40
+    pt, rc, npg = synth.make_page_table(R, N, P, seed=8, ragged=True)
+    g = torch.Generator().manual_seed(8)
+    anc = torch.sort(torch.randint(0, N, (R, N), generator=g), 1).values.int()
+    pt_out = torch.empty_like(pt, device=dev)
+    rc_d = rc.to(dev)
+    flags = torch.zeros(1, dtype=torch.int32, device=dev)
+    smcsd.smcsd_remap_pages(ancestors=anc.to(dev), page_table_in=pt.to(dev),
+                            page_table_out=pt_out, refcount=rc_d, error_flags=flags)
+    torch.cuda.synchronize()
+    assert int(flags.item()) == 0
+    rc_ref = rc.numpy().copy()
+    for r in range(R):
+        out_r, rc_ref, st = oracle.remap_request(anc[r].numpy(), pt[r].numpy(), rc_ref)
+        assert st == 0
+        assert np.array_equal(pt_out[r].cpu().numpy(), out_r)
+    assert np.array_equal(rc_d.cpu().numpy(), rc_ref)
+    # an out-of-range ancestor and page id are flagged and skipped, never followed
+    bad_anc = anc.clone()
+    bad_anc[1, 3] = N + 5
+    bad_pt = pt.clone()
+    bad_pt[2, 0, 0] = npg + 100
+    flags.zero_()
+    smcsd.smcsd_remap_pages(ancestors=bad_anc.to(dev), page_table_in=bad_pt.to(dev),
+                            page_table_out=pt_out, refcount=rc.to(dev).clone(), error_flags=flags)
+    torch.cuda.synchronize()
+    f = int(flags.item())
+    assert f & smcsd.DEVERR_ANCESTOR
+    assert torch.all(pt_out[1, 3] == -1)
+
+
+def test_out_of_range_token_is_flagged(dev):
+    w = W["r16-n16-k4-v128256-bf16"].scaled(name="bad-token", R=2, V=3000, ctx=64)
+    inp = synth.make_inputs(w, 9, device=dev)
+    inp["tokens"][1, 2, 0] = w.V + 7
+    out = smcsd.run_round(inp)
+    torch.cuda.synchronize()
+    assert int(out["error_flags"].item()) & smcsd.DEVERR_TOKEN
+    assert torch.isfinite(out["log_w_incr"]).all()
