@@ -31,7 +31,8 @@ bool make_plan(int32_t R, int32_t N, int32_t K, int32_t V, int64_t ld, int32_t d
     q.tv = tv;
     q.epc = dtype == SMCSD_F32 ? 4 : 8;
     q.chunks = (int32_t)(((int64_t)V + q.epc - 1) / q.epc);
-    const int32_t s0 = (q.chunks + kMaxSliceChunks - 1) / kMaxSliceChunks;
+    const int32_t per_slice = kThreads * (tv ? kTvCPL : kStreamCPL);
+    const int32_t s0 = (q.chunks + per_slice - 1) / per_slice;
     q.cps = (q.chunks + s0 - 1) / s0;
     q.S = (q.chunks + q.cps - 1) / q.cps;   // no empty slice
     q.pairs = (int64_t)R * N * K;

@@ -8,26 +8,32 @@
 // signal of the METASD page, section 2). For every particle it also reduces the bonus row
 // with its precomputed Gumbel noise to the Gumbel-max token (STAND page, method item 2).
 //
-// Work decomposition. A row is cut into 16-byte chunks and the chunks into S slices of at
-// most 256 lanes x 8 chunks. One 256-thread workgroup handles one slice of one row pair
-// (target row k, draft row k), or one slice of one bonus row plus its noise row. A slice
-// is read once with 16-byte non-temporal loads and kept in registers (64 VGPRs a lane for
-// a bf16 pair). Then:
-//   phase 1: slice max of z and sum of exp2((z - max) * log2e/T) for p and q -> partials;
-//   phase 2 (TV only): the S workgroups of a row pair swap partials through the workspace,
-//            all combine them in the same fixed order into the row's normalisers, and each
-//            sums |p - q| over its own slice from registers. No logit is read twice.
-// The final combination over slices (normalisers, weights, argmax) happens in the
-// finalize kernel, in fixed order, so every result is deterministic.
+// Work decomposition. A row is cut into 16-byte chunks and the chunks into S slices. One
+// 256-thread workgroup handles one slice of one row pair (target row k, draft row k) or one
+// slice of one bonus row plus its noise row. Each lane loads its CPL chunks of both rows
+// with 16-byte non-temporal loads. Chunks outside the slice and elements >= V are loaded as
+// -inf, which adds nothing to any max, sum, TV or argmax, so the arithmetic has no
+// per-element branch.
+//   phase 1: slice max m of z, then e = exp2((z - m) * log2e/T) and its sum, for p and q;
+//   phase 2 (TV only): the S workgroups of the row pair swap their (m, sum) partials and
+//            combine them in one fixed order into the row's maxima M and sums S. With
+//            f = exp2((m - M) * log2e/T) the slice's |p - q| terms are
+//            (f_p / S_p) |e_p - rho e_q|, rho = (f_q S_p) / (f_p S_q). The slice keeps
+//            its e values in fp32 registers from phase 1, so phase 2 costs one fma and one
+//            add per element and no exponential. rho is exactly 1 when the two rows are
+//            equal, and then TV is exactly 0.
+// The finalize kernel combines slices (normalisers, weights, argmax) in fixed order, so every
+// result is deterministic.
 //
 // Launch shapes. Without TV, every (row, slice) is an independent workgroup of an ordinary
-// grid. With TV, the S workgroups of a row pair must be resident at the same time to swap
-// partials, so the TV pass runs as a persistent cooperative grid
-// (hipLaunchCooperativeKernel, which guarantees co-residency): C clusters of S consecutive
-// workgroups, each cluster walking the row pairs c, c+C, c+2C, ... in lockstep, then its
-// share of the bonus rows. A wall-clock limit still bounds every wait; a workgroup that
-// times out raises SMCSD_DEVERR_EXCHANGE and an abort flag, every later wait returns at
-// once, and the kernel always drains.
+// grid (8 chunks a lane). With TV, the S workgroups of a row pair must be resident together
+// to swap partials, so the pass runs as a persistent cooperative grid
+// (hipLaunchCooperativeKernel guarantees co-residency). It has C clusters of S consecutive
+// workgroups, and each cluster walks the row pairs c, c+C, c+2C, ... in lockstep, then its
+// share of the bonus rows (4 chunks a lane, so the fp32 e values fit in registers). A
+// wall-clock limit bounds every wait. A workgroup that times out raises
+// SMCSD_DEVERR_EXCHANGE and an abort flag, every later wait returns at once, and the kernel
+// always drains.
 #include <algorithm>
 #include <atomic>
 
@@ -40,13 +46,177 @@ constexpr float kLog2e = 1.44269504088896340736f;
 // 4e8 ticks of the 100 MHz constant clock: 4 s, ~10^4 times the longest expected wait.
 constexpr uint64_t kExchangeTimeoutTicks = 400000000ull;
 
+template <int DT>
+struct Elem {
+    static constexpr int EPC = DT == SMCSD_F32 ? 4 : 8;              // elements per chunk
+    static constexpr size_t ESZ = DT == SMCSD_F32 ? 4 : 2;           // bytes per element
+    static constexpr uint32_t kNegInf = DT == SMCSD_F32 ? 0xFF800000u : 0xFF80FF80u;
+};
+
 __device__ __forceinline__ u32x4 load_chunk(const char* row, int64_t chunk) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + chunk);
 }
 
+// A chunk whose elements >= nv are replaced by -inf (nv < EPC: the row's tail chunk).
+template <int DT>
+__device__ __forceinline__ u32x4 mask_tail(u32x4 c, int nv) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+        if constexpr (DT == SMCSD_F32) {
+            if (w >= nv) c[w] = 0xFF800000u;
+        } else {
+            if (2 * w >= nv) c[w] = 0xFF80FF80u;
+            else if (2 * w + 1 >= nv) c[w] = (c[w] & 0x0000FFFFu) | 0xFF800000u;
+        }
+    }
+    return c;
+}
+
+// Issue the loads of the CPL chunks this lane owns in slice [c0, c1) of a row. Chunks
+// outside the slice stay -inf. The loads may still be in flight on return.
+template <int DT, int CPL>
+__device__ __forceinline__ void issue_slice(u32x4 (&R)[CPL], const char* row, int c0, int c1) {
+    const int tid = threadIdx.x;
+    const uint32_t ni = Elem<DT>::kNegInf;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) R[j] = u32x4{ni, ni, ni, ni};
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int ch = c0 + j * kThreads + tid;
+        if (ch < c1) R[j] = load_chunk(row, ch);   // masked load: other lanes keep -inf
+    }
+}
+
+// Elements >= V (only in the row's last chunk) become -inf. Waits for that chunk's load.
+template <int DT, int CPL>
+__device__ __forceinline__ void mask_slice_tail(u32x4 (&R)[CPL], int c0, int c1, int V) {
+    constexpr int EPC = Elem<DT>::EPC;
+    const int tid = threadIdx.x;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+        const int ch = c0 + j * kThreads + tid;
+        const int nv = V - ch * EPC;
+        if (ch < c1 && nv < EPC) R[j] = mask_tail<DT>(R[j], nv);
+    }
+}
+
+template <int DT, int CPL>
+__device__ __forceinline__ void load_slice(u32x4 (&R)[CPL], const char* row, int c0, int c1,
+                                           int V) {
+    issue_slice<DT, CPL>(R, row, c0, c1);
+    mask_slice_tail<DT, CPL>(R, c0, c1, V);
+}
+
+typedef short i16x2 __attribute__((ext_vector_type(2)));
+
+// Slice max. For bf16 it works on the raw bit patterns with packed 16-bit integer max and
+// min: read as int16, non-negative bf16 values order like their floats and negative ones
+// in reverse. So the float max is the int16 max when that is >= 0 (some element is
+// non-negative), and otherwise the int16 min (the negative value of least magnitude). -inf
+// (0xFF80) is the int16 -128, above every finite negative, so masked elements never win.
+template <int DT, int CPL>
+__device__ __forceinline__ float slice_max(const u32x4 (&R)[CPL]) {
+    if constexpr (DT == SMCSD_F32) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+            for (int w = 0; w < 4; w += 2)
+                m = fmaxf(m, fmaxf(__uint_as_float(R[j][w]), __uint_as_float(R[j][w + 1])));
+        return m;
+    } else {
+        i16x2 mx = {(short)-32768, (short)-32768}, mn = {(short)32767, (short)32767};
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const i16x2 x = __builtin_bit_cast(i16x2, R[j][w]);
+                mx = __builtin_elementwise_max(mx, x);
+                mn = __builtin_elementwise_min(mn, x);
+            }
+        const short hi = mx[0] > mx[1] ? mx[0] : mx[1];
+        const short lo = mn[0] < mn[1] ? mn[0] : mn[1];
+        const uint32_t bits = (uint32_t)(uint16_t)(hi >= 0 ? hi : lo);
+        return __uint_as_float(bits << 16);
+    }
+}
+
+// sum over the slice of exp2(z * c - m * c)
+template <int DT, int CPL>
+__device__ __forceinline__ float slice_sumexp(const u32x4 (&R)[CPL], float c, float nmc) {
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+#pragma unroll
+        for (int e = 0; e < Elem<DT>::EPC; e += 2) {
+            s0 += __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(R[j], e), c, nmc));
+            s1 += __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(R[j], e + 1), c, nmc));
+        }
+    }
+    return s0 + s1;
+}
+
+// Same sum, keeping every term: E[j * EPC + e] = exp2(z * c - m * c).
+template <int DT, int CPL>
+__device__ __forceinline__ float slice_exp(const u32x4 (&R)[CPL], float c, float nmc,
+                                           float (&E)[CPL * Elem<DT>::EPC]) {
+    constexpr int EPC = Elem<DT>::EPC;
+    float s0 = 0.0f, s1 = 0.0f;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+#pragma unroll
+        for (int e = 0; e < EPC; e += 2) {
+            E[j * EPC + e] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(R[j], e), c, nmc));
+            E[j * EPC + e + 1] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(R[j], e + 1), c, nmc));
+            s0 += E[j * EPC + e];
+            s1 += E[j * EPC + e + 1];
+        }
+    }
+    return s0 + s1;
+}
+
+struct PairLoc {
+    int64_t r;
+    const char* zp;
+    const char* zq;
+    int c0, c1;
+};
+
+template <int DT>
+__device__ __forceinline__ PairLoc pair_location(const LogitsArgs& a, int64_t u, int s) {
+    constexpr size_t ESZ = Elem<DT>::ESZ;
+    const int64_t nk = (int64_t)a.N * a.K;
+    const int64_t r = u / nk;
+    const int64_t ik = u - r * nk;
+    const int64_t i = ik / a.K;
+    const int64_t k = ik - i * a.K;
+    PairLoc L;
+    L.r = r;
+    L.zp = static_cast<const char*>(a.target) + (size_t)(((r * a.N + i) * (a.K + 1) + k) * a.ld) * ESZ;
+    L.zq = static_cast<const char*>(a.draft) + (size_t)(((r * a.N + i) * a.K + k) * a.ld) * ESZ;
+    L.c0 = s * a.cps;
+    L.c1 = min(L.c0 + a.cps, a.chunks);
+    return L;
+}
+
+// TV off: slice partials only.
+template <int DT>
+__device__ void pair_slice_stream(const LogitsArgs& a, int64_t u, int s, float* red) {
+    const PairLoc L = pair_location<DT>(a, u, s);
+    const float c = kLog2e / a.temperature[L.r];   // exp(z/T) = exp2(z * c)
+    u32x4 P[kStreamCPL], Q[kStreamCPL];
+    load_slice<DT, kStreamCPL>(P, L.zp, L.c0, L.c1, a.V);
+    load_slice<DT, kStreamCPL>(Q, L.zq, L.c0, L.c1, a.V);
+    const float mp = block_max(slice_max<DT, kStreamCPL>(P), red);
+    const float mq = block_max(slice_max<DT, kStreamCPL>(Q), red);
+    const float sp = block_sum(slice_sumexp<DT, kStreamCPL>(P, c, -mp * c), red);
+    const float sq = block_sum(slice_sumexp<DT, kStreamCPL>(Q, c, -mq * c), red);
+    if (threadIdx.x == 0) a.pp[u * a.S + s] = PairPart{mp, sp, mq, sq};
+}
+
 // Slice exchange of the TV pass. Every (row pair, slice) partial is two 64-bit words, (max,
 // sum) of the target row and of the draft row. Before the launch, every word holds kEmpty,
-// a bit pattern no finite partial can take. A slice publishes its two words with relaxed
+// a bit pattern no partial can take. A slice publishes its two words with relaxed
 // agent-scope atomic stores. Wave 0 of every slice polls all 2S words of its row pair with
 // relaxed agent-scope atomic loads until none is kEmpty. Each value is read from the very
 // location it was stored to, so coherence of that location suffices: no release/acquire
@@ -56,17 +226,22 @@ constexpr uint64_t kEmpty = ~0ull;
 __device__ __forceinline__ uint64_t pack2(float lo, float hi) {
     return (uint64_t)__float_as_uint(lo) | ((uint64_t)__float_as_uint(hi) << 32);
 }
+__device__ __forceinline__ float word_lo(uint64_t w) { return __uint_as_float((uint32_t)w); }
+__device__ __forceinline__ float word_hi(uint64_t w) { return __uint_as_float((uint32_t)(w >> 32)); }
 
-// Wave 0 only. Copies the 2S words of row pair u into lds[0..2S) once all are published.
+// Wave 0 only. Copies the nwords (<= 128) words of a row pair into lds once all are published.
 __device__ void wait_for_slices(const uint64_t* words, int nwords, Ctrl* ctrl,
                                 int32_t* error_flags, uint64_t* lds) {
     const int lane = threadIdx.x & 63;
     const uint64_t t0 = wall_clock64();
-    uint64_t v = 0;
+    uint64_t v0 = 0, v1 = 0;
     while (true) {
-        v = lane < nwords ? __hip_atomic_load(words + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                          : 0ull;
-        if (!__any(v == kEmpty)) break;
+        v0 = lane < nwords ? __hip_atomic_load(words + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                           : 0ull;
+        v1 = lane + 64 < nwords
+                 ? __hip_atomic_load(words + lane + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                 : 0ull;
+        if (!__any(v0 == kEmpty || v1 == kEmpty)) break;
         if (__hip_atomic_load(&ctrl->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
         if (wall_clock64() - t0 > kExchangeTimeoutTicks) {
             if (lane == 0) {
@@ -77,140 +252,72 @@ __device__ void wait_for_slices(const uint64_t* words, int nwords, Ctrl* ctrl,
         }
         __builtin_amdgcn_s_sleep(1);
     }
-    if (lane < nwords) lds[lane] = v;
+    if (lane < nwords) lds[lane] = v0;
+    if (lane + 64 < nwords) lds[lane + 64] = v1;
 }
 
-template <int DT, bool TV>
-__device__ void pair_slice(const LogitsArgs& a, int64_t u, int s, float* red, float* bcast,
-                           uint64_t* xch) {
-    constexpr int EPC = DT == SMCSD_F32 ? 4 : 8;
-    constexpr size_t ESZ = DT == SMCSD_F32 ? 4 : 2;
+// TV on: partials, exchange, and this slice's share of sum |p - q|.
+template <int DT>
+__device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, float* red, float* bcast,
+                              uint64_t* xch) {
+    constexpr int NE = kTvCPL * Elem<DT>::EPC;
     const int tid = threadIdx.x;
-    const int64_t nk = (int64_t)a.N * a.K;
-    const int64_t r = u / nk;
-    const int64_t ik = u - r * nk;
-    const int64_t i = ik / a.K;
-    const int64_t k = ik - i * a.K;
-    const char* zp = static_cast<const char*>(a.target) +
-                     (size_t)(((r * a.N + i) * (a.K + 1) + k) * a.ld) * ESZ;
-    const char* zq = static_cast<const char*>(a.draft) +
-                     (size_t)(((r * a.N + i) * a.K + k) * a.ld) * ESZ;
-    const float c = kLog2e / a.temperature[r];   // exp(z/T) = exp2(z * c)
-    const int c0 = s * a.cps;
-    const int c1 = min(c0 + a.cps, a.chunks);
-
-    u32x4 P[kChunksPerLane], Q[kChunksPerLane];
-#pragma unroll
-    for (int j = 0; j < kChunksPerLane; ++j) {
-        const int ch = c0 + j * kThreads + tid;
-        if (ch < c1) {
-            P[j] = load_chunk(zp, ch);
-            Q[j] = load_chunk(zq, ch);
-        } else {
-            P[j] = u32x4{0u, 0u, 0u, 0u};
-            Q[j] = u32x4{0u, 0u, 0u, 0u};
-        }
-    }
-
-    // phase 1a: slice maxima (elements >= V in the row's last chunk are skipped)
-    float mp = -INFINITY, mq = -INFINITY;
-#pragma unroll
-    for (int j = 0; j < kChunksPerLane; ++j) {
-        const int ch = c0 + j * kThreads + tid;
-        if (ch < c1) {
-            const int nv = min(EPC, a.V - ch * EPC);
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                if (e < nv) {
-                    mp = fmaxf(mp, chunk_elem<DT>(P[j], e));
-                    mq = fmaxf(mq, chunk_elem<DT>(Q[j], e));
-                }
-            }
-        }
-    }
-    mp = block_max(mp, red);
-    mq = block_max(mq, red);
-
-    // phase 1b: sums of exp2((z - max) * c)
-    const float nmp = -mp * c, nmq = -mq * c;
-    float sp = 0.0f, sq = 0.0f;
-#pragma unroll
-    for (int j = 0; j < kChunksPerLane; ++j) {
-        const int ch = c0 + j * kThreads + tid;
-        if (ch < c1) {
-            const int nv = min(EPC, a.V - ch * EPC);
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                if (e < nv) {
-                    sp += __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(P[j], e), c, nmp));
-                    sq += __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(Q[j], e), c, nmq));
-                }
-            }
-        }
+    const PairLoc L = pair_location<DT>(a, u, s);
+    const float c = kLog2e / a.temperature[L.r];
+    float Ep[NE], Eq[NE];
+    float mp, mq, sp, sq;
+    {
+        u32x4 P[kTvCPL], Q[kTvCPL];
+        load_slice<DT, kTvCPL>(P, L.zp, L.c0, L.c1, a.V);
+        load_slice<DT, kTvCPL>(Q, L.zq, L.c0, L.c1, a.V);
+        mp = block_max(slice_max<DT, kTvCPL>(P), red);
+        mq = block_max(slice_max<DT, kTvCPL>(Q), red);
+        sp = slice_exp<DT, kTvCPL>(P, c, -mp * c, Ep);
+        sq = slice_exp<DT, kTvCPL>(Q, c, -mq * c, Eq);
     }
     sp = block_sum(sp, red);
     sq = block_sum(sq, red);
-    if constexpr (!TV) {
-        if (tid == 0) a.pp[u * a.S + s] = PairPart{mp, sp, mq, sq};
-    } else {
-        uint64_t* words = reinterpret_cast<uint64_t*>(a.pp + u * a.S);
-        if (tid == 0) {
-            __hip_atomic_store(words + 2 * s, pack2(mp, sp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            __hip_atomic_store(words + 2 * s + 1, pack2(mq, sq), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        }
-        if (tid < 64) wait_for_slices(words, 2 * a.S, a.ctrl, a.error_flags, xch);
-        __syncthreads();
-        if (tid == 0) {
-            // the row's normalisers from all slices, in slice order
-            float Mp = -INFINITY, Mq = -INFINITY;
-            for (int t = 0; t < a.S; ++t) {
-                Mp = fmaxf(Mp, __uint_as_float((uint32_t)xch[2 * t]));
-                Mq = fmaxf(Mq, __uint_as_float((uint32_t)xch[2 * t + 1]));
-            }
-            float Sp = 0.0f, Sq = 0.0f;
-            for (int t = 0; t < a.S; ++t) {
-                const float mpt = __uint_as_float((uint32_t)xch[2 * t]);
-                const float spt = __uint_as_float((uint32_t)(xch[2 * t] >> 32));
-                const float mqt = __uint_as_float((uint32_t)xch[2 * t + 1]);
-                const float sqt = __uint_as_float((uint32_t)(xch[2 * t + 1] >> 32));
-                Sp += spt * __builtin_amdgcn_exp2f((mpt - Mp) * c);
-                Sq += sqt * __builtin_amdgcn_exp2f((mqt - Mq) * c);
-            }
-            bcast[0] = Mp;
-            bcast[1] = Mq;
-            bcast[2] = Sp / Sq;
-            bcast[3] = 1.0f / Sp;
-        }
-        __syncthreads();
-        const float nMp = -bcast[0] * c, nMq = -bcast[1] * c, ratio = bcast[2];
-        // phase 2, from registers: with e = exp2(z c - M c), p = e_p / Sp and q = e_q / Sq, so
-        // sum |p - q| = (1/Sp) sum |e_p - (Sp/Sq) e_q|: one fma per element, and exactly 0
-        // when the draft row equals the target row (the ratio is then exactly 1).
-        float acc = 0.0f;
-#pragma unroll
-        for (int j = 0; j < kChunksPerLane; ++j) {
-            const int ch = c0 + j * kThreads + tid;
-            if (ch < c1) {
-                const int nv = min(EPC, a.V - ch * EPC);
-#pragma unroll
-                for (int e = 0; e < EPC; ++e) {
-                    if (e < nv) {
-                        const float ep = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(P[j], e), c, nMp));
-                        const float eq = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(Q[j], e), c, nMq));
-                        acc += fabsf(fmaf(-ratio, eq, ep));
-                    }
-                }
-            }
-        }
-        acc = block_sum(acc, red);
-        if (tid == 0) a.tvp[u * a.S + s] = acc * bcast[3];
+
+    uint64_t* words = reinterpret_cast<uint64_t*>(a.pp + u * a.S);
+    if (tid == 0) {
+        __hip_atomic_store(words + 2 * s, pack2(mp, sp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        __hip_atomic_store(words + 2 * s + 1, pack2(mq, sq), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
+    if (tid < 64) wait_for_slices(words, 2 * a.S, a.ctrl, a.error_flags, xch);
+    __syncthreads();
+    if (tid == 0) {
+        // the row's maxima and sums from all slices, in slice order
+        float Mp = -INFINITY, Mq = -INFINITY;
+        for (int t = 0; t < a.S; ++t) {
+            Mp = fmaxf(Mp, word_lo(xch[2 * t]));
+            Mq = fmaxf(Mq, word_lo(xch[2 * t + 1]));
+        }
+        float Sp = 0.0f, Sq = 0.0f;
+        for (int t = 0; t < a.S; ++t) {
+            Sp += word_hi(xch[2 * t]) * __builtin_amdgcn_exp2f((word_lo(xch[2 * t]) - Mp) * c);
+            Sq += word_hi(xch[2 * t + 1]) * __builtin_amdgcn_exp2f((word_lo(xch[2 * t + 1]) - Mq) * c);
+        }
+        const float fp = __builtin_amdgcn_exp2f((mp - Mp) * c);
+        const float fq = __builtin_amdgcn_exp2f((mq - Mq) * c);
+        bcast[0] = (fq * Sp) / (fp * Sq);   // rho
+        bcast[1] = fp / Sp;                 // scale of this slice's sum
+    }
+    __syncthreads();
+    const float rho = bcast[0];
+    float acc0 = 0.0f, acc1 = 0.0f;
+#pragma unroll
+    for (int e = 0; e < NE; e += 2) {
+        acc0 += fabsf(fmaf(-rho, Eq[e], Ep[e]));
+        acc1 += fabsf(fmaf(-rho, Eq[e + 1], Ep[e + 1]));
+    }
+    const float acc = block_sum(acc0 + acc1, red);
+    if (tid == 0) a.tvp[u * a.S + s] = acc * bcast[1];
 }
 
-template <int DT>
+template <int DT, int CPL>
 __device__ void bonus_slice(const LogitsArgs& a, int64_t b, int s, float* red, int32_t* redi) {
-    constexpr int EPC = DT == SMCSD_F32 ? 4 : 8;
-    constexpr size_t ESZ = DT == SMCSD_F32 ? 4 : 2;
+    constexpr int EPC = Elem<DT>::EPC;
+    constexpr size_t ESZ = Elem<DT>::ESZ;
     const int tid = threadIdx.x;
     const int64_t r = b / a.N;
     const char* zrow = static_cast<const char*>(a.target) +
@@ -222,24 +329,37 @@ __device__ void bonus_slice(const LogitsArgs& a, int64_t b, int s, float* red, i
 
     float best = -INFINITY;
     int32_t besti = INT32_MAX;
-#pragma unroll 2
-    for (int j = 0; j < kChunksPerLane; ++j) {
-        const int ch = c0 + j * kThreads + tid;
-        if (ch < c1) {
-            const u32x4 z = load_chunk(zrow, ch);
-            u32x4 g[EPC / 4];
+    // two chunks at a time keeps the noise (twice the bytes of the logits) from piling up
+    // in registers
+#pragma unroll 1
+    for (int j0 = 0; j0 < CPL; j0 += 2) {
+        u32x4 Z[2];
+        u32x4 g[2][EPC / 4];
 #pragma unroll
-            for (int h = 0; h < EPC / 4; ++h) g[h] = load_chunk(grow, (int64_t)ch * (EPC / 4) + h);
-            const int nv = min(EPC, a.V - ch * EPC);
+        for (int jj = 0; jj < 2; ++jj) {
+            const int ch = c0 + (j0 + jj) * kThreads + tid;
+            const uint32_t ni = Elem<DT>::kNegInf;
+            Z[jj] = u32x4{ni, ni, ni, ni};
+#pragma unroll
+            for (int h = 0; h < EPC / 4; ++h) g[jj][h] = u32x4{0u, 0u, 0u, 0u};
+            if (ch < c1) {
+                Z[jj] = load_chunk(zrow, ch);
+#pragma unroll
+                for (int h = 0; h < EPC / 4; ++h) g[jj][h] = load_chunk(grow, (int64_t)ch * (EPC / 4) + h);
+                const int nv = a.V - ch * EPC;
+                if (nv < EPC) Z[jj] = mask_tail<DT>(Z[jj], nv);
+            }
+        }
+#pragma unroll
+        for (int jj = 0; jj < 2; ++jj) {
+            const int ch = c0 + (j0 + jj) * kThreads + tid;
 #pragma unroll
             for (int e = 0; e < EPC; ++e) {
-                if (e < nv) {
-                    const float key = fmaf(chunk_elem<DT>(z, e), invT, __uint_as_float(g[e >> 2][e & 3]));
-                    if (key > best) {   // a lane visits its indices in increasing order
-                        best = key;
-                        besti = ch * EPC + e;
-                    }
-                }
+                // key = z/T + G, one rounding; -inf for positions outside the slice or >= V
+                const float key = fmaf(chunk_elem<DT>(Z[jj], e), invT, __uint_as_float(g[jj][e >> 2][e & 3]));
+                const bool win = key > best;   // a lane visits its indices in increasing order
+                best = win ? key : best;
+                besti = win ? ch * EPC + e : besti;
             }
         }
     }
@@ -267,6 +387,7 @@ __device__ void bonus_slice(const LogitsArgs& a, int64_t b, int s, float* red, i
             }
         a.bp[b * a.S + s] = BonusPart{best, besti};
     }
+    __syncthreads();   // red / redi are reused by the caller
 }
 
 // TV off: one workgroup per (row, slice).
@@ -274,13 +395,12 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void k_logits_stream(LogitsArgs a) {
     __shared__ float red[kWaves];
     __shared__ int32_t redi[kWaves];
-    __shared__ float bcast[4];
     const int64_t t = blockIdx.x;
     if (t < a.pair_wgs) {
-        pair_slice<DT, false>(a, t / a.S, (int)(t % a.S), red, bcast, nullptr);
+        pair_slice_stream<DT>(a, t / a.S, (int)(t % a.S), red);
     } else if (t < a.total_wgs) {
         const int64_t tb = t - a.pair_wgs;
-        bonus_slice<DT>(a, tb / a.S, (int)(tb % a.S), red, redi);
+        bonus_slice<DT, kStreamCPL>(a, tb / a.S, (int)(tb % a.S), red, redi);
     }
 }
 
@@ -289,16 +409,16 @@ template <int DT>
 __global__ __launch_bounds__(kThreads, 4) void k_logits_tv(LogitsArgs a) {
     __shared__ float red[kWaves];
     __shared__ int32_t redi[kWaves];
-    __shared__ float bcast[4];
+    __shared__ float bcast[2];
     __shared__ uint64_t xch[2 * kMaxTvSlices];
     const int s = (int)(blockIdx.x % (unsigned)a.S);
     const int64_t cluster = blockIdx.x / (unsigned)a.S;
     const int64_t clusters = gridDim.x / (unsigned)a.S;
     const int64_t items = a.pairs + (a.total_wgs - a.pair_wgs) / a.S;
     for (int64_t it = cluster; it < items; it += clusters) {
-        if (it < a.pairs) pair_slice<DT, true>(a, it, s, red, bcast, xch);
-        else bonus_slice<DT>(a, it - a.pairs, s, red, redi);
-        __syncthreads();   // red / bcast are reused by the next item
+        if (it < a.pairs) pair_slice_tv<DT>(a, it, s, red, bcast, xch);
+        else bonus_slice<DT, kTvCPL>(a, it - a.pairs, s, red, redi);
+        __syncthreads();   // bcast / xch are reused by the next item
     }
 }
 

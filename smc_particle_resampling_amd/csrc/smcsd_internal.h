@@ -13,9 +13,9 @@ namespace smcsd {
 
 constexpr int kThreads = 256;        // workgroup size of every kernel (4 wave64)
 constexpr int kWaves = kThreads / 64;
-constexpr int kChunksPerLane = 8;    // 16-byte chunks each lane holds per row of a slice
-constexpr int kMaxSliceChunks = kThreads * kChunksPerLane;
-constexpr int kMaxTvSlices = 32;     // TV exchange: wave 0 reads the 2*S partial words
+constexpr int kStreamCPL = 8;        // 16-byte chunks a lane holds per row of a slice, TV off
+constexpr int kTvCPL = 4;            // ... TV on (its fp32 exponentials stay in registers)
+constexpr int kMaxTvSlices = 64;     // TV exchange: wave 0 reads the 2*S partial words
 
 // How one logits row is cut into 16-byte chunks and the chunks into slices, one workgroup
 // per slice. Every slice is non-empty and every chunk has at least one element < V.
