@@ -50,6 +50,8 @@ bool make_plan(int32_t R, int32_t N, int32_t K, int32_t V, int64_t ld, int32_t d
     off = align256(off + (tv ? sizeof(float) * (size_t)q.pair_wgs : 0));
     q.off_bp = off;
     off = align256(off + sizeof(BonusPart) * (size_t)(q.bonus_rows * q.S));
+    q.off_terms = off;
+    off = align256(off + sizeof(double) * (size_t)q.pairs);
     q.bytes = off;
     *p = q;
     return true;
@@ -175,6 +177,7 @@ smcsd_status smcsd_round(const smcsd_round_args* args, smcsd_stream stream) {
     fa.pp = la.pp;
     fa.tvp = plan.tv ? la.tvp : nullptr;
     fa.bp = la.bp;
+    fa.terms = reinterpret_cast<double*>(ws + plan.off_terms);
     fa.log_w_incr = a.log_w_incr;
     fa.log_weights = a.log_weights;
     fa.uniform = a.uniform;

@@ -38,44 +38,44 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
 
     if constexpr (FROM_PARTIALS) {
         const float T = a.temperature[r];
-        const float c32 = kLog2e / T;          // the scale the logits pass used
-        const double c = (double)c32;
+        const float c = kLog2e / T;             // the scale the logits pass used
         const double invT = 1.0 / (double)T;
-        for (int32_t i = tid; i < N; i += kThreads) {
+        // one thread per (particle, position): the position's log p(x) - log q(x) and TV
+        for (int32_t ik = tid; ik < N * K; ik += kThreads) {
+            const int32_t i = ik / K, k = ik - i * K;
             const int64_t ri = r * N + i;
-            double lw = 0.0;
-            for (int32_t k = 0; k < K; ++k) {
-                const int64_t u = ri * K + k;
-                const PairPart* part = a.pp + u * a.S;
-                float Mp = -INFINITY, Mq = -INFINITY;
-                for (int t = 0; t < a.S; ++t) {
-                    Mp = fmaxf(Mp, part[t].mp);
-                    Mq = fmaxf(Mq, part[t].mq);
-                }
-                double Sp = 0.0, Sq = 0.0;
-                for (int t = 0; t < a.S; ++t) {
-                    Sp += (double)part[t].sp * exp2(((double)part[t].mp - (double)Mp) * c);
-                    Sq += (double)part[t].sq * exp2(((double)part[t].mq - (double)Mq) * c);
-                }
-                const int32_t x = a.tokens[u];
-                if (x < 0 || x >= a.V) {
-                    flag_error(a.error_flags, SMCSD_DEVERR_TOKEN);
-                } else {
-                    // (zp[x] - Mp)/T - log Sp  -  ((zq[x] - Mq)/T - log Sq)
-                    const double zp = logit_at<DT>(a.target, ri * (K + 1) + k, a.ld, x);
-                    const double zq = logit_at<DT>(a.draft, u, a.ld, x);
-                    lw += ((zp - (double)Mp) - (zq - (double)Mq)) * invT - (log(Sp) - log(Sq));
-                }
-                if (a.tv) {
-                    double s = 0.0;
-                    for (int t = 0; t < a.S; ++t) s += (double)a.tvp[u * a.S + t];
-                    a.tv[u] = (float)fmin(fmax(0.5 * s, 0.0), 1.0);
-                }
+            const int64_t u = ri * K + k;
+            const PairPart* part = a.pp + u * a.S;
+            float Mp = -INFINITY, Mq = -INFINITY;
+            for (int t = 0; t < a.S; ++t) {
+                Mp = fmaxf(Mp, part[t].mp);
+                Mq = fmaxf(Mq, part[t].mq);
             }
-            a.log_w_incr[ri] = (float)lw;
-            s_l[i] = (double)a.log_weights[ri] + lw;
-            // bonus token of original particle i: best (key, index) over the slices
-            const BonusPart* bpart = a.bp + ri * a.S;
+            double Sp = 0.0, Sq = 0.0;
+            for (int t = 0; t < a.S; ++t) {
+                Sp += (double)(part[t].sp * __builtin_amdgcn_exp2f((part[t].mp - Mp) * c));
+                Sq += (double)(part[t].sq * __builtin_amdgcn_exp2f((part[t].mq - Mq) * c));
+            }
+            double term = 0.0;
+            const int32_t x = a.tokens[u];
+            if (x < 0 || x >= a.V) {
+                flag_error(a.error_flags, SMCSD_DEVERR_TOKEN);
+            } else {
+                // (zp[x] - Mp)/T - log Sp  -  ((zq[x] - Mq)/T - log Sq)
+                const double zp = logit_at<DT>(a.target, ri * (K + 1) + k, a.ld, x);
+                const double zq = logit_at<DT>(a.draft, u, a.ld, x);
+                term = ((zp - (double)Mp) - (zq - (double)Mq)) * invT - (log(Sp) - log(Sq));
+            }
+            a.terms[u] = term;
+            if (a.tv) {
+                double t2 = 0.0;
+                for (int t = 0; t < a.S; ++t) t2 += (double)a.tvp[u * a.S + t];
+                a.tv[u] = (float)fmin(fmax(0.5 * t2, 0.0), 1.0);
+            }
+        }
+        // one thread per particle: its bonus token, the best (key, index) over the slices
+        for (int32_t i = tid; i < N; i += kThreads) {
+            const BonusPart* bpart = a.bp + (r * N + i) * a.S;
             float best = bpart[0].key;
             int32_t besti = bpart[0].idx;
             for (int t = 1; t < a.S; ++t)
@@ -84,8 +84,16 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
                     besti = bpart[t].idx;
                 }
             if (besti < 0 || besti >= a.V) besti = 0;   // only if every key was NaN
-            a.bonus[ri] = besti;
+            a.bonus[r * N + i] = besti;
             s_bonus[i] = besti;
+        }
+        __syncthreads();   // terms written above are read by other threads below
+        for (int32_t i = tid; i < N; i += kThreads) {
+            const int64_t ri = r * N + i;
+            double lw = 0.0;
+            for (int32_t k = 0; k < K; ++k) lw += a.terms[ri * K + k];   // k in order
+            a.log_w_incr[ri] = (float)lw;
+            s_l[i] = (double)a.log_weights[ri] + lw;
         }
     } else {
         for (int32_t i = tid; i < N; i += kThreads)

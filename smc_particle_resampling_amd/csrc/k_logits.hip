@@ -130,7 +130,11 @@ __device__ __forceinline__ float slice_max(const u32x4 (&R)[CPL]) {
         for (int j = 0; j < CPL; ++j)
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                const i16x2 x = __builtin_bit_cast(i16x2, R[j][w]);
+                const uint32_t word = R[j][w];
+                // copy the element first: a bit cast applied to a vector element directly
+                // reads the vector's first element instead (clang lowers it as a load from
+                // the vector's address)
+                const i16x2 x = __builtin_bit_cast(i16x2, word);
                 mx = __builtin_elementwise_max(mx, x);
                 mn = __builtin_elementwise_min(mn, x);
             }
@@ -297,18 +301,35 @@ __device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, float* red,
             Sp += word_hi(xch[2 * t]) * __builtin_amdgcn_exp2f((word_lo(xch[2 * t]) - Mp) * c);
             Sq += word_hi(xch[2 * t + 1]) * __builtin_amdgcn_exp2f((word_lo(xch[2 * t + 1]) - Mq) * c);
         }
+        // p = e_p f_p / S_p and q = e_q f_q / S_q with f = exp2((m_slice - M_row) c). Factor
+        // out the larger of f_p / S_p and f_q / S_q, so the ratio stays finite even when the
+        // other factor underflows (a slice far below its row's max). Equal rows take the
+        // first branch with rho exactly 1.
         const float fp = __builtin_amdgcn_exp2f((mp - Mp) * c);
         const float fq = __builtin_amdgcn_exp2f((mq - Mq) * c);
-        bcast[0] = (fq * Sp) / (fp * Sq);   // rho
-        bcast[1] = fp / Sp;                 // scale of this slice's sum
+        const bool p_major = fp * Sq >= fq * Sp;
+        const float num = p_major ? fq * Sp : fp * Sq;
+        const float den = p_major ? fp * Sq : fq * Sp;
+        bcast[0] = den > 0.0f ? num / den : 0.0f;   // rho
+        bcast[1] = p_major ? fp / Sp : fq / Sq;     // scale of this slice's sum
+        bcast[2] = p_major ? 1.0f : 0.0f;
     }
     __syncthreads();
     const float rho = bcast[0];
+    const bool p_major = bcast[2] != 0.0f;          // uniform across the workgroup
     float acc0 = 0.0f, acc1 = 0.0f;
+    if (p_major) {
 #pragma unroll
-    for (int e = 0; e < NE; e += 2) {
-        acc0 += fabsf(fmaf(-rho, Eq[e], Ep[e]));
-        acc1 += fabsf(fmaf(-rho, Eq[e + 1], Ep[e + 1]));
+        for (int e = 0; e < NE; e += 2) {
+            acc0 += fabsf(fmaf(-rho, Eq[e], Ep[e]));
+            acc1 += fabsf(fmaf(-rho, Eq[e + 1], Ep[e + 1]));
+        }
+    } else {
+#pragma unroll
+        for (int e = 0; e < NE; e += 2) {
+            acc0 += fabsf(fmaf(-rho, Ep[e], Eq[e]));
+            acc1 += fabsf(fmaf(-rho, Ep[e + 1], Eq[e + 1]));
+        }
     }
     const float acc = block_sum(acc0 + acc1, red);
     if (tid == 0) a.tvp[u * a.S + s] = acc * bcast[1];
@@ -409,7 +430,7 @@ template <int DT>
 __global__ __launch_bounds__(kThreads, 4) void k_logits_tv(LogitsArgs a) {
     __shared__ float red[kWaves];
     __shared__ int32_t redi[kWaves];
-    __shared__ float bcast[2];
+    __shared__ float bcast[3];
     __shared__ uint64_t xch[2 * kMaxTvSlices];
     const int s = (int)(blockIdx.x % (unsigned)a.S);
     const int64_t cluster = blockIdx.x / (unsigned)a.S;

@@ -33,7 +33,7 @@ struct Plan {
     int64_t total_wgs = 0;   // (pairs + bonus_rows) * S
     bool tv = false;
     // workspace offsets in bytes
-    size_t off_ctrl = 0, off_pp = 0, off_tvp = 0, off_bp = 0, bytes = 0;
+    size_t off_ctrl = 0, off_pp = 0, off_tvp = 0, off_bp = 0, off_terms = 0, bytes = 0;
 };
 
 // Control block at the start of the workspace (zeroed before each TV launch).
@@ -83,6 +83,7 @@ struct FinalizeArgs {
     const PairPart* pp;
     const float* tvp;
     const BonusPart* bp;
+    double* terms;            // [R][N][K] per-position log-ratios (workspace)
     // weights
     float* log_w_incr;        // out (from partials) or in
     float* log_weights;       // in/out

@@ -76,7 +76,7 @@ def test_scaled_workloads(w, dev):
                                         (9, "bf16", True), (33, "f32", False),
                                         (5001, "bf16", True), (16385, "bf16", True),
                                         (16384 * 3 + 8, "bf16", True), (8191, "f32", True),
-                                        (524288, "bf16", True), (524281, "bf16", True)])
+                                        (524288, "bf16", True), (524281, "bf16", True), (262144, "f32", True)])
 def test_ragged_and_tiny_vocabularies(V, dtype, tv, dev):
     w = W["r16-n16-k4-v128256-bf16"].scaled(name="ragged", R=2, N=8, K=3, V=V, dtype=dtype,
                                             tv=tv, ctx=128)
@@ -109,6 +109,38 @@ def test_identical_target_and_draft(dev):
     assert np.all(gpu["tv"] == 0.0)
     assert np.all(gpu["ess"] == w.N)
     assert np.all(gpu["ancestors"] == np.arange(w.N))
+
+
+def test_extreme_logit_ranges(dev):
+    # slices whose max lies hundreds of nats below the row max (their exponentials underflow
+    # to 0) and rows whose draft is far from the target must give finite, exact-to-tolerance
+    # weights and TV
+    w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="extreme-range", R=2, N=4, K=3, V=40000,
+                                               ctx=64)
+
+    def widen(inp):
+        inp["target"][:, :, :, 5000:30000] -= 300.0
+        inp["draft"][:, 1:, :, 20000:39000] -= 250.0
+        inp["target"][:, 0, 0, 7] += 200.0
+
+    run_and_compare(w, dev, seed=10, modify=widen)
+
+
+@pytest.mark.parametrize("tv", [True, False])
+def test_row_max_at_every_chunk_position(tv, dev):
+    # a +200 spike (its exp overflows unless the slice max sees it) at each of the 8 element
+    # positions of a 16-byte chunk, in different rows, plus one at the row's last element
+    w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="spikes", R=1, N=10, K=2, V=20001, ctx=64,
+                                               tv=tv)
+
+    def spike(inp):
+        for i in range(8):
+            inp["target"][0, i, 0, 8 * 37 + i] += 200.0
+            inp["draft"][0, i, 1, 8 * 1000 + i] += 200.0
+        inp["target"][0, 8, 1, w.V - 1] += 200.0
+        inp["draft"][0, 9, 0, w.V - 1] += 200.0
+
+    run_and_compare(w, dev, seed=11, modify=spike)
 
 
 def test_empty_batch(dev):
