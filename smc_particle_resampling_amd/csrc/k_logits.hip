@@ -100,13 +100,6 @@ __device__ __forceinline__ void mask_slice_tail(u32x4 (&R)[CPL], int c0, int c1,
     }
 }
 
-template <int DT, int CPL>
-__device__ __forceinline__ void load_slice(u32x4 (&R)[CPL], const char* row, int c0, int c1,
-                                           int V) {
-    issue_slice<DT, CPL>(R, row, c0, c1);
-    mask_slice_tail<DT, CPL>(R, c0, c1, V);
-}
-
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 
 // Slice max. For bf16 it works on the raw bit patterns with packed 16-bit integer max and
@@ -203,18 +196,48 @@ __device__ __forceinline__ PairLoc pair_location(const LogitsArgs& a, int64_t u,
     return L;
 }
 
+// Two block-wide reductions at once (max or sum), in a fixed order: lanes by xor tree, then
+// waves 0..3. lds holds 2 * kWaves floats. One barrier: a later call must use other lds
+// (or come after another barrier) so that no wave overwrites values still being read.
+template <bool kMax>
+__device__ __forceinline__ void block_reduce2(float& a, float& b, float* lds) {
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+        const float oa = __shfl_xor(a, off, 64), ob = __shfl_xor(b, off, 64);
+        a = kMax ? fmaxf(a, oa) : a + oa;
+        b = kMax ? fmaxf(b, ob) : b + ob;
+    }
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        lds[2 * w] = a;
+        lds[2 * w + 1] = b;
+    }
+    __syncthreads();
+    a = lds[0];
+    b = lds[1];
+#pragma unroll
+    for (int i = 1; i < kWaves; ++i) {
+        a = kMax ? fmaxf(a, lds[2 * i]) : a + lds[2 * i];
+        b = kMax ? fmaxf(b, lds[2 * i + 1]) : b + lds[2 * i + 1];
+    }
+}
+
 // TV off: slice partials only.
 template <int DT>
-__device__ void pair_slice_stream(const LogitsArgs& a, int64_t u, int s, float* red) {
+__device__ void pair_slice_stream(const LogitsArgs& a, int64_t u, int s, float* red2a,
+                                  float* red2b) {
     const PairLoc L = pair_location<DT>(a, u, s);
     const float c = kLog2e / a.temperature[L.r];   // exp(z/T) = exp2(z * c)
     u32x4 P[kStreamCPL], Q[kStreamCPL];
-    load_slice<DT, kStreamCPL>(P, L.zp, L.c0, L.c1, a.V);
-    load_slice<DT, kStreamCPL>(Q, L.zq, L.c0, L.c1, a.V);
-    const float mp = block_max(slice_max<DT, kStreamCPL>(P), red);
-    const float mq = block_max(slice_max<DT, kStreamCPL>(Q), red);
-    const float sp = block_sum(slice_sumexp<DT, kStreamCPL>(P, c, -mp * c), red);
-    const float sq = block_sum(slice_sumexp<DT, kStreamCPL>(Q, c, -mq * c), red);
+    issue_slice<DT, kStreamCPL>(P, L.zp, L.c0, L.c1);
+    issue_slice<DT, kStreamCPL>(Q, L.zq, L.c0, L.c1);
+    mask_slice_tail<DT, kStreamCPL>(P, L.c0, L.c1, a.V);
+    mask_slice_tail<DT, kStreamCPL>(Q, L.c0, L.c1, a.V);
+    float mp = slice_max<DT, kStreamCPL>(P), mq = slice_max<DT, kStreamCPL>(Q);
+    block_reduce2<true>(mp, mq, red2a);
+    float sp = slice_sumexp<DT, kStreamCPL>(P, c, -mp * c);
+    float sq = slice_sumexp<DT, kStreamCPL>(Q, c, -mq * c);
+    block_reduce2<false>(sp, sq, red2b);
     if (threadIdx.x == 0) a.pp[u * a.S + s] = PairPart{mp, sp, mq, sq};
 }
 
@@ -260,63 +283,75 @@ __device__ void wait_for_slices(const uint64_t* words, int nwords, Ctrl* ctrl,
     if (lane + 64 < nwords) lds[lane + 64] = v1;
 }
 
-// TV on: partials, exchange, and this slice's share of sum |p - q|.
+// LDS of the TV pass. Each step of a row pair has its own buffer, so one barrier per step
+// suffices: a buffer is rewritten only after every wave has passed a later barrier.
+struct TvLds {
+    float max2[2 * kWaves];          // slice maxima of p and q
+    float sum2[2 * kWaves];          // slice sums of p and q
+    float tv[kWaves];                // per-wave |p - q| sums
+    uint64_t xch[2 * kMaxTvSlices];  // the row pair's exchange words
+};
+
+// TV on: partials, exchange, and this slice's share of sum |p - q|. Four barriers per row
+// pair: slice max, slice sum, exchange words in LDS, per-wave TV sums.
 template <int DT>
-__device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, float* red, float* bcast,
-                              uint64_t* xch) {
+__device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, TvLds& sh) {
     constexpr int NE = kTvCPL * Elem<DT>::EPC;
     const int tid = threadIdx.x;
+    const int lane = tid & 63;
     const PairLoc L = pair_location<DT>(a, u, s);
     const float c = kLog2e / a.temperature[L.r];
     float Ep[NE], Eq[NE];
     float mp, mq, sp, sq;
     {
         u32x4 P[kTvCPL], Q[kTvCPL];
-        load_slice<DT, kTvCPL>(P, L.zp, L.c0, L.c1, a.V);
-        load_slice<DT, kTvCPL>(Q, L.zq, L.c0, L.c1, a.V);
-        mp = block_max(slice_max<DT, kTvCPL>(P), red);
-        mq = block_max(slice_max<DT, kTvCPL>(Q), red);
+        // both rows' loads are in flight before the first wait on either
+        issue_slice<DT, kTvCPL>(P, L.zp, L.c0, L.c1);
+        issue_slice<DT, kTvCPL>(Q, L.zq, L.c0, L.c1);
+        mask_slice_tail<DT, kTvCPL>(P, L.c0, L.c1, a.V);
+        mask_slice_tail<DT, kTvCPL>(Q, L.c0, L.c1, a.V);
+        mp = slice_max<DT, kTvCPL>(P);
+        mq = slice_max<DT, kTvCPL>(Q);
+        block_reduce2<true>(mp, mq, sh.max2);
         sp = slice_exp<DT, kTvCPL>(P, c, -mp * c, Ep);
         sq = slice_exp<DT, kTvCPL>(Q, c, -mq * c, Eq);
     }
-    sp = block_sum(sp, red);
-    sq = block_sum(sq, red);
+    block_reduce2<false>(sp, sq, sh.sum2);
 
     uint64_t* words = reinterpret_cast<uint64_t*>(a.pp + u * a.S);
     if (tid == 0) {
         __hip_atomic_store(words + 2 * s, pack2(mp, sp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(words + 2 * s + 1, pack2(mq, sq), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (tid < 64) wait_for_slices(words, 2 * a.S, a.ctrl, a.error_flags, xch);
+    if (tid < 64) wait_for_slices(words, 2 * a.S, a.ctrl, a.error_flags, sh.xch);
     __syncthreads();
-    if (tid == 0) {
-        // the row's maxima and sums from all slices, in slice order
-        float Mp = -INFINITY, Mq = -INFINITY;
-        for (int t = 0; t < a.S; ++t) {
-            Mp = fmaxf(Mp, word_lo(xch[2 * t]));
-            Mq = fmaxf(Mq, word_lo(xch[2 * t + 1]));
-        }
-        float Sp = 0.0f, Sq = 0.0f;
-        for (int t = 0; t < a.S; ++t) {
-            Sp += word_hi(xch[2 * t]) * __builtin_amdgcn_exp2f((word_lo(xch[2 * t]) - Mp) * c);
-            Sq += word_hi(xch[2 * t + 1]) * __builtin_amdgcn_exp2f((word_lo(xch[2 * t + 1]) - Mq) * c);
-        }
-        // p = e_p f_p / S_p and q = e_q f_q / S_q with f = exp2((m_slice - M_row) c). Factor
-        // out the larger of f_p / S_p and f_q / S_q, so the ratio stays finite even when the
-        // other factor underflows (a slice far below its row's max). Equal rows take the
-        // first branch with rho exactly 1.
-        const float fp = __builtin_amdgcn_exp2f((mp - Mp) * c);
-        const float fq = __builtin_amdgcn_exp2f((mq - Mq) * c);
-        const bool p_major = fp * Sq >= fq * Sp;
-        const float num = p_major ? fq * Sp : fp * Sq;
-        const float den = p_major ? fp * Sq : fq * Sp;
-        bcast[0] = den > 0.0f ? num / den : 0.0f;   // rho
-        bcast[1] = p_major ? fp / Sp : fq / Sq;     // scale of this slice's sum
-        bcast[2] = p_major ? 1.0f : 0.0f;
-    }
-    __syncthreads();
-    const float rho = bcast[0];
-    const bool p_major = bcast[2] != 0.0f;          // uniform across the workgroup
+
+    // Every wave combines the 2S (<= 128) words itself: lane t holds words t and t + 64
+    // (target words at even t, draft words at odd t), and xor steps of 2..32 reduce over
+    // lanes of one parity in a fixed tree. Unused slots hold (-inf, 0), which adds nothing.
+    const uint64_t kNone = pack2(-INFINITY, 0.0f);
+    const uint64_t w0 = lane < 2 * a.S ? sh.xch[lane] : kNone;
+    const uint64_t w1 = lane + 64 < 2 * a.S ? sh.xch[lane + 64] : kNone;
+    float M = fmaxf(word_lo(w0), word_lo(w1));
+#pragma unroll
+    for (int off = 2; off <= 32; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
+    float Z = word_hi(w0) * __builtin_amdgcn_exp2f((word_lo(w0) - M) * c) +
+              word_hi(w1) * __builtin_amdgcn_exp2f((word_lo(w1) - M) * c);
+#pragma unroll
+    for (int off = 2; off <= 32; off <<= 1) Z += __shfl_xor(Z, off, 64);
+    const float Mp = __shfl(M, 0, 64), Mq = __shfl(M, 1, 64);
+    const float Sp = __shfl(Z, 0, 64), Sq = __shfl(Z, 1, 64);
+    // p = e_p f_p / S_p and q = e_q f_q / S_q with f = exp2((m_slice - M_row) c). Factor out
+    // the larger of f_p / S_p and f_q / S_q, so the ratio stays finite even when the other
+    // factor underflows (a slice far below its row's max). Equal rows take the first branch
+    // with rho exactly 1.
+    const float fp = __builtin_amdgcn_exp2f((mp - Mp) * c);
+    const float fq = __builtin_amdgcn_exp2f((mq - Mq) * c);
+    const bool p_major = fp * Sq >= fq * Sp;   // the same in every lane
+    const float num = p_major ? fq * Sp : fp * Sq;
+    const float den = p_major ? fp * Sq : fq * Sp;
+    const float rho = den > 0.0f ? num / den : 0.0f;
+    const float scale = p_major ? fp / Sp : fq / Sq;
     float acc0 = 0.0f, acc1 = 0.0f;
     if (p_major) {
 #pragma unroll
@@ -331,8 +366,15 @@ __device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, float* red,
             acc1 += fabsf(fmaf(-rho, Ep[e + 1], Eq[e + 1]));
         }
     }
-    const float acc = block_sum(acc0 + acc1, red);
-    if (tid == 0) a.tvp[u * a.S + s] = acc * bcast[1];
+    const float acc = wave_sum(acc0 + acc1);
+    if (lane == 0) sh.tv[tid >> 6] = acc;
+    __syncthreads();
+    if (tid == 0) {
+        float t = sh.tv[0];
+#pragma unroll
+        for (int i = 1; i < kWaves; ++i) t += sh.tv[i];
+        a.tvp[u * a.S + s] = t * scale;
+    }
 }
 
 template <int DT, int CPL>
@@ -416,9 +458,10 @@ template <int DT>
 __global__ __launch_bounds__(kThreads) void k_logits_stream(LogitsArgs a) {
     __shared__ float red[kWaves];
     __shared__ int32_t redi[kWaves];
+    __shared__ float red2a[2 * kWaves], red2b[2 * kWaves];
     const int64_t t = blockIdx.x;
     if (t < a.pair_wgs) {
-        pair_slice_stream<DT>(a, t / a.S, (int)(t % a.S), red);
+        pair_slice_stream<DT>(a, t / a.S, (int)(t % a.S), red2a, red2b);
     } else if (t < a.total_wgs) {
         const int64_t tb = t - a.pair_wgs;
         bonus_slice<DT, kStreamCPL>(a, tb / a.S, (int)(tb % a.S), red, redi);
@@ -428,19 +471,16 @@ __global__ __launch_bounds__(kThreads) void k_logits_stream(LogitsArgs a) {
 // TV on: persistent cooperative grid, gridDim.x = C * S.
 template <int DT>
 __global__ __launch_bounds__(kThreads, 4) void k_logits_tv(LogitsArgs a) {
+    __shared__ TvLds sh;
     __shared__ float red[kWaves];
     __shared__ int32_t redi[kWaves];
-    __shared__ float bcast[3];
-    __shared__ uint64_t xch[2 * kMaxTvSlices];
     const int s = (int)(blockIdx.x % (unsigned)a.S);
     const int64_t cluster = blockIdx.x / (unsigned)a.S;
     const int64_t clusters = gridDim.x / (unsigned)a.S;
     const int64_t items = a.pairs + (a.total_wgs - a.pair_wgs) / a.S;
-    for (int64_t it = cluster; it < items; it += clusters) {
-        if (it < a.pairs) pair_slice_tv<DT>(a, it, s, red, bcast, xch);
-        else bonus_slice<DT, kTvCPL>(a, it - a.pairs, s, red, redi);
-        __syncthreads();   // bcast / xch are reused by the next item
-    }
+    int64_t it = cluster;
+    for (; it < a.pairs; it += clusters) pair_slice_tv<DT>(a, it, s, sh);
+    for (; it < items; it += clusters) bonus_slice<DT, kTvCPL>(a, it - a.pairs, s, red, redi);
 }
 
 __global__ void k_fill_words(uint32_t* p, int64_t n, uint32_t value) {

@@ -154,32 +154,6 @@ __device__ __forceinline__ float wave_sum(float v) {
     return v;
 }
 
-// Block-wide reductions in a fixed order (lanes by xor tree, then waves 0..3), so results
-// are bit-identical from run to run. `lds` needs kWaves floats. All threads get the result.
-__device__ __forceinline__ float block_max(float v, float* lds) {
-    v = wave_max(v);
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) lds[w] = v;
-    __syncthreads();
-    float r = lds[0];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) r = fmaxf(r, lds[i]);
-    __syncthreads();
-    return r;
-}
-
-__device__ __forceinline__ float block_sum(float v, float* lds) {
-    v = wave_sum(v);
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) lds[w] = v;
-    __syncthreads();
-    float r = lds[0];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) r += lds[i];
-    __syncthreads();
-    return r;
-}
-
 // (key, index) argmax: the larger key wins, the lower index wins on equal keys.
 __device__ __forceinline__ bool better(float k1, int32_t i1, float k2, int32_t i2) {
     return k1 > k2 || (k1 == k2 && i1 < i2);
