@@ -196,17 +196,14 @@ __device__ __forceinline__ PairLoc pair_location(const LogitsArgs& a, int64_t u,
     return L;
 }
 
-// Two block-wide reductions at once (max or sum), in a fixed order: lanes by xor tree, then
-// waves 0..3. lds holds 2 * kWaves floats. One barrier: a later call must use other lds
-// (or come after another barrier) so that no wave overwrites values still being read.
+// Two block-wide reductions at once (max or sum), in a fixed order: within each wave as in
+// wave_max / wave_sum, then waves 0..3. lds holds 2 * kWaves floats. One barrier: a later
+// call must use other lds (or come after another barrier) so that no wave overwrites values
+// still being read.
 template <bool kMax>
 __device__ __forceinline__ void block_reduce2(float& a, float& b, float* lds) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float oa = __shfl_xor(a, off, 64), ob = __shfl_xor(b, off, 64);
-        a = kMax ? fmaxf(a, oa) : a + oa;
-        b = kMax ? fmaxf(b, ob) : b + ob;
-    }
+    a = kMax ? wave_max(a) : wave_sum(a);
+    b = kMax ? wave_max(b) : wave_sum(b);
     const int w = threadIdx.x >> 6;
     if ((threadIdx.x & 63) == 0) {
         lds[2 * w] = a;
@@ -326,21 +323,15 @@ __device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, TvLds& sh) 
     if (tid < 64) wait_for_slices(words, 2 * a.S, a.ctrl, a.error_flags, sh.xch);
     __syncthreads();
 
-    // Every wave combines the 2S (<= 128) words itself: lane t holds words t and t + 64
-    // (target words at even t, draft words at odd t), and xor steps of 2..32 reduce over
-    // lanes of one parity in a fixed tree. Unused slots hold (-inf, 0), which adds nothing.
+    // Every wave combines the S (<= 64) slices itself: lane t holds slice t's target and
+    // draft words, and whole-wave reductions (fixed order) give the row maxima and sums.
+    // Lanes without a slice hold (-inf, 0), which adds nothing.
     const uint64_t kNone = pack2(-INFINITY, 0.0f);
-    const uint64_t w0 = lane < 2 * a.S ? sh.xch[lane] : kNone;
-    const uint64_t w1 = lane + 64 < 2 * a.S ? sh.xch[lane + 64] : kNone;
-    float M = fmaxf(word_lo(w0), word_lo(w1));
-#pragma unroll
-    for (int off = 2; off <= 32; off <<= 1) M = fmaxf(M, __shfl_xor(M, off, 64));
-    float Z = word_hi(w0) * __builtin_amdgcn_exp2f((word_lo(w0) - M) * c) +
-              word_hi(w1) * __builtin_amdgcn_exp2f((word_lo(w1) - M) * c);
-#pragma unroll
-    for (int off = 2; off <= 32; off <<= 1) Z += __shfl_xor(Z, off, 64);
-    const float Mp = __shfl(M, 0, 64), Mq = __shfl(M, 1, 64);
-    const float Sp = __shfl(Z, 0, 64), Sq = __shfl(Z, 1, 64);
+    const uint64_t wp = lane < a.S ? sh.xch[2 * lane] : kNone;
+    const uint64_t wq = lane < a.S ? sh.xch[2 * lane + 1] : kNone;
+    const float Mp = wave_max(word_lo(wp)), Mq = wave_max(word_lo(wq));
+    const float Sp = wave_sum(word_hi(wp) * __builtin_amdgcn_exp2f((word_lo(wp) - Mp) * c));
+    const float Sq = wave_sum(word_hi(wq) * __builtin_amdgcn_exp2f((word_lo(wq) - Mq) * c));
     // p = e_p f_p / S_p and q = e_q f_q / S_q with f = exp2((m_slice - M_row) c). Factor out
     // the larger of f_p / S_p and f_q / S_q, so the ratio stays finite even when the other
     // factor underflows (a slice far below its row's max). Equal rows take the first branch
@@ -375,6 +366,20 @@ __device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, TvLds& sh) 
         for (int i = 1; i < kWaves; ++i) t += sh.tv[i];
         a.tvp[u * a.S + s] = t * scale;
     }
+}
+
+// Every lane of each 16-lane row ends with the row's best (key, index), as in row_max.
+__device__ __forceinline__ void argmax_step(float& k, int32_t& i, float ok, int32_t oi) {
+    if (better(ok, oi, k, i)) {
+        k = ok;
+        i = oi;
+    }
+}
+__device__ __forceinline__ void row_argmax(float& k, int32_t& i) {
+    argmax_step(k, i, dpp_f32<kDppXor1>(k), dpp_i32<kDppXor1>(i));
+    argmax_step(k, i, dpp_f32<kDppXor2>(k), dpp_i32<kDppXor2>(i));
+    argmax_step(k, i, dpp_f32<kDppRowHalfMirror>(k), dpp_i32<kDppRowHalfMirror>(i));
+    argmax_step(k, i, dpp_f32<kDppRowMirror>(k), dpp_i32<kDppRowMirror>(i));
 }
 
 template <int DT, int CPL>
@@ -426,15 +431,23 @@ __device__ void bonus_slice(const LogitsArgs& a, int64_t b, int s, float* red, i
             }
         }
     }
-    // block argmax in fixed order
+    // block argmax; (key, index) with the lower index winning ties is a total order, so
+    // the result does not depend on the order of the steps
+    row_argmax(best, besti);
+    {
+        float k = readlane_f32(best, 0);
+        int32_t i = __builtin_amdgcn_readlane(besti, 0);
 #pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-        const float ok = __shfl_xor(best, off, 64);
-        const int32_t oi = __shfl_xor(besti, off, 64);
-        if (better(ok, oi, best, besti)) {
-            best = ok;
-            besti = oi;
+        for (int r = 16; r < 64; r += 16) {
+            const float ok = readlane_f32(best, r);
+            const int32_t oi = __builtin_amdgcn_readlane(besti, r);
+            if (better(ok, oi, k, i)) {
+                k = ok;
+                i = oi;
+            }
         }
+        best = k;
+        besti = i;
     }
     const int w = tid >> 6;
     if ((tid & 63) == 0) {

@@ -142,16 +142,53 @@ __device__ __forceinline__ void flag_error(int32_t* flags, uint32_t bit) {
     if (flags) atomicOr(reinterpret_cast<unsigned int*>(flags), bit);
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
-    return v;
+// Cross-lane reductions by DPP moves, which stay in the VALU (no LDS round trip as with
+// ds_bpermute). Steps xor 1 and xor 2 (quad permutes), then the half-row mirror (lane i of
+// 8 reads 7 - i) and the row mirror (lane i of 16 reads 15 - i): after them every lane of a
+// 16-lane row holds the row's result, because each step combines two disjoint groups whose
+// results every lane already holds. The four row results are then read from lanes 0, 16,
+// 32 and 48 and combined in that order. The order is fixed, so a sum is bit-identical from
+// run to run, and the result is uniform (a scalar register).
+constexpr int kDppXor1 = 0xB1;          // quad_perm [1, 0, 3, 2]
+constexpr int kDppXor2 = 0x4E;          // quad_perm [2, 3, 0, 1]
+constexpr int kDppRowHalfMirror = 0x141;
+constexpr int kDppRowMirror = 0x140;
+
+template <int kCtrl>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), kCtrl,
+                                                                 0xF, 0xF, true));
+}
+template <int kCtrl>
+__device__ __forceinline__ int32_t dpp_i32(int32_t v) {
+    return __builtin_amdgcn_update_dpp(0, v, kCtrl, 0xF, 0xF, true);
+}
+__device__ __forceinline__ float readlane_f32(float v, int lane) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), lane));
 }
 
+__device__ __forceinline__ float row_max(float v) {
+    v = fmaxf(v, dpp_f32<kDppXor1>(v));
+    v = fmaxf(v, dpp_f32<kDppXor2>(v));
+    v = fmaxf(v, dpp_f32<kDppRowHalfMirror>(v));
+    return fmaxf(v, dpp_f32<kDppRowMirror>(v));
+}
+__device__ __forceinline__ float row_sum(float v) {
+    v += dpp_f32<kDppXor1>(v);
+    v += dpp_f32<kDppXor2>(v);
+    v += dpp_f32<kDppRowHalfMirror>(v);
+    return v + dpp_f32<kDppRowMirror>(v);
+}
+
+// Whole-wave max and sum; every lane must be active. The result is wave-uniform.
+__device__ __forceinline__ float wave_max(float v) {
+    v = row_max(v);
+    return fmaxf(fmaxf(readlane_f32(v, 0), readlane_f32(v, 16)),
+                 fmaxf(readlane_f32(v, 32), readlane_f32(v, 48)));
+}
 __device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
-    return v;
+    v = row_sum(v);
+    return ((readlane_f32(v, 0) + readlane_f32(v, 16)) + readlane_f32(v, 32)) + readlane_f32(v, 48);
 }
 
 // (key, index) argmax: the larger key wins, the lower index wins on equal keys.
