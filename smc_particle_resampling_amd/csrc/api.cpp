@@ -47,7 +47,7 @@ bool make_plan(int32_t R, int32_t N, int32_t K, int32_t V, int64_t ld, int32_t d
     q.off_pp = off;
     off = align256(off + sizeof(PairPart) * (size_t)q.pair_wgs);
     q.off_tvp = off;
-    off = align256(off + (tv ? sizeof(float) * (size_t)q.pair_wgs : 0));
+    off = align256(off + (tv ? sizeof(float) * (size_t)q.pair_wgs * kWaves : 0));
     q.off_bp = off;
     off = align256(off + sizeof(BonusPart) * (size_t)(q.bonus_rows * q.S));
     q.off_terms = off;

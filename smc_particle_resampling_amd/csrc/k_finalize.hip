@@ -69,7 +69,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
             a.terms[u] = term;
             if (a.tv) {
                 double t2 = 0.0;
-                for (int t = 0; t < a.S; ++t) t2 += (double)a.tvp[u * a.S + t];
+                for (int t = 0; t < a.S * kWaves; ++t) t2 += (double)a.tvp[u * a.S * kWaves + t];
                 a.tv[u] = (float)fmin(fmax(0.5 * t2, 0.0), 1.0);
             }
         }

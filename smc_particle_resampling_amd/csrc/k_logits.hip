@@ -53,6 +53,13 @@ struct Elem {
     static constexpr uint32_t kNegInf = DT == SMCSD_F32 ? 0xFF800000u : 0xFF80FF80u;
 };
 
+// A per-request value that no kernel of the round writes (the temperatures), read through
+// the scalar cache. A plain load would be a vector load, and waiting for it would also wait
+// for every logits load issued before it.
+__device__ __forceinline__ float load_constant(const float* p, int64_t i) {
+    return ((const __attribute__((address_space(4))) float*)p)[i];
+}
+
 __device__ __forceinline__ u32x4 load_chunk(const char* row, int64_t chunk) {
     return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + chunk);
 }
@@ -72,31 +79,42 @@ __device__ __forceinline__ u32x4 mask_tail(u32x4 c, int nv) {
     return c;
 }
 
-// Issue the loads of the CPL chunks this lane owns in slice [c0, c1) of a row. Chunks
-// outside the slice stay -inf. The loads may still be in flight on return.
-template <int DT, int CPL>
+// Slice loads go through a buffer resource that covers exactly the slice [c0, c1) of a row:
+// one scalar base, one lane offset (16 * lane) shared by every load, the chunk group in the
+// scalar offset, and the hardware range check returning zeros past the slice end (no
+// memory access there). Word 3 is the gfx9-family raw-buffer setting (32-bit data format,
+// no swizzle); cache policy 2 marks the loads non-temporal.
+constexpr int kRsrcWord3 = 0x00020000;
+constexpr int kLoadNontemporal = 2;
+
+// Issue the loads of the CPL chunks this lane owns in slice [c0, c1) of a row (chunk
+// c0 + j * kThreads + lane). They may still be in flight on return.
+template <int CPL>
 __device__ __forceinline__ void issue_slice(u32x4 (&R)[CPL], const char* row, int c0, int c1) {
-    const int tid = threadIdx.x;
-    const uint32_t ni = Elem<DT>::kNegInf;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<char*>(row) + (size_t)c0 * 16, 0, (c1 - c0) * 16, kRsrcWord3);
+    const int voff = (int)threadIdx.x * 16;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) R[j] = u32x4{ni, ni, ni, ni};
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int ch = c0 + j * kThreads + tid;
-        if (ch < c1) R[j] = load_chunk(row, ch);   // masked load: other lanes keep -inf
-    }
+    for (int j = 0; j < CPL; ++j)
+        R[j] = __builtin_amdgcn_raw_buffer_load_b128(r, voff, j * kThreads * 16, kLoadNontemporal);
 }
 
-// Elements >= V (only in the row's last chunk) become -inf. Waits for that chunk's load.
+// After the loads: chunks past the slice end and elements >= V (only in the row's last
+// chunk, when V is not a multiple of EPC) become -inf. The branches are uniform.
 template <int DT, int CPL>
-__device__ __forceinline__ void mask_slice_tail(u32x4 (&R)[CPL], int c0, int c1, int V) {
+__device__ __forceinline__ void mask_slice(u32x4 (&R)[CPL], int c0, int c1, int V) {
     constexpr int EPC = Elem<DT>::EPC;
     const int tid = threadIdx.x;
+    const int n = c1 - c0;
+    const uint32_t ni = Elem<DT>::kNegInf;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-        const int ch = c0 + j * kThreads + tid;
-        const int nv = V - ch * EPC;
-        if (ch < c1 && nv < EPC) R[j] = mask_tail<DT>(R[j], nv);
+    for (int j = 0; j < CPL; ++j)
+        if ((j + 1) * kThreads > n && j * kThreads + tid >= n) R[j] = u32x4{ni, ni, ni, ni};
+    if ((int64_t)c1 * EPC > V) {
+        const int last = c1 - 1 - c0;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+            if (j * kThreads + tid == last) R[j] = mask_tail<DT>(R[j], V - (c1 - 1) * EPC);
     }
 }
 
@@ -224,12 +242,12 @@ template <int DT>
 __device__ void pair_slice_stream(const LogitsArgs& a, int64_t u, int s, float* red2a,
                                   float* red2b) {
     const PairLoc L = pair_location<DT>(a, u, s);
-    const float c = kLog2e / a.temperature[L.r];   // exp(z/T) = exp2(z * c)
+    const float c = kLog2e / load_constant(a.temperature, L.r);   // exp(z/T) = exp2(z * c)
     u32x4 P[kStreamCPL], Q[kStreamCPL];
-    issue_slice<DT, kStreamCPL>(P, L.zp, L.c0, L.c1);
-    issue_slice<DT, kStreamCPL>(Q, L.zq, L.c0, L.c1);
-    mask_slice_tail<DT, kStreamCPL>(P, L.c0, L.c1, a.V);
-    mask_slice_tail<DT, kStreamCPL>(Q, L.c0, L.c1, a.V);
+    issue_slice<kStreamCPL>(P, L.zp, L.c0, L.c1);
+    issue_slice<kStreamCPL>(Q, L.zq, L.c0, L.c1);
+    mask_slice<DT, kStreamCPL>(P, L.c0, L.c1, a.V);
+    mask_slice<DT, kStreamCPL>(Q, L.c0, L.c1, a.V);
     float mp = slice_max<DT, kStreamCPL>(P), mq = slice_max<DT, kStreamCPL>(Q);
     block_reduce2<true>(mp, mq, red2a);
     float sp = slice_sumexp<DT, kStreamCPL>(P, c, -mp * c);
@@ -253,31 +271,151 @@ __device__ __forceinline__ uint64_t pack2(float lo, float hi) {
 __device__ __forceinline__ float word_lo(uint64_t w) { return __uint_as_float((uint32_t)w); }
 __device__ __forceinline__ float word_hi(uint64_t w) { return __uint_as_float((uint32_t)(w >> 32)); }
 
-// Wave 0 only. Copies the nwords (<= 128) words of a row pair into lds once all are published.
-__device__ void wait_for_slices(const uint64_t* words, int nwords, Ctrl* ctrl,
-                                int32_t* error_flags, uint64_t* lds) {
+// Wave 0 only: one poll of the nwords (<= 128) words of a row pair, with the abort flag in the
+// same round trip. Returns true (wave-uniform) once every word is published, the pass was
+// aborted, or the wait has lasted longer than the limit (then it raises the abort flag and
+// SMCSD_DEVERR_EXCHANGE). On true, lds holds the words.
+__device__ bool poll_slices(const uint64_t* words, int nwords, Ctrl* ctrl, int32_t* error_flags,
+                            uint64_t* lds, uint64_t t0) {
     const int lane = threadIdx.x & 63;
-    const uint64_t t0 = wall_clock64();
-    uint64_t v0 = 0, v1 = 0;
-    while (true) {
-        v0 = lane < nwords ? __hip_atomic_load(words + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                           : 0ull;
-        v1 = lane + 64 < nwords
-                 ? __hip_atomic_load(words + lane + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
-                 : 0ull;
-        if (!__any(v0 == kEmpty || v1 == kEmpty)) break;
-        if (__hip_atomic_load(&ctrl->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)) break;
-        if (wall_clock64() - t0 > kExchangeTimeoutTicks) {
-            if (lane == 0) {
-                __hip_atomic_store(&ctrl->abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-                flag_error(error_flags, SMCSD_DEVERR_EXCHANGE);
-            }
-            break;
+    const uint64_t v0 = lane < nwords
+                            ? __hip_atomic_load(words + lane, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                            : 0ull;
+    const uint64_t v1 = lane + 64 < nwords
+                            ? __hip_atomic_load(words + lane + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                            : 0ull;
+    const uint32_t abort = __hip_atomic_load(&ctrl->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool done = !__any(v0 == kEmpty || v1 == kEmpty) || abort != 0;
+    if (!done && wall_clock64() - t0 > kExchangeTimeoutTicks) {
+        if (lane == 0) {
+            __hip_atomic_store(&ctrl->abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            flag_error(error_flags, SMCSD_DEVERR_EXCHANGE);
         }
-        __builtin_amdgcn_s_sleep(1);
+        done = true;
     }
-    if (lane < nwords) lds[lane] = v0;
-    if (lane + 64 < nwords) lds[lane + 64] = v1;
+    if (done) {
+        if (lane < nwords) lds[lane] = v0;
+        if (lane + 64 < nwords) lds[lane + 64] = v1;
+    }
+    return done;
+}
+
+// Every lane of each 16-lane row ends with the row's best (key, index), as in row_max.
+__device__ __forceinline__ void argmax_step(float& k, int32_t& i, float ok, int32_t oi) {
+    if (better(ok, oi, k, i)) {
+        k = ok;
+        i = oi;
+    }
+}
+__device__ __forceinline__ void row_argmax(float& k, int32_t& i) {
+    argmax_step(k, i, dpp_f32<kDppXor1>(k), dpp_i32<kDppXor1>(i));
+    argmax_step(k, i, dpp_f32<kDppXor2>(k), dpp_i32<kDppXor2>(i));
+    argmax_step(k, i, dpp_f32<kDppRowHalfMirror>(k), dpp_i32<kDppRowHalfMirror>(i));
+    argmax_step(k, i, dpp_f32<kDppRowMirror>(k), dpp_i32<kDppRowMirror>(i));
+}
+
+// Bonus rows. A workgroup handles slice s of a bonus row two chunks per lane at a time (a
+// "piece"). key = z/T + G with one
+// rounding; -inf for positions outside the slice or >= V. A lane visits its indices in
+// increasing order, so the strict comparison keeps the lowest index among equal keys.
+struct BonusRow {
+    const char* zrow;
+    const char* grow;
+    float invT;
+    int c0, c1;
+};
+
+template <int DT>
+__device__ __forceinline__ BonusRow bonus_row(const LogitsArgs& a, int64_t b, int s) {
+    constexpr size_t ESZ = Elem<DT>::ESZ;
+    BonusRow B;
+    B.zrow = static_cast<const char*>(a.target) + (size_t)((b * (a.K + 1) + a.K) * a.ld) * ESZ;
+    B.grow = reinterpret_cast<const char*>(a.gumbel + (size_t)b * a.ld);
+    B.invT = __fdiv_rn(1.0f, load_constant(a.temperature, b / a.N));
+    B.c0 = s * a.cps;
+    B.c1 = min(B.c0 + a.cps, a.chunks);
+    return B;
+}
+
+// Chunk groups j0 and j0 + 1 of this lane (two chunks keep the noise, twice the bytes of
+// the logits, from piling up in registers).
+template <int DT>
+__device__ __forceinline__ void bonus_piece(const LogitsArgs& a, const BonusRow& B, int j0,
+                                            float& best, int32_t& besti) {
+    constexpr int EPC = Elem<DT>::EPC;
+    const int tid = threadIdx.x;
+    u32x4 Z[2];
+    u32x4 g[2][EPC / 4];
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int ch = B.c0 + (j0 + jj) * kThreads + tid;
+        const uint32_t ni = Elem<DT>::kNegInf;
+        Z[jj] = u32x4{ni, ni, ni, ni};
+#pragma unroll
+        for (int h = 0; h < EPC / 4; ++h) g[jj][h] = u32x4{0u, 0u, 0u, 0u};
+        if (ch < B.c1) {
+            Z[jj] = load_chunk(B.zrow, ch);
+#pragma unroll
+            for (int h = 0; h < EPC / 4; ++h) g[jj][h] = load_chunk(B.grow, (int64_t)ch * (EPC / 4) + h);
+            const int nv = a.V - ch * EPC;
+            if (nv < EPC) Z[jj] = mask_tail<DT>(Z[jj], nv);
+        }
+    }
+#pragma unroll
+    for (int jj = 0; jj < 2; ++jj) {
+        const int ch = B.c0 + (j0 + jj) * kThreads + tid;
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+            const float key = fmaf(chunk_elem<DT>(Z[jj], e), B.invT, __uint_as_float(g[jj][e >> 2][e & 3]));
+            const bool win = key > best;
+            best = win ? key : best;
+            besti = win ? ch * EPC + e : besti;
+        }
+    }
+}
+
+// Block argmax of the lanes' (key, index) and its store. (key, index) with the lower index
+// winning ties is a total order, so the result does not depend on the order of the steps.
+__device__ void bonus_finish(const LogitsArgs& a, int64_t b, int s, float best, int32_t besti,
+                             float* red, int32_t* redi) {
+    const int tid = threadIdx.x;
+    row_argmax(best, besti);
+    float k = readlane_f32(best, 0);
+    int32_t i = __builtin_amdgcn_readlane(besti, 0);
+#pragma unroll
+    for (int r = 16; r < 64; r += 16) {
+        const float ok = readlane_f32(best, r);
+        const int32_t oi = __builtin_amdgcn_readlane(besti, r);
+        if (better(ok, oi, k, i)) {
+            k = ok;
+            i = oi;
+        }
+    }
+    const int w = tid >> 6;
+    if ((tid & 63) == 0) {
+        red[w] = k;
+        redi[w] = i;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        for (int t = 1; t < kWaves; ++t)
+            if (better(red[t], redi[t], k, i)) {
+                k = red[t];
+                i = redi[t];
+            }
+        a.bp[b * a.S + s] = BonusPart{k, i};
+    }
+    __syncthreads();   // red / redi are reused by the next call
+}
+
+template <int DT, int CPL>
+__device__ void bonus_slice(const LogitsArgs& a, int64_t b, int s, float* red, int32_t* redi) {
+    const BonusRow B = bonus_row<DT>(a, b, s);
+    float best = -INFINITY;
+    int32_t besti = INT32_MAX;
+#pragma unroll 1
+    for (int j0 = 0; j0 < CPL; j0 += 2) bonus_piece<DT>(a, B, j0, best, besti);
+    bonus_finish(a, b, s, best, besti, red, redi);
 }
 
 // LDS of the TV pass. Each step of a row pair has its own buffer, so one barrier per step
@@ -285,33 +423,41 @@ __device__ void wait_for_slices(const uint64_t* words, int nwords, Ctrl* ctrl,
 struct TvLds {
     float max2[2 * kWaves];          // slice maxima of p and q
     float sum2[2 * kWaves];          // slice sums of p and q
-    float tv[kWaves];                // per-wave |p - q| sums
     uint64_t xch[2 * kMaxTvSlices];  // the row pair's exchange words
 };
 
-// TV on: partials, exchange, and this slice's share of sum |p - q|. Four barriers per row
-// pair: slice max, slice sum, exchange words in LDS, per-wave TV sums.
+// TV on: partials, exchange, and this slice's share of sum |p - q|, one partial per wave.
+// P and Q hold this slice's loads, issued one row pair earlier. Once they are turned into
+// exponentials, the loads of row pair `next` (if >= 0) go into P and Q, so they are in flight
+// during the exchange and phase 2. Three barriers per row pair: slice max, slice sum,
+// exchange words in LDS. LDS reuse by the next row pair is safe without a fourth: each buffer
+// is rewritten only after every wave has passed the barrier that follows its last read.
 template <int DT>
-__device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, TvLds& sh) {
+__device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, int64_t next,
+                              u32x4 (&P)[kTvCPL], u32x4 (&Q)[kTvCPL], TvLds& sh) {
     constexpr int NE = kTvCPL * Elem<DT>::EPC;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const PairLoc L = pair_location<DT>(a, u, s);
-    const float c = kLog2e / a.temperature[L.r];
+    const float c = kLog2e / load_constant(a.temperature, L.r);
     float Ep[NE], Eq[NE];
     float mp, mq, sp, sq;
+    // Raised wave priority until this slice's partials are published: the other slices of
+    // the row pair wait for them, while the work after the exchange delays only this one.
+    __builtin_amdgcn_s_setprio(2);
     {
-        u32x4 P[kTvCPL], Q[kTvCPL];
-        // both rows' loads are in flight before the first wait on either
-        issue_slice<DT, kTvCPL>(P, L.zp, L.c0, L.c1);
-        issue_slice<DT, kTvCPL>(Q, L.zq, L.c0, L.c1);
-        mask_slice_tail<DT, kTvCPL>(P, L.c0, L.c1, a.V);
-        mask_slice_tail<DT, kTvCPL>(Q, L.c0, L.c1, a.V);
+        mask_slice<DT, kTvCPL>(P, L.c0, L.c1, a.V);
+        mask_slice<DT, kTvCPL>(Q, L.c0, L.c1, a.V);
         mp = slice_max<DT, kTvCPL>(P);
         mq = slice_max<DT, kTvCPL>(Q);
         block_reduce2<true>(mp, mq, sh.max2);
         sp = slice_exp<DT, kTvCPL>(P, c, -mp * c, Ep);
         sq = slice_exp<DT, kTvCPL>(Q, c, -mq * c, Eq);
+    }
+    if (next >= 0) {
+        const PairLoc N = pair_location<DT>(a, next, s);
+        issue_slice<kTvCPL>(P, N.zp, N.c0, N.c1);
+        issue_slice<kTvCPL>(Q, N.zq, N.c0, N.c1);
     }
     block_reduce2<false>(sp, sq, sh.sum2);
 
@@ -320,7 +466,12 @@ __device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, TvLds& sh) 
         __hip_atomic_store(words + 2 * s, pack2(mp, sp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
         __hip_atomic_store(words + 2 * s + 1, pack2(mq, sq), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    if (tid < 64) wait_for_slices(words, 2 * a.S, a.ctrl, a.error_flags, sh.xch);
+    __builtin_amdgcn_s_setprio(0);
+    // wave 0 waits for the other slices; the rest of the workgroup waits at the barrier
+    if (tid < 64) {
+        const uint64_t t0 = wall_clock64();
+        while (!poll_slices(words, 2 * a.S, a.ctrl, a.error_flags, sh.xch, t0)) __builtin_amdgcn_s_sleep(1);
+    }
     __syncthreads();
 
     // Every wave combines the S (<= 64) slices itself: lane t holds slice t's target and
@@ -357,114 +508,11 @@ __device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, TvLds& sh) 
             acc1 += fabsf(fmaf(-rho, Ep[e + 1], Eq[e + 1]));
         }
     }
+    // one partial per wave, so no barrier ends the row pair
     const float acc = wave_sum(acc0 + acc1);
-    if (lane == 0) sh.tv[tid >> 6] = acc;
-    __syncthreads();
-    if (tid == 0) {
-        float t = sh.tv[0];
-#pragma unroll
-        for (int i = 1; i < kWaves; ++i) t += sh.tv[i];
-        a.tvp[u * a.S + s] = t * scale;
-    }
+    if (lane == 0) a.tvp[(u * a.S + s) * kWaves + (tid >> 6)] = acc * scale;
 }
 
-// Every lane of each 16-lane row ends with the row's best (key, index), as in row_max.
-__device__ __forceinline__ void argmax_step(float& k, int32_t& i, float ok, int32_t oi) {
-    if (better(ok, oi, k, i)) {
-        k = ok;
-        i = oi;
-    }
-}
-__device__ __forceinline__ void row_argmax(float& k, int32_t& i) {
-    argmax_step(k, i, dpp_f32<kDppXor1>(k), dpp_i32<kDppXor1>(i));
-    argmax_step(k, i, dpp_f32<kDppXor2>(k), dpp_i32<kDppXor2>(i));
-    argmax_step(k, i, dpp_f32<kDppRowHalfMirror>(k), dpp_i32<kDppRowHalfMirror>(i));
-    argmax_step(k, i, dpp_f32<kDppRowMirror>(k), dpp_i32<kDppRowMirror>(i));
-}
-
-template <int DT, int CPL>
-__device__ void bonus_slice(const LogitsArgs& a, int64_t b, int s, float* red, int32_t* redi) {
-    constexpr int EPC = Elem<DT>::EPC;
-    constexpr size_t ESZ = Elem<DT>::ESZ;
-    const int tid = threadIdx.x;
-    const int64_t r = b / a.N;
-    const char* zrow = static_cast<const char*>(a.target) +
-                       (size_t)((b * (a.K + 1) + a.K) * a.ld) * ESZ;
-    const char* grow = reinterpret_cast<const char*>(a.gumbel + (size_t)b * a.ld);
-    const float invT = __fdiv_rn(1.0f, a.temperature[r]);
-    const int c0 = s * a.cps;
-    const int c1 = min(c0 + a.cps, a.chunks);
-
-    float best = -INFINITY;
-    int32_t besti = INT32_MAX;
-    // two chunks at a time keeps the noise (twice the bytes of the logits) from piling up
-    // in registers
-#pragma unroll 1
-    for (int j0 = 0; j0 < CPL; j0 += 2) {
-        u32x4 Z[2];
-        u32x4 g[2][EPC / 4];
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int ch = c0 + (j0 + jj) * kThreads + tid;
-            const uint32_t ni = Elem<DT>::kNegInf;
-            Z[jj] = u32x4{ni, ni, ni, ni};
-#pragma unroll
-            for (int h = 0; h < EPC / 4; ++h) g[jj][h] = u32x4{0u, 0u, 0u, 0u};
-            if (ch < c1) {
-                Z[jj] = load_chunk(zrow, ch);
-#pragma unroll
-                for (int h = 0; h < EPC / 4; ++h) g[jj][h] = load_chunk(grow, (int64_t)ch * (EPC / 4) + h);
-                const int nv = a.V - ch * EPC;
-                if (nv < EPC) Z[jj] = mask_tail<DT>(Z[jj], nv);
-            }
-        }
-#pragma unroll
-        for (int jj = 0; jj < 2; ++jj) {
-            const int ch = c0 + (j0 + jj) * kThreads + tid;
-#pragma unroll
-            for (int e = 0; e < EPC; ++e) {
-                // key = z/T + G, one rounding; -inf for positions outside the slice or >= V
-                const float key = fmaf(chunk_elem<DT>(Z[jj], e), invT, __uint_as_float(g[jj][e >> 2][e & 3]));
-                const bool win = key > best;   // a lane visits its indices in increasing order
-                best = win ? key : best;
-                besti = win ? ch * EPC + e : besti;
-            }
-        }
-    }
-    // block argmax; (key, index) with the lower index winning ties is a total order, so
-    // the result does not depend on the order of the steps
-    row_argmax(best, besti);
-    {
-        float k = readlane_f32(best, 0);
-        int32_t i = __builtin_amdgcn_readlane(besti, 0);
-#pragma unroll
-        for (int r = 16; r < 64; r += 16) {
-            const float ok = readlane_f32(best, r);
-            const int32_t oi = __builtin_amdgcn_readlane(besti, r);
-            if (better(ok, oi, k, i)) {
-                k = ok;
-                i = oi;
-            }
-        }
-        best = k;
-        besti = i;
-    }
-    const int w = tid >> 6;
-    if ((tid & 63) == 0) {
-        red[w] = best;
-        redi[w] = besti;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        for (int t = 1; t < kWaves; ++t)
-            if (better(red[t], redi[t], best, besti)) {
-                best = red[t];
-                besti = redi[t];
-            }
-        a.bp[b * a.S + s] = BonusPart{best, besti};
-    }
-    __syncthreads();   // red / redi are reused by the caller
-}
 
 // TV off: one workgroup per (row, slice).
 template <int DT>
@@ -492,7 +540,14 @@ __global__ __launch_bounds__(kThreads, 4) void k_logits_tv(LogitsArgs a) {
     const int64_t clusters = gridDim.x / (unsigned)a.S;
     const int64_t items = a.pairs + (a.total_wgs - a.pair_wgs) / a.S;
     int64_t it = cluster;
-    for (; it < a.pairs; it += clusters) pair_slice_tv<DT>(a, it, s, sh);
+    u32x4 P[kTvCPL], Q[kTvCPL];
+    if (it < a.pairs) {
+        const PairLoc L0 = pair_location<DT>(a, it, s);
+        issue_slice<kTvCPL>(P, L0.zp, L0.c0, L0.c1);
+        issue_slice<kTvCPL>(Q, L0.zq, L0.c0, L0.c1);
+    }
+    for (; it < a.pairs; it += clusters)
+        pair_slice_tv<DT>(a, it, s, it + clusters < a.pairs ? it + clusters : -1, P, Q, sh);
     for (; it < items; it += clusters) bonus_slice<DT, kTvCPL>(a, it - a.pairs, s, red, redi);
 }
 
