@@ -70,6 +70,11 @@ typedef enum smcsd_resample_mode {
 /* Build limits. */
 #define SMCSD_MAX_N 1024 /* particles per request */
 #define SMCSD_MAX_K 256  /* drafted tokens per particle */
+/* With TV on (tv != NULL), the S slices of a row pair exchange their partials within one
+   wave, so S <= 64 and V is at most 64 slices x 512 lanes x 4 chunks x 8 (bf16) or x 4
+   (fp32) elements. Larger V with TV returns SMCSD_ERR_UNSUPPORTED; without TV any V works. */
+#define SMCSD_MAX_TV_V_BF16 1048576
+#define SMCSD_MAX_TV_V_F32 524288
 
 /*
  * Arguments of smcsd_round. Sizes first, then device pointers.

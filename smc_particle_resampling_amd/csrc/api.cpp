@@ -40,7 +40,7 @@ bool make_plan(int32_t R, int32_t N, int32_t K, int32_t V, int64_t ld, int32_t d
     q.pair_wgs = q.pairs * q.S;
     q.total_wgs = (q.pairs + q.bonus_rows) * q.S;
     if (q.total_wgs >= (int64_t)INT32_MAX) return false;     // grid range
-    if (tv && q.S > kMaxTvSlices) return false;               // V > 524288 (bf16) with TV
+    if (tv && q.S > kMaxTvSlices) return false;               // V > 1048576 (bf16) with TV
     size_t off = 0;
     q.off_ctrl = off;
     off = align256(off + sizeof(Ctrl));

@@ -9,10 +9,10 @@
 // with its precomputed Gumbel noise to the Gumbel-max token (STAND page, method item 2).
 //
 // Work decomposition. A row is cut into 16-byte chunks and the chunks into S slices. One
-// 256-thread workgroup handles one slice of one row pair (target row k, draft row k) or one
-// slice of one bonus row plus its noise row. Each lane loads its CPL chunks of both rows
-// with 16-byte non-temporal loads. Chunks outside the slice and elements >= V are loaded as
-// -inf, which adds nothing to any max, sum, TV or argmax, so the arithmetic has no
+// 512-thread workgroup (8 wave64) handles one slice of one row pair (target row k, draft row
+// k) or one slice of one bonus row plus its noise row. Each lane loads its CPL chunks of both
+// rows with 16-byte non-temporal buffer loads. Chunks outside the slice and elements >= V
+// become -inf, which adds nothing to any max, sum, TV or argmax, so the arithmetic has no
 // per-element branch.
 //   phase 1: slice max m of z, then e = exp2((z - m) * log2e/T) and its sum, for p and q;
 //   phase 2 (TV only): the S workgroups of the row pair swap their (m, sum) partials and
@@ -22,16 +22,17 @@
 //            its e values in fp32 registers from phase 1, so phase 2 costs one fma and one
 //            add per element and no exponential. rho is exactly 1 when the two rows are
 //            equal, and then TV is exactly 0.
-// The finalize kernel combines slices (normalisers, weights, argmax) in fixed order, so every
-// result is deterministic.
+// The finalize kernel combines slices (normalisers, weights, TV, argmax) in fixed order, so
+// every result is deterministic.
 //
 // Launch shapes. Without TV, every (row, slice) is an independent workgroup of an ordinary
 // grid (8 chunks a lane). With TV, the S workgroups of a row pair must be resident together
 // to swap partials, so the pass runs as a persistent cooperative grid
 // (hipLaunchCooperativeKernel guarantees co-residency). It has C clusters of S consecutive
 // workgroups, and each cluster walks the row pairs c, c+C, c+2C, ... in lockstep, then its
-// share of the bonus rows (4 chunks a lane, so the fp32 e values fit in registers). A
-// wall-clock limit bounds every wait. A workgroup that times out raises
+// share of the bonus rows (4 chunks a lane, so the fp32 e values fit in registers). The
+// loads of a cluster's next row pair are issued while the current one is exchanged and
+// finished. A wall-clock limit bounds every wait. A workgroup that times out raises
 // SMCSD_DEVERR_EXCHANGE and an abort flag, every later wait returns at once, and the kernel
 // always drains.
 #include <algorithm>
@@ -442,9 +443,10 @@ __device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, int64_t nex
     const float c = kLog2e / load_constant(a.temperature, L.r);
     float Ep[NE], Eq[NE];
     float mp, mq, sp, sq;
-    // Raised wave priority until this slice's partials are published: the other slices of
-    // the row pair wait for them, while the work after the exchange delays only this one.
-    __builtin_amdgcn_s_setprio(2);
+    // Wave priority: highest until this slice's partials are published (the other slices of
+    // the row pair wait for them), lowest while polling, in between after the exchange (that
+    // work delays only this slice's next publish).
+    __builtin_amdgcn_s_setprio(3);
     {
         mask_slice<DT, kTvCPL>(P, L.c0, L.c1, a.V);
         mask_slice<DT, kTvCPL>(Q, L.c0, L.c1, a.V);
@@ -473,6 +475,7 @@ __device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, int64_t nex
         while (!poll_slices(words, 2 * a.S, a.ctrl, a.error_flags, sh.xch, t0)) __builtin_amdgcn_s_sleep(1);
     }
     __syncthreads();
+    __builtin_amdgcn_s_setprio(1);
 
     // Every wave combines the S (<= 64) slices itself: lane t holds slice t's target and
     // draft words, and whole-wave reductions (fixed order) give the row maxima and sums.

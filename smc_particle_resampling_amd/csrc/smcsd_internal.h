@@ -11,7 +11,7 @@
 
 namespace smcsd {
 
-constexpr int kThreads = 256;        // workgroup size of every kernel (4 wave64)
+constexpr int kThreads = 512;        // workgroup size of the round's kernels (8 wave64)
 constexpr int kWaves = kThreads / 64;
 constexpr int kStreamCPL = 8;        // 16-byte chunks a lane holds per row of a slice, TV off
 constexpr int kTvCPL = 4;            // ... TV on (its fp32 exponentials stay in registers)

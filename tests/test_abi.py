@@ -100,10 +100,10 @@ def test_round_validation_ess_and_pages():
     assert _round(_args(page_table_in=pt, page_table_out=pt + 64, P=4, num_pages=10)) == S.ERR_ARG
     assert _round(_args(page_table_in=pt, page_table_out=None, P=4, num_pages=10)) == S.ERR_ARG
     assert _round(_args(page_table_in=pt, page_table_out=pt + (1 << 20), P=0, num_pages=10)) == S.ERR_ARG
-    # TV: at most 64 slices of 256 lanes x 4 chunks (V <= 524288 bf16, 262144 f32)
-    assert _round(_args(V=524288 + 8, ld=524288 + 8)) == S.ERR_UNSUPPORTED
-    assert _round(_args(V=524288 + 8, ld=524288 + 8, tv=None, workspace_bytes=100)) == S.ERR_WORKSPACE
-    assert _round(_args(dtype=S.F32, V=262144 + 4, ld=262144 + 4)) == S.ERR_UNSUPPORTED
+    # TV: at most 64 slices of 512 lanes x 4 chunks (V <= 1048576 bf16, 524288 f32)
+    assert _round(_args(V=1048576 + 8, ld=1048576 + 8)) == S.ERR_UNSUPPORTED
+    assert _round(_args(V=1048576 + 8, ld=1048576 + 8, tv=None, workspace_bytes=100)) == S.ERR_WORKSPACE
+    assert _round(_args(dtype=S.F32, V=524288 + 4, ld=524288 + 4)) == S.ERR_UNSUPPORTED
     # fp32 rows need ld % 4 == 0 only
     assert _round(_args(dtype=S.F32, ld=1004, workspace_bytes=100)) == S.ERR_WORKSPACE
 

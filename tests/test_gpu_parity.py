@@ -76,7 +76,8 @@ def test_scaled_workloads(w, dev):
                                         (9, "bf16", True), (33, "f32", False),
                                         (5001, "bf16", True), (16385, "bf16", True),
                                         (16384 * 3 + 8, "bf16", True), (8191, "f32", True),
-                                        (524288, "bf16", True), (524281, "bf16", True), (262144, "f32", True)])
+                                        (524288, "bf16", True), (524281, "bf16", True), (262144, "f32", True),
+                                        (1048576, "bf16", True), (1048569, "bf16", True), (524288, "f32", True)])
 def test_ragged_and_tiny_vocabularies(V, dtype, tv, dev):
     w = W["r16-n16-k4-v128256-bf16"].scaled(name="ragged", R=2, N=8, K=3, V=V, dtype=dtype,
                                             tv=tv, ctx=128)
