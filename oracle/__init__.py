@@ -61,7 +61,7 @@ def lib() -> ctypes.CDLL:
             L.orc_remap_request.argtypes = [i32, i32, p, p, p, p, i32]
             L.orc_round.restype = i32
             L.orc_round.argtypes = [i32, i32, i32, i64, i64, i32, p, p, p, p, p, p, i32, f32, p,
-                                    p, p, p, p, p, p, p, p, p, i32, i32, p, p, p, p, p]
+                                    p, p, p, p, p, p, p, p, p, i32, i32, p, p, p, p, p, p]
             L.orc_num_threads.restype = i32
             L.orc_num_threads.argtypes = []
             _lib = L
@@ -144,7 +144,8 @@ def round(inputs: dict, *, V: int | None = None, mode="always", ess_frac: float 
     ``inputs`` holds numpy arrays: target [R,N,K+1,ld], draft [R,N,K,ld] (float32 or bf16
     bits as uint16), tokens [R,N,K] int32, temperature [R], gumbel [R,N,ld], uniform [R],
     log_weights [R,N] float32 and optionally page_table [R,N,P] int32 + refcount
-    [num_pages] int32. ``V`` defaults to ld.
+    [num_pages] int32, and optionally log_potential [R,N] float32 (log phi added to each
+    particle's incremental log weight). ``V`` defaults to ld.
     """
     tgt, dt = _logits(inputs["target"])
     dft, dt2 = _logits(inputs["draft"])
@@ -162,6 +163,10 @@ def round(inputs: dict, *, V: int | None = None, mode="always", ess_frac: float 
     lwin = np.ascontiguousarray(inputs["log_weights"], dtype=np.float32)
     assert tok.shape == (R, N, K) and temp.shape == (R,) and gum.shape == (R, N, ld)
     assert uni.shape == (R,) and lwin.shape == (R, N)
+    lpot = inputs.get("log_potential")
+    if lpot is not None:
+        lpot = np.ascontiguousarray(lpot, dtype=np.float32)
+        assert lpot.shape == (R, N)
     out = dict(
         log_w_incr=np.zeros((R, N)), log_weights=np.zeros((R, N)), log_norm=np.zeros(R),
         ess=np.zeros(R), resampled=np.zeros(R, np.int32), ancestors=np.zeros((R, N), np.int32),
@@ -184,7 +189,7 @@ def round(inputs: dict, *, V: int | None = None, mode="always", ess_frac: float 
                          _ptr(out["ess"]), _ptr(out["resampled"]), _ptr(out["ancestors"]),
                          _ptr(out["bonus"]), _ptr(out["out_tokens"]), _ptr(out["tv"]),
                          P, num_pages, _ptr(pt), _ptr(pt_out), _ptr(rc), _ptr(out["anc_gap"]),
-                         _ptr(out["bonus_gap"]))
+                         _ptr(out["bonus_gap"]), _ptr(lpot))
     out["status"] = int(st)
     out["page_table"] = pt_out
     out["refcount"] = rc

@@ -34,6 +34,10 @@
  *      lowest index on ties -- the precision the GPU kernel decides in.
  *   R8 page table: [N][P] int32 per request, negative = unused; a refcount counts table
  *      entries that reference a page.
+ *   R9 potential (optional): the SMC-SD page's section 5 names constrained generation and
+ *      reward-weighted decoding as targets the same machinery can sample. Reading: the
+ *      target becomes p times a potential phi, so particle i's incremental log weight gains
+ *      log phi_i (given per particle and round; -inf removes the particle).
  * Summation order: over v ascending within a row, over k ascending, over i ascending.
  */
 #include <math.h>
@@ -255,7 +259,8 @@ int32_t orc_remap_request(int32_t N, int32_t P, const int32_t *anc, const int32_
  *   logw_in [R][N] fp32 (normalised), page tables [R][N][P] int32, refcount [num_pages].
  * Outputs in double where the value is real: lw [R][N], logw_out [R][N], log_norm [R],
  * ess [R], tv [R][N][K] (NULL skips TV), anc_gap [R][N], bonus_gap [R][N]; int32 elsewhere.
- * out_tokens [R][N][K+1] may be NULL; pt_in == NULL skips the remap.
+ * out_tokens [R][N][K+1] may be NULL; pt_in == NULL skips the remap. log_potential [R][N]
+ * (R9) may be NULL.
  * Returns 0, or a negative code on an out-of-range token (-1) or remap error (-2).
  */
 int32_t orc_round(int32_t R, int32_t N, int32_t K, int64_t V, int64_t ld, int32_t dtype,
@@ -265,7 +270,8 @@ int32_t orc_round(int32_t R, int32_t N, int32_t K, int64_t V, int64_t ld, int32_
                   double *lw, double *logw_out, double *log_norm, double *ess,
                   int32_t *resampled, int32_t *anc, int32_t *bonus, int32_t *out_tokens,
                   double *tv, int32_t P, int32_t num_pages, const int32_t *pt_in,
-                  int32_t *pt_out, int32_t *refcount, double *anc_gap, double *bonus_gap)
+                  int32_t *pt_out, int32_t *refcount, double *anc_gap, double *bonus_gap,
+                  const float *log_potential)
 {
     const size_t es = esize(dtype);
     const int64_t rows = (int64_t)R * N * K;
@@ -311,6 +317,8 @@ int32_t orc_round(int32_t R, int32_t N, int32_t K, int64_t V, int64_t ld, int32_
             double s = 0.0;
             for (int32_t k = 0; k < K; ++k)
                 s += d[((size_t)r * N + i) * K + k];
+            if (log_potential)
+                s += (double)log_potential[(size_t)r * N + i];
             lw[(size_t)r * N + i] = s;
             prev[i] = (double)logw_in[(size_t)r * N + i];
         }
