@@ -132,6 +132,12 @@ typedef struct smcsd_round_args {
 
     smcsd_event timing_begin;    /* optional: recorded on `stream` right before and after */
     smcsd_event timing_end;      /* the logits-pass kernel (for roofline timing) */
+
+    const float *log_potential;  /* optional [R][N]: log phi_i, added to particle i's
+                                    incremental log weight (the tilted target p*phi of
+                                    constrained or reward-weighted decoding, SMC-SD page,
+                                    section 5). -inf removes a particle; at least one particle
+                                    per request must stay finite. NULL = phi = 1. */
 } smcsd_round_args;
 
 /*
@@ -140,6 +146,7 @@ typedef struct smcsd_round_args {
  * Per request r, particle i, position k < K, with a = target/T_r and b = draft/T_r:
  *   A_ik = LSE_v a[k,v],  B_ik = LSE_v b[k,v]                 (log-softmax normalisers)
  *   log_w_incr_i = sum_k (a[k,x_k] - A_ik) - (b[k,x_k] - B_ik) (importance weight p/q)
+ *                  + log_potential_i                         (if given)
  *   tv_ik = 1/2 sum_v |exp(a[k,v]-A_ik) - exp(b[k,v]-B_ik)|    (METASD block divergence)
  *   bonus_i = argmax_v fl32(fma(target[K,v], fl32(1/T_r), gumbel[v])), lowest v on ties
  *   l_i = log_weights_i + log_w_incr_i, logZ = LSE_i l_i, W_i = exp(l_i - logZ),

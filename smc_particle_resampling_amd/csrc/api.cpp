@@ -178,6 +178,7 @@ smcsd_status smcsd_round(const smcsd_round_args* args, smcsd_stream stream) {
     fa.tvp = plan.tv ? la.tvp : nullptr;
     fa.bp = la.bp;
     fa.terms = reinterpret_cast<double*>(ws + plan.off_terms);
+    fa.log_potential = a.log_potential;
     fa.log_w_incr = a.log_w_incr;
     fa.log_weights = a.log_weights;
     fa.uniform = a.uniform;

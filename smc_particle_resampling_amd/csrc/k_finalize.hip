@@ -92,6 +92,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
             const int64_t ri = r * N + i;
             double lw = 0.0;
             for (int32_t k = 0; k < K; ++k) lw += a.terms[ri * K + k];   // k in order
+            if (a.log_potential) lw += (double)a.log_potential[ri];
             a.log_w_incr[ri] = (float)lw;
             s_l[i] = (double)a.log_weights[ri] + lw;
         }

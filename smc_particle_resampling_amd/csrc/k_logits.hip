@@ -483,9 +483,20 @@ __device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, int64_t nex
     const uint64_t kNone = pack2(-INFINITY, 0.0f);
     const uint64_t wp = lane < a.S ? sh.xch[2 * lane] : kNone;
     const uint64_t wq = lane < a.S ? sh.xch[2 * lane + 1] : kNone;
-    const float Mp = wave_max(word_lo(wp)), Mq = wave_max(word_lo(wq));
-    const float Sp = wave_sum(word_hi(wp) * __builtin_amdgcn_exp2f((word_lo(wp) - Mp) * c));
-    const float Sq = wave_sum(word_hi(wq) * __builtin_amdgcn_exp2f((word_lo(wq) - Mq) * c));
+    float Mp, Mq, Sp, Sq;
+    if (a.S <= 16) {
+        // all slices sit in the first 16-lane row; the other rows hold (-inf, 0), so the
+        // whole-wave result is the first row's result exactly
+        Mp = readlane_f32(row_max(word_lo(wp)), 0);
+        Mq = readlane_f32(row_max(word_lo(wq)), 0);
+        Sp = readlane_f32(row_sum(word_hi(wp) * __builtin_amdgcn_exp2f((word_lo(wp) - Mp) * c)), 0);
+        Sq = readlane_f32(row_sum(word_hi(wq) * __builtin_amdgcn_exp2f((word_lo(wq) - Mq) * c)), 0);
+    } else {
+        Mp = wave_max(word_lo(wp));
+        Mq = wave_max(word_lo(wq));
+        Sp = wave_sum(word_hi(wp) * __builtin_amdgcn_exp2f((word_lo(wp) - Mp) * c));
+        Sq = wave_sum(word_hi(wq) * __builtin_amdgcn_exp2f((word_lo(wq) - Mq) * c));
+    }
     // p = e_p f_p / S_p and q = e_q f_q / S_q with f = exp2((m_slice - M_row) c). Factor out
     // the larger of f_p / S_p and f_q / S_q, so the ratio stays finite even when the other
     // factor underflows (a slice far below its row's max). Equal rows take the first branch

@@ -85,6 +85,7 @@ struct FinalizeArgs {
     const BonusPart* bp;
     double* terms;            // [R][N][K] per-position log-ratios (workspace)
     // weights
+    const float* log_potential;  // optional [R][N], added to the increment (from partials)
     float* log_w_incr;        // out (from partials) or in
     float* log_weights;       // in/out
     const float* uniform;

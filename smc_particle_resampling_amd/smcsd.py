@@ -39,7 +39,7 @@ class RoundArgs(ctypes.Structure):
         ("log_norm", _p), ("ess", _p), ("resampled", _p), ("ancestors", _p), ("bonus", _p),
         ("out_tokens", _p), ("tv", _p), ("page_table_in", _p), ("page_table_out", _p),
         ("refcount", _p), ("error_flags", _p), ("workspace", _p), ("workspace_bytes", _sz),
-        ("timing_begin", _p), ("timing_end", _p),
+        ("timing_begin", _p), ("timing_end", _p), ("log_potential", _p),
     ]
 
 
@@ -117,8 +117,8 @@ def _stream(device, stream):
 def smcsd_round(*, target_logits, draft_logits, draft_tokens, temperature, gumbel, uniform,
                 log_weights, log_w_incr, log_norm, ess, resampled, ancestors, bonus,
                 workspace, out_tokens=None, tv=None, page_table_in=None, page_table_out=None,
-                refcount=None, error_flags=None, V: int | None = None, mode="always",
-                ess_frac: float = 0.5, timing_events=None, stream=None) -> None:
+                refcount=None, error_flags=None, log_potential=None, V: int | None = None,
+                mode="always", ess_frac: float = 0.5, timing_events=None, stream=None) -> None:
     """Enqueue one SMC-SD round (smcsd_round). Shapes: target [R,N,K+1,ld], draft
     [R,N,K,ld] (both float32 or bfloat16), draft_tokens [R,N,K] int32, temperature [R],
     gumbel [R,N,ld], uniform [R], per-request/per-particle outputs as in include/smcsd.h."""
@@ -158,6 +158,8 @@ def smcsd_round(*, target_logits, draft_logits, draft_tokens, temperature, gumbe
         num_pages = refcount.numel()
     if error_flags is not None:
         _check(error_flags, "error_flags", i32, None, dev)
+    if log_potential is not None:
+        _check(log_potential, "log_potential", f32, (R, N), dev)
     a = RoundArgs()
     a.R, a.N, a.K, a.V, a.ld = R, N, K, V, ld
     a.dtype = BF16 if target_logits.dtype == torch.bfloat16 else F32
@@ -172,6 +174,7 @@ def smcsd_round(*, target_logits, draft_logits, draft_tokens, temperature, gumbe
     a.out_tokens, a.tv = _ptr(out_tokens), _ptr(tv)
     a.page_table_in, a.page_table_out = _ptr(page_table_in), _ptr(page_table_out)
     a.refcount, a.error_flags = _ptr(refcount), _ptr(error_flags)
+    a.log_potential = _ptr(log_potential)
     a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
     if timing_events is not None:
         a.timing_begin, a.timing_end = timing_events
@@ -276,7 +279,8 @@ def run_round(inputs: dict, *, mode="always", ess_frac=0.5, tv=False, pages=True
                 out_tokens=out.get("out_tokens"), tv=out.get("tv"), page_table_in=pt_in,
                 page_table_out=out.get("page_table_out") if pt_in is not None else None,
                 refcount=inputs.get("refcount") if pt_in is not None else None,
-                error_flags=out["error_flags"], workspace=out["workspace"], V=inputs["V"],
+                error_flags=out["error_flags"], workspace=out["workspace"],
+                log_potential=inputs.get("log_potential"), V=inputs["V"],
                 mode=mode, ess_frac=ess_frac, timing_events=timing_events, stream=stream)
     return out
 

@@ -33,7 +33,7 @@ import math
 import torch
 
 STREAMS = dict(target=1, peaks=2, draft=3, tokens=4, gumbel=5, uniform=6, temp=7, pages=8,
-               ragged=9, zipf_q=10)
+               ragged=9, zipf_q=10, potential=11)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -140,6 +140,16 @@ def _rows_normal(n_rows, w, g_main, g_peaks, device):
         boost.scatter_(1, idx, w.peak_boost)
         z = z + boost
     return z
+
+
+def make_log_potential(R: int, N: int, seed: int, device="cpu", p_removed: float = 0.1):
+    """Per-particle log potentials [R, N] float32: N(0, 1), with a fraction of particles
+    removed (-inf), always keeping at least one finite particle per request."""
+    g = _gen(seed, "potential", device)
+    lp = torch.randn((R, N), generator=g, device=device, dtype=torch.float32)
+    removed = torch.rand((R, N), generator=g, device=device) < p_removed
+    removed[:, 0] = False
+    return lp.masked_fill(removed, float("-inf"))
 
 
 def make_page_table(R: int, N: int, P: int, seed: int, ragged: bool = False):
@@ -252,6 +262,8 @@ def to_host(inputs: dict, requests=None) -> dict:
 
     out = {k: host(inputs[k]) for k in ("target", "draft", "tokens", "temperature", "gumbel",
                                          "uniform", "log_weights")}
+    if inputs.get("log_potential") is not None:
+        out["log_potential"] = host(inputs["log_potential"])
     if "page_table" in inputs:
         out["page_table"] = host(inputs["page_table"])
         out["refcount"] = host(inputs["refcount"], per_request=False)

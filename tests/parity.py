@@ -40,7 +40,11 @@ def _close(name, got, ref, rel, abs_=0.0, floor=False):
     got = np.asarray(got, np.float64)
     ref = np.asarray(ref, np.float64)
     scale = np.maximum(1.0, np.abs(ref)) if floor else np.abs(ref)
-    bad = np.abs(got - ref) > rel * scale + abs_
+    with np.errstate(invalid="ignore"):
+        bad = np.abs(got - ref) > rel * scale + abs_
+    # infinities (a particle removed by its potential) must match exactly, NaN nowhere
+    bad |= (np.isinf(got) | np.isinf(ref)) & (got != ref)
+    bad |= np.isnan(got) | np.isnan(ref)
     if np.any(bad):
         idx = np.argwhere(bad)[:5]
         raise AssertionError("%s: %d mismatches, first %s: got %s ref %s" % (

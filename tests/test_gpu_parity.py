@@ -84,6 +84,23 @@ def test_ragged_and_tiny_vocabularies(V, dtype, tv, dev):
     run_and_compare(w, dev, seed=2, ragged=True)
 
 
+@pytest.mark.parametrize("mode,tv", [("always", True), ("never", False), ("ess", True)])
+def test_log_potential(mode, tv, dev):
+    """Optional per-particle log potential (tilted target p*phi), with removed particles."""
+    w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="potential", R=3, V=20000, ctx=128,
+                                                mode=mode, tv=tv)
+
+    def add(inp):
+        inp["log_potential"] = synth.make_log_potential(w.R, w.N, 7, dev)
+
+    inp, out, ora, gpu = run_and_compare(w, dev, seed=9, modify=add)
+    removed = torch.isinf(inp["log_potential"]).cpu().numpy()
+    assert removed.any()
+    if mode == "always":
+        dead = [set(np.nonzero(removed[r])[0]) for r in range(w.R)]
+        assert all(not (set(gpu["ancestors"][r].tolist()) & dead[r]) for r in range(w.R))
+
+
 @pytest.mark.parametrize("N,K", [(1, 1), (1, 4), (3, 1), (1024, 2), (40, 17)])
 def test_particle_and_position_extremes(N, K, dev):
     w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="extreme", R=2, N=N, K=K, V=3000, ctx=64)
