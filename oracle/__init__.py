@@ -62,6 +62,9 @@ def lib() -> ctypes.CDLL:
             L.orc_round.restype = i32
             L.orc_round.argtypes = [i32, i32, i32, i64, i64, i32, p, p, p, p, p, p, i32, f32, p,
                                     p, p, p, p, p, p, p, p, p, i32, i32, p, p, p, p, p, p]
+            L.orc_sd_verify.restype = None
+            L.orc_sd_verify.argtypes = [i32, i32, i32, i64, i64, i32, p, p, p, p, p, p, p, p,
+                                        p, p, p]
             L.orc_num_threads.restype = i32
             L.orc_num_threads.argtypes = []
             _lib = L
@@ -193,4 +196,30 @@ def round(inputs: dict, *, V: int | None = None, mode="always", ess_frac: float 
     out["status"] = int(st)
     out["page_table"] = pt_out
     out["refcount"] = rc
+    return out
+
+
+def sd_verify(inputs: dict, *, V: int | None = None) -> dict:
+    """Standard speculative-decoding verification of every particle's drafted tokens.
+
+    ``inputs`` as for ``round`` plus accept_uniform [R,N,K] and residual_uniform [R,N]
+    float32. Returns n_accepted [R,N], next_token [R,N] (int32) and the decision gaps
+    acc_gap, res_gap [R,N] (float64).
+    """
+    tgt, dt = _logits(inputs["target"])
+    dft, _ = _logits(inputs["draft"])
+    R, N, K1, ld = tgt.shape
+    K = K1 - 1
+    V = ld if V is None else int(V)
+    tok = np.ascontiguousarray(inputs["tokens"], dtype=np.int32)
+    temp = np.ascontiguousarray(inputs["temperature"], dtype=np.float32)
+    gum = np.ascontiguousarray(inputs["gumbel"], dtype=np.float32)
+    au = np.ascontiguousarray(inputs["accept_uniform"], dtype=np.float32)
+    bu = np.ascontiguousarray(inputs["residual_uniform"], dtype=np.float32)
+    assert au.shape == (R, N, K) and bu.shape == (R, N)
+    out = dict(n_accepted=np.zeros((R, N), np.int32), next_token=np.zeros((R, N), np.int32),
+               acc_gap=np.zeros((R, N)), res_gap=np.zeros((R, N)))
+    lib().orc_sd_verify(R, N, K, V, ld, dt, _ptr(tgt), _ptr(dft), _ptr(tok), _ptr(temp),
+                        _ptr(gum), _ptr(au), _ptr(bu), _ptr(out["n_accepted"]),
+                        _ptr(out["next_token"]), _ptr(out["acc_gap"]), _ptr(out["res_gap"]))
     return out

@@ -347,6 +347,102 @@ int32_t orc_round(int32_t R, int32_t N, int32_t K, int64_t V, int64_t ld, int32_
     return err;
 }
 
+/*
+ * Standard speculative-decoding verification of one particle's K drafted tokens, the
+ * baseline the SMC-SD page compares against (section 1: the target verifies the draft, the
+ * first rejection discards every later draft token). The pages give no formulas; this is
+ * standard speculative sampling written from its definition (readings S1-S3):
+ *   S1 positions k = 0..K-1 in order; x_k is accepted iff acc_u[k] < min(1, p_k(x_k)/q_k(x_k)),
+ *      and the first rejection ends the block;
+ *   S2 at the first rejection k*, the next token is drawn from the residual
+ *      r(v) = max(p_k*(v) - q_k*(v), 0) / sum_w max(p_k*(w) - q_k*(w), 0) by inverse CDF over
+ *      increasing v with one uniform b: the first v whose inclusive prefix sum of the
+ *      unnormalised residual exceeds b * sum r (clamped to the last v with r > 0);
+ *   S3 if all K tokens are accepted, the next token is the bonus draw from p_K (the Gumbel-max
+ *      of the round, reading R7).
+ * p and q are temperature-scaled softmaxes as in the round (R2). Outputs: *n_acc in 0..K and
+ * *next the token that follows the accepted ones. *acc_gap = min over the examined positions
+ * of |acc_u[k] - min(1, p/q)|; *res_gap = min over v of |b sum r - C_v| / sum r (1 if no
+ * residual was drawn) -- distances of the decisions from their boundaries.
+ */
+static void sd_verify_particle(int32_t K, int64_t V, int64_t ld, int32_t dtype,
+                               const char *tgt, const char *dft, const int32_t *tok, float Tf,
+                               const float *gumbel, const float *acc_u, float res_u,
+                               int32_t *n_acc, int32_t *next, double *acc_gap, double *res_gap)
+{
+    const size_t es = esize(dtype);
+    const double T = (double)Tf;
+    double agap = INFINITY;
+    *res_gap = 1.0;
+    for (int32_t k = 0; k < K; ++k) {
+        const char *zp = tgt + (size_t)k * (size_t)ld * es;
+        const char *zq = dft + (size_t)k * (size_t)ld * es;
+        double A = orc_row_logsumexp(zp, dtype, V, T);
+        double B = orc_row_logsumexp(zq, dtype, V, T);
+        int32_t x = tok[k];
+        double ratio = exp((elem(zp, dtype, x) / T - A) - (elem(zq, dtype, x) / T - B));
+        double m = ratio < 1.0 ? ratio : 1.0;
+        double d = fabs((double)acc_u[k] - m);
+        if (d < agap)
+            agap = d;
+        if ((double)acc_u[k] < m)
+            continue;
+        /* first rejection: residual draw */
+        double R = 0.0;
+        for (int64_t v = 0; v < V; ++v) {
+            double r = exp(elem(zp, dtype, v) / T - A) - exp(elem(zq, dtype, v) / T - B);
+            if (r > 0.0)
+                R += r;
+        }
+        double target = (double)res_u * R;
+        double C = 0.0, rg = INFINITY;
+        int32_t pick = -1, last = 0;
+        for (int64_t v = 0; v < V; ++v) {
+            double r = exp(elem(zp, dtype, v) / T - A) - exp(elem(zq, dtype, v) / T - B);
+            if (r <= 0.0)
+                continue;
+            C += r;
+            last = (int32_t)v;
+            double g = fabs(target - C);
+            if (g < rg)
+                rg = g;
+            if (pick < 0 && target < C)
+                pick = (int32_t)v;
+        }
+        *n_acc = k;
+        *next = pick >= 0 ? pick : last;
+        *acc_gap = agap;
+        *res_gap = R > 0.0 ? rg / R : 0.0;
+        return;
+    }
+    *n_acc = K;
+    *next = orc_row_gumbel_argmax(tgt + (size_t)K * (size_t)ld * es, dtype, gumbel, V, Tf, NULL);
+    *acc_gap = agap;
+}
+
+/*
+ * sd_verify_particle over a batch: R requests x N particles, each an independent sequence.
+ * Layouts as in orc_round; acc_u [R][N][K], res_u [R][N]; outputs [R][N].
+ */
+void orc_sd_verify(int32_t R, int32_t N, int32_t K, int64_t V, int64_t ld, int32_t dtype,
+                   const void *target, const void *draft, const int32_t *tokens,
+                   const float *temperature, const float *gumbel, const float *acc_u,
+                   const float *res_u, int32_t *n_acc, int32_t *next, double *acc_gap,
+                   double *res_gap)
+{
+    const size_t es = esize(dtype);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t ri = 0; ri < (int64_t)R * N; ++ri) {
+        int64_t r = ri / N;
+        sd_verify_particle(K, V, ld, dtype,
+                           (const char *)target + (size_t)(ri * (K + 1)) * (size_t)ld * es,
+                           (const char *)draft + (size_t)(ri * K) * (size_t)ld * es,
+                           tokens + (size_t)ri * K, temperature[r], gumbel + (size_t)ri * ld,
+                           acc_u + (size_t)ri * K, res_u[ri], &n_acc[ri], &next[ri],
+                           &acc_gap[ri], &res_gap[ri]);
+    }
+}
+
 /* Threads OpenMP would use for the parallel loops above (1 when built without OpenMP). */
 int32_t orc_num_threads(void)
 {
