@@ -197,6 +197,58 @@ const char *smcsd_status_string(smcsd_status status);
 /* sizeof(smcsd_round_args) as compiled into the library (for bindings to check layout). */
 size_t smcsd_round_args_size(void);
 
+/*
+ * Standard speculative-decoding verification of drafted blocks, on the same logits layout as
+ * smcsd_round. It is the baseline the SMC-SD page compares against ("Faster LLM Inference via
+ * Sequential Monte Carlo", section 1: the target verifies the draft, and the first rejection
+ * discards the rest of the block), run here on every particle as an independent sequence.
+ * Per request r, particle i (p_k, q_k the temperature-scaled softmaxes of row k):
+ *   x_k is accepted iff accept_uniform[k] < min(1, p_k(x_k) / q_k(x_k)), for k = 0, 1, ...
+ *   until the first rejection k*;
+ *   n_accepted_i = k* (or K if all are accepted);
+ *   next_token_i = the residual draw at k*: the first v (increasing) whose inclusive prefix
+ *   sum of max(p_k* - q_k*, 0) exceeds residual_uniform * sum_v max(p_k* - q_k*, 0);
+ *   or, if all K are accepted, the bonus argmax_v fl32(fma(target[K,v], fl32(1/T), gumbel[v])).
+ * The residual mass is the position's TV, so the pass is the TV pass of smcsd_round plus a
+ * short kernel that scans one slice of the rejected row per particle.
+ * Decisions are taken on f32 logits with f64 per-particle arithmetic; a residual draw whose
+ * uniform lies within ~1e-4 of the residual mass from a cumulative-sum boundary may pick the
+ * neighbouring token. Sizes, layouts, alignment and limits as for smcsd_round with TV on.
+ */
+typedef struct smcsd_verify_args {
+    int32_t R, N, K, V;          /* as smcsd_round_args */
+    int64_t ld;
+    int32_t dtype;
+    int32_t reserved0;           /* must be 0 */
+
+    const void *target_logits;   /* [R][N][K+1][ld] */
+    const void *draft_logits;    /* [R][N][K][ld] */
+    const int32_t *draft_tokens; /* [R][N][K] */
+    const float *temperature;    /* [R] */
+    const float *gumbel;         /* [R][N][ld] bonus noise (used when a block is accepted) */
+    const float *accept_uniform; /* [R][N][K] in [0,1) */
+    const float *residual_uniform; /* [R][N] in [0,1) */
+
+    int32_t *n_accepted;         /* [R][N] out: accepted drafted tokens, 0..K */
+    int32_t *next_token;         /* [R][N] out: the token after the accepted ones */
+    float *tv;                   /* [R][N][K] out, optional (NULL): TV(p_k, q_k) */
+    int32_t *error_flags;        /* optional device int32, SMCSD_DEVERR_* bits OR-ed in */
+
+    void *workspace;             /* >= smcsd_verify_workspace_size() bytes, 256-byte aligned */
+    size_t workspace_bytes;
+
+    smcsd_event timing_begin;    /* optional, around the logits pass as in smcsd_round */
+    smcsd_event timing_end;
+} smcsd_verify_args;
+
+smcsd_status smcsd_sd_verify(const smcsd_verify_args *args, smcsd_stream stream);
+
+/* Workspace bytes smcsd_sd_verify needs for these sizes (0 if the sizes are invalid). */
+size_t smcsd_verify_workspace_size(int32_t R, int32_t N, int32_t K, int32_t V, int32_t dtype);
+
+/* sizeof(smcsd_verify_args) as compiled into the library. */
+size_t smcsd_verify_args_size(void);
+
 #ifdef __cplusplus
 }
 #endif

@@ -64,7 +64,7 @@ def lib() -> ctypes.CDLL:
                                     p, p, p, p, p, p, p, p, p, i32, i32, p, p, p, p, p, p]
             L.orc_sd_verify.restype = None
             L.orc_sd_verify.argtypes = [i32, i32, i32, i64, i64, i32, p, p, p, p, p, p, p, p,
-                                        p, p, p]
+                                        p, p, p, p]
             L.orc_num_threads.restype = i32
             L.orc_num_threads.argtypes = []
             _lib = L
@@ -203,8 +203,11 @@ def sd_verify(inputs: dict, *, V: int | None = None) -> dict:
     """Standard speculative-decoding verification of every particle's drafted tokens.
 
     ``inputs`` as for ``round`` plus accept_uniform [R,N,K] and residual_uniform [R,N]
-    float32. Returns n_accepted [R,N], next_token [R,N] (int32) and the decision gaps
-    acc_gap, res_gap [R,N] (float64).
+    float32. Returns n_accepted [R,N], next_token [R,N] (int32), acc_gap [R,N] (distance
+    of the acceptance uniforms from min(1, p/q)), and for residual draws res_lo / res_hi
+    [R,N] (distances of the target from the chosen token's cumulative-sum boundaries, as
+    fractions of the residual mass) with res_below / res_above [R,N] (the neighbouring
+    tokens with positive residual, -1 if none).
     """
     tgt, dt = _logits(inputs["target"])
     dft, _ = _logits(inputs["draft"])
@@ -218,8 +221,13 @@ def sd_verify(inputs: dict, *, V: int | None = None) -> dict:
     bu = np.ascontiguousarray(inputs["residual_uniform"], dtype=np.float32)
     assert au.shape == (R, N, K) and bu.shape == (R, N)
     out = dict(n_accepted=np.zeros((R, N), np.int32), next_token=np.zeros((R, N), np.int32),
-               acc_gap=np.zeros((R, N)), res_gap=np.zeros((R, N)))
+               acc_gap=np.zeros((R, N)))
+    res = np.zeros((R, N, 2))
+    nb = np.zeros((R, N, 2), np.int32)
     lib().orc_sd_verify(R, N, K, V, ld, dt, _ptr(tgt), _ptr(dft), _ptr(tok), _ptr(temp),
                         _ptr(gum), _ptr(au), _ptr(bu), _ptr(out["n_accepted"]),
-                        _ptr(out["next_token"]), _ptr(out["acc_gap"]), _ptr(out["res_gap"]))
+                        _ptr(out["next_token"]), _ptr(out["acc_gap"]), _ptr(res), _ptr(nb))
+    out["res_lo"], out["res_hi"] = res[..., 0], res[..., 1]
+    out["res_below"], out["res_above"] = nb[..., 0], nb[..., 1]
+    out["res_gap"] = np.minimum(out["res_lo"], out["res_hi"])
     return out

@@ -362,18 +362,22 @@ int32_t orc_round(int32_t R, int32_t N, int32_t K, int64_t V, int64_t ld, int32_
  *      of the round, reading R7).
  * p and q are temperature-scaled softmaxes as in the round (R2). Outputs: *n_acc in 0..K and
  * *next the token that follows the accepted ones. *acc_gap = min over the examined positions
- * of |acc_u[k] - min(1, p/q)|; *res_gap = min over v of |b sum r - C_v| / sum r (1 if no
- * residual was drawn) -- distances of the decisions from their boundaries.
+ * of |acc_u[k] - min(1, p/q)|. For a residual draw with target t = b sum r landing in
+ * (C_lo, C_hi] of the chosen token: res[0] = (t - C_lo) / sum r and res[1] = (C_hi - t) / sum r
+ * (distances to the two boundaries), nb[0] / nb[1] the nearest tokens with positive residual
+ * below / above the chosen one (-1 if none). Without a residual draw res = {1, 1}, nb = {-1, -1}.
  */
 static void sd_verify_particle(int32_t K, int64_t V, int64_t ld, int32_t dtype,
                                const char *tgt, const char *dft, const int32_t *tok, float Tf,
                                const float *gumbel, const float *acc_u, float res_u,
-                               int32_t *n_acc, int32_t *next, double *acc_gap, double *res_gap)
+                               int32_t *n_acc, int32_t *next, double *acc_gap, double *res,
+                               int32_t *nb)
 {
     const size_t es = esize(dtype);
     const double T = (double)Tf;
     double agap = INFINITY;
-    *res_gap = 1.0;
+    res[0] = res[1] = 1.0;
+    nb[0] = nb[1] = -1;
     for (int32_t k = 0; k < K; ++k) {
         const char *zp = tgt + (size_t)k * (size_t)ld * es;
         const char *zq = dft + (size_t)k * (size_t)ld * es;
@@ -395,24 +399,41 @@ static void sd_verify_particle(int32_t K, int64_t V, int64_t ld, int32_t dtype,
                 R += r;
         }
         double target = (double)res_u * R;
-        double C = 0.0, rg = INFINITY;
-        int32_t pick = -1, last = 0;
+        double C = 0.0, lo = 0.0, hi = 0.0;
+        int32_t pick = -1, last = -1, before = -1, after = -1;
         for (int64_t v = 0; v < V; ++v) {
             double r = exp(elem(zp, dtype, v) / T - A) - exp(elem(zq, dtype, v) / T - B);
             if (r <= 0.0)
                 continue;
+            if (pick >= 0) {
+                after = (int32_t)v;
+                break;
+            }
+            double prev_c = C;
             C += r;
-            last = (int32_t)v;
-            double g = fabs(target - C);
-            if (g < rg)
-                rg = g;
-            if (pick < 0 && target < C)
+            if (target < C) {
                 pick = (int32_t)v;
+                before = last;
+                lo = prev_c;
+                hi = C;
+            }
+            last = (int32_t)v;
+        }
+        if (pick < 0) {            /* rounding past the end: the last token with r > 0 */
+            pick = last;
+            lo = hi = C;
         }
         *n_acc = k;
-        *next = pick >= 0 ? pick : last;
+        *next = pick >= 0 ? pick : 0;
         *acc_gap = agap;
-        *res_gap = R > 0.0 ? rg / R : 0.0;
+        if (R > 0.0) {
+            res[0] = (target - lo) / R;
+            res[1] = (hi - target) / R;
+        } else {
+            res[0] = res[1] = 0.0;
+        }
+        nb[0] = before;
+        nb[1] = after;
         return;
     }
     *n_acc = K;
@@ -422,13 +443,13 @@ static void sd_verify_particle(int32_t K, int64_t V, int64_t ld, int32_t dtype,
 
 /*
  * sd_verify_particle over a batch: R requests x N particles, each an independent sequence.
- * Layouts as in orc_round; acc_u [R][N][K], res_u [R][N]; outputs [R][N].
+ * Layouts as in orc_round; acc_u [R][N][K], res_u [R][N]; outputs [R][N], res and nb [R][N][2].
  */
 void orc_sd_verify(int32_t R, int32_t N, int32_t K, int64_t V, int64_t ld, int32_t dtype,
                    const void *target, const void *draft, const int32_t *tokens,
                    const float *temperature, const float *gumbel, const float *acc_u,
                    const float *res_u, int32_t *n_acc, int32_t *next, double *acc_gap,
-                   double *res_gap)
+                   double *res, int32_t *nb)
 {
     const size_t es = esize(dtype);
 #pragma omp parallel for schedule(dynamic, 1)
@@ -439,7 +460,7 @@ void orc_sd_verify(int32_t R, int32_t N, int32_t K, int64_t V, int64_t ld, int32
                            (const char *)draft + (size_t)(ri * K) * (size_t)ld * es,
                            tokens + (size_t)ri * K, temperature[r], gumbel + (size_t)ri * ld,
                            acc_u + (size_t)ri * K, res_u[ri], &n_acc[ri], &next[ri],
-                           &acc_gap[ri], &res_gap[ri]);
+                           &acc_gap[ri], res + 2 * (size_t)ri, nb + 2 * (size_t)ri);
     }
 }
 

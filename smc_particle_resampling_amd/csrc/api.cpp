@@ -94,6 +94,49 @@ static smcsd_status check_round(const smcsd_round_args* a, Plan* plan) {
     return SMCSD_OK;
 }
 
+static size_t verify_jobs_offset(const Plan& p) { return p.bytes; }
+
+static size_t verify_bytes(const Plan& p) {
+    return verify_jobs_offset(p) + align256(sizeof(ResidualJob) * (size_t)p.R * p.N);
+}
+
+static smcsd_status check_verify(const smcsd_verify_args* a, Plan* plan) {
+    if (!a) return SMCSD_ERR_ARG;
+    if (a->R < 0 || a->N < 1 || a->K < 1 || a->V < 1 || a->reserved0 != 0) return SMCSD_ERR_ARG;
+    if (a->dtype != SMCSD_F32 && a->dtype != SMCSD_BF16) return SMCSD_ERR_ARG;
+    const int64_t epc = a->dtype == SMCSD_F32 ? 4 : 8;
+    if (a->ld < a->V || a->ld % epc != 0) return SMCSD_ERR_ARG;
+    if (a->N > SMCSD_MAX_N || a->K > SMCSD_MAX_K) return SMCSD_ERR_UNSUPPORTED;
+    if (a->R == 0) return SMCSD_OK;
+    if (!a->target_logits || !a->draft_logits || !a->draft_tokens || !a->temperature ||
+        !a->gumbel || !a->accept_uniform || !a->residual_uniform || !a->n_accepted ||
+        !a->next_token)
+        return SMCSD_ERR_ARG;
+    if (!aligned16(a->target_logits) || !aligned16(a->draft_logits) || !aligned16(a->gumbel))
+        return SMCSD_ERR_ARG;
+    if (!make_plan(a->R, a->N, a->K, a->V, a->ld, a->dtype, true, plan))
+        return SMCSD_ERR_UNSUPPORTED;
+    if (!a->workspace || a->workspace_bytes < verify_bytes(*plan)) return SMCSD_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(a->workspace) & 255u) return SMCSD_ERR_WORKSPACE;
+    return SMCSD_OK;
+}
+
+// The TV pass of the round over the given logits: exchange slots filled, then the pass,
+// bracketed by the optional timing events.
+static hipError_t run_tv_pass(const Plan& plan, const LogitsArgs& la, char* ws,
+                              smcsd_event begin, smcsd_event end, hipStream_t s) {
+    hipError_t e = launch_fill_words(reinterpret_cast<uint32_t*>(ws + plan.off_ctrl),
+                                     (int64_t)sizeof(Ctrl) / 4, 0u, s);
+    if (e == hipSuccess)
+        e = launch_fill_words(reinterpret_cast<uint32_t*>(la.pp),
+                              (int64_t)(plan.pair_wgs * sizeof(PairPart) / 4), ~0u, s);
+    if (e != hipSuccess) return e;
+    if (begin && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(begin), s)) != hipSuccess) return e;
+    if ((e = launch_logits(plan, la, s)) != hipSuccess) return e;
+    if (end && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(end), s)) != hipSuccess) return e;
+    return hipSuccess;
+}
+
 }  // namespace smcsd
 
 using namespace smcsd;
@@ -281,6 +324,73 @@ smcsd_status smcsd_bench_copy(const void* src, void* dst, size_t bytes, smcsd_st
     if (overlap(src, bytes, dst, bytes)) return SMCSD_ERR_ARG;
     const hipError_t e = launch_bench_copy(src, dst, bytes, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? SMCSD_OK : SMCSD_ERR_DEVICE;
+}
+
+size_t smcsd_verify_args_size(void) { return sizeof(smcsd_verify_args); }
+
+size_t smcsd_verify_workspace_size(int32_t R, int32_t N, int32_t K, int32_t V, int32_t dtype) {
+    Plan p;
+    const int64_t epc = dtype == SMCSD_F32 ? 4 : 8;
+    if (!make_plan(R, N, K, V, ((int64_t)V + epc - 1) / epc * epc, dtype, true, &p)) return 0;
+    return verify_bytes(p);
+}
+
+smcsd_status smcsd_sd_verify(const smcsd_verify_args* args, smcsd_stream stream) {
+    Plan plan;
+    const smcsd_status st = check_verify(args, &plan);
+    if (st != SMCSD_OK || args->R == 0) return st;
+    const smcsd_verify_args& a = *args;
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    char* ws = static_cast<char*>(a.workspace);
+
+    LogitsArgs la{};
+    la.target = a.target_logits;
+    la.draft = a.draft_logits;
+    la.temperature = a.temperature;
+    la.gumbel = a.gumbel;
+    la.ctrl = reinterpret_cast<Ctrl*>(ws + plan.off_ctrl);
+    la.pp = reinterpret_cast<PairPart*>(ws + plan.off_pp);
+    la.tvp = reinterpret_cast<float*>(ws + plan.off_tvp);
+    la.bp = reinterpret_cast<BonusPart*>(ws + plan.off_bp);
+    la.error_flags = a.error_flags;
+    la.ld = a.ld;
+    la.pairs = plan.pairs;
+    la.pair_wgs = plan.pair_wgs;
+    la.total_wgs = plan.total_wgs;
+    la.N = a.N;
+    la.K = a.K;
+    la.V = a.V;
+    la.chunks = plan.chunks;
+    la.S = plan.S;
+    la.cps = plan.cps;
+    if (run_tv_pass(plan, la, ws, a.timing_begin, a.timing_end, s) != hipSuccess)
+        return SMCSD_ERR_DEVICE;
+
+    VerifyArgs va{};
+    va.target = a.target_logits;
+    va.draft = a.draft_logits;
+    va.tokens = a.draft_tokens;
+    va.temperature = a.temperature;
+    va.accept_u = a.accept_uniform;
+    va.residual_u = a.residual_uniform;
+    va.pp = la.pp;
+    va.tvp = la.tvp;
+    va.bp = la.bp;
+    va.terms = reinterpret_cast<double*>(ws + plan.off_terms);
+    va.jobs = reinterpret_cast<ResidualJob*>(ws + verify_jobs_offset(plan));
+    va.n_accepted = a.n_accepted;
+    va.next_token = a.next_token;
+    va.tv = a.tv;
+    va.error_flags = a.error_flags;
+    va.ld = a.ld;
+    va.N = a.N;
+    va.K = a.K;
+    va.V = a.V;
+    va.S = plan.S;
+    va.cps = plan.cps;
+    va.chunks = plan.chunks;
+    if (launch_verify(a.R, a.dtype, va, s) != hipSuccess) return SMCSD_ERR_DEVICE;
+    return SMCSD_OK;
 }
 
 }  // extern "C"

@@ -15,16 +15,6 @@ namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
 
-template <int DT>
-__device__ __forceinline__ double logit_at(const void* base, int64_t row, int64_t ld, int32_t v) {
-    if constexpr (DT == SMCSD_F32) {
-        return (double)static_cast<const float*>(base)[row * ld + v];
-    } else {
-        const uint16_t bits = static_cast<const uint16_t*>(base)[row * ld + v];
-        return (double)__uint_as_float((uint32_t)bits << 16);
-    }
-}
-
 template <int DT, bool FROM_PARTIALS>
 __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
     __shared__ double s_l[SMCSD_MAX_N];    // l_i = log_weights_i + log_w_incr_i
@@ -45,17 +35,9 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
             const int32_t i = ik / K, k = ik - i * K;
             const int64_t ri = r * N + i;
             const int64_t u = ri * K + k;
-            const PairPart* part = a.pp + u * a.S;
-            float Mp = -INFINITY, Mq = -INFINITY;
-            for (int t = 0; t < a.S; ++t) {
-                Mp = fmaxf(Mp, part[t].mp);
-                Mq = fmaxf(Mq, part[t].mq);
-            }
-            double Sp = 0.0, Sq = 0.0;
-            for (int t = 0; t < a.S; ++t) {
-                Sp += (double)(part[t].sp * __builtin_amdgcn_exp2f((part[t].mp - Mp) * c));
-                Sq += (double)(part[t].sq * __builtin_amdgcn_exp2f((part[t].mq - Mq) * c));
-            }
+            float Mp, Mq;
+            double Sp, Sq;
+            pair_norms(a.pp + u * a.S, a.S, c, Mp, Mq, Sp, Sq);
             double term = 0.0;
             const int32_t x = a.tokens[u];
             if (x < 0 || x >= a.V) {

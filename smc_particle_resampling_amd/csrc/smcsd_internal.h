@@ -103,6 +103,37 @@ struct FinalizeArgs {
     float ess_frac;
 };
 
+// Speculative-decoding verification: the residual draw one particle still needs after the
+// decide kernel (k < 0: none). The draw is in slice `slice` of row pair (particle, k), at
+// `remainder` of residual mass past the slice start; lp, lq are the row's log2 normalisers
+// (log2 of the temperature softmax denominators, in units of the scaled logits).
+struct ResidualJob {
+    int32_t k;
+    int32_t slice;
+    float remainder;
+    float lp, lq;
+};
+
+struct VerifyArgs {
+    const void* target;
+    const void* draft;
+    const int32_t* tokens;
+    const float* temperature;
+    const float* accept_u;
+    const float* residual_u;
+    const PairPart* pp;
+    const float* tvp;
+    const BonusPart* bp;
+    double* terms;           // [R][N][K] workspace
+    ResidualJob* jobs;       // [R][N] workspace
+    int32_t* n_accepted;
+    int32_t* next_token;
+    float* tv;
+    int32_t* error_flags;
+    int64_t ld;
+    int32_t N, K, V, S, cps, chunks;
+};
+
 struct RemapArgs {
     const int32_t* ancestors;
     const int32_t* pt_in;
@@ -118,6 +149,7 @@ hipError_t launch_logits(const Plan& plan, const LogitsArgs& a, hipStream_t s);
 hipError_t launch_finalize(int32_t R, bool from_partials, int32_t dtype, const FinalizeArgs& a,
                            hipStream_t s);
 hipError_t launch_remap(int32_t R, const RemapArgs& a, hipStream_t s);
+hipError_t launch_verify(int32_t R, int32_t dtype, const VerifyArgs& a, hipStream_t s);
 hipError_t launch_bench_read(const void* src, size_t bytes, uint32_t* sink, int32_t grid,
                              hipStream_t s);
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
@@ -190,6 +222,35 @@ __device__ __forceinline__ float wave_max(float v) {
 __device__ __forceinline__ float wave_sum(float v) {
     v = row_sum(v);
     return ((readlane_f32(v, 0) + readlane_f32(v, 16)) + readlane_f32(v, 32)) + readlane_f32(v, 48);
+}
+
+// One logit of a row, widened exactly to double.
+template <int DT>
+__device__ __forceinline__ double logit_at(const void* base, int64_t row, int64_t ld, int32_t v) {
+    if constexpr (DT == SMCSD_F32) {
+        return (double)static_cast<const float*>(base)[row * ld + v];
+    } else {
+        const uint16_t bits = static_cast<const uint16_t*>(base)[row * ld + v];
+        return (double)__uint_as_float((uint32_t)bits << 16);
+    }
+}
+
+// Row maxima and softmax denominators of one row pair from its S slice partials, in slice
+// order: M = max_t m_t, S = sum_t s_t * exp2((m_t - M) * c) accumulated in double.
+__device__ __forceinline__ void pair_norms(const PairPart* part, int S, float c, float& Mp,
+                                           float& Mq, double& Sp, double& Sq) {
+    Mp = -INFINITY;
+    Mq = -INFINITY;
+    for (int t = 0; t < S; ++t) {
+        Mp = fmaxf(Mp, part[t].mp);
+        Mq = fmaxf(Mq, part[t].mq);
+    }
+    Sp = 0.0;
+    Sq = 0.0;
+    for (int t = 0; t < S; ++t) {
+        Sp += (double)(part[t].sp * __builtin_amdgcn_exp2f((part[t].mp - Mp) * c));
+        Sq += (double)(part[t].sq * __builtin_amdgcn_exp2f((part[t].mq - Mq) * c));
+    }
 }
 
 // (key, index) argmax: the larger key wins, the lower index wins on equal keys.

@@ -43,6 +43,18 @@ class RoundArgs(ctypes.Structure):
     ]
 
 
+class VerifyArgs(ctypes.Structure):
+    """Mirror of smcsd_verify_args."""
+    _fields_ = [
+        ("R", _i32), ("N", _i32), ("K", _i32), ("V", _i32), ("ld", _i64), ("dtype", _i32),
+        ("reserved0", _i32),
+        ("target_logits", _p), ("draft_logits", _p), ("draft_tokens", _p), ("temperature", _p),
+        ("gumbel", _p), ("accept_uniform", _p), ("residual_uniform", _p),
+        ("n_accepted", _p), ("next_token", _p), ("tv", _p), ("error_flags", _p),
+        ("workspace", _p), ("workspace_bytes", _sz), ("timing_begin", _p), ("timing_end", _p),
+    ]
+
+
 _lib.smcsd_round.restype = _i32
 _lib.smcsd_round.argtypes = [ctypes.POINTER(RoundArgs), _p]
 _lib.smcsd_resample.restype = _i32
@@ -55,6 +67,12 @@ _lib.smcsd_status_string.restype = ctypes.c_char_p
 _lib.smcsd_status_string.argtypes = [_i32]
 _lib.smcsd_round_args_size.restype = _sz
 _lib.smcsd_round_args_size.argtypes = []
+_lib.smcsd_sd_verify.restype = _i32
+_lib.smcsd_sd_verify.argtypes = [ctypes.POINTER(VerifyArgs), _p]
+_lib.smcsd_verify_workspace_size.restype = _sz
+_lib.smcsd_verify_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
+_lib.smcsd_verify_args_size.restype = _sz
+_lib.smcsd_verify_args_size.argtypes = []
 _lib.smcsd_bench_stream_read.restype = _i32
 _lib.smcsd_bench_stream_read.argtypes = [_p, _sz, _p, _i32, _p]
 _lib.smcsd_bench_copy.restype = _i32
@@ -81,6 +99,14 @@ def smcsd_status_string(status: int) -> str:
 
 def smcsd_round_args_size() -> int:
     return int(_lib.smcsd_round_args_size())
+
+
+def smcsd_verify_args_size() -> int:
+    return int(_lib.smcsd_verify_args_size())
+
+
+def smcsd_verify_workspace_size(R: int, N: int, K: int, V: int, dtype: int) -> int:
+    return int(_lib.smcsd_verify_workspace_size(R, N, K, V, dtype))
 
 
 def smcsd_workspace_size(R: int, N: int, K: int, V: int, dtype: int, tv_enabled: bool) -> int:
@@ -181,6 +207,53 @@ def smcsd_round(*, target_logits, draft_logits, draft_tokens, temperature, gumbe
     st = _lib.smcsd_round(ctypes.byref(a), _stream(dev, stream))
     if st != OK:
         raise SmcsdError(st, "smcsd_round")
+
+
+def smcsd_sd_verify(*, target_logits, draft_logits, draft_tokens, temperature, gumbel,
+                    accept_uniform, residual_uniform, n_accepted, next_token, workspace, tv=None,
+                    error_flags=None, V: int | None = None, timing_events=None,
+                    stream=None) -> None:
+    """Enqueue standard speculative-decoding verification (smcsd_sd_verify) of every
+    particle's drafted block. Shapes as for smcsd_round plus accept_uniform [R,N,K] and
+    residual_uniform [R,N] float32; outputs n_accepted, next_token [R,N] int32."""
+    dev = target_logits.device
+    if target_logits.dtype not in (torch.float32, torch.bfloat16):
+        raise ValueError("logits must be float32 or bfloat16")
+    if target_logits.dim() != 4:
+        raise ValueError("target_logits must be [R, N, K+1, ld]")
+    R, N, K1, ld = target_logits.shape
+    K = K1 - 1
+    V = ld if V is None else int(V)
+    f32, i32 = torch.float32, torch.int32
+    _check(target_logits, "target_logits", None, None, dev)
+    _check(draft_logits, "draft_logits", target_logits.dtype, (R, N, K, ld), dev)
+    _check(draft_tokens, "draft_tokens", i32, (R, N, K), dev)
+    _check(temperature, "temperature", f32, (R,), dev)
+    _check(gumbel, "gumbel", f32, (R, N, ld), dev)
+    _check(accept_uniform, "accept_uniform", f32, (R, N, K), dev)
+    _check(residual_uniform, "residual_uniform", f32, (R, N), dev)
+    _check(n_accepted, "n_accepted", i32, (R, N), dev)
+    _check(next_token, "next_token", i32, (R, N), dev)
+    _check(workspace, "workspace", torch.uint8, None, dev)
+    if tv is not None:
+        _check(tv, "tv", f32, (R, N, K), dev)
+    if error_flags is not None:
+        _check(error_flags, "error_flags", i32, None, dev)
+    a = VerifyArgs()
+    a.R, a.N, a.K, a.V, a.ld = R, N, K, V, ld
+    a.dtype = BF16 if target_logits.dtype == torch.bfloat16 else F32
+    a.reserved0 = 0
+    a.target_logits, a.draft_logits = _ptr(target_logits), _ptr(draft_logits)
+    a.draft_tokens, a.temperature, a.gumbel = _ptr(draft_tokens), _ptr(temperature), _ptr(gumbel)
+    a.accept_uniform, a.residual_uniform = _ptr(accept_uniform), _ptr(residual_uniform)
+    a.n_accepted, a.next_token, a.tv = _ptr(n_accepted), _ptr(next_token), _ptr(tv)
+    a.error_flags = _ptr(error_flags)
+    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    if timing_events is not None:
+        a.timing_begin, a.timing_end = timing_events
+    st = _lib.smcsd_sd_verify(ctypes.byref(a), _stream(dev, stream))
+    if st != OK:
+        raise SmcsdError(st, "smcsd_sd_verify")
 
 
 def smcsd_resample(*, log_w_incr, log_weights, uniform, log_norm, ess, resampled, ancestors,
@@ -285,5 +358,35 @@ def run_round(inputs: dict, *, mode="always", ess_frac=0.5, tv=False, pages=True
     return out
 
 
+def run_sd_verify(inputs: dict, *, tv=False, outputs=None, timing_events=None, stream=None) -> dict:
+    """smcsd_sd_verify on a dict from ``synth.make_inputs`` that also holds accept_uniform
+    and residual_uniform (``synth.make_verify_uniforms``). Returns the output tensors."""
+    tgt = inputs["target"]
+    R, N, K1, ld = tgt.shape
+    K = K1 - 1
+    dev = tgt.device
+    dt = BF16 if tgt.dtype == torch.bfloat16 else F32
+    if outputs is None:
+        ws = smcsd_verify_workspace_size(R, N, K, inputs["V"], dt)
+        if ws == 0 and R > 0:
+            raise ValueError("sizes unsupported: R=%d N=%d K=%d V=%d" % (R, N, K, inputs["V"]))
+        outputs = dict(
+            n_accepted=torch.empty((R, N), dtype=torch.int32, device=dev),
+            next_token=torch.empty((R, N), dtype=torch.int32, device=dev),
+            tv=torch.empty((R, N, K), dtype=torch.float32, device=dev) if tv else None,
+            error_flags=torch.zeros((1,), dtype=torch.int32, device=dev),
+            workspace=torch.empty((max(ws, 256),), dtype=torch.uint8, device=dev))
+    o = outputs
+    smcsd_sd_verify(target_logits=tgt, draft_logits=inputs["draft"], draft_tokens=inputs["tokens"],
+                    temperature=inputs["temperature"], gumbel=inputs["gumbel"],
+                    accept_uniform=inputs["accept_uniform"],
+                    residual_uniform=inputs["residual_uniform"], n_accepted=o["n_accepted"],
+                    next_token=o["next_token"], workspace=o["workspace"], tv=o.get("tv"),
+                    error_flags=o["error_flags"], V=inputs["V"], timing_events=timing_events,
+                    stream=stream)
+    return o
+
+
 __all__ = [n for n in dir() if n.startswith("smcsd_")] + [
-    "RoundArgs", "SmcsdError", "alloc_outputs", "run_round", "library_path", "MODES"]
+    "RoundArgs", "VerifyArgs", "SmcsdError", "alloc_outputs", "run_round", "run_sd_verify",
+    "library_path", "MODES"]

@@ -33,7 +33,7 @@ import math
 import torch
 
 STREAMS = dict(target=1, peaks=2, draft=3, tokens=4, gumbel=5, uniform=6, temp=7, pages=8,
-               ragged=9, zipf_q=10, potential=11)
+               ragged=9, zipf_q=10, potential=11, accept=12, residual=13)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -152,6 +152,16 @@ def make_log_potential(R: int, N: int, seed: int, device="cpu", p_removed: float
     return lp.masked_fill(removed, float("-inf"))
 
 
+def make_verify_uniforms(R: int, N: int, K: int, seed: int, device="cpu") -> dict:
+    """Uniforms of speculative-decoding verification: accept_uniform [R, N, K] and
+    residual_uniform [R, N], float32 in [0, 1)."""
+    return dict(
+        accept_uniform=torch.rand((R, N, K), generator=_gen(seed, "accept", device),
+                                  device=device, dtype=torch.float32),
+        residual_uniform=torch.rand((R, N), generator=_gen(seed, "residual", device),
+                                    device=device, dtype=torch.float32))
+
+
 def make_page_table(R: int, N: int, P: int, seed: int, ragged: bool = False):
     """Page table [R,N,P] int32 (negative = unused), refcount, num_pages (CPU tensors)."""
     g = _gen(seed, "pages", "cpu")
@@ -262,8 +272,9 @@ def to_host(inputs: dict, requests=None) -> dict:
 
     out = {k: host(inputs[k]) for k in ("target", "draft", "tokens", "temperature", "gumbel",
                                          "uniform", "log_weights")}
-    if inputs.get("log_potential") is not None:
-        out["log_potential"] = host(inputs["log_potential"])
+    for k in ("log_potential", "accept_uniform", "residual_uniform"):
+        if inputs.get(k) is not None:
+            out[k] = host(inputs[k])
     if "page_table" in inputs:
         out["page_table"] = host(inputs["page_table"])
         out["refcount"] = host(inputs["refcount"], per_request=False)

@@ -27,13 +27,16 @@ def test_every_declared_symbol_is_exported():
     names = _declared_functions()
     assert {"smcsd_round", "smcsd_resample", "smcsd_remap_pages", "smcsd_workspace_size",
             "smcsd_status_string", "smcsd_round_args_size", "smcsd_bench_stream_read",
-            "smcsd_bench_copy"} <= names
+            "smcsd_bench_copy", "smcsd_sd_verify", "smcsd_verify_workspace_size",
+            "smcsd_verify_args_size"} <= names
     lib = ctypes.CDLL(S.library_path())
     for n in sorted(names):
         assert hasattr(lib, n), n
 
 
 def test_struct_layout_matches():
+    assert S.smcsd_verify_args_size() == ctypes.sizeof(S.VerifyArgs)
+    assert S.VerifyArgs.target_logits.offset == 32
     assert S.smcsd_round_args_size() == ctypes.sizeof(S.RoundArgs)
     assert S.RoundArgs.ld.offset == 16
     assert S.RoundArgs.target_logits.offset == 48
@@ -143,3 +146,42 @@ def test_binding_rejects_bad_tensors_before_the_library():
                       temperature=None, gumbel=None, uniform=None, log_weights=None,
                       log_w_incr=None, log_norm=None, ess=None, resampled=None, ancestors=None,
                       bonus=None, workspace=None)
+
+
+def _vargs(**kw):
+    a = S.VerifyArgs()
+    a.R, a.N, a.K, a.V, a.ld, a.dtype = 2, 8, 4, 1000, 1000, S.BF16
+    base = 0x20000000
+    for i, name in enumerate(("target_logits", "draft_logits", "draft_tokens", "temperature",
+                              "gumbel", "accept_uniform", "residual_uniform", "n_accepted",
+                              "next_token")):
+        setattr(a, name, base + i * (1 << 24))
+    a.workspace = 0x70000000
+    a.workspace_bytes = S.smcsd_verify_workspace_size(2, 8, 4, 1000, S.BF16)
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _verify(a):
+    return S.raw_library().smcsd_sd_verify(ctypes.byref(a), None)
+
+
+def test_verify_validation():
+    ws = S.smcsd_verify_workspace_size(2, 8, 4, 1000, S.BF16)
+    assert ws > 0 and ws % 256 == 0
+    assert ws > S.smcsd_workspace_size(2, 8, 4, 1000, S.BF16, True)
+    assert _verify(_vargs(R=0)) == S.OK
+    assert _verify(_vargs(N=0)) == S.ERR_ARG
+    assert _verify(_vargs(reserved0=1)) == S.ERR_ARG
+    assert _verify(_vargs(ld=1001)) == S.ERR_ARG
+    assert _verify(_vargs(accept_uniform=None)) == S.ERR_ARG
+    assert _verify(_vargs(residual_uniform=None)) == S.ERR_ARG
+    assert _verify(_vargs(next_token=None)) == S.ERR_ARG
+    assert _verify(_vargs(target_logits=0x20000008)) == S.ERR_ARG
+    assert _verify(_vargs(N=S.MAX_N + 1)) == S.ERR_UNSUPPORTED
+    assert _verify(_vargs(workspace_bytes=100)) == S.ERR_WORKSPACE
+    assert _verify(_vargs(workspace=0x70000010)) == S.ERR_WORKSPACE
+    # TV is always on here: V beyond the TV limit is unsupported
+    big = 1048576 + 8
+    assert _verify(_vargs(V=big, ld=big)) == S.ERR_UNSUPPORTED

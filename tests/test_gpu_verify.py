@@ -1,0 +1,147 @@
+"""GPU parity of standard speculative-decoding verification (smcsd_sd_verify) against the
+oracle, through the C ABI.
+
+The bar: n_accepted bit-exact for every particle whose acceptance uniforms lie >= 1e-5 from
+min(1, p/q) at every examined position; for those particles next_token bit-exact when the
+block was accepted (the bonus is decided in binary32 on both sides); for a residual draw
+the GPU token is the oracle's, or -- only where the draw's target lies within 1e-5 of the
+residual mass of the boundary between them -- the oracle's neighbouring token on that side
+(the cumulative sums are f32 on the GPU, f64 in the oracle). TV within 1e-4 relative.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from smc_particle_resampling_amd import smcsd, synth
+
+pytestmark = pytest.mark.gpu
+
+W = synth.WORKLOADS
+ACC_GAP = 1e-5
+RES_TIE = 1e-5
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def run_and_compare(w, dev, seed=0, modify=None, max_excluded=0.05):
+    _say("verify case", w.name, "R N K V", w.R, w.N, w.K, w.V, "seed", seed)
+    inp = synth.make_inputs(w, seed, device=dev, pages=False)
+    inp.update(synth.make_verify_uniforms(w.R, w.N, w.K, seed, device=dev))
+    if modify:
+        modify(inp)
+    out = smcsd.run_sd_verify(inp, tv=True)
+    torch.cuda.synchronize()
+    assert int(out["error_flags"].item()) == 0
+    n_gpu = out["n_accepted"].cpu().numpy()
+    t_gpu = out["next_token"].cpu().numpy()
+    tv_gpu = out["tv"].cpu().numpy()
+    host = synth.to_host(inp)
+    ora = oracle.sd_verify(host, V=w.V)
+    tv_ora = oracle.round(host, V=w.V, tv=True, with_pages=False)["tv"]
+    assert np.all((t_gpu >= 0) & (t_gpu < w.V))
+    assert np.all((n_gpu >= 0) & (n_gpu <= w.K))
+    ok = ora["acc_gap"] >= ACC_GAP
+    bad = ok & (n_gpu != ora["n_accepted"])
+    assert not bad.any(), ("n_accepted", np.argwhere(bad)[:5].tolist(), n_gpu[bad][:5],
+                           ora["n_accepted"][bad][:5])
+    full = ok & (ora["n_accepted"] == w.K)
+    resid = ok & (ora["n_accepted"] < w.K)
+    bad = full & (t_gpu != ora["next_token"])
+    assert not bad.any(), ("bonus", np.argwhere(bad)[:5].tolist(), t_gpu[bad][:5],
+                           ora["next_token"][bad][:5])
+    ties = residual_ties(t_gpu, ora, resid)
+    err = np.abs(tv_gpu - tv_ora) > 1e-4 * np.abs(tv_ora) + 1e-6
+    assert not err.any(), ("tv", np.argwhere(err)[:5].tolist())
+    excluded = 1.0 - ok.mean()
+    _say("  ok: accepted-all %d, residual draws %d (boundary ties %d), excluded %.4f, "
+         "mean accepted %.2f" % (int(full.sum()), int(resid.sum()), ties, excluded,
+                                 float(n_gpu.mean())))
+    assert excluded <= max_excluded
+    return inp, out, ora
+
+
+def residual_ties(t_gpu, ora, mask):
+    """Residual draws: the GPU token must be the oracle's, or its neighbour across a boundary
+    that the draw's target lies within RES_TIE of. Returns how many were such ties."""
+    same = t_gpu == ora["next_token"]
+    below = (t_gpu == ora["res_below"]) & (ora["res_lo"] < RES_TIE)
+    above = (t_gpu == ora["res_above"]) & (ora["res_hi"] < RES_TIE)
+    bad = mask & ~(same | below | above)
+    assert not bad.any(), ("residual", np.argwhere(bad)[:5].tolist(), t_gpu[bad][:5],
+                           ora["next_token"][bad][:5], ora["res_lo"][bad][:5],
+                           ora["res_hi"][bad][:5])
+    return int((mask & ~same).sum())
+
+
+SMALL = [
+    W["r64-n32-k8-v128256-bf16-tv"].scaled(name="verify-c3", R=2, V=20000, ctx=128),
+    W["r32-n32-k8-v256000-bf16-tv-mixT"].scaled(name="verify-c5", R=4, V=36000, ctx=128),
+    W["r16-n16-k4-v128256-bf16"].scaled(name="verify-c2", R=3, V=40000, ctx=128),
+    W["r1-n8-k4-v32000-f32"].scaled(name="verify-c1", R=2),
+    W["r8-n16-k4-v152064-bf16-zipf-ess"].scaled(name="verify-c4", R=3, V=30000, ctx=128),
+]
+
+
+@pytest.mark.parametrize("w", SMALL, ids=[w.name for w in SMALL])
+def test_verify_scaled_workloads(w, dev):
+    run_and_compare(w, dev, seed=5)
+
+
+@pytest.mark.parametrize("V,dtype", [(1, "bf16"), (9, "bf16"), (7, "f32"), (5001, "bf16"),
+                                     (16385, "bf16"), (1048569, "bf16")])
+def test_verify_ragged_vocabularies(V, dtype, dev):
+    w = W["r16-n16-k4-v128256-bf16"].scaled(name="verify-ragged", R=2, N=8, K=3, V=V,
+                                            dtype=dtype, ctx=128)
+    run_and_compare(w, dev, seed=6, max_excluded=0.2 if V < 16 else 0.05)
+
+
+@pytest.mark.parametrize("N,K", [(1, 1), (3, 1), (1024, 2), (40, 17)])
+def test_verify_particle_and_position_extremes(N, K, dev):
+    w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="verify-extreme", R=2, N=N, K=K, V=3000,
+                                                ctx=64)
+    run_and_compare(w, dev, seed=7)
+
+
+def test_verify_identical_rows_accept_everything(dev):
+    w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="verify-p-equals-q", R=2, V=20000, ctx=64)
+
+    def same(inp):
+        inp["draft"] = inp["target"][:, :, : w.K].clone()
+
+    inp, out, ora = run_and_compare(w, dev, seed=8, modify=same)
+    assert np.all(out["n_accepted"].cpu().numpy() == w.K)
+    assert np.all(out["tv"].cpu().numpy() == 0.0)
+
+
+def test_verify_full_size_sampled(dev):
+    """The headline shape (64 x 32 x 8, V = 128256, bf16): every particle through the GPU,
+    the oracle on a sample of requests."""
+    w = W["r64-n32-k8-v128256-bf16-tv"]
+    inp = synth.make_inputs(w, 3, device=dev, pages=False)
+    inp.update(synth.make_verify_uniforms(w.R, w.N, w.K, 3, device=dev))
+    out = smcsd.run_sd_verify(inp, tv=False)
+    torch.cuda.synchronize()
+    assert int(out["error_flags"].item()) == 0
+    reqs = [0, 17, 63]
+    host = synth.to_host(inp, reqs)
+    ora = oracle.sd_verify(host, V=w.V)
+    n_gpu = out["n_accepted"].cpu().numpy()[reqs]
+    t_gpu = out["next_token"].cpu().numpy()[reqs]
+    ok = ora["acc_gap"] >= ACC_GAP
+    assert np.array_equal(n_gpu[ok], ora["n_accepted"][ok])
+    full = ok & (ora["n_accepted"] == w.K)
+    assert np.array_equal(t_gpu[full], ora["next_token"][full])
+    residual_ties(t_gpu, ora, ok & (ora["n_accepted"] < w.K))
+    assert ok.mean() > 0.99

@@ -101,6 +101,17 @@ def test_hand_worked_residuals():
     for b, want in ((0.0, 0), (0.62, 0), (0.63, 1), (0.999, 1)):
         out = oracle.sd_verify(_inputs(zp, zq, tok, 1.0, np.array([0.5]), np.array([b])))
         assert out["n_accepted"][0, 0] == 0 and out["next_token"][0, 0] == want, (b, out)
+    # the chosen token's cumulative-sum interval and its neighbours
+    out = oracle.sd_verify(_inputs(zp, zq, tok, 1.0, np.array([0.5]), np.array([0.3])))
+    assert out["next_token"][0, 0] == 0
+    assert out["res_lo"][0, 0] == pytest.approx(0.3, abs=1e-6)        # b is float32
+    assert out["res_hi"][0, 0] == pytest.approx((0.5 - 0.24) / 0.8, abs=1e-6)
+    assert (out["res_below"][0, 0], out["res_above"][0, 0]) == (-1, 1)
+    out = oracle.sd_verify(_inputs(zp, zq, tok, 1.0, np.array([0.5]), np.array([0.9])))
+    assert out["next_token"][0, 0] == 1
+    assert out["res_lo"][0, 0] == pytest.approx((0.72 - 0.5) / 0.8, abs=1e-6)
+    assert out["res_hi"][0, 0] == pytest.approx(0.1, abs=1e-6)
+    assert (out["res_below"][0, 0], out["res_above"][0, 0]) == (0, -1)
     # a boundary: b * R exactly on C_0 = 0.5 (R = 0.8, b = 0.625) goes to the next token
     out = oracle.sd_verify(_inputs(zp, zq, tok, 1.0, np.array([0.5]), np.array([0.625])))
     assert out["res_gap"][0, 0] < 1e-6
