@@ -98,7 +98,7 @@ def stored_traffic(workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, target_s=12.0, sample_requests=4):
+def cpu_baseline(w, target_s=12.0, sample_requests=4, path="round"):
     """The oracle (as it is) on a bounded sample of the workload: the first few requests
     (all N particles, K positions, V logits each), timed with a wall clock around
     oracle.round and repeated until ~target_s of CPU work; rounds/s = 1 / (R * seconds per
@@ -106,19 +106,28 @@ def cpu_baseline(w, target_s=12.0, sample_requests=4):
     import oracle
     from smc_particle_resampling_amd import synth
     rs = min(w.R, sample_requests)
-    host = synth.to_host(synth.make_inputs(w.scaled(R=rs), 11, device="cpu"))
+    small = w.scaled(R=rs)
+    inputs = synth.make_inputs(small, 11, device="cpu", pages=path == "round")
+    if path == "sd_verify":
+        inputs.update(synth.make_verify_uniforms(rs, w.N, w.K, 11, device="cpu"))
+    host = synth.to_host(inputs)
     times = []
     while not times or (sum(times) < target_s and len(times) < 1000):
         t = time.perf_counter()
-        oracle.round(host, V=w.V, mode=w.mode, ess_frac=w.ess_frac, tv=w.tv)
+        if path == "sd_verify":
+            oracle.sd_verify(host, V=w.V)
+        else:
+            oracle.round(host, V=w.V, mode=w.mode, ess_frac=w.ess_frac, tv=w.tv)
         times.append(time.perf_counter() - t)
     per_request = sum(times) / (len(times) * rs)
-    return {"value": 1.0 / (w.R * per_request), "unit": "rounds/s", "cores": oracle.num_threads(),
+    unit = "passes/s" if path == "sd_verify" else "rounds/s"
+    what = "SD verification" if path == "sd_verify" else "round"
+    return {"value": 1.0 / (w.R * per_request), "unit": unit, "cores": oracle.num_threads(),
             "kind": "oracle",
-            "sample": "%d of %d requests (N=%d, K=%d, V=%d, TV %s), fp64 oracle round over them "
-                      "repeated %d times (%.1f s in all), %.4f s per request; rounds/s = "
-                      "1/(%d * that)" % (rs, w.R, w.N, w.K, w.V, "on" if w.tv else "off",
-                                         len(times), sum(times), per_request, w.R)}
+            "sample": "%d of %d requests (N=%d, K=%d, V=%d, TV %s), fp64 oracle %s over them "
+                      "repeated %d times (%.1f s in all), %.4f s per request; %s = "
+                      "1/(%d * that)" % (rs, w.R, w.N, w.K, w.V, "on" if w.tv else "off", what,
+                                         len(times), sum(times), per_request, unit, w.R)}
 
 
 def main():
@@ -131,6 +140,10 @@ def main():
     ap.add_argument("--no-read-roofline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run N launches of a plain 1 GiB copy (for counter scaling)")
+    ap.add_argument("--path", choices=("round", "sd_verify"), default="round",
+                    help="round: one SMC-SD round (smcsd_round, the headline); sd_verify: "
+                         "standard speculative-decoding verification of the same blocks "
+                         "(smcsd_sd_verify)")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -146,19 +159,28 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print("# building inputs for %s" % name, file=sys.stderr, flush=True)
-    inp = synth.make_inputs(w, 0, device=dev)
-    torch.cuda.synchronize()
-    out = smcsd.alloc_outputs(w.R, w.N, w.K, dev, tv=w.tv, V=w.V,
-                              dtype=smcsd.BF16 if w.dtype == "bf16" else smcsd.F32)
-    tables = [inp["page_table"], torch.empty_like(inp["page_table"])]
+    verify = args.path == "sd_verify"
+    inp = synth.make_inputs(w, 0, device=dev, pages=not verify)
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    if verify:
+        inp.update(synth.make_verify_uniforms(w.R, w.N, w.K, 0, device=dev))
+        out = smcsd.run_sd_verify(inp)          # allocates the outputs once
+        torch.cuda.synchronize()
 
-    def step(t, timing=None):
-        out["page_table_out"] = tables[(t + 1) % 2]
-        inp["page_table"] = tables[t % 2]
-        smcsd.run_round(inp, mode=w.mode, ess_frac=w.ess_frac, tv=w.tv, outputs=out,
-                        timing_events=timing)
+        def step(t, timing=None):
+            smcsd.run_sd_verify(inp, outputs=out, timing_events=timing)
+    else:
+        torch.cuda.synchronize()
+        out = smcsd.alloc_outputs(w.R, w.N, w.K, dev, tv=w.tv, V=w.V,
+                                  dtype=smcsd.BF16 if w.dtype == "bf16" else smcsd.F32)
+        tables = [inp["page_table"], torch.empty_like(inp["page_table"])]
+
+        def step(t, timing=None):
+            out["page_table_out"] = tables[(t + 1) % 2]
+            inp["page_table"] = tables[t % 2]
+            smcsd.run_round(inp, mode=w.mode, ess_frac=w.ess_frac, tv=w.tv, outputs=out,
+                            timing_events=timing)
 
     for t in range(args.warmup):
         step(t)
@@ -181,8 +203,8 @@ def main():
     alg = w.algorithmic_bytes()
     logits_bytes = alg["target"] + alg["draft"] + alg["noise"]
     achieved = logits_bytes / (k_mean_ms * 1e-3) / 1e9
-    print("# round %.3f ms, logits kernel %.3f ms (min %.3f max %.3f)" % (
-        ms_per_step, k_mean_ms, min(kms), max(kms)), file=sys.stderr, flush=True)
+    print("# %s %.3f ms, logits kernel %.3f ms (min %.3f max %.3f)" % (
+        args.path, ms_per_step, k_mean_ms, min(kms), max(kms)), file=sys.stderr, flush=True)
 
     for _ in range(args.copy_calibration):
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
@@ -192,11 +214,20 @@ def main():
         del src, dst
 
     rr = None if args.no_read_roofline else read_roofline(smcsd, torch, dev)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w)
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, path=args.path)
+    if verify:
+        metric = ("SD verification passes/s and achieved HBM GB/s (% of peak), "
+                  "N=32 K=8 V=128256 bf16")
+        unit = "passes/s"
+        table_bytes = 0
+    else:
+        metric = "SMC-SD rounds/s and achieved HBM GB/s (% of peak), N=32 K=8 V=128256 bf16"
+        unit = "rounds/s"
+        table_bytes = alg["table"]
     line = {
-        "metric": "SMC-SD rounds/s and achieved HBM GB/s (% of peak), N=32 K=8 V=128256 bf16",
+        "metric": metric,
         "value": args.steps / elapsed,
-        "unit": "rounds/s",
+        "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
@@ -206,9 +237,10 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic",
-        "config": {"workload": name, "R": w.R, "N": w.N, "K": w.K, "V": w.V,
-                   "tv": w.tv, "resample": w.mode, "pages_per_particle": w.P,
-                   "round_GBps": (logits_bytes + alg["table"]) / (ms_per_step * 1e-3) / 1e9},
+        "config": {"workload": name, "path": args.path, "R": w.R, "N": w.N, "K": w.K, "V": w.V,
+                   "tv": w.tv or verify, "resample": None if verify else w.mode,
+                   "pages_per_particle": None if verify else w.P,
+                   "round_GBps": (logits_bytes + table_bytes) / (ms_per_step * 1e-3) / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS, "traffic": stored_traffic(name),
                      "kernel": "k_logits", "kernel_ms": k_mean_ms,
