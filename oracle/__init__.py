@@ -65,6 +65,8 @@ def lib() -> ctypes.CDLL:
             L.orc_sd_verify.restype = None
             L.orc_sd_verify.argtypes = [i32, i32, i32, i64, i64, i32, p, p, p, p, p, p, p, p,
                                         p, p, p, p]
+            L.orc_gumbel_topk.restype = None
+            L.orc_gumbel_topk.argtypes = [i64, i64, i64, i32, p, p, p, i32, p, p]
             L.orc_num_threads.restype = i32
             L.orc_num_threads.argtypes = []
             _lib = L
@@ -231,3 +233,23 @@ def sd_verify(inputs: dict, *, V: int | None = None) -> dict:
     out["res_below"], out["res_above"] = nb[..., 0], nb[..., 1]
     out["res_gap"] = np.minimum(out["res_lo"], out["res_hi"])
     return out
+
+
+def gumbel_topk(logits: np.ndarray, temperature: np.ndarray, gumbel: np.ndarray, k: int, *,
+                V: int | None = None) -> tuple[np.ndarray, np.ndarray]:
+    """Gumbel-Top-K of every row: logits [rows, ld] (float32 or bf16 bits as uint16),
+    temperature [rows], gumbel [rows, ld] float32. Returns tokens [rows, k] int32 and keys
+    [rows, k] float32, in decreasing key order (equal keys by increasing index)."""
+    z, dt = _logits(logits)
+    rows, ld = z.shape
+    V = ld if V is None else int(V)
+    if not 1 <= k <= V:
+        raise ValueError("k must be in [1, V]")
+    temp = np.ascontiguousarray(temperature, dtype=np.float32)
+    g = np.ascontiguousarray(gumbel, dtype=np.float32)
+    assert temp.shape == (rows,) and g.shape == (rows, ld)
+    tok = np.zeros((rows, k), np.int32)
+    key = np.zeros((rows, k), np.float32)
+    lib().orc_gumbel_topk(rows, V, ld, dt, _ptr(z), _ptr(temp), _ptr(g), int(k), _ptr(tok),
+                          _ptr(key))
+    return tok, key

@@ -464,6 +464,54 @@ void orc_sd_verify(int32_t R, int32_t N, int32_t K, int64_t V, int64_t ld, int32
     }
 }
 
+/*
+ * Gumbel-Top-K: k distinct tokens drawn without replacement from softmax(z/T) in one step,
+ * as the STAND page describes for drafting (method item 2: add Gumbel noise to the
+ * log-probabilities and keep the indices of the k largest sums; the noise is precomputed and
+ * cached). Keys are taken in binary32 exactly as for the bonus token (reading R7),
+ * key_v = fl32(fma(z_v, fl32(1/T), G_v)); the k tokens come out in decreasing key order,
+ * equal keys in increasing index. out_keys may be NULL. k <= V.
+ */
+typedef struct {
+    float key;
+    int32_t idx;
+} orc_kv;
+
+static int kv_order(const void *a, const void *b)
+{
+    const orc_kv *x = (const orc_kv *)a, *y = (const orc_kv *)b;
+    if (x->key > y->key)
+        return -1;
+    if (x->key < y->key)
+        return 1;
+    return x->idx < y->idx ? -1 : (x->idx > y->idx ? 1 : 0);
+}
+
+void orc_gumbel_topk(int64_t rows, int64_t V, int64_t ld, int32_t dtype, const void *logits,
+                     const float *temperature, const float *gumbel, int32_t k,
+                     int32_t *out_tokens, float *out_keys)
+{
+    const size_t es = esize(dtype);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < rows; ++r) {
+        const char *z = (const char *)logits + (size_t)r * (size_t)ld * es;
+        const float *g = gumbel + (size_t)r * (size_t)ld;
+        float invT = 1.0f / temperature[r];
+        orc_kv *kv = malloc(sizeof(orc_kv) * (size_t)V);
+        for (int64_t v = 0; v < V; ++v) {
+            kv[v].key = fmaf(elem_f32(z, dtype, v), invT, g[v]);
+            kv[v].idx = (int32_t)v;
+        }
+        qsort(kv, (size_t)V, sizeof(orc_kv), kv_order);
+        for (int32_t j = 0; j < k; ++j) {
+            out_tokens[(size_t)r * k + j] = kv[j].idx;
+            if (out_keys)
+                out_keys[(size_t)r * k + j] = kv[j].key;
+        }
+        free(kv);
+    }
+}
+
 /* Threads OpenMP would use for the parallel loops above (1 when built without OpenMP). */
 int32_t orc_num_threads(void)
 {
