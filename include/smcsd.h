@@ -249,6 +249,28 @@ size_t smcsd_verify_workspace_size(int32_t R, int32_t N, int32_t K, int32_t V, i
 /* sizeof(smcsd_verify_args) as compiled into the library. */
 size_t smcsd_verify_args_size(void);
 
+/*
+ * Gumbel-Top-K: k distinct tokens per row drawn without replacement from softmax(z/T) in one
+ * step, as the STAND page describes for drafting (method item 2: add precomputed, cached
+ * Gumbel noise to the log-probabilities and keep the indices of the k largest sums).
+ *   key_v = fl32(fma(logits[row][v], fl32(1/temperature[row]), gumbel[row][v]))
+ *   out_tokens[row][0..k-1] = the k largest keys' indices, by decreasing key, equal keys by
+ *   increasing index; out_keys (optional, NULL) the keys themselves.
+ * rows >= 0, 1 <= k <= min(V, SMCSD_MAX_TOPK), V <= SMCSD_MAX_TV_V_* for the dtype; ld and
+ * alignment as for smcsd_round (logits and gumbel 16-byte aligned, ld a multiple of 8 for
+ * bf16, 4 for f32). Exact (no tolerance): both passes rank the same binary32 keys.
+ */
+#define SMCSD_MAX_TOPK 64
+
+smcsd_status smcsd_gumbel_topk(int32_t rows, int32_t V, int64_t ld, int32_t dtype,
+                               const void *logits, const float *temperature,
+                               const float *gumbel, int32_t k, int32_t *out_tokens,
+                               float *out_keys, void *workspace, size_t workspace_bytes,
+                               smcsd_stream stream);
+
+/* Workspace bytes smcsd_gumbel_topk needs (0 if the sizes are invalid). */
+size_t smcsd_topk_workspace_size(int32_t rows, int32_t V, int32_t dtype, int32_t k);
+
 #ifdef __cplusplus
 }
 #endif

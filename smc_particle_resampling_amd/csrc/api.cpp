@@ -137,6 +137,26 @@ static hipError_t run_tv_pass(const Plan& plan, const LogitsArgs& la, char* ws,
     return hipSuccess;
 }
 
+// Slices of a Gumbel-Top-K row: as the TV pass (512 lanes x 4 chunks at most per slice).
+static bool topk_plan(int32_t rows, int32_t V, int32_t dtype, int32_t k, int32_t* chunks,
+                      int32_t* S, int32_t* cps, size_t* bytes) {
+    if (rows < 0 || V < 1 || k < 1 || k > kMaxTopk || k > V) return false;
+    if (dtype != SMCSD_F32 && dtype != SMCSD_BF16) return false;
+    const int32_t epc = dtype == SMCSD_F32 ? 4 : 8;
+    const int32_t c = (int32_t)(((int64_t)V + epc - 1) / epc);
+    const int32_t per_slice = kThreads * kTopkCPL;
+    const int32_t s0 = (c + per_slice - 1) / per_slice;
+    const int32_t q = (c + s0 - 1) / s0;
+    const int32_t s = (c + q - 1) / q;
+    if (s > kMaxTopkSlices) return false;
+    if ((int64_t)rows * s >= (int64_t)INT32_MAX) return false;
+    *chunks = c;
+    *S = s;
+    *cps = q;
+    *bytes = align256(sizeof(BonusPart) * (size_t)rows * s * k);
+    return true;
+}
+
 }  // namespace smcsd
 
 using namespace smcsd;
@@ -390,6 +410,47 @@ smcsd_status smcsd_sd_verify(const smcsd_verify_args* args, smcsd_stream stream)
     va.cps = plan.cps;
     va.chunks = plan.chunks;
     if (launch_verify(a.R, a.dtype, va, s) != hipSuccess) return SMCSD_ERR_DEVICE;
+    return SMCSD_OK;
+}
+
+size_t smcsd_topk_workspace_size(int32_t rows, int32_t V, int32_t dtype, int32_t k) {
+    int32_t chunks, S, cps;
+    size_t bytes;
+    if (!topk_plan(rows, V, dtype, k, &chunks, &S, &cps, &bytes)) return 0;
+    return bytes > 0 ? bytes : 256;
+}
+
+smcsd_status smcsd_gumbel_topk(int32_t rows, int32_t V, int64_t ld, int32_t dtype,
+                               const void* logits, const float* temperature, const float* gumbel,
+                               int32_t k, int32_t* out_tokens, float* out_keys, void* workspace,
+                               size_t workspace_bytes, smcsd_stream stream) {
+    if (rows < 0 || V < 1 || k < 1) return SMCSD_ERR_ARG;
+    if (dtype != SMCSD_F32 && dtype != SMCSD_BF16) return SMCSD_ERR_ARG;
+    const int64_t epc = dtype == SMCSD_F32 ? 4 : 8;
+    if (ld < V || ld % epc != 0 || k > V) return SMCSD_ERR_ARG;
+    int32_t chunks, S, cps;
+    size_t bytes;
+    if (!topk_plan(rows, V, dtype, k, &chunks, &S, &cps, &bytes)) return SMCSD_ERR_UNSUPPORTED;
+    if (rows == 0) return SMCSD_OK;
+    if (!logits || !temperature || !gumbel || !out_tokens) return SMCSD_ERR_ARG;
+    if (!aligned16(logits) || !aligned16(gumbel)) return SMCSD_ERR_ARG;
+    if (!workspace || workspace_bytes < bytes) return SMCSD_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return SMCSD_ERR_WORKSPACE;
+    TopkArgs a{};
+    a.logits = logits;
+    a.temperature = temperature;
+    a.gumbel = gumbel;
+    a.cand = static_cast<BonusPart*>(workspace);
+    a.out_tokens = out_tokens;
+    a.out_keys = out_keys;
+    a.ld = ld;
+    a.V = V;
+    a.k = k;
+    a.chunks = chunks;
+    a.S = S;
+    a.cps = cps;
+    if (launch_topk(rows, dtype, a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+        return SMCSD_ERR_DEVICE;
     return SMCSD_OK;
 }
 

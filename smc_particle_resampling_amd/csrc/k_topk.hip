@@ -1,0 +1,164 @@
+// k_topk.hip -- Gumbel-Top-K: k tokens drawn without replacement from softmax(z/T) in one
+// step, as the STAND page describes for drafting (method item 2): add precomputed, cached
+// Gumbel noise to the log-probabilities and keep the indices of the k largest sums. Adding
+// the row's normaliser to every key changes no ranking, so the keys are the bonus token's,
+// key_v = fl32(fma(z_v, fl32(1/T), G_v)), ranked by decreasing key and then increasing index
+// (a total order, so the selection is exact and deterministic).
+//
+// Pass 1: one 512-thread workgroup per (row, slice), 4 chunks a lane as in the TV pass. Each
+// lane holds its keys in registers and its own best; k rounds of a block argmax over the
+// lanes' bests pick the slice's k best, and only the lane that lost its best rescans. Pass 2:
+// one workgroup per row takes the S * k candidates the same way.
+#include "smcsd_internal.h"
+
+namespace smcsd {
+namespace {
+
+__device__ __forceinline__ void argmax_step(float& k, int32_t& i, float ok, int32_t oi) {
+    if (better(ok, oi, k, i)) {
+        k = ok;
+        i = oi;
+    }
+}
+
+// Block argmax of every lane's (key, index); all threads get the winner. lds holds 2 *
+// kWaves entries per buffer; callers alternate buffers between rounds, so one barrier per
+// round suffices.
+__device__ __forceinline__ void block_argmax(float& k, int32_t& i, float* lk, int32_t* li) {
+    argmax_step(k, i, dpp_f32<kDppXor1>(k), dpp_i32<kDppXor1>(i));
+    argmax_step(k, i, dpp_f32<kDppXor2>(k), dpp_i32<kDppXor2>(i));
+    argmax_step(k, i, dpp_f32<kDppRowHalfMirror>(k), dpp_i32<kDppRowHalfMirror>(i));
+    argmax_step(k, i, dpp_f32<kDppRowMirror>(k), dpp_i32<kDppRowMirror>(i));
+    float bk = readlane_f32(k, 0);
+    int32_t bi = __builtin_amdgcn_readlane(i, 0);
+#pragma unroll
+    for (int r = 16; r < 64; r += 16)
+        argmax_step(bk, bi, readlane_f32(k, r), __builtin_amdgcn_readlane(i, r));
+    const int w = threadIdx.x >> 6;
+    if ((threadIdx.x & 63) == 0) {
+        lk[w] = bk;
+        li[w] = bi;
+    }
+    __syncthreads();
+    bk = lk[0];
+    bi = li[0];
+    for (int t = 1; t < kWaves; ++t) argmax_step(bk, bi, lk[t], li[t]);
+    k = bk;
+    i = bi;
+}
+
+// The lane's best among n (key, index) pairs held in registers.
+template <int n>
+__device__ __forceinline__ void lane_best(const float (&key)[n], const int32_t (&idx)[n], float& bk,
+                                          int32_t& bi) {
+    bk = -INFINITY;
+    bi = INT32_MAX;
+#pragma unroll
+    for (int e = 0; e < n; ++e) argmax_step(bk, bi, key[e], idx[e]);
+}
+
+// k rounds of selection over keys held in registers; writes the winners to out (k entries).
+template <int n>
+__device__ __forceinline__ void select_k(float (&key)[n], int32_t (&idx)[n], int k,
+                                         BonusPart* out, float* lk, int32_t* li) {
+    float bk;
+    int32_t bi;
+    lane_best<n>(key, idx, bk, bi);
+    for (int it = 0; it < k; ++it) {
+        float wk = bk;
+        int32_t wi = bi;
+        const int buf = (it & 1) * kWaves;
+        block_argmax(wk, wi, lk + buf, li + buf);
+        if (threadIdx.x == 0) out[it] = BonusPart{wk, wk == -INFINITY ? INT32_MAX : wi};
+        if (bi == wi && bk != -INFINITY) {
+            // this lane held the winner: drop it and rescan
+#pragma unroll
+            for (int e = 0; e < n; ++e)
+                if (idx[e] == wi) key[e] = -INFINITY;
+            lane_best<n>(key, idx, bk, bi);
+        }
+    }
+}
+
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_topk_slice(TopkArgs a) {
+    constexpr int EPC = DT == SMCSD_F32 ? 4 : 8;
+    constexpr size_t ESZ = DT == SMCSD_F32 ? 4 : 2;
+    constexpr int n = kTopkCPL * EPC;
+    __shared__ float lk[2 * kWaves];
+    __shared__ int32_t li[2 * kWaves];
+    const int64_t row = blockIdx.x / (unsigned)a.S;
+    const int s = (int)(blockIdx.x % (unsigned)a.S);
+    const int tid = threadIdx.x;
+    const char* zrow = static_cast<const char*>(a.logits) + (size_t)(row * a.ld) * ESZ;
+    const float* grow = a.gumbel + (size_t)row * a.ld;
+    const float invT = __fdiv_rn(1.0f, a.temperature[row]);
+    const int c0 = s * a.cps;
+    const int c1 = min(c0 + a.cps, a.chunks);
+    float key[n];
+    int32_t idx[n];
+#pragma unroll
+    for (int j = 0; j < kTopkCPL; ++j) {
+        const int ch = c0 + j * kThreads + tid;
+        u32x4 Z = u32x4{0u, 0u, 0u, 0u};
+        u32x4 G[EPC / 4];
+#pragma unroll
+        for (int h = 0; h < EPC / 4; ++h) G[h] = u32x4{0u, 0u, 0u, 0u};
+        if (ch < c1) {
+            Z = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(zrow) + ch);
+#pragma unroll
+            for (int h = 0; h < EPC / 4; ++h)
+                G[h] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(grow) + (int64_t)ch * (EPC / 4) + h);
+        }
+#pragma unroll
+        for (int e = 0; e < EPC; ++e) {
+            const int32_t v = ch * EPC + e;
+            const bool in = ch < c1 && v < a.V;
+            key[j * EPC + e] = in ? fmaf(chunk_elem<DT>(Z, e), invT, __uint_as_float(G[e >> 2][e & 3]))
+                                  : -INFINITY;
+            idx[j * EPC + e] = in ? v : INT32_MAX;
+        }
+    }
+    select_k<n>(key, idx, a.k, a.cand + (row * a.S + s) * a.k, lk, li);
+}
+
+__global__ __launch_bounds__(kThreads) void k_topk_merge(TopkArgs a) {
+    constexpr int n = kMaxTopk * kMaxTopkSlices / kThreads;   // 8 candidates a lane at most
+    __shared__ float lk[2 * kWaves];
+    __shared__ int32_t li[2 * kWaves];
+    __shared__ BonusPart res[kMaxTopk];
+    const int64_t row = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int m = a.S * a.k;
+    const BonusPart* c = a.cand + row * m;
+    float key[n];
+    int32_t idx[n];
+#pragma unroll
+    for (int e = 0; e < n; ++e) {
+        const int t = e * kThreads + tid;
+        key[e] = t < m ? c[t].key : -INFINITY;
+        idx[e] = t < m ? c[t].idx : INT32_MAX;
+    }
+    select_k<n>(key, idx, a.k, res, lk, li);
+    __syncthreads();
+    for (int j = tid; j < a.k; j += kThreads) {
+        a.out_tokens[row * a.k + j] = res[j].idx;
+        if (a.out_keys) a.out_keys[row * a.k + j] = res[j].key;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_topk(int64_t rows, int32_t dtype, const TopkArgs& a, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    const dim3 block(kThreads);
+    const dim3 g1((unsigned)(rows * a.S));
+    if (dtype == SMCSD_BF16) k_topk_slice<SMCSD_BF16><<<g1, block, 0, s>>>(a);
+    else k_topk_slice<SMCSD_F32><<<g1, block, 0, s>>>(a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    k_topk_merge<<<dim3((unsigned)rows), block, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+}  // namespace smcsd

@@ -134,6 +134,23 @@ struct VerifyArgs {
     int32_t N, K, V, S, cps, chunks;
 };
 
+// Gumbel-Top-K. Slices as in the TV pass (4 chunks a lane); every slice keeps its k best
+// (key, index) pairs, and one workgroup per row merges the S * k candidates.
+constexpr int kTopkCPL = 4;
+constexpr int kMaxTopk = 64;           // == SMCSD_MAX_TOPK
+constexpr int kMaxTopkSlices = 64;     // S * k candidates, at most 8 per lane of the merge
+
+struct TopkArgs {
+    const void* logits;
+    const float* temperature;
+    const float* gumbel;
+    BonusPart* cand;       // [rows][S][k] workspace
+    int32_t* out_tokens;
+    float* out_keys;
+    int64_t ld;
+    int32_t V, k, chunks, S, cps;
+};
+
 struct RemapArgs {
     const int32_t* ancestors;
     const int32_t* pt_in;
@@ -150,6 +167,7 @@ hipError_t launch_finalize(int32_t R, bool from_partials, int32_t dtype, const F
                            hipStream_t s);
 hipError_t launch_remap(int32_t R, const RemapArgs& a, hipStream_t s);
 hipError_t launch_verify(int32_t R, int32_t dtype, const VerifyArgs& a, hipStream_t s);
+hipError_t launch_topk(int64_t rows, int32_t dtype, const TopkArgs& a, hipStream_t s);
 hipError_t launch_bench_read(const void* src, size_t bytes, uint32_t* sink, int32_t grid,
                              hipStream_t s);
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);

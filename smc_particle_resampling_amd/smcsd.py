@@ -73,6 +73,10 @@ _lib.smcsd_verify_workspace_size.restype = _sz
 _lib.smcsd_verify_workspace_size.argtypes = [_i32, _i32, _i32, _i32, _i32]
 _lib.smcsd_verify_args_size.restype = _sz
 _lib.smcsd_verify_args_size.argtypes = []
+_lib.smcsd_gumbel_topk.restype = _i32
+_lib.smcsd_gumbel_topk.argtypes = [_i32, _i32, _i64, _i32, _p, _p, _p, _i32, _p, _p, _p, _sz, _p]
+_lib.smcsd_topk_workspace_size.restype = _sz
+_lib.smcsd_topk_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
 _lib.smcsd_bench_stream_read.restype = _i32
 _lib.smcsd_bench_stream_read.argtypes = [_p, _sz, _p, _i32, _p]
 _lib.smcsd_bench_copy.restype = _i32
@@ -99,6 +103,13 @@ def smcsd_status_string(status: int) -> str:
 
 def smcsd_round_args_size() -> int:
     return int(_lib.smcsd_round_args_size())
+
+
+MAX_TOPK = 64
+
+
+def smcsd_topk_workspace_size(rows: int, V: int, dtype: int, k: int) -> int:
+    return int(_lib.smcsd_topk_workspace_size(rows, V, dtype, k))
 
 
 def smcsd_verify_args_size() -> int:
@@ -256,6 +267,53 @@ def smcsd_sd_verify(*, target_logits, draft_logits, draft_tokens, temperature, g
         raise SmcsdError(st, "smcsd_sd_verify")
 
 
+def smcsd_gumbel_topk(*, logits, temperature, gumbel, k: int, out_tokens, workspace,
+                      out_keys=None, V: int | None = None, stream=None) -> None:
+    """Enqueue Gumbel-Top-K (smcsd_gumbel_topk): logits [rows, ld] float32/bfloat16,
+    temperature [rows], gumbel [rows, ld] float32 -> out_tokens [rows, k] int32 (and
+    out_keys [rows, k] float32), by decreasing key."""
+    dev = logits.device
+    if logits.dtype not in (torch.float32, torch.bfloat16) or logits.dim() != 2:
+        raise ValueError("logits must be a [rows, ld] float32 or bfloat16 tensor")
+    rows, ld = logits.shape
+    V = ld if V is None else int(V)
+    f32, i32 = torch.float32, torch.int32
+    _check(logits, "logits", None, None, dev)
+    _check(temperature, "temperature", f32, (rows,), dev)
+    _check(gumbel, "gumbel", f32, (rows, ld), dev)
+    _check(out_tokens, "out_tokens", i32, (rows, k), dev)
+    if out_keys is not None:
+        _check(out_keys, "out_keys", f32, (rows, k), dev)
+    _check(workspace, "workspace", torch.uint8, None, dev)
+    dt = BF16 if logits.dtype == torch.bfloat16 else F32
+    st = _lib.smcsd_gumbel_topk(rows, V, ld, dt, _ptr(logits), _ptr(temperature), _ptr(gumbel),
+                                int(k), _ptr(out_tokens), _ptr(out_keys), _ptr(workspace),
+                                workspace.numel(), _stream(dev, stream))
+    if st != OK:
+        raise SmcsdError(st, "smcsd_gumbel_topk")
+
+
+def gumbel_topk(logits, temperature, gumbel, k: int, *, V: int | None = None, outputs=None,
+                stream=None) -> dict:
+    """smcsd_gumbel_topk with outputs and workspace allocated here (or reused from
+    ``outputs``). Returns dict(tokens, keys, workspace)."""
+    rows, ld = logits.shape
+    V = ld if V is None else int(V)
+    dev = logits.device
+    if outputs is None:
+        dt = BF16 if logits.dtype == torch.bfloat16 else F32
+        ws = smcsd_topk_workspace_size(rows, V, dt, k)
+        if ws == 0 and rows > 0:
+            raise ValueError("sizes unsupported: rows=%d V=%d k=%d" % (rows, V, k))
+        outputs = dict(tokens=torch.empty((rows, k), dtype=torch.int32, device=dev),
+                       keys=torch.empty((rows, k), dtype=torch.float32, device=dev),
+                       workspace=torch.empty((max(ws, 256),), dtype=torch.uint8, device=dev))
+    smcsd_gumbel_topk(logits=logits, temperature=temperature, gumbel=gumbel, k=k,
+                      out_tokens=outputs["tokens"], out_keys=outputs["keys"],
+                      workspace=outputs["workspace"], V=V, stream=stream)
+    return outputs
+
+
 def smcsd_resample(*, log_w_incr, log_weights, uniform, log_norm, ess, resampled, ancestors,
                    mode="always", ess_frac: float = 0.5, stream=None) -> None:
     """Enqueue normalise + ESS + systematic resampling from given log-weight increments."""
@@ -389,4 +447,4 @@ def run_sd_verify(inputs: dict, *, tv=False, outputs=None, timing_events=None, s
 
 __all__ = [n for n in dir() if n.startswith("smcsd_")] + [
     "RoundArgs", "VerifyArgs", "SmcsdError", "alloc_outputs", "run_round", "run_sd_verify",
-    "library_path", "MODES"]
+    "gumbel_topk", "library_path", "MODES", "MAX_TOPK"]

@@ -162,6 +162,15 @@ def make_verify_uniforms(R: int, N: int, K: int, seed: int, device="cpu") -> dic
                                     device=device, dtype=torch.float32))
 
 
+def topk_rows(inputs: dict):
+    """Gumbel-Top-K drafting inputs from a round's inputs: every particle's first target row
+    as a [R*N, ld] logits matrix, its noise row, and the request temperature per row."""
+    R, N, _, ld = inputs["target"].shape
+    return (inputs["target"][:, :, 0].contiguous().view(R * N, ld),
+            inputs["temperature"].repeat_interleave(N).contiguous(),
+            inputs["gumbel"].view(R * N, ld))
+
+
 def make_page_table(R: int, N: int, P: int, seed: int, ragged: bool = False):
     """Page table [R,N,P] int32 (negative = unused), refcount, num_pages (CPU tensors)."""
     g = _gen(seed, "pages", "cpu")

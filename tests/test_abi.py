@@ -28,7 +28,7 @@ def test_every_declared_symbol_is_exported():
     assert {"smcsd_round", "smcsd_resample", "smcsd_remap_pages", "smcsd_workspace_size",
             "smcsd_status_string", "smcsd_round_args_size", "smcsd_bench_stream_read",
             "smcsd_bench_copy", "smcsd_sd_verify", "smcsd_verify_workspace_size",
-            "smcsd_verify_args_size"} <= names
+            "smcsd_verify_args_size", "smcsd_gumbel_topk", "smcsd_topk_workspace_size"} <= names
     lib = ctypes.CDLL(S.library_path())
     for n in sorted(names):
         assert hasattr(lib, n), n
@@ -185,3 +185,29 @@ def test_verify_validation():
     # TV is always on here: V beyond the TV limit is unsupported
     big = 1048576 + 8
     assert _verify(_vargs(V=big, ld=big)) == S.ERR_UNSUPPORTED
+
+
+def _topk(rows=4, V=1000, ld=1000, dtype=S.BF16, logits=0x20000000, temperature=0x21000000,
+          gumbel=0x22000000, k=8, out_tokens=0x23000000, ws=0x70000000, ws_bytes=None):
+    if ws_bytes is None:
+        ws_bytes = S.smcsd_topk_workspace_size(max(rows, 0), V, dtype, max(k, 1))
+    return S.raw_library().smcsd_gumbel_topk(rows, V, ld, dtype, logits, temperature, gumbel, k,
+                                             out_tokens, None, ws, ws_bytes, None)
+
+
+def test_topk_validation():
+    assert S.smcsd_topk_workspace_size(4, 1000, S.BF16, 8) > 0
+    assert S.smcsd_topk_workspace_size(4, 1000, S.BF16, 0) == 0
+    assert S.smcsd_topk_workspace_size(4, 1000, S.BF16, S.MAX_TOPK + 1) == 0
+    assert S.smcsd_topk_workspace_size(4, 10, S.BF16, 11) == 0              # k > V
+    assert _topk(rows=0) == S.OK
+    assert _topk(k=0) == S.ERR_ARG
+    assert _topk(k=S.MAX_TOPK + 1) == S.ERR_UNSUPPORTED
+    assert _topk(V=10, ld=16, k=11) == S.ERR_ARG                              # k > V
+    assert _topk(ld=1004) == S.ERR_ARG                                        # bf16 ld % 8
+    assert _topk(logits=None) == S.ERR_ARG
+    assert _topk(gumbel=0x22000004) == S.ERR_ARG                              # alignment
+    assert _topk(ws_bytes=16) == S.ERR_WORKSPACE
+    assert _topk(ws=0x70000010) == S.ERR_WORKSPACE
+    big = 1048576 + 8
+    assert _topk(V=big, ld=big) == S.ERR_UNSUPPORTED                         # > 64 slices

@@ -1,0 +1,86 @@
+"""GPU parity of Gumbel-Top-K (smcsd_gumbel_topk) against the oracle, through the C ABI.
+
+Bit-exact: both sides rank the same binary32 keys fl32(fma(z, fl32(1/T), G)) by decreasing
+key and increasing index, so tokens and keys must match exactly, including on heavy ties.
+"""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from smc_particle_resampling_amd import smcsd, synth
+
+pytestmark = pytest.mark.gpu
+W = synth.WORKLOADS
+
+
+def _say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.fixture(scope="module")
+def dev():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch.device("cuda:0")
+
+
+def _host(t):
+    t = t.detach().cpu().contiguous()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def compare(logits, temp, noise, k, V, rows_checked=None):
+    _say("topk case rows", logits.shape[0], "ld", logits.shape[1], "V", V, "k", k, logits.dtype)
+    out = smcsd.gumbel_topk(logits, temp, noise, k, V=V)
+    torch.cuda.synchronize()
+    tok, key = out["tokens"].cpu().numpy(), out["keys"].cpu().numpy()
+    sel = slice(None) if rows_checked is None else rows_checked
+    z, T, G = _host(logits[sel]), _host(temp[sel]), _host(noise[sel])
+    otok, okey = oracle.gumbel_topk(z, T, G, k, V=V)
+    assert np.array_equal(tok[sel], otok), np.argwhere(tok[sel] != otok)[:5].tolist()
+    assert np.array_equal(key[sel], okey)
+    return tok, key
+
+
+@pytest.mark.parametrize("k", [1, 2, 8, 17, 64])
+def test_topk_k_values(k, dev):
+    w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="topk", R=2, N=8, V=40000, ctx=64)
+    inp = synth.make_inputs(w, 1, device=dev, pages=False)
+    z, T, G = synth.topk_rows(inp)
+    compare(z, T, G, k, w.V)
+
+
+@pytest.mark.parametrize("V,dtype,k", [(1, "bf16", 1), (9, "bf16", 9), (7, "f32", 3),
+                                       (64, "bf16", 64), (5001, "bf16", 13), (16385, "f32", 8),
+                                       (1048569, "bf16", 8), (524288, "f32", 5)])
+def test_topk_ragged_and_maximal(V, dtype, k, dev):
+    w = W["r16-n16-k4-v128256-bf16"].scaled(name="topk-ragged", R=2, N=3, V=V, dtype=dtype, ctx=64)
+    inp = synth.make_inputs(w, 2, device=dev, pages=False)
+    z, T, G = synth.topk_rows(inp)
+    compare(z, T, G, k, V)
+
+
+def test_topk_heavy_ties(dev):
+    """Zero noise and logits taking only a few values: ranking is decided by index."""
+    rows, V, k = 6, 30000, 40
+    g = torch.Generator(device=dev)
+    g.manual_seed(5)
+    z = torch.randint(0, 4, (rows, V), generator=g, device=dev).to(torch.bfloat16)
+    T = torch.ones(rows, dtype=torch.float32, device=dev)
+    G = torch.zeros((rows, V), dtype=torch.float32, device=dev)
+    tok, _ = compare(z, T, G, k, V)
+    assert np.all(np.diff(tok, axis=1) > 0)      # all keys equal -> increasing indices
+
+
+def test_topk_full_size_sampled(dev):
+    """2048 rows of V = 128256 bf16 (the headline shape's particles), k = 8; the oracle checks
+    a sample of rows."""
+    w = W["r64-n32-k8-v128256-bf16-tv"]
+    inp = synth.make_inputs(w, 4, device=dev, pages=False)
+    z, T, G = synth.topk_rows(inp)
+    compare(z, T, G, 8, w.V, rows_checked=[0, 1, 777, 2047])
