@@ -64,6 +64,11 @@ class HipEvents:
             raise RuntimeError("hipEventElapsedTime failed")
         return float(ms.value)
 
+    def record(self, e, stream: int):
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        if self.hip.hipEventRecord(e, stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
     def destroy(self, e):
         self.hip.hipEventDestroy(e)
 
@@ -98,11 +103,13 @@ def stored_traffic(workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(w, target_s=12.0, sample_requests=4, path="round"):
+def cpu_baseline(w, target_s=12.0, sample_requests=4, path="round", k=8):
     """The oracle (as it is) on a bounded sample of the workload: the first few requests
     (all N particles, K positions, V logits each), timed with a wall clock around
     oracle.round and repeated until ~target_s of CPU work; rounds/s = 1 / (R * seconds per
     request)."""
+    import numpy as np
+
     import oracle
     from smc_particle_resampling_amd import synth
     rs = min(w.R, sample_requests)
@@ -111,17 +118,24 @@ def cpu_baseline(w, target_s=12.0, sample_requests=4, path="round"):
     if path == "sd_verify":
         inputs.update(synth.make_verify_uniforms(rs, w.N, w.K, 11, device="cpu"))
     host = synth.to_host(inputs)
+    if path == "gumbel_topk":
+        tz, tT, tG = (np.ascontiguousarray(x) for x in (
+            host["target"][:, :, 0].reshape(rs * w.N, -1),
+            np.repeat(host["temperature"], w.N), host["gumbel"].reshape(rs * w.N, -1)))
     times = []
     while not times or (sum(times) < target_s and len(times) < 1000):
         t = time.perf_counter()
-        if path == "sd_verify":
+        if path == "gumbel_topk":
+            oracle.gumbel_topk(tz, tT, tG, k, V=w.V)
+        elif path == "sd_verify":
             oracle.sd_verify(host, V=w.V)
         else:
             oracle.round(host, V=w.V, mode=w.mode, ess_frac=w.ess_frac, tv=w.tv)
         times.append(time.perf_counter() - t)
     per_request = sum(times) / (len(times) * rs)
-    unit = "passes/s" if path == "sd_verify" else "rounds/s"
-    what = "SD verification" if path == "sd_verify" else "round"
+    unit = "rounds/s" if path == "round" else "passes/s"
+    what = {"round": "round", "sd_verify": "SD verification",
+            "gumbel_topk": "Gumbel-Top-K (k=%d) of every particle row" % k}[path]
     return {"value": 1.0 / (w.R * per_request), "unit": unit, "cores": oracle.num_threads(),
             "kind": "oracle",
             "sample": "%d of %d requests (N=%d, K=%d, V=%d, TV %s), fp64 oracle %s over them "
@@ -140,10 +154,12 @@ def main():
     ap.add_argument("--no-read-roofline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run N launches of a plain 1 GiB copy (for counter scaling)")
-    ap.add_argument("--path", choices=("round", "sd_verify"), default="round",
+    ap.add_argument("--path", choices=("round", "sd_verify", "gumbel_topk"), default="round",
                     help="round: one SMC-SD round (smcsd_round, the headline); sd_verify: "
                          "standard speculative-decoding verification of the same blocks "
-                         "(smcsd_sd_verify)")
+                         "(smcsd_sd_verify); gumbel_topk: Gumbel-Top-K drafting of k tokens "
+                         "per particle row (smcsd_gumbel_topk)")
+    ap.add_argument("--topk", type=int, default=8, help="k of --path gumbel_topk")
     args = ap.parse_args()
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
@@ -160,10 +176,24 @@ def main():
     torch.cuda.set_device(dev)
     print("# building inputs for %s" % name, file=sys.stderr, flush=True)
     verify = args.path == "sd_verify"
-    inp = synth.make_inputs(w, 0, device=dev, pages=not verify)
+    topk = args.path == "gumbel_topk"
+    inp = synth.make_inputs(w, 0, device=dev, pages=args.path == "round")
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
-    if verify:
+    if topk:
+        tz, tT, tG = synth.topk_rows(inp)
+        out = smcsd.gumbel_topk(tz, tT, tG, args.topk, V=w.V)
+        out["error_flags"] = torch.zeros((1,), dtype=torch.int32, device=dev)
+        torch.cuda.synchronize()
+        cur = torch.cuda.current_stream(dev).cuda_stream
+
+        def step(t, timing=None):
+            if timing is not None:
+                ev.record(timing[0], cur)
+            smcsd.gumbel_topk(tz, tT, tG, args.topk, V=w.V, outputs=out)
+            if timing is not None:
+                ev.record(timing[1], cur)
+    elif verify:
         inp.update(synth.make_verify_uniforms(w.R, w.N, w.K, 0, device=dev))
         out = smcsd.run_sd_verify(inp)          # allocates the outputs once
         torch.cuda.synchronize()
@@ -202,6 +232,9 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     alg = w.algorithmic_bytes()
     logits_bytes = alg["target"] + alg["draft"] + alg["noise"]
+    if topk:        # one logits row and one noise row per particle
+        e = 2 if w.dtype == "bf16" else 4
+        logits_bytes = w.R * w.N * w.V * (e + 4)
     achieved = logits_bytes / (k_mean_ms * 1e-3) / 1e9
     print("# %s %.3f ms, logits kernel %.3f ms (min %.3f max %.3f)" % (
         args.path, ms_per_step, k_mean_ms, min(kms), max(kms)), file=sys.stderr, flush=True)
@@ -214,8 +247,13 @@ def main():
         del src, dst
 
     rr = None if args.no_read_roofline else read_roofline(smcsd, torch, dev)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, path=args.path)
-    if verify:
+    cpu = None if args.no_cpu_baseline else cpu_baseline(w, path=args.path, k=args.topk)
+    if topk:
+        metric = ("Gumbel-Top-K drafting passes/s and achieved HBM GB/s (%% of peak), "
+                  "%d rows V=%d bf16 k=%d" % (w.R * w.N, w.V, args.topk))
+        unit = "passes/s"
+        table_bytes = 0
+    elif verify:
         metric = ("SD verification passes/s and achieved HBM GB/s (% of peak), "
                   "N=32 K=8 V=128256 bf16")
         unit = "passes/s"
@@ -238,12 +276,16 @@ def main():
         "dtype": w.dtype,
         "data": "synthetic",
         "config": {"workload": name, "path": args.path, "R": w.R, "N": w.N, "K": w.K, "V": w.V,
-                   "tv": w.tv or verify, "resample": None if verify else w.mode,
-                   "pages_per_particle": None if verify else w.P,
+                   "tv": (w.tv or verify) and not topk,
+                   "resample": w.mode if args.path == "round" else None,
+                   "pages_per_particle": w.P if args.path == "round" else None,
+                   "topk": args.topk if topk else None,
                    "round_GBps": (logits_bytes + table_bytes) / (ms_per_step * 1e-3) / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-                     "frac": achieved / PEAK_HBM_GBPS, "traffic": stored_traffic(name),
-                     "kernel": "k_logits", "kernel_ms": k_mean_ms,
+                     "frac": achieved / PEAK_HBM_GBPS,
+                     "traffic": None if topk else stored_traffic(name),
+                     "kernel": "k_topk_slice+k_topk_merge" if topk else "k_logits",
+                     "kernel_ms": k_mean_ms,
                      "algorithmic_bytes_per_launch": logits_bytes,
                      "attainable_read_GBps": rr},
         "cpu_baseline": cpu,

@@ -80,6 +80,20 @@ __device__ __forceinline__ void select_k(float (&key)[n], int32_t (&idx)[n], int
     }
 }
 
+// The lane's best position among n keys whose indices increase with the position: the first
+// position holding the maximum (-1 if every key is -inf).
+template <int n>
+__device__ __forceinline__ int lane_best_pos(const float (&key)[n], float& bk) {
+    float m = key[0];
+#pragma unroll
+    for (int e = 1; e < n; ++e) m = fmaxf(m, key[e]);
+    int pos = -1;
+#pragma unroll
+    for (int e = n - 1; e >= 0; --e) pos = key[e] == m ? e : pos;
+    bk = m;
+    return m == -INFINITY ? -1 : pos;
+}
+
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_topk_slice(TopkArgs a) {
     constexpr int EPC = DT == SMCSD_F32 ? 4 : 8;
@@ -96,7 +110,6 @@ __global__ __launch_bounds__(kThreads) void k_topk_slice(TopkArgs a) {
     const int c0 = s * a.cps;
     const int c1 = min(c0 + a.cps, a.chunks);
     float key[n];
-    int32_t idx[n];
 #pragma unroll
     for (int j = 0; j < kTopkCPL; ++j) {
         const int ch = c0 + j * kThreads + tid;
@@ -116,10 +129,29 @@ __global__ __launch_bounds__(kThreads) void k_topk_slice(TopkArgs a) {
             const bool in = ch < c1 && v < a.V;
             key[j * EPC + e] = in ? fmaf(chunk_elem<DT>(Z, e), invT, __uint_as_float(G[e >> 2][e & 3]))
                                   : -INFINITY;
-            idx[j * EPC + e] = in ? v : INT32_MAX;
         }
     }
-    select_k<n>(key, idx, a.k, a.cand + (row * a.S + s) * a.k, lk, li);
+    // k rounds: block argmax of the lanes' bests; the winning lane drops that key and finds
+    // its next best. A lane's keys are in increasing index order (chunk group, then element).
+    BonusPart* out = a.cand + (row * a.S + s) * a.k;
+    float bk;
+    int pos = lane_best_pos<n>(key, bk);
+    auto index_of = [&](int p) {
+        return p < 0 ? INT32_MAX : (c0 + (p / EPC) * kThreads + tid) * EPC + p % EPC;
+    };
+    for (int it = 0; it < a.k; ++it) {
+        float wk = bk;
+        int32_t wi = index_of(pos);
+        const int32_t mine = wi;
+        const int buf = (it & 1) * kWaves;
+        block_argmax(wk, wi, lk + buf, li + buf);
+        if (tid == 0) out[it] = BonusPart{wk, wk == -INFINITY ? INT32_MAX : wi};
+        if (pos >= 0 && mine == wi) {
+#pragma unroll
+            for (int e = 0; e < n; ++e) key[e] = e == pos ? -INFINITY : key[e];
+            pos = lane_best_pos<n>(key, bk);
+        }
+    }
 }
 
 __global__ __launch_bounds__(kThreads) void k_topk_merge(TopkArgs a) {
