@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
                                         p, p, p, p]
             L.orc_gumbel_topk.restype = None
             L.orc_gumbel_topk.argtypes = [i64, i64, i64, i32, p, p, p, i32, p, p]
+            L.orc_pages_advance.restype = i32
+            L.orc_pages_advance.argtypes = [i32, i32, i32, i32, p, p, p, i32, p, p, p, p, i64]
             L.orc_num_threads.restype = i32
             L.orc_num_threads.argtypes = []
             _lib = L
@@ -253,3 +255,28 @@ def gumbel_topk(logits: np.ndarray, temperature: np.ndarray, gumbel: np.ndarray,
     lib().orc_gumbel_topk(rows, V, ld, dt, _ptr(z), _ptr(temp), _ptr(g), int(k), _ptr(tok),
                           _ptr(key))
     return tok, key
+
+
+def pages_advance(page_table: np.ndarray, refcount: np.ndarray, free_ids: np.ndarray,
+                  n_free: int, len_before, len_after, page_size: int,
+                  kv: np.ndarray | None = None) -> dict:
+    """Page lifecycle between rounds (release at refcount 0, copy-on-write of shared tail
+    pages, fresh pages for new columns) on copies of the given host arrays. page_table
+    [R,N,P] int32, refcount and free_ids [num_pages] int32, kv [num_pages, page_bytes] uint8
+    or None. Returns dict(page_table, refcount, free_ids, n_free, kv, status)."""
+    pt = np.array(page_table, dtype=np.int32, copy=True)
+    rc = np.array(refcount, dtype=np.int32, copy=True)
+    fl = np.array(free_ids, dtype=np.int32, copy=True)
+    R, N, P = pt.shape
+    lb = np.ascontiguousarray(len_before, dtype=np.int32)
+    la = np.ascontiguousarray(len_after, dtype=np.int32)
+    assert lb.shape == (R,) and la.shape == (R,)
+    if kv is None:
+        kvc = np.zeros((rc.size, 1), np.uint8)
+    else:
+        kvc = np.array(kv, dtype=np.uint8, copy=True)
+    nf = np.array([n_free], np.int32)
+    st = lib().orc_pages_advance(R, N, P, int(page_size), _ptr(lb), _ptr(la), _ptr(pt), rc.size,
+                                 _ptr(rc), _ptr(fl), _ptr(nf), _ptr(kvc), kvc.shape[1])
+    return dict(page_table=pt, refcount=rc, free_ids=fl, n_free=int(nf[0]),
+                kv=None if kv is None else kvc, status=int(st))

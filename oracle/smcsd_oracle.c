@@ -512,6 +512,89 @@ void orc_gumbel_topk(int64_t rows, int64_t V, int64_t ld, int32_t dtype, const v
     }
 }
 
+/*
+ * Page lifecycle between rounds (the steps around the SMC-SD round: the page says duplicated
+ * particles share KV pages by copying page metadata and exchanging pointers, section 2; a
+ * shared page that will be written must then be copied first, and pages nobody references
+ * return to the pool). The pages fix none of this; readings P1-P4:
+ *   P1 a page's refcount is -1 while it is free (on the free list) and otherwise counts the
+ *      table entries naming it; the free list is a stack of page ids, popped from the top;
+ *   P2 release: every page with refcount 0 becomes free (refcount -1), pushed in increasing
+ *      page id;
+ *   P3 copy-on-write of the tail: if a request's length is not a multiple of page_size, its
+ *      last (partly filled) column will be written next; there, the first particle (lowest j)
+ *      naming a page keeps it, and every later particle naming the same page gets a fresh
+ *      page (popped), a copy of the page's KV bytes, and refcount 1, the shared page losing
+ *      one reference each time;
+ *   P4 append: the columns the request's new length needs beyond the old one get fresh
+ *      pages, particle by particle (j ascending), column by column.
+ * Pops happen request by request, within a request first every copy (j ascending), then every
+ * append (j, then column ascending). If the free list runs dry, the remaining entries stay -1
+ * and -3 is returned.
+ * Layouts: pt [R][N][P] int32, refcount / free_ids [num_pages], kv [num_pages][page_bytes].
+ */
+int32_t orc_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_size,
+                          const int32_t *len_before, const int32_t *len_after, int32_t *pt,
+                          int32_t num_pages, int32_t *refcount, int32_t *free_ids,
+                          int32_t *n_free, uint8_t *kv, int64_t page_bytes)
+{
+    int32_t err = 0;
+    /* P2 */
+    for (int32_t p = 0; p < num_pages; ++p) {
+        if (refcount[p] == 0) {
+            refcount[p] = -1;
+            free_ids[(*n_free)++] = p;
+        }
+    }
+    for (int32_t r = 0; r < R; ++r) {
+        int32_t *row0 = pt + (size_t)r * N * P;
+        /* P3 */
+        int32_t lb = len_before[r];
+        if (lb > 0 && lb % page_size != 0) {
+            int32_t c = (lb - 1) / page_size;
+            for (int32_t j = 0; j < N; ++j) {
+                int32_t p = row0[(size_t)j * P + c];
+                if (p < 0)
+                    continue;
+                int shared = 0;
+                for (int32_t jj = 0; jj < j; ++jj)
+                    if (row0[(size_t)jj * P + c] == p)
+                        shared = 1;
+                if (!shared)
+                    continue;
+                if (*n_free == 0) {
+                    err = -3;
+                    row0[(size_t)j * P + c] = -1;
+                    refcount[p] -= 1;
+                    continue;
+                }
+                int32_t q = free_ids[--(*n_free)];
+                memcpy(kv + (size_t)q * (size_t)page_bytes, kv + (size_t)p * (size_t)page_bytes,
+                       (size_t)page_bytes);
+                row0[(size_t)j * P + c] = q;
+                refcount[p] -= 1;
+                refcount[q] = 1;
+            }
+        }
+        /* P4 */
+        int32_t c0 = (lb + page_size - 1) / page_size;
+        int32_t c1 = (len_after[r] + page_size - 1) / page_size;
+        for (int32_t j = 0; j < N; ++j) {
+            for (int32_t c = c0; c < c1 && c < P; ++c) {
+                if (*n_free == 0) {
+                    err = -3;
+                    row0[(size_t)j * P + c] = -1;
+                    continue;
+                }
+                int32_t q = free_ids[--(*n_free)];
+                row0[(size_t)j * P + c] = q;
+                refcount[q] = 1;
+            }
+        }
+    }
+    return err;
+}
+
 /* Threads OpenMP would use for the parallel loops above (1 when built without OpenMP). */
 int32_t orc_num_threads(void)
 {

@@ -1,0 +1,122 @@
+"""Pins of the oracle's page lifecycle between rounds (CPU only).
+
+The SMC-SD page (section 2) shares KV pages between duplicated particles by copying page
+metadata and exchanging pointers; the pages say nothing about the pool. Readings P1-P4 (the
+oracle's header): refcount -1 = free, a stack free list, release at refcount 0 in increasing
+id, copy-on-write of a shared partly filled tail page (the lowest particle keeps it), fresh
+pages for new columns. Pinned by a hand-worked case and, on random genealogies over several
+rounds, by invariants recounted with numpy: every table entry names an allocated page, every
+allocated page's refcount equals its number of table entries, the free list holds exactly the
+free pages once each, the written tail column is private to each particle, copied pages carry
+the source's KV bytes, and pages are conserved.
+"""
+import numpy as np
+import pytest
+
+import oracle
+from smc_particle_resampling_amd import synth
+
+
+def test_hand_worked_advance():
+    num_pages, page_bytes = 16, 8
+    rc = np.full(num_pages, -1, np.int32)
+    free = np.zeros(num_pages, np.int32)
+    init_free = list(range(10)) + [14, 15]
+    free[:12] = init_free
+    pt = np.array([[[10, 11, -1], [10, 11, -1], [10, 12, -1]]], np.int32)
+    rc[10], rc[11], rc[12], rc[13] = 3, 2, 1, 0
+    kv = np.arange(num_pages * page_bytes, dtype=np.uint8).reshape(num_pages, page_bytes)
+    out = oracle.pages_advance(pt, rc, free, 12, [6], [9], 4, kv)
+    assert out["status"] == 0
+    # release pushes 13; copy-on-write pops it for particle 1; appends pop 15, 14, 9
+    assert out["page_table"].tolist() == [[[10, 11, 15], [10, 13, 14], [10, 12, 9]]]
+    assert out["n_free"] == 9 and out["free_ids"][:9].tolist() == list(range(9))
+    assert out["refcount"][[10, 11, 12, 13, 14, 15, 9]].tolist() == [3, 1, 1, 1, 1, 1, 1]
+    assert np.array_equal(out["kv"][13], kv[11])
+    assert np.array_equal(np.delete(out["kv"], 13, 0), np.delete(kv, 13, 0))
+
+
+def test_release_order_and_no_copy_on_full_tail():
+    num_pages = 8
+    rc = np.array([0, -1, 0, 2, -1, 0, -1, -1], np.int32)
+    free = np.array([1, 4, 6, 7, 0, 0, 0, 0], np.int32)
+    pt = np.array([[[3, -1], [3, -1]]], np.int32)
+    # length 4 with page size 4: the tail page is full, nothing is written into it
+    out = oracle.pages_advance(pt, rc, free, 4, [4], [4], 4)
+    assert out["n_free"] == 7
+    assert out["free_ids"][:7].tolist() == [1, 4, 6, 7, 0, 2, 5]
+    assert out["page_table"].tolist() == pt.tolist() and out["refcount"][3] == 2
+
+
+def test_out_of_pages():
+    rc = np.array([3, -1], np.int32)
+    free = np.array([1, 0], np.int32)
+    pt = np.array([[[0, -1], [0, -1], [0, -1]]], np.int32)
+    out = oracle.pages_advance(pt, rc, free, 1, [2], [3], 2)   # 2 copies, 1 free page
+    assert out["status"] == -3
+
+
+def _check_invariants(pt, rc, free, n_free, num_pages, tail_cols=None):
+    used = pt[pt >= 0]
+    counts = np.bincount(used, minlength=num_pages)
+    allocated = rc >= 0
+    assert np.all(allocated[used])                                   # entries name live pages
+    assert np.array_equal(rc[allocated], counts[allocated])          # refcount = entries
+    fl = free[:n_free]
+    assert len(set(fl.tolist())) == n_free                           # no duplicates
+    assert np.all(rc[fl] == -1) and int((rc == -1).sum()) == n_free  # exactly the free pages
+    assert np.all(counts[rc == -1] == 0)
+    if tail_cols is not None:
+        for r, c in enumerate(tail_cols):
+            if c is not None:
+                col = pt[r, :, c]
+                col = col[col >= 0]
+                assert len(set(col.tolist())) == col.size                # private tail pages
+
+
+@pytest.mark.parametrize("page_size,K", [(16, 8), (4, 3), (5, 4)])
+def test_multi_round_invariants(page_size, K):
+    rng = np.random.default_rng(page_size * 10 + K)
+    R, N, ctx, rounds = 3, 12, 37, 6
+    P = (ctx + rounds * (K + 1) + page_size - 1) // page_size + 1
+    P0 = (ctx + page_size - 1) // page_size
+    pt0, rc0, _ = synth.make_page_table(R, N, P0, seed=4)
+    pt = np.full((R, N, P), -1, np.int32)
+    pt[:, :, :P0] = pt0.numpy()
+    used_pages = rc0.numel()
+    num_pages = used_pages + R * N * (P - P0) * 2
+    rc = np.full(num_pages, -1, np.int32)
+    rc[:used_pages] = rc0.numpy()
+    free = np.zeros(num_pages, np.int32)
+    n_free = num_pages - used_pages
+    free[:n_free] = np.arange(used_pages, num_pages)[::-1]
+    kv = rng.integers(0, 256, (num_pages, 4), dtype=np.uint8)
+    length = np.full(R, ctx, np.int32)
+    _check_invariants(pt, rc, free, n_free, num_pages)
+    for t in range(rounds):
+        anc = np.sort(rng.integers(0, N, (R, N)), axis=1).astype(np.int32)
+        new = np.empty_like(pt)
+        for r in range(R):
+            new[r], rc, st = oracle.remap_request(anc[r], pt[r], rc)
+            assert st == 0
+        pt = new
+        nxt = length + K + 1
+        out = oracle.pages_advance(pt, rc, free, n_free, length, nxt, page_size, kv)
+        assert out["status"] == 0
+        tail = [int((l - 1) // page_size) if l % page_size else None for l in length]
+        copied = {}
+        for r in range(R):
+            for j in range(N):
+                for c in range(P):
+                    a, b = pt[r, j, c], out["page_table"][r, j, c]
+                    if a >= 0 and b != a:
+                        copied[b] = a
+        for dst, src in copied.items():
+            assert np.array_equal(out["kv"][dst], kv[src])
+        pt, rc, free, n_free, kv = (out["page_table"], out["refcount"], out["free_ids"],
+                                    out["n_free"], out["kv"])
+        _check_invariants(pt, rc, free, n_free, num_pages, tail)
+        need = (nxt + page_size - 1) // page_size
+        for r in range(R):
+            assert np.all(pt[r, :, :need[r]] >= 0) and np.all(pt[r, :, need[r]:] < 0)
+        length = nxt
