@@ -44,7 +44,7 @@ def lib() -> ctypes.CDLL:
     global _lib
     with _lock:
         if _lib is None:
-            if not os.path.exists(_SO):
+            if not os.path.exists(_SO) or os.path.getmtime(_SO) < os.path.getmtime(_SRC):
                 build()
             L = ctypes.CDLL(_SO)
             p, i32, i64, f64, f32 = (ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64,
@@ -68,7 +68,7 @@ def lib() -> ctypes.CDLL:
             L.orc_gumbel_topk.restype = None
             L.orc_gumbel_topk.argtypes = [i64, i64, i64, i32, p, p, p, i32, p, p]
             L.orc_pages_advance.restype = i32
-            L.orc_pages_advance.argtypes = [i32, i32, i32, i32, p, p, p, i32, p, p, p, p, i64]
+            L.orc_pages_advance.argtypes = [i32, i32, i32, i32, p, p, p, i32, p, p, p, p, i64, i32]
             L.orc_num_threads.restype = i32
             L.orc_num_threads.argtypes = []
             _lib = L
@@ -262,8 +262,10 @@ def pages_advance(page_table: np.ndarray, refcount: np.ndarray, free_ids: np.nda
                   kv: np.ndarray | None = None) -> dict:
     """Page lifecycle between rounds (release at refcount 0, copy-on-write of shared tail
     pages, fresh pages for new columns) on copies of the given host arrays. page_table
-    [R,N,P] int32, refcount and free_ids [num_pages] int32, kv [num_pages, page_bytes] uint8
-    or None. Returns dict(page_table, refcount, free_ids, n_free, kv, status)."""
+    [R,N,P] int32, refcount and free_ids [num_pages] int32, kv uint8 [num_pages, page_bytes]
+    or [kv_count, num_pages, page_bytes] (one tensor per layer and K / V) or None.
+    Lengths satisfy 0 <= len_before <= len_after <= P * page_size.
+    Returns dict(page_table, refcount, free_ids, n_free, kv, status)."""
     pt = np.array(page_table, dtype=np.int32, copy=True)
     rc = np.array(refcount, dtype=np.int32, copy=True)
     fl = np.array(free_ids, dtype=np.int32, copy=True)
@@ -271,12 +273,20 @@ def pages_advance(page_table: np.ndarray, refcount: np.ndarray, free_ids: np.nda
     lb = np.ascontiguousarray(len_before, dtype=np.int32)
     la = np.ascontiguousarray(len_after, dtype=np.int32)
     assert lb.shape == (R,) and la.shape == (R,)
+    assert page_size >= 1 and (lb >= 0).all() and (lb <= la).all() and (la <= P * page_size).all()
+    assert fl.size == rc.size and 0 <= n_free <= fl.size
     if kv is None:
-        kvc = np.zeros((rc.size, 1), np.uint8)
+        kvc = np.zeros((1, rc.size, 1), np.uint8)
     else:
         kvc = np.array(kv, dtype=np.uint8, copy=True)
+        if kvc.ndim == 2:
+            kvc = kvc[None]
+        assert kvc.ndim == 3 and kvc.shape[1] == rc.size
     nf = np.array([n_free], np.int32)
     st = lib().orc_pages_advance(R, N, P, int(page_size), _ptr(lb), _ptr(la), _ptr(pt), rc.size,
-                                 _ptr(rc), _ptr(fl), _ptr(nf), _ptr(kvc), kvc.shape[1])
+                                 _ptr(rc), _ptr(fl), _ptr(nf), _ptr(kvc), kvc.shape[2],
+                                 kvc.shape[0])
+    if kv is not None and np.ndim(kv) == 2:
+        kvc = kvc[0]
     return dict(page_table=pt, refcount=rc, free_ids=fl, n_free=int(nf[0]),
                 kv=None if kv is None else kvc, status=int(st))

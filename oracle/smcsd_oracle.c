@@ -531,13 +531,16 @@ void orc_gumbel_topk(int64_t rows, int64_t V, int64_t ld, int32_t dtype, const v
  * Pops happen request by request, within a request first every copy (j ascending), then every
  * append (j, then column ascending). If the free list runs dry, the remaining entries stay -1
  * and -3 is returned.
- * Layouts: pt [R][N][P] int32, refcount / free_ids [num_pages], kv [num_pages][page_bytes].
+ * Layouts: pt [R][N][P] int32, refcount / free_ids [num_pages], kv [kv_count][num_pages]
+ * [page_bytes]: a page id names the same page in every one of the kv_count KV tensors (one
+ * per layer and per K / V), and a copy copies it in all of them.
  */
 int32_t orc_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_size,
                           const int32_t *len_before, const int32_t *len_after, int32_t *pt,
                           int32_t num_pages, int32_t *refcount, int32_t *free_ids,
-                          int32_t *n_free, uint8_t *kv, int64_t page_bytes)
+                          int32_t *n_free, uint8_t *kv, int64_t page_bytes, int32_t kv_count)
 {
+    const size_t tensor_bytes = (size_t)num_pages * (size_t)page_bytes;
     int32_t err = 0;
     /* P2 */
     for (int32_t p = 0; p < num_pages; ++p) {
@@ -569,8 +572,10 @@ int32_t orc_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_size,
                     continue;
                 }
                 int32_t q = free_ids[--(*n_free)];
-                memcpy(kv + (size_t)q * (size_t)page_bytes, kv + (size_t)p * (size_t)page_bytes,
-                       (size_t)page_bytes);
+                for (int32_t t = 0; t < kv_count; ++t)
+                    memcpy(kv + t * tensor_bytes + (size_t)q * (size_t)page_bytes,
+                           kv + t * tensor_bytes + (size_t)p * (size_t)page_bytes,
+                           (size_t)page_bytes);
                 row0[(size_t)j * P + c] = q;
                 refcount[p] -= 1;
                 refcount[q] = 1;

@@ -120,3 +120,21 @@ def test_multi_round_invariants(page_size, K):
         for r in range(R):
             assert np.all(pt[r, :, :need[r]] >= 0) and np.all(pt[r, :, need[r]:] < 0)
         length = nxt
+
+
+def test_layered_kv_copies_every_tensor():
+    # Three KV tensors (say K and V of two layers) share the page ids: the copy-on-write of
+    # page 11 into the popped page 13 happens in each of them, and nothing else changes.
+    num_pages, page_bytes, T = 16, 8, 3
+    rc = np.full(num_pages, -1, np.int32)
+    free = np.zeros(num_pages, np.int32)
+    free[:12] = list(range(10)) + [14, 15]
+    pt = np.array([[[10, 11, -1], [10, 11, -1], [10, 12, -1]]], np.int32)
+    rc[10], rc[11], rc[12], rc[13] = 3, 2, 1, 0
+    kv = np.random.default_rng(5).integers(0, 256, (T, num_pages, page_bytes), dtype=np.uint8)
+    out = oracle.pages_advance(pt, rc, free, 12, [6], [9], 4, kv)
+    assert out["page_table"].tolist() == [[[10, 11, 15], [10, 13, 14], [10, 12, 9]]]
+    want = kv.copy()
+    want[:, 13] = kv[:, 11]
+    assert np.array_equal(out["kv"], want)
+    assert np.array_equal(kv, np.random.default_rng(5).integers(0, 256, kv.shape, dtype=np.uint8))
