@@ -66,6 +66,10 @@ typedef enum smcsd_resample_mode {
 #define SMCSD_DEVERR_PAGE 4u      /* page id >= num_pages; its refcount update is skipped */
 #define SMCSD_DEVERR_REFCOUNT 8u  /* a refcount went below zero (inconsistent input table) */
 #define SMCSD_DEVERR_EXCHANGE 16u /* a TV slice exchange exceeded its time limit (results void) */
+#define SMCSD_DEVERR_POOL 32u     /* page free list ran dry (or its count was out of range): the
+                                     entries it could not fill are left -1 */
+#define SMCSD_DEVERR_LENGTH 64u   /* a request's lengths are not 0 <= before <= after <=
+                                     P * page_size: its pages are left as they were */
 
 /* Build limits. */
 #define SMCSD_MAX_N 1024 /* particles per request */
@@ -186,6 +190,48 @@ smcsd_status smcsd_remap_pages(int32_t R, int32_t N, int32_t P, const int32_t *a
                                const int32_t *page_table_in, int32_t *page_table_out,
                                int32_t *refcount, int32_t num_pages, int32_t *error_flags,
                                smcsd_stream stream);
+
+/*
+ * Page lifecycle between rounds, the steps on either side of the remap ("Faster LLM
+ * Inference via Sequential Monte Carlo", section 2, KV-cache management: duplicated
+ * particles share KV pages through page metadata; the page leaves the pool itself open).
+ * Readings, applied in this order:
+ *  1. release: every page with refcount 0 goes on the free list, in increasing page id, and
+ *     gets refcount -1 (the mark of a free page). free_ids[0 .. *n_free) is a stack: pushes
+ *     go to free_ids[*n_free], pops take free_ids[*n_free - 1].
+ *  2. copy-on-write: when len_before[r] is not a multiple of page_size, column
+ *     c = (len_before[r] - 1) / page_size is partly filled and is written next. In that
+ *     column the lowest particle naming a page keeps it; every later particle naming the same
+ *     page pops a fresh page q, the KV bytes of the page are copied to q in every KV tensor,
+ *     refcount[q] = 1 and the shared page's refcount drops by one.
+ *  3. append: columns ceil(len_before/page_size) .. ceil(len_after/page_size) - 1 of every
+ *     particle get fresh pages with refcount 1, particle by particle, column by column.
+ *  Pops go request by request; within a request the copies (particle order) come before the
+ *  appends. The result equals that sequential order exactly.
+ * Arguments (device memory unless stated):
+ *  len_before, len_after [R] int32: tokens held before and after the round, with
+ *    0 <= len_before <= len_after <= P * page_size (else SMCSD_DEVERR_LENGTH and the request
+ *    is left untouched);
+ *  page_table [R][N][P] int32, in/out: page ids, -1 = unused; the entries appended to must
+ *    be -1 on entry;
+ *  refcount, free_ids [num_pages] int32, in/out; n_free [1] int32, in/out;
+ *  kv: NULL (tables only) or kv_count KV tensors, tensor t's page p at byte
+ *    kv + t * kv_stride + p * page_bytes; kv, page_bytes and kv_stride multiples of 16,
+ *    kv_stride >= num_pages * page_bytes when kv_count > 1;
+ *  workspace of smcsd_pages_workspace_size(R, N, P, num_pages) bytes; error_flags optional.
+ * A page must not be named by two requests' tables. If the free list runs dry, the
+ * entries it cannot fill stay -1 and SMCSD_DEVERR_POOL is set.
+ */
+smcsd_status smcsd_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_size,
+                                 const int32_t *len_before, const int32_t *len_after,
+                                 int32_t *page_table, int32_t num_pages, int32_t *refcount,
+                                 int32_t *free_ids, int32_t *n_free, void *kv,
+                                 int64_t page_bytes, int32_t kv_count, int64_t kv_stride,
+                                 void *workspace, size_t workspace_bytes, int32_t *error_flags,
+                                 smcsd_stream stream);
+
+/* Workspace bytes smcsd_pages_advance needs (0 if the sizes are invalid). */
+size_t smcsd_pages_workspace_size(int32_t R, int32_t N, int32_t P, int32_t num_pages);
 
 /* Workspace bytes smcsd_round needs for these sizes (0 if the sizes are invalid). */
 size_t smcsd_workspace_size(int32_t R, int32_t N, int32_t K, int32_t V, int32_t dtype,

@@ -332,6 +332,106 @@ smcsd_status smcsd_remap_pages(int32_t R, int32_t N, int32_t P, const int32_t* a
     return e == hipSuccess ? SMCSD_OK : SMCSD_ERR_DEVICE;
 }
 
+// Workspace of the page lifecycle; false if the sizes are invalid or too large.
+struct PagesLayout {
+    int64_t chunks = 0;
+    size_t off_hdr = 0, off_req = 0, off_rank = 0, off_chunk = 0, off_copies = 0, bytes = 0;
+};
+
+static bool pages_layout(int32_t R, int32_t N, int32_t P, int32_t num_pages, PagesLayout* L) {
+    if (R < 0 || N < 1 || P < 1 || num_pages < 1) return false;
+    if (N > SMCSD_MAX_N) return false;
+    // Pops, page-table offsets and grid sizes are int32 on the device.
+    if ((int64_t)R * N * P >= (int64_t)INT32_MAX) return false;
+    L->chunks = ((int64_t)num_pages + kPageChunk - 1) / kPageChunk;
+    if ((int64_t)R + L->chunks >= (int64_t)INT32_MAX) return false;
+    size_t o = 0;
+    L->off_hdr = o;
+    o = align256(o + 4 * sizeof(int32_t));
+    L->off_req = o;                                   // req_cow, req_pops, req_base, cow_base
+    o = align256(o + 4 * sizeof(int32_t) * (size_t)R);
+    L->off_rank = o;
+    o = align256(o + sizeof(int32_t) * (size_t)R * N);
+    L->off_chunk = o;                                 // chunk_cnt, chunk_off
+    o = align256(o + 2 * sizeof(int32_t) * (size_t)L->chunks);
+    L->off_copies = o;
+    o = align256(o + sizeof(int2) * (size_t)R * N);
+    L->bytes = o;
+    return true;
+}
+
+size_t smcsd_pages_workspace_size(int32_t R, int32_t N, int32_t P, int32_t num_pages) {
+    PagesLayout L;
+    return pages_layout(R, N, P, num_pages, &L) ? L.bytes : 0;
+}
+
+smcsd_status smcsd_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_size,
+                                 const int32_t* len_before, const int32_t* len_after,
+                                 int32_t* page_table, int32_t num_pages, int32_t* refcount,
+                                 int32_t* free_ids, int32_t* n_free, void* kv,
+                                 int64_t page_bytes, int32_t kv_count, int64_t kv_stride,
+                                 void* workspace, size_t workspace_bytes, int32_t* error_flags,
+                                 smcsd_stream stream) {
+    if (R < 0 || N < 1 || P < 1 || page_size < 1 || num_pages < 1) return SMCSD_ERR_ARG;
+    PagesLayout L;
+    if (!pages_layout(R, N, P, num_pages, &L)) return SMCSD_ERR_UNSUPPORTED;
+    if (!refcount || !free_ids || !n_free) return SMCSD_ERR_ARG;
+    if (R > 0 && (!len_before || !len_after || !page_table)) return SMCSD_ERR_ARG;
+    int64_t max_units = 0;
+    if (kv) {
+        if (page_bytes < 16 || page_bytes % 16 != 0 || !aligned16(kv) || kv_count < 1)
+            return SMCSD_ERR_ARG;
+        if (page_bytes > INT64_MAX / num_pages) return SMCSD_ERR_ARG;
+        if (kv_count > 1 && (kv_stride % 16 != 0 || kv_stride < page_bytes * num_pages))
+            return SMCSD_ERR_ARG;
+        const int64_t tiles = (page_bytes + kCopyTile - 1) / kCopyTile;
+        max_units = (int64_t)R * N * kv_count * tiles;
+    }
+    if (!workspace || workspace_bytes < L.bytes) return SMCSD_ERR_WORKSPACE;
+    const size_t pb = sizeof(int32_t) * (size_t)num_pages;
+    const size_t tb = sizeof(int32_t) * (size_t)R * N * P;
+    const void* bufs[5] = {page_table, refcount, free_ids, n_free, workspace};
+    const size_t sizes[5] = {tb, pb, pb, sizeof(int32_t), L.bytes};
+    for (int i = 0; i < 5; ++i)
+        for (int k = i + 1; k < 5; ++k)
+            if (bufs[i] && bufs[k] && overlap(bufs[i], sizes[i], bufs[k], sizes[k]))
+                return SMCSD_ERR_ARG;
+    char* ws = static_cast<char*>(workspace);
+    PagesArgs a{};
+    a.len_before = len_before;
+    a.len_after = len_after;
+    a.page_table = page_table;
+    a.refcount = refcount;
+    a.free_ids = free_ids;
+    a.n_free = n_free;
+    a.kv = kv;
+    a.page_bytes = page_bytes;
+    a.kv_stride = kv_stride;
+    a.kv_count = kv ? kv_count : 0;
+    int32_t* req = reinterpret_cast<int32_t*>(ws + L.off_req);
+    a.hdr = reinterpret_cast<int32_t*>(ws + L.off_hdr);
+    a.req_cow = req;
+    a.req_pops = req + R;
+    a.req_base = req + 2 * (size_t)R;
+    a.cow_base = req + 3 * (size_t)R;
+    a.cow_rank = reinterpret_cast<int32_t*>(ws + L.off_rank);
+    a.chunk_cnt = reinterpret_cast<int32_t*>(ws + L.off_chunk);
+    a.chunk_off = a.chunk_cnt + L.chunks;
+    a.copies = reinterpret_cast<int2*>(ws + L.off_copies);
+    a.error_flags = error_flags;
+    a.R = R;
+    a.N = N;
+    a.P = P;
+    a.page_size = page_size;
+    a.num_pages = num_pages;
+    a.chunks = (int32_t)L.chunks;
+    // The copy kernel strides over the device-side number of copies; 2048 workgroups
+    // (8 per CU) keep every CU streaming when there are many.
+    const int32_t copy_grid = (int32_t)std::min<int64_t>(max_units, 2048);
+    const hipError_t e = launch_pages(a, copy_grid, reinterpret_cast<hipStream_t>(stream));
+    return e == hipSuccess ? SMCSD_OK : SMCSD_ERR_DEVICE;
+}
+
 smcsd_status smcsd_bench_stream_read(const void* src, size_t bytes, uint32_t* sink,
                                      int32_t grid, smcsd_stream stream) {
     if (!src || !sink || grid < 1 || bytes % 16 != 0 || !aligned16(src)) return SMCSD_ERR_ARG;

@@ -151,6 +151,35 @@ struct TopkArgs {
     int32_t V, k, chunks, S, cps;
 };
 
+// Page lifecycle between rounds. Workspace: a header (free count before and after release,
+// pops, copies), per-request counts and offsets, per-particle copy ranks, per-chunk release
+// counts and offsets, and the list of (source, destination) page copies.
+constexpr int kPageChunk = 4096;       // pages per workgroup of the release count / push
+constexpr int kCopyTile = 32768;       // bytes per workgroup step of the KV page copy
+
+struct PagesArgs {
+    const int32_t* len_before;
+    const int32_t* len_after;
+    int32_t* page_table;
+    int32_t* refcount;
+    int32_t* free_ids;
+    int32_t* n_free;
+    void* kv;
+    int64_t page_bytes, kv_stride;
+    int32_t kv_count;
+    int32_t* hdr;          // [4]: free count before release, after release, pops, copies
+    int32_t* req_cow;      // [R]
+    int32_t* req_pops;     // [R]
+    int32_t* req_base;     // [R] first pop of the request
+    int32_t* cow_base;     // [R] first copy of the request
+    int32_t* cow_rank;     // [R][N] copy rank within the request, -1 = no copy
+    int32_t* chunk_cnt;    // [chunks]
+    int32_t* chunk_off;    // [chunks]
+    int2* copies;          // [R*N] (source page, destination page or -1)
+    int32_t* error_flags;
+    int32_t R, N, P, page_size, num_pages, chunks;
+};
+
 struct RemapArgs {
     const int32_t* ancestors;
     const int32_t* pt_in;
@@ -168,6 +197,7 @@ hipError_t launch_finalize(int32_t R, bool from_partials, int32_t dtype, const F
 hipError_t launch_remap(int32_t R, const RemapArgs& a, hipStream_t s);
 hipError_t launch_verify(int32_t R, int32_t dtype, const VerifyArgs& a, hipStream_t s);
 hipError_t launch_topk(int64_t rows, int32_t dtype, const TopkArgs& a, hipStream_t s);
+hipError_t launch_pages(const PagesArgs& a, int32_t copy_grid, hipStream_t s);
 hipError_t launch_bench_read(const void* src, size_t bytes, uint32_t* sink, int32_t grid,
                              hipStream_t s);
 hipError_t launch_bench_copy(const void* src, void* dst, size_t bytes, hipStream_t s);

@@ -24,6 +24,7 @@ F32, BF16 = 0, 1
 RESAMPLE_ALWAYS, RESAMPLE_ESS, RESAMPLE_NEVER = 0, 1, 2
 MODES = {"always": RESAMPLE_ALWAYS, "ess": RESAMPLE_ESS, "never": RESAMPLE_NEVER}
 DEVERR_TOKEN, DEVERR_ANCESTOR, DEVERR_PAGE, DEVERR_REFCOUNT, DEVERR_EXCHANGE = 1, 2, 4, 8, 16
+DEVERR_POOL, DEVERR_LENGTH = 32, 64
 MAX_N, MAX_K = 1024, 256
 
 _i32, _i64, _f32, _p, _sz = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_void_p, ctypes.c_size_t
@@ -78,6 +79,11 @@ _lib.smcsd_gumbel_topk.argtypes = [_i32, _i32, _i64, _i32, _p, _p, _p, _i32, _p,
 _lib.smcsd_topk_workspace_size.restype = _sz
 _lib.smcsd_topk_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
 _lib.smcsd_bench_stream_read.restype = _i32
+_lib.smcsd_pages_advance.restype = _i32
+_lib.smcsd_pages_advance.argtypes = [_i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p, _p, _p,
+                                     _i64, _i32, _i64, _p, _sz, _p, _p]
+_lib.smcsd_pages_workspace_size.restype = _sz
+_lib.smcsd_pages_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
 _lib.smcsd_bench_stream_read.argtypes = [_p, _sz, _p, _i32, _p]
 _lib.smcsd_bench_copy.restype = _i32
 _lib.smcsd_bench_copy.argtypes = [_p, _p, _sz, _p]
@@ -352,6 +358,50 @@ def smcsd_remap_pages(*, ancestors, page_table_in, page_table_out, refcount, err
                                 _ptr(error_flags), _stream(dev, stream))
     if st != OK:
         raise SmcsdError(st, "smcsd_remap_pages")
+
+
+def smcsd_pages_workspace_size(R: int, N: int, P: int, num_pages: int) -> int:
+    return int(_lib.smcsd_pages_workspace_size(R, N, P, num_pages))
+
+
+def smcsd_pages_advance(*, len_before, len_after, page_table, refcount, free_ids, n_free,
+                        page_size: int, workspace, kv=None, error_flags=None,
+                        stream=None) -> None:
+    """Enqueue the page lifecycle between rounds (smcsd_pages_advance). page_table [R,N,P],
+    len_before / len_after [R], refcount / free_ids [num_pages], n_free [1], all int32; kv
+    None or a uint8 tensor [num_pages, page_bytes] or [kv_count, num_pages, page_bytes]."""
+    dev = page_table.device
+    R, N, P = page_table.shape
+    i32 = torch.int32
+    _check(page_table, "page_table", i32, (R, N, P), dev)
+    _check(len_before, "len_before", i32, (R,), dev)
+    _check(len_after, "len_after", i32, (R,), dev)
+    _check(refcount, "refcount", i32, None, dev)
+    num_pages = refcount.numel()
+    _check(free_ids, "free_ids", i32, (num_pages,), dev)
+    _check(n_free, "n_free", i32, (1,), dev)
+    _check(workspace, "workspace", torch.uint8, None, dev)
+    page_bytes, kv_count, kv_stride = 0, 0, 0
+    if kv is not None:
+        _check(kv, "kv", torch.uint8, None, dev)
+        if kv.dim() == 2:
+            kv_count, page_bytes = 1, kv.shape[1]
+        elif kv.dim() == 3:
+            kv_count, page_bytes = kv.shape[0], kv.shape[2]
+        else:
+            raise ValueError("kv must be [num_pages, page_bytes] or [kv_count, num_pages, page_bytes]")
+        if kv.shape[-2] != num_pages:
+            raise ValueError("kv holds %d pages, refcount %d" % (kv.shape[-2], num_pages))
+        kv_stride = num_pages * page_bytes
+    if error_flags is not None:
+        _check(error_flags, "error_flags", i32, None, dev)
+    st = _lib.smcsd_pages_advance(R, N, P, int(page_size), _ptr(len_before), _ptr(len_after),
+                                  _ptr(page_table), num_pages, _ptr(refcount), _ptr(free_ids),
+                                  _ptr(n_free), _ptr(kv), page_bytes, kv_count, kv_stride,
+                                  _ptr(workspace), workspace.numel(), _ptr(error_flags),
+                                  _stream(dev, stream))
+    if st != OK:
+        raise SmcsdError(st, "smcsd_pages_advance")
 
 
 def smcsd_bench_stream_read(src: torch.Tensor, sink: torch.Tensor, grid: int, stream=None) -> None:

@@ -24,6 +24,11 @@ and rounded to bf16 with round-to-nearest-even where the workload is bf16):
     each later column first copies every particle's earlier columns from an ancestor drawn
     uniformly, then gives each particle a fresh page; ids are finally mapped through a
     seeded permutation of the pool; refcount = number of table entries naming each page.
+  * page pool between rounds (make_page_pool): per request a length drawn uniformly, its
+    columns grown with the same genealogy, then one last uniform draw of ancestors (as a
+    resampling step leaves them, duplicates sharing every page, tail included); pages the
+    draws dropped keep refcount 0, ``spare`` more pages sit on the free list (refcount -1)
+    in a seeded order; KV bytes uniform.
 """
 from __future__ import annotations
 
@@ -33,7 +38,7 @@ import math
 import torch
 
 STREAMS = dict(target=1, peaks=2, draft=3, tokens=4, gumbel=5, uniform=6, temp=7, pages=8,
-               ragged=9, zipf_q=10, potential=11, accept=12, residual=13)
+               ragged=9, zipf_q=10, potential=11, accept=12, residual=13, pool=14, kv=15)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -198,6 +203,61 @@ def make_page_table(R: int, N: int, P: int, seed: int, ragged: bool = False):
     valid = table[table >= 0].to(torch.int64)
     refcount = torch.bincount(valid, minlength=num_pages).to(torch.int32)
     return table.contiguous(), refcount.contiguous(), int(num_pages)
+
+
+def make_page_pool(R: int, N: int, P: int, page_size: int, seed: int, steps=None,
+                   spare: int = 64, kv_count: int = 0, page_bytes: int = 0,
+                   min_len: int = 1) -> dict:
+    """A consistent paged-KV pool between two rounds, as CPU tensors: page_table [R,N,P]
+    int32 (-1 past each request's length), refcount [num_pages] (-1 = free, else the
+    entries naming the page; pages dropped by the genealogy hold 0), free_ids [num_pages]
+    (the free pages at [0, n_free), the rest -7), n_free, len_before and len_after [R]
+    (len_after = len_before + steps[r]; steps default: uniform in [0, 2 * page_size]), kv
+    [kv_count, num_pages, page_bytes] uint8 or None."""
+    g = _gen(seed, "pool", "cpu")
+    if steps is None:
+        steps = torch.randint(0, 2 * page_size + 1, (R,), generator=g)
+    steps = torch.as_tensor(steps, dtype=torch.int64).expand(R).clone()
+    cap = P * page_size
+    if int(steps.max()) + min_len > cap:
+        raise ValueError("steps do not fit P * page_size")
+    hi = cap - steps
+    len_before = torch.stack([torch.randint(min_len, int(h) + 1, (1,), generator=g)[0]
+                              for h in hi])
+    tables = []
+    nxt = 0
+    for r in range(R):
+        nc = -(-int(len_before[r]) // page_size)
+        t = torch.full((N, P), -1, dtype=torch.int64)
+        for c in range(nc):
+            if c == 0:
+                t[:, 0] = nxt                         # prompt page shared by every particle
+                nxt += 1
+                continue
+            a = torch.randint(0, N, (N,), generator=g)
+            t[:, :c] = t[a, :c]
+            t[:, c] = torch.arange(nxt, nxt + N)
+            nxt += N
+        a = torch.randint(0, N, (N,), generator=g)
+        tables.append(t[a])
+    table = torch.stack(tables) if R else torch.full((0, N, P), -1, dtype=torch.int64)
+    num_pages = nxt + spare
+    perm = torch.randperm(num_pages, generator=g)
+    table = torch.where(table >= 0, perm[table.clamp(min=0)], table).to(torch.int32)
+    valid = table[table >= 0].to(torch.int64)
+    refcount = torch.bincount(valid, minlength=num_pages).to(torch.int32)
+    free = perm[nxt:].to(torch.int32)                 # never referenced: on the free list
+    refcount[free.long()] = -1
+    free_ids = torch.full((num_pages,), -7, dtype=torch.int32)
+    free_ids[:spare] = free
+    kv = None
+    if kv_count:
+        gk = _gen(seed, "kv", "cpu")
+        kv = torch.randint(0, 256, (kv_count, num_pages, page_bytes), generator=gk,
+                           dtype=torch.int32).to(torch.uint8)
+    return dict(page_table=table.contiguous(), refcount=refcount, free_ids=free_ids,
+                n_free=spare, len_before=len_before.to(torch.int32),
+                len_after=(len_before + steps).to(torch.int32), kv=kv, page_size=page_size)
 
 
 @torch.no_grad()

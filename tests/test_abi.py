@@ -28,7 +28,8 @@ def test_every_declared_symbol_is_exported():
     assert {"smcsd_round", "smcsd_resample", "smcsd_remap_pages", "smcsd_workspace_size",
             "smcsd_status_string", "smcsd_round_args_size", "smcsd_bench_stream_read",
             "smcsd_bench_copy", "smcsd_sd_verify", "smcsd_verify_workspace_size",
-            "smcsd_verify_args_size", "smcsd_gumbel_topk", "smcsd_topk_workspace_size"} <= names
+            "smcsd_verify_args_size", "smcsd_gumbel_topk", "smcsd_topk_workspace_size",
+            "smcsd_pages_advance", "smcsd_pages_workspace_size"} <= names
     lib = ctypes.CDLL(S.library_path())
     for n in sorted(names):
         assert hasattr(lib, n), n
@@ -211,3 +212,55 @@ def test_topk_validation():
     assert _topk(ws=0x70000010) == S.ERR_WORKSPACE
     big = 1048576 + 8
     assert _topk(V=big, ld=big) == S.ERR_UNSUPPORTED                         # > 64 slices
+
+
+def test_pages_workspace_size():
+    a = S.smcsd_pages_workspace_size(64, 32, 64, 100000)
+    assert a > 0 and a % 256 == 0
+    assert S.smcsd_pages_workspace_size(64, 32, 64, 200000) > a            # more chunks
+    assert S.smcsd_pages_workspace_size(0, 32, 64, 100) > 0                # release only
+    assert S.smcsd_pages_workspace_size(1, 0, 64, 100) == 0
+    assert S.smcsd_pages_workspace_size(1, 8, 64, 0) == 0
+    assert S.smcsd_pages_workspace_size(1, S.MAX_N + 1, 4, 100) == 0
+    assert S.smcsd_pages_workspace_size(4096, 1024, 1024, 100) == 0        # R*N*P >= 2^31
+
+
+def _pages(**kw):
+    base = 0x10000000
+    a = dict(R=2, N=4, P=8, page_size=16, len_before=base, len_after=base + 0x1000,
+             page_table=base + 0x2000, num_pages=100, refcount=base + 0x10000,
+             free_ids=base + 0x20000, n_free=base + 0x30000, kv=None, page_bytes=0,
+             kv_count=0, kv_stride=0, workspace=base + 0x40000, workspace_bytes=1 << 20,
+             error_flags=None)
+    a.update(kw)
+    return S.raw_library().smcsd_pages_advance(
+        a["R"], a["N"], a["P"], a["page_size"], a["len_before"], a["len_after"],
+        a["page_table"], a["num_pages"], a["refcount"], a["free_ids"], a["n_free"], a["kv"],
+        a["page_bytes"], a["kv_count"], a["kv_stride"], a["workspace"], a["workspace_bytes"],
+        a["error_flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), S.ERR_ARG),
+    (dict(R=-1), S.ERR_ARG),
+    (dict(P=0), S.ERR_ARG),
+    (dict(page_size=0), S.ERR_ARG),
+    (dict(num_pages=0), S.ERR_ARG),
+    (dict(N=S.MAX_N + 1), S.ERR_UNSUPPORTED),
+    (dict(R=4096, N=1024, P=1024), S.ERR_UNSUPPORTED),
+    (dict(refcount=None), S.ERR_ARG),
+    (dict(free_ids=None), S.ERR_ARG),
+    (dict(n_free=None), S.ERR_ARG),
+    (dict(len_before=None), S.ERR_ARG),
+    (dict(page_table=None), S.ERR_ARG),
+    (dict(workspace=None), S.ERR_WORKSPACE),
+    (dict(workspace_bytes=64), S.ERR_WORKSPACE),
+    (dict(kv=0x50000000, page_bytes=8, kv_count=1), S.ERR_ARG),          # not a multiple of 16
+    (dict(kv=0x50000008, page_bytes=64, kv_count=1), S.ERR_ARG),         # misaligned
+    (dict(kv=0x50000000, page_bytes=64, kv_count=0), S.ERR_ARG),
+    (dict(kv=0x50000000, page_bytes=64, kv_count=2, kv_stride=64 * 99), S.ERR_ARG),  # overlap
+    (dict(free_ids=0x10010100), S.ERR_ARG),                              # overlaps refcount
+    (dict(n_free=0x10040010), S.ERR_ARG),                                # inside the workspace
+])
+def test_pages_validation(kw, status):
+    assert _pages(**kw) == status
