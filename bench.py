@@ -12,6 +12,11 @@ Prints one JSON line with:
     by its mean duration from HIP events the library records around that launch on the
     round's stream;
   * cpu_baseline: the CPU oracle timed on a bounded sample of the same workload.
+
+Other paths (--path): sd_verify and gumbel_topk time those entry points on the same logits;
+driver times the multi-round driver: an ESS-adaptive round followed by the page lifecycle
+(release, copy-on-write of shared tail pages across every KV tensor, appends), with a
+paged KV cache of --kv-tensors tensors and --kv-page-bytes per page in HBM.
 """
 from __future__ import annotations
 
@@ -103,6 +108,41 @@ def stored_traffic(workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def cpu_baseline_driver(w, pool_args, target_s=12.0, sample_requests=2):
+    """The oracle's round plus its page lifecycle on a bounded sample: the first requests of
+    the workload with a page pool of the same geometry (KV tensors zero-filled), each pass
+    timed with a wall clock; driver steps/s = 1 / (R * seconds per request)."""
+    import numpy as np
+
+    import oracle
+    from smc_particle_resampling_amd import synth
+    rs = min(w.R, sample_requests)
+    small = w.scaled(R=rs)
+    host = synth.to_host(synth.make_inputs(small, 11, device="cpu", pages=False))
+    ps, P, kv_tensors, page_bytes = pool_args
+    pool = synth.make_page_pool(rs, w.N, P, ps, 11, steps=w.K + 1, spare=256)
+    num_pages = pool["refcount"].numel()
+    kv = np.zeros((kv_tensors, num_pages, page_bytes), np.uint8)
+    host.update(page_table=pool["page_table"].numpy(), refcount=pool["refcount"].numpy())
+    times = []
+    while not times or (sum(times) < target_s and len(times) < 1000):
+        t = time.perf_counter()
+        ora = oracle.round(host, V=w.V, mode=w.mode, ess_frac=w.ess_frac, tv=w.tv)
+        oracle.pages_advance(ora["page_table"], ora["refcount"], pool["free_ids"].numpy(),
+                             pool["n_free"], pool["len_before"].numpy(),
+                             pool["len_after"].numpy(), ps, kv, kv_inplace=True)
+        times.append(time.perf_counter() - t)
+    per_request = sum(times) / (len(times) * rs)
+    return {"value": 1.0 / (w.R * per_request), "unit": "driver steps/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": "%d of %d requests (N=%d, K=%d, V=%d, TV %s, %s resampling) with a pool of "
+                      "%d pages x %d KV tensors x %d B: fp64 oracle round then the oracle's "
+                      "page lifecycle (its KV copies included), repeated %d times (%.1f s in "
+                      "all), %.4f s per request; driver steps/s = 1/(%d * that)" % (
+                          rs, w.R, w.N, w.K, w.V, "on" if w.tv else "off", w.mode, num_pages,
+                          kv_tensors, page_bytes, len(times), sum(times), per_request, w.R)}
+
+
 def cpu_baseline(w, target_s=12.0, sample_requests=4, path="round", k=8):
     """The oracle (as it is) on a bounded sample of the workload: the first few requests
     (all N particles, K positions, V logits each), timed with a wall clock around
@@ -147,20 +187,33 @@ def cpu_baseline(w, target_s=12.0, sample_requests=4, path="round", k=8):
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=None,
+                    help="timed steps (default 50; 20 for --path driver, whose page pool "
+                         "grows with the run)")
+    ap.add_argument("--warmup", type=int, default=None, help="untimed steps (default 5; 3)")
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-read-roofline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run N launches of a plain 1 GiB copy (for counter scaling)")
-    ap.add_argument("--path", choices=("round", "sd_verify", "gumbel_topk"), default="round",
+    ap.add_argument("--path", choices=("round", "sd_verify", "gumbel_topk", "driver"),
+                    default="round",
                     help="round: one SMC-SD round (smcsd_round, the headline); sd_verify: "
                          "standard speculative-decoding verification of the same blocks "
                          "(smcsd_sd_verify); gumbel_topk: Gumbel-Top-K drafting of k tokens "
-                         "per particle row (smcsd_gumbel_topk)")
+                         "per particle row (smcsd_gumbel_topk); driver: an ESS-adaptive round "
+                         "then the page lifecycle (smcsd_round + smcsd_pages_advance)")
     ap.add_argument("--topk", type=int, default=8, help="k of --path gumbel_topk")
+    ap.add_argument("--kv-tensors", type=int, default=64,
+                    help="driver: KV tensors sharing the page ids (32 layers x K and V)")
+    ap.add_argument("--kv-page-bytes", type=int, default=32768,
+                    help="driver: bytes of one page in one KV tensor (16 tokens x 8 KV heads x "
+                         "128 dims x bf16)")
     args = ap.parse_args()
+    if args.steps is None:
+        args.steps = 20 if args.path == "driver" else 50
+    if args.warmup is None:
+        args.warmup = 3 if args.path == "driver" else 5
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: the round shards by request with no "
@@ -177,6 +230,9 @@ def main():
     print("# building inputs for %s" % name, file=sys.stderr, flush=True)
     verify = args.path == "sd_verify"
     topk = args.path == "gumbel_topk"
+    driver = args.path == "driver"
+    if driver:
+        w = w.scaled(mode="ess")
     inp = synth.make_inputs(w, 0, device=dev, pages=args.path == "round")
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
@@ -200,6 +256,54 @@ def main():
 
         def step(t, timing=None):
             smcsd.run_sd_verify(inp, outputs=out, timing_events=timing)
+    elif driver:
+        # Page pool: every particle's length grows K + 1 tokens a step; the table holds a
+        # context of up to 256 tokens before the first step plus what the run appends, and
+        # the free list starts with enough pages for every append even if nothing is
+        # released.
+        ps = 16
+        total = args.warmup + args.steps
+        grow = -(-(total * (w.K + 1)) // ps) + 1       # columns the run appends, at most
+        P = 16 + grow
+        pool = synth.make_page_pool(w.R, w.N, P, ps, 0, steps=total * (w.K + 1),
+                                    spare=w.R * w.N * grow)
+        num_pages = pool["refcount"].numel()
+        print("# page pool: %d pages x %d KV tensors x %d B = %.1f GiB" % (
+            num_pages, args.kv_tensors, args.kv_page_bytes,
+            num_pages * args.kv_tensors * args.kv_page_bytes / 2**30), file=sys.stderr, flush=True)
+        kv = torch.zeros((args.kv_tensors, num_pages, args.kv_page_bytes), dtype=torch.uint8,
+                         device=dev)
+        inp["page_table"] = pool["page_table"].to(dev)
+        inp["refcount"] = pool["refcount"].to(dev)
+        free_ids = pool["free_ids"].to(dev)
+        n_free = torch.tensor([pool["n_free"]], dtype=torch.int32, device=dev)
+        lens = torch.stack([pool["len_before"] + t * (w.K + 1) for t in range(total + 1)])
+        lens = lens.to(torch.int32).to(dev)
+        stats = torch.zeros((total, 4), dtype=torch.int32, device=dev)
+        pws = torch.empty(smcsd.smcsd_pages_workspace_size(w.R, w.N, P, num_pages),
+                          dtype=torch.uint8, device=dev)
+        out = smcsd.alloc_outputs(w.R, w.N, w.K, dev, tv=w.tv, V=w.V,
+                                  dtype=smcsd.BF16 if w.dtype == "bf16" else smcsd.F32)
+        tables = [inp["page_table"], torch.empty_like(inp["page_table"])]
+        life = [(ev.create(), ev.create()) for _ in range(args.steps)]
+        cur = torch.cuda.current_stream(dev).cuda_stream
+        torch.cuda.synchronize()
+
+        def step(t, timing=None):
+            out["page_table_out"] = tables[(t + 1) % 2]
+            inp["page_table"] = tables[t % 2]
+            smcsd.run_round(inp, mode=w.mode, ess_frac=w.ess_frac, tv=w.tv, outputs=out,
+                            timing_events=timing)
+            lt = life[t - args.warmup] if timing is not None else None
+            if lt:
+                ev.record(lt[0], cur)
+            smcsd.smcsd_pages_advance(len_before=lens[t], len_after=lens[t + 1],
+                                      page_table=out["page_table_out"],
+                                      refcount=inp["refcount"], free_ids=free_ids,
+                                      n_free=n_free, page_size=ps, workspace=pws, kv=kv,
+                                      stats=stats[t], error_flags=out["error_flags"])
+            if lt:
+                ev.record(lt[1], cur)
     else:
         torch.cuda.synchronize()
         out = smcsd.alloc_outputs(w.R, w.N, w.K, dev, tv=w.tv, V=w.V,
@@ -239,6 +343,24 @@ def main():
     print("# %s %.3f ms, logits kernel %.3f ms (min %.3f max %.3f)" % (
         args.path, ms_per_step, k_mean_ms, min(kms), max(kms)), file=sys.stderr, flush=True)
 
+    lifecycle = None
+    if driver:
+        lms = [ev.elapsed_ms(a, b) for a, b in life]
+        st = stats[args.warmup:].cpu().numpy()
+        copied = float(st[:, 2].mean())
+        moved = 2.0 * copied * args.kv_tensors * args.kv_page_bytes    # read + write per copy
+        lifecycle = {"ms_mean": sum(lms) / len(lms), "ms_min": min(lms), "ms_max": max(lms),
+                     "released_per_step": float(st[:, 0].mean()),
+                     "pops_per_step": float(st[:, 1].mean()),
+                     "pages_copied_per_step": copied,
+                     "pops_unserved": int(st[:, 3].sum()),
+                     "kv_copy_bytes_per_step": moved,
+                     "kv_copy_GBps_over_lifecycle": moved / (sum(lms) / len(lms) * 1e-3) / 1e9}
+        if lifecycle["pops_unserved"]:
+            raise SystemExit("page pool ran dry: %d pops unserved" % lifecycle["pops_unserved"])
+        print("# lifecycle %.3f ms, %.1f pages copied / step" % (lifecycle["ms_mean"], copied),
+              file=sys.stderr, flush=True)
+
     for _ in range(args.copy_calibration):
         src = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -247,8 +369,18 @@ def main():
         del src, dst
 
     rr = None if args.no_read_roofline else read_roofline(smcsd, torch, dev)
-    cpu = None if args.no_cpu_baseline else cpu_baseline(w, path=args.path, k=args.topk)
-    if topk:
+    if args.no_cpu_baseline:
+        cpu = None
+    elif driver:
+        cpu = cpu_baseline_driver(w, (ps, P, args.kv_tensors, args.kv_page_bytes))
+    else:
+        cpu = cpu_baseline(w, path=args.path, k=args.topk)
+    if driver:
+        metric = ("SMC-SD driver steps/s (ESS-adaptive round + page lifecycle with KV "
+                  "copy-on-write), N=32 K=8 V=128256 bf16")
+        unit = "steps/s"
+        table_bytes = alg["table"]
+    elif topk:
         metric = ("Gumbel-Top-K drafting passes/s and achieved HBM GB/s (%% of peak), "
                   "%d rows V=%d bf16 k=%d" % (w.R * w.N, w.V, args.topk))
         unit = "passes/s"
@@ -277,8 +409,11 @@ def main():
         "data": "synthetic",
         "config": {"workload": name, "path": args.path, "R": w.R, "N": w.N, "K": w.K, "V": w.V,
                    "tv": (w.tv or verify) and not topk,
-                   "resample": w.mode if args.path == "round" else None,
-                   "pages_per_particle": w.P if args.path == "round" else None,
+                   "resample": w.mode if args.path in ("round", "driver") else None,
+                   "pages_per_particle": (w.P if args.path == "round" else
+                                          P if driver else None),
+                   "kv_cache": ({"tensors": args.kv_tensors, "page_bytes": args.kv_page_bytes,
+                                 "page_tokens": ps, "pages": num_pages} if driver else None),
                    "topk": args.topk if topk else None,
                    "round_GBps": (logits_bytes + table_bytes) / (ms_per_step * 1e-3) / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
@@ -290,6 +425,8 @@ def main():
                      "attainable_read_GBps": rr},
         "cpu_baseline": cpu,
     }
+    if driver:
+        line["lifecycle"] = lifecycle
     print(json.dumps(line), flush=True)
 
 

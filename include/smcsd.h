@@ -218,7 +218,9 @@ smcsd_status smcsd_remap_pages(int32_t R, int32_t N, int32_t P, const int32_t *a
  *  kv: NULL (tables only) or kv_count KV tensors, tensor t's page p at byte
  *    kv + t * kv_stride + p * page_bytes; kv, page_bytes and kv_stride multiples of 16,
  *    kv_stride >= num_pages * page_bytes when kv_count > 1;
- *  workspace of smcsd_pages_workspace_size(R, N, P, num_pages) bytes; error_flags optional.
+ *  workspace of smcsd_pages_workspace_size(R, N, P, num_pages) bytes;
+ *  stats: NULL or [4] int32 out: pages released, pops served, pages copied, pops that found
+ *    the free list empty; error_flags optional.
  * A page must not be named by two requests' tables. If the free list runs dry, the
  * entries it cannot fill stay -1 and SMCSD_DEVERR_POOL is set.
  */
@@ -227,8 +229,8 @@ smcsd_status smcsd_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_s
                                  int32_t *page_table, int32_t num_pages, int32_t *refcount,
                                  int32_t *free_ids, int32_t *n_free, void *kv,
                                  int64_t page_bytes, int32_t kv_count, int64_t kv_stride,
-                                 void *workspace, size_t workspace_bytes, int32_t *error_flags,
-                                 smcsd_stream stream);
+                                 void *workspace, size_t workspace_bytes, int32_t *stats,
+                                 int32_t *error_flags, smcsd_stream stream);
 
 /* Workspace bytes smcsd_pages_advance needs (0 if the sizes are invalid). */
 size_t smcsd_pages_workspace_size(int32_t R, int32_t N, int32_t P, int32_t num_pages);

@@ -259,11 +259,12 @@ def gumbel_topk(logits: np.ndarray, temperature: np.ndarray, gumbel: np.ndarray,
 
 def pages_advance(page_table: np.ndarray, refcount: np.ndarray, free_ids: np.ndarray,
                   n_free: int, len_before, len_after, page_size: int,
-                  kv: np.ndarray | None = None) -> dict:
+                  kv: np.ndarray | None = None, kv_inplace: bool = False) -> dict:
     """Page lifecycle between rounds (release at refcount 0, copy-on-write of shared tail
     pages, fresh pages for new columns) on copies of the given host arrays. page_table
     [R,N,P] int32, refcount and free_ids [num_pages] int32, kv uint8 [num_pages, page_bytes]
-    or [kv_count, num_pages, page_bytes] (one tensor per layer and K / V) or None.
+    or [kv_count, num_pages, page_bytes] (one tensor per layer and K / V) or None; with
+    kv_inplace the (C-contiguous uint8) kv array itself receives the copies.
     Lengths satisfy 0 <= len_before <= len_after <= P * page_size.
     Returns dict(page_table, refcount, free_ids, n_free, kv, status)."""
     pt = np.array(page_table, dtype=np.int32, copy=True)
@@ -278,7 +279,11 @@ def pages_advance(page_table: np.ndarray, refcount: np.ndarray, free_ids: np.nda
     if kv is None:
         kvc = np.zeros((1, rc.size, 1), np.uint8)
     else:
-        kvc = np.array(kv, dtype=np.uint8, copy=True)
+        if kv_inplace:
+            assert kv.dtype == np.uint8 and kv.flags.c_contiguous
+            kvc = kv
+        else:
+            kvc = np.array(kv, dtype=np.uint8, copy=True)
         if kvc.ndim == 2:
             kvc = kvc[None]
         assert kvc.ndim == 3 and kvc.shape[1] == rc.size

@@ -370,8 +370,8 @@ smcsd_status smcsd_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_s
                                  int32_t* page_table, int32_t num_pages, int32_t* refcount,
                                  int32_t* free_ids, int32_t* n_free, void* kv,
                                  int64_t page_bytes, int32_t kv_count, int64_t kv_stride,
-                                 void* workspace, size_t workspace_bytes, int32_t* error_flags,
-                                 smcsd_stream stream) {
+                                 void* workspace, size_t workspace_bytes, int32_t* stats,
+                                 int32_t* error_flags, smcsd_stream stream) {
     if (R < 0 || N < 1 || P < 1 || page_size < 1 || num_pages < 1) return SMCSD_ERR_ARG;
     PagesLayout L;
     if (!pages_layout(R, N, P, num_pages, &L)) return SMCSD_ERR_UNSUPPORTED;
@@ -390,10 +390,10 @@ smcsd_status smcsd_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_s
     if (!workspace || workspace_bytes < L.bytes) return SMCSD_ERR_WORKSPACE;
     const size_t pb = sizeof(int32_t) * (size_t)num_pages;
     const size_t tb = sizeof(int32_t) * (size_t)R * N * P;
-    const void* bufs[5] = {page_table, refcount, free_ids, n_free, workspace};
-    const size_t sizes[5] = {tb, pb, pb, sizeof(int32_t), L.bytes};
-    for (int i = 0; i < 5; ++i)
-        for (int k = i + 1; k < 5; ++k)
+    const void* bufs[6] = {page_table, refcount, free_ids, n_free, workspace, stats};
+    const size_t sizes[6] = {tb, pb, pb, sizeof(int32_t), L.bytes, 4 * sizeof(int32_t)};
+    for (int i = 0; i < 6; ++i)
+        for (int k = i + 1; k < 6; ++k)
             if (bufs[i] && bufs[k] && overlap(bufs[i], sizes[i], bufs[k], sizes[k]))
                 return SMCSD_ERR_ARG;
     char* ws = static_cast<char*>(workspace);
@@ -418,6 +418,7 @@ smcsd_status smcsd_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_s
     a.chunk_cnt = reinterpret_cast<int32_t*>(ws + L.off_chunk);
     a.chunk_off = a.chunk_cnt + L.chunks;
     a.copies = reinterpret_cast<int2*>(ws + L.off_copies);
+    a.stats = stats;
     a.error_flags = error_flags;
     a.R = R;
     a.N = N;

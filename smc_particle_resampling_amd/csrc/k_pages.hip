@@ -161,6 +161,7 @@ __global__ __launch_bounds__(kThreads) void k_pages_scan(PagesArgs a) {
     const int pops = excl_scan_array(a.req_base, a.R, s_scan);
     const int cows = excl_scan_array(a.cow_base, a.R, s_scan);
     const int released = excl_scan_array(a.chunk_off, a.chunks, s_scan);
+    __shared__ int32_t s_F;
     if (threadIdx.x == 0) {
         int32_t n0 = *a.n_free;
         if (n0 < 0 || n0 > a.num_pages) {
@@ -179,6 +180,23 @@ __global__ __launch_bounds__(kThreads) void k_pages_scan(PagesArgs a) {
         a.hdr[2] = pops;
         a.hdr[3] = cows;
         *a.n_free = max(0, F - pops);
+        s_F = F;
+    }
+    __syncthreads();
+    if (a.stats) {
+        // Copies served: request r's copies are pops req_base[r] .. req_base[r] + req_cow[r] - 1.
+        const int32_t F = s_F;
+        int mine = 0;
+        for (int64_t i = threadIdx.x; i < a.R; i += kThreads)
+            mine += max(0, min(a.req_cow[i], F - a.req_base[i]));
+        int copied;
+        block_excl_scan(mine, s_scan, &copied);
+        if (threadIdx.x == 0) {
+            a.stats[0] = F - a.hdr[0];
+            a.stats[1] = min(pops, F);
+            a.stats[2] = copied;
+            a.stats[3] = max(0, pops - F);
+        }
     }
 }
 

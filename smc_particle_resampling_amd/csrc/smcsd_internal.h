@@ -176,6 +176,7 @@ struct PagesArgs {
     int32_t* chunk_cnt;    // [chunks]
     int32_t* chunk_off;    // [chunks]
     int2* copies;          // [R*N] (source page, destination page or -1)
+    int32_t* stats;        // optional [4]: released, pops served, copies served, pops unserved
     int32_t* error_flags;
     int32_t R, N, P, page_size, num_pages, chunks;
 };

@@ -231,13 +231,13 @@ def _pages(**kw):
              page_table=base + 0x2000, num_pages=100, refcount=base + 0x10000,
              free_ids=base + 0x20000, n_free=base + 0x30000, kv=None, page_bytes=0,
              kv_count=0, kv_stride=0, workspace=base + 0x40000, workspace_bytes=1 << 20,
-             error_flags=None)
+             stats=None, error_flags=None)
     a.update(kw)
     return S.raw_library().smcsd_pages_advance(
         a["R"], a["N"], a["P"], a["page_size"], a["len_before"], a["len_after"],
         a["page_table"], a["num_pages"], a["refcount"], a["free_ids"], a["n_free"], a["kv"],
         a["page_bytes"], a["kv_count"], a["kv_stride"], a["workspace"], a["workspace_bytes"],
-        a["error_flags"], None)
+        a["stats"], a["error_flags"], None)
 
 
 @pytest.mark.parametrize("kw,status", [
@@ -261,6 +261,7 @@ def _pages(**kw):
     (dict(kv=0x50000000, page_bytes=64, kv_count=2, kv_stride=64 * 99), S.ERR_ARG),  # overlap
     (dict(free_ids=0x10010100), S.ERR_ARG),                              # overlaps refcount
     (dict(n_free=0x10040010), S.ERR_ARG),                                # inside the workspace
+    (dict(stats=0x10030000), S.ERR_ARG),                                 # overlaps n_free
 ])
 def test_pages_validation(kw, status):
     assert _pages(**kw) == status

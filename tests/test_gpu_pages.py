@@ -47,12 +47,35 @@ def _gpu_advance(pool, dev, lens=None):
     ws = torch.empty(max(256, smcsd.smcsd_pages_workspace_size(R, N, P, num_pages)),
                      dtype=torch.uint8, device=dev)
     flags = torch.zeros(1, dtype=torch.int32, device=dev)
-    smcsd.smcsd_pages_advance(page_size=pool["page_size"], workspace=ws, error_flags=flags, **t)
+    stats = torch.full((4,), -5, dtype=torch.int32, device=dev)
+    smcsd.smcsd_pages_advance(page_size=pool["page_size"], workspace=ws, error_flags=flags,
+                              stats=stats, **t)
     torch.cuda.synchronize()
     out = {k: (None if v is None else v.cpu().numpy()) for k, v in t.items()}
     out["n_free"] = int(out["n_free"][0])
     out["flags"] = int(flags.item())
+    out["stats"] = stats.cpu().numpy().tolist()
     return out
+
+
+def _expected_stats(pool, o, lens=None):
+    """[released, pops served, pages copied, pops unserved] read off the oracle's result."""
+    lb, la = lens if lens is not None else (pool["len_before"], pool["len_after"])
+    lb, la = np.asarray(lb, np.int64), np.asarray(la, np.int64)
+    ps = pool["page_size"]
+    pt0, pt1 = pool["page_table"].numpy(), o["page_table"]
+    released = int((pool["refcount"].numpy() == 0).sum())
+    served = pool["n_free"] + released - o["n_free"]
+    copied = unserved = 0
+    for r in range(pt0.shape[0]):
+        if lb[r] > 0 and lb[r] % ps:
+            c = (lb[r] - 1) // ps
+            changed = pt1[r, :, c] != pt0[r, :, c]
+            copied += int((changed & (pt1[r, :, c] >= 0)).sum())
+            unserved += int((changed & (pt1[r, :, c] < 0)).sum())
+        c0, c1 = -(-lb[r] // ps), -(-la[r] // ps)
+        unserved += int((pt1[r, :, c0:c1] < 0).sum())
+    return [released, served, copied, unserved]
 
 
 def _oracle_advance(pool, lens=None):
@@ -118,7 +141,8 @@ def test_advance_matches_oracle(case, dev):
     o = _oracle_advance(pool)
     g = _gpu_advance(pool, dev)
     _compare(g, o, expect_flags=smcsd.DEVERR_POOL if o["status"] == -3 else 0)
-    _say("  ok: status", o["status"], "free", pool["n_free"], "->", o["n_free"])
+    assert g["stats"] == _expected_stats(pool, o)
+    _say("  ok: status", o["status"], "free", pool["n_free"], "->", o["n_free"], "stats", g["stats"])
 
 
 def test_free_list_runs_dry(dev):
@@ -130,6 +154,7 @@ def test_free_list_runs_dry(dev):
     g = _gpu_advance(pool, dev)
     _compare(g, o, expect_flags=smcsd.DEVERR_POOL)
     assert g["n_free"] == 0 and o["n_free"] == 0
+    assert g["stats"] == _expected_stats(pool, o) and g["stats"][3] > 0
 
 
 def test_release_only(dev):
