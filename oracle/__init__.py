@@ -67,6 +67,8 @@ def lib() -> ctypes.CDLL:
                                         p, p, p, p]
             L.orc_gumbel_topk.restype = None
             L.orc_gumbel_topk.argtypes = [i64, i64, i64, i32, p, p, p, i32, p, p]
+            L.orc_bonus_resampled.restype = i32
+            L.orc_bonus_resampled.argtypes = [i32, i32, i32, i64, i64, i32, p, p, p, p, p, p]
             L.orc_pages_advance.restype = i32
             L.orc_pages_advance.argtypes = [i32, i32, i32, i32, p, p, p, i32, p, p, p, p, i64, i32]
             L.orc_num_threads.restype = i32
@@ -255,6 +257,26 @@ def gumbel_topk(logits: np.ndarray, temperature: np.ndarray, gumbel: np.ndarray,
     lib().orc_gumbel_topk(rows, V, ld, dt, _ptr(z), _ptr(temp), _ptr(g), int(k), _ptr(tok),
                           _ptr(key))
     return tok, key
+
+
+def bonus_resampled(target: np.ndarray, temperature: np.ndarray, ancestors: np.ndarray,
+                    gumbel: np.ndarray, *, V: int | None = None) -> dict:
+    """Bonus token per new slot after resampling: slot j of request r takes the Gumbel-max
+    of its ancestor's target row K with noise row gumbel[r, j]. target [R,N,K+1,ld]
+    (float32 or bf16 bits as uint16), temperature [R], ancestors [R,N] int32, gumbel
+    [R,N,ld] float32. Returns dict(bonus [R,N] int32, gap [R,N], status)."""
+    tgt, dt = _logits(target)
+    R, N, K1, ld = tgt.shape
+    V = ld if V is None else int(V)
+    temp = np.ascontiguousarray(temperature, dtype=np.float32)
+    anc = np.ascontiguousarray(ancestors, dtype=np.int32)
+    g = np.ascontiguousarray(gumbel, dtype=np.float32)
+    assert temp.shape == (R,) and anc.shape == (R, N) and g.shape == (R, N, ld)
+    bonus = np.zeros((R, N), np.int32)
+    gap = np.zeros((R, N))
+    st = lib().orc_bonus_resampled(R, N, K1 - 1, V, ld, dt, _ptr(tgt), _ptr(temp), _ptr(anc),
+                                   _ptr(g), _ptr(bonus), _ptr(gap))
+    return dict(bonus=bonus, gap=gap, status=int(st))
 
 
 def pages_advance(page_table: np.ndarray, refcount: np.ndarray, free_ids: np.ndarray,

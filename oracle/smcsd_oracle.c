@@ -513,6 +513,37 @@ void orc_gumbel_topk(int64_t rows, int64_t V, int64_t ld, int32_t dtype, const v
 }
 
 /*
+ * Bonus token drawn after resampling, the alternative to drawing it per original particle
+ * inside the pass (the SMC-SD page, section 2, emits K + 1 tokens a round without saying when
+ * the last one is drawn). Reading: new slot j of request r draws from the target's bonus row
+ * of its ancestor, row K of particle ancestors[r][j], with its own noise row gumbel[r][j],
+ * by the same Gumbel-max key as the in-pass bonus (STAND page, method item 2, k = 1).
+ * bonus [R][N] out; gap [R][N] optional (key(best) - key(second)). Returns -1 if an
+ * ancestor is outside [0, N) (that slot's bonus is -1), else 0.
+ */
+int32_t orc_bonus_resampled(int32_t R, int32_t N, int32_t K, int64_t V, int64_t ld, int32_t dtype,
+                            const void *target, const float *temperature,
+                            const int32_t *ancestors, const float *gumbel, int32_t *bonus,
+                            double *gap)
+{
+    const size_t es = esize(dtype);
+    int32_t err = 0;
+    for (int64_t rj = 0; rj < (int64_t)R * N; ++rj) {
+        int64_t r = rj / N;
+        int32_t a = ancestors[rj];
+        if (a < 0 || a >= N) {
+            bonus[rj] = -1;
+            err = -1;
+            continue;
+        }
+        const char *zb = (const char *)target + (size_t)(((r * N + a) * (K + 1) + K) * ld) * es;
+        bonus[rj] = orc_row_gumbel_argmax(zb, dtype, gumbel + (size_t)rj * ld, V, temperature[r],
+                                          gap ? &gap[rj] : NULL);
+    }
+    return err;
+}
+
+/*
  * Page lifecycle between rounds (the steps around the SMC-SD round: the page says duplicated
  * particles share KV pages by copying page metadata and exchanging pointers, section 2; a
  * shared page that will be written must then be copied first, and pages nobody references
