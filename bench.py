@@ -204,6 +204,10 @@ def main():
                          "per particle row (smcsd_gumbel_topk); driver: an ESS-adaptive round "
                          "then the page lifecycle (smcsd_round + smcsd_pages_advance)")
     ap.add_argument("--topk", type=int, default=8, help="k of --path gumbel_topk")
+    ap.add_argument("--bonus", choices=("pass", "after"), default="pass",
+                    help="round / driver: draw the bonus inside the logits pass per original "
+                         "particle (pass), or after resampling per new slot with fresh noise "
+                         "(after: smcsd_round without noise, then smcsd_bonus_resampled)")
     ap.add_argument("--kv-tensors", type=int, default=64,
                     help="driver: KV tensors sharing the page ids (32 layers x K and V)")
     ap.add_argument("--kv-page-bytes", type=int, default=32768,
@@ -234,6 +238,8 @@ def main():
     if driver:
         w = w.scaled(mode="ess")
     inp = synth.make_inputs(w, 0, device=dev, pages=args.path == "round")
+    after = args.bonus == "after" and args.path in ("round", "driver")
+    bonus_noise = synth.make_gumbel(w, 1, device=dev) if after else None
     ev = HipEvents()
     pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
     if topk:
@@ -293,7 +299,7 @@ def main():
             out["page_table_out"] = tables[(t + 1) % 2]
             inp["page_table"] = tables[t % 2]
             smcsd.run_round(inp, mode=w.mode, ess_frac=w.ess_frac, tv=w.tv, outputs=out,
-                            timing_events=timing)
+                            timing_events=timing, bonus_noise=bonus_noise)
             lt = life[t - args.warmup] if timing is not None else None
             if lt:
                 ev.record(lt[0], cur)
@@ -314,7 +320,7 @@ def main():
             out["page_table_out"] = tables[(t + 1) % 2]
             inp["page_table"] = tables[t % 2]
             smcsd.run_round(inp, mode=w.mode, ess_frac=w.ess_frac, tv=w.tv, outputs=out,
-                            timing_events=timing)
+                            timing_events=timing, bonus_noise=bonus_noise)
 
     for t in range(args.warmup):
         step(t)
@@ -415,6 +421,7 @@ def main():
                    "kv_cache": ({"tensors": args.kv_tensors, "page_bytes": args.kv_page_bytes,
                                  "page_tokens": ps, "pages": num_pages} if driver else None),
                    "topk": args.topk if topk else None,
+                   "bonus": (args.bonus if args.path in ("round", "driver") else None),
                    "round_GBps": (logits_bytes + table_bytes) / (ms_per_step * 1e-3) / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,

@@ -106,7 +106,10 @@ typedef struct smcsd_round_args {
     const void *draft_logits;    /* [R][N][K][ld]: row k is the distribution x_k came from */
     const int32_t *draft_tokens; /* [R][N][K] drafted tokens x_k */
     const float *temperature;    /* [R] T_r > 0, divides target and draft logits */
-    const float *gumbel;         /* [R][N][ld] f32 standard Gumbel noise for the bonus */
+    const float *gumbel;         /* [R][N][ld] f32 standard Gumbel noise for the bonus;
+                                    NULL = no bonus in the round (bonus may be NULL, column K
+                                    of out_tokens gets -1): for callers that draw it after
+                                    resampling with smcsd_bonus_resampled */
     const float *uniform;        /* [R] u_r in [0,1) for systematic resampling */
 
     /* in/out */
@@ -318,6 +321,32 @@ smcsd_status smcsd_gumbel_topk(int32_t rows, int32_t V, int64_t ld, int32_t dtyp
 
 /* Workspace bytes smcsd_gumbel_topk needs (0 if the sizes are invalid). */
 size_t smcsd_topk_workspace_size(int32_t rows, int32_t V, int32_t dtype, int32_t k);
+
+/*
+ * Bonus token drawn after resampling, one per NEW slot: the alternative to the in-pass bonus
+ * of smcsd_round. The SMC-SD page ("Faster LLM Inference via Sequential Monte Carlo",
+ * section 2) yields K + 1 tokens per particle and round without fixing when the last one is
+ * drawn. Here slot j of request r takes the Gumbel-max (STAND page, method item 2, k = 1)
+ * of its ancestor's bonus row with its own noise row:
+ *   bonus[r][j] = argmax_v fl32(fma(target[r][a][K][v], fl32(1/T_r), gumbel[r][j][v])),
+ *   a = ancestors[r][j], lowest v on equal keys.
+ * Run smcsd_round with gumbel = NULL first (it then skips its own bonus), then this call
+ * with the round's ancestors and a fresh noise tensor.
+ * target_logits [R][N][K+1][ld], temperature [R], ancestors [R][N] in; gumbel [R][N][ld]
+ * f32 in; bonus [R][N] out; out_tokens NULL or [R][N][K+1] whose column K receives the
+ * bonus. Sizes, dtype, ld and alignment as for smcsd_round. Workspace:
+ * smcsd_bonus_workspace_size bytes, 256-byte aligned. An ancestor outside [0, N) gives -1 and
+ * sets SMCSD_DEVERR_ANCESTOR. Exact: the same binary32 keys as the in-pass bonus.
+ */
+smcsd_status smcsd_bonus_resampled(int32_t R, int32_t N, int32_t K, int32_t V, int64_t ld,
+                                   int32_t dtype, const void *target_logits,
+                                   const float *temperature, const int32_t *ancestors,
+                                   const float *gumbel, int32_t *bonus, int32_t *out_tokens,
+                                   void *workspace, size_t workspace_bytes,
+                                   int32_t *error_flags, smcsd_stream stream);
+
+/* Workspace bytes smcsd_bonus_resampled needs (0 if the sizes are invalid). */
+size_t smcsd_bonus_workspace_size(int32_t R, int32_t N, int32_t V, int32_t dtype);
 
 #ifdef __cplusplus
 }

@@ -75,9 +75,10 @@ static smcsd_status check_round(const smcsd_round_args* a, Plan* plan) {
     if (a->ld < a->V || a->ld % epc != 0) return SMCSD_ERR_ARG;
     if (a->N > SMCSD_MAX_N || a->K > SMCSD_MAX_K) return SMCSD_ERR_UNSUPPORTED;
     if (a->R == 0) return SMCSD_OK;
+    // gumbel NULL: no bonus inside the pass (bonus may then be NULL too)
     if (!a->target_logits || !a->draft_logits || !a->draft_tokens || !a->temperature ||
-        !a->gumbel || !a->uniform || !a->log_weights || !a->log_w_incr || !a->log_norm ||
-        !a->ess || !a->resampled || !a->ancestors || !a->bonus)
+        !a->uniform || !a->log_weights || !a->log_w_incr || !a->log_norm || !a->ess ||
+        !a->resampled || !a->ancestors || (a->gumbel && !a->bonus))
         return SMCSD_ERR_ARG;
     if (!aligned16(a->target_logits) || !aligned16(a->draft_logits) || !aligned16(a->gumbel))
         return SMCSD_ERR_ARG;
@@ -91,6 +92,10 @@ static smcsd_status check_round(const smcsd_round_args* a, Plan* plan) {
         return SMCSD_ERR_UNSUPPORTED;
     if (!a->workspace || a->workspace_bytes < plan->bytes) return SMCSD_ERR_WORKSPACE;
     if (reinterpret_cast<uintptr_t>(a->workspace) & 255u) return SMCSD_ERR_WORKSPACE;
+    if (!a->gumbel) {                       // the logits pass reads no bonus row
+        plan->bonus_rows = 0;
+        plan->total_wgs = plan->pair_wgs;
+    }
     return SMCSD_OK;
 }
 
@@ -239,7 +244,7 @@ smcsd_status smcsd_round(const smcsd_round_args* args, smcsd_stream stream) {
     fa.temperature = a.temperature;
     fa.pp = la.pp;
     fa.tvp = plan.tv ? la.tvp : nullptr;
-    fa.bp = la.bp;
+    fa.bp = a.gumbel ? la.bp : nullptr;
     fa.terms = reinterpret_cast<double*>(ws + plan.off_terms);
     fa.log_potential = a.log_potential;
     fa.log_w_incr = a.log_w_incr;
@@ -511,6 +516,56 @@ smcsd_status smcsd_sd_verify(const smcsd_verify_args* args, smcsd_stream stream)
     va.cps = plan.cps;
     va.chunks = plan.chunks;
     if (launch_verify(a.R, a.dtype, va, s) != hipSuccess) return SMCSD_ERR_DEVICE;
+    return SMCSD_OK;
+}
+
+size_t smcsd_bonus_workspace_size(int32_t R, int32_t N, int32_t V, int32_t dtype) {
+    if (R < 0 || N < 1 || N > SMCSD_MAX_N || (int64_t)R * N >= (int64_t)INT32_MAX) return 0;
+    int32_t chunks, S, cps;
+    size_t bytes;
+    if (!topk_plan(R * N, V, dtype, 1, &chunks, &S, &cps, &bytes)) return 0;
+    return bytes > 0 ? bytes : 256;
+}
+
+smcsd_status smcsd_bonus_resampled(int32_t R, int32_t N, int32_t K, int32_t V, int64_t ld,
+                                   int32_t dtype, const void* target_logits,
+                                   const float* temperature, const int32_t* ancestors,
+                                   const float* gumbel, int32_t* bonus, int32_t* out_tokens,
+                                   void* workspace, size_t workspace_bytes,
+                                   int32_t* error_flags, smcsd_stream stream) {
+    if (R < 0 || N < 1 || K < 1 || V < 1) return SMCSD_ERR_ARG;
+    if (dtype != SMCSD_F32 && dtype != SMCSD_BF16) return SMCSD_ERR_ARG;
+    const int64_t epc = dtype == SMCSD_F32 ? 4 : 8;
+    if (ld < V || ld % epc != 0) return SMCSD_ERR_ARG;
+    if (N > SMCSD_MAX_N || K > SMCSD_MAX_K) return SMCSD_ERR_UNSUPPORTED;
+    if ((int64_t)R * N >= (int64_t)INT32_MAX) return SMCSD_ERR_UNSUPPORTED;
+    int32_t chunks, S, cps;
+    size_t bytes;
+    if (!topk_plan(R * N, V, dtype, 1, &chunks, &S, &cps, &bytes)) return SMCSD_ERR_UNSUPPORTED;
+    if (R == 0) return SMCSD_OK;
+    if (!target_logits || !temperature || !ancestors || !gumbel || !bonus) return SMCSD_ERR_ARG;
+    if (!aligned16(target_logits) || !aligned16(gumbel)) return SMCSD_ERR_ARG;
+    if (!workspace || workspace_bytes < bytes) return SMCSD_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return SMCSD_ERR_WORKSPACE;
+    TopkArgs a{};
+    a.logits = target_logits;
+    a.temperature = temperature;
+    a.gumbel = gumbel;
+    a.cand = static_cast<BonusPart*>(workspace);
+    a.out_tokens = bonus;
+    a.ancestors = ancestors;
+    a.slot_tokens = out_tokens;
+    a.error_flags = error_flags;
+    a.ld = ld;
+    a.V = V;
+    a.k = 1;
+    a.chunks = chunks;
+    a.S = S;
+    a.cps = cps;
+    a.N = N;
+    a.K = K;
+    if (launch_topk((int64_t)R * N, dtype, a, reinterpret_cast<hipStream_t>(stream)) != hipSuccess)
+        return SMCSD_ERR_DEVICE;
     return SMCSD_OK;
 }
 

@@ -56,7 +56,12 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
             }
         }
         // one thread per particle: its bonus token, the best (key, index) over the slices
+        // (none without noise: out_tokens then get -1 in column K)
         for (int32_t i = tid; i < N; i += kThreads) {
+            if (!a.bp) {
+                s_bonus[i] = -1;
+                continue;
+            }
             const BonusPart* bpart = a.bp + (r * N + i) * a.S;
             float best = bpart[0].key;
             int32_t besti = bpart[0].idx;

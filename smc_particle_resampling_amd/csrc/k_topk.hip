@@ -104,9 +104,16 @@ __global__ __launch_bounds__(kThreads) void k_topk_slice(TopkArgs a) {
     const int64_t row = blockIdx.x / (unsigned)a.S;
     const int s = (int)(blockIdx.x % (unsigned)a.S);
     const int tid = threadIdx.x;
-    const char* zrow = static_cast<const char*>(a.logits) + (size_t)(row * a.ld) * ESZ;
+    int64_t lrow = row, trow = row;
+    if (a.ancestors) {
+        const int32_t x = a.ancestors[row];
+        if (x < 0 || x >= a.N) return;       // the merge writes -1 for this row
+        trow = row / a.N;
+        lrow = (trow * a.N + x) * (a.K + 1) + a.K;
+    }
+    const char* zrow = static_cast<const char*>(a.logits) + (size_t)(lrow * a.ld) * ESZ;
     const float* grow = a.gumbel + (size_t)row * a.ld;
-    const float invT = __fdiv_rn(1.0f, a.temperature[row]);
+    const float invT = __fdiv_rn(1.0f, a.temperature[trow]);
     const int c0 = s * a.cps;
     const int c1 = min(c0 + a.cps, a.chunks);
     float key[n];
@@ -161,6 +168,17 @@ __global__ __launch_bounds__(kThreads) void k_topk_merge(TopkArgs a) {
     __shared__ BonusPart res[kMaxTopk];
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x;
+    if (a.ancestors) {
+        const int32_t x = a.ancestors[row];
+        if (x < 0 || x >= a.N) {
+            if (tid == 0) {
+                flag_error(a.error_flags, SMCSD_DEVERR_ANCESTOR);
+                a.out_tokens[row] = -1;
+                if (a.slot_tokens) a.slot_tokens[row * (a.K + 1) + a.K] = -1;
+            }
+            return;
+        }
+    }
     const int m = a.S * a.k;
     const BonusPart* c = a.cand + row * m;
     float key[n];
@@ -177,6 +195,7 @@ __global__ __launch_bounds__(kThreads) void k_topk_merge(TopkArgs a) {
         a.out_tokens[row * a.k + j] = res[j].idx;
         if (a.out_keys) a.out_keys[row * a.k + j] = res[j].key;
     }
+    if (a.slot_tokens && tid == 0) a.slot_tokens[row * (a.K + 1) + a.K] = res[0].idx;
 }
 
 }  // namespace

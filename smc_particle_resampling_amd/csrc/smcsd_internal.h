@@ -147,8 +147,14 @@ struct TopkArgs {
     BonusPart* cand;       // [rows][S][k] workspace
     int32_t* out_tokens;
     float* out_keys;
+    // Bonus after resampling: row i = (r, j) reads target row ((r*N + ancestors[i])*(K+1) + K)
+    // and temperature[r]; nullptr ancestors = logits row i and temperature[i].
+    const int32_t* ancestors;
+    int32_t* slot_tokens;  // optional [rows][K+1]: column K receives the token
+    int32_t* error_flags;
     int64_t ld;
     int32_t V, k, chunks, S, cps;
+    int32_t N, K;
 };
 
 // Page lifecycle between rounds. Workspace: a header (free count before and after release,

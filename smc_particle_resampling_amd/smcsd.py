@@ -79,6 +79,11 @@ _lib.smcsd_gumbel_topk.argtypes = [_i32, _i32, _i64, _i32, _p, _p, _p, _i32, _p,
 _lib.smcsd_topk_workspace_size.restype = _sz
 _lib.smcsd_topk_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
 _lib.smcsd_bench_stream_read.restype = _i32
+_lib.smcsd_bonus_resampled.restype = _i32
+_lib.smcsd_bonus_resampled.argtypes = [_i32, _i32, _i32, _i32, _i64, _i32, _p, _p, _p, _p, _p, _p,
+                                       _p, _sz, _p, _p]
+_lib.smcsd_bonus_workspace_size.restype = _sz
+_lib.smcsd_bonus_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
 _lib.smcsd_pages_advance.restype = _i32
 _lib.smcsd_pages_advance.argtypes = [_i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p, _p, _p,
                                      _i64, _i32, _i64, _p, _sz, _p, _p, _p]
@@ -178,7 +183,8 @@ def smcsd_round(*, target_logits, draft_logits, draft_tokens, temperature, gumbe
     _check(draft_logits, "draft_logits", target_logits.dtype, (R, N, K, ld), dev)
     _check(draft_tokens, "draft_tokens", i32, (R, N, K), dev)
     _check(temperature, "temperature", f32, (R,), dev)
-    _check(gumbel, "gumbel", f32, (R, N, ld), dev)
+    if gumbel is not None:                     # None: no bonus inside the round
+        _check(gumbel, "gumbel", f32, (R, N, ld), dev)
     _check(uniform, "uniform", f32, (R,), dev)
     _check(log_weights, "log_weights", f32, (R, N), dev)
     _check(log_w_incr, "log_w_incr", f32, (R, N), dev)
@@ -186,7 +192,8 @@ def smcsd_round(*, target_logits, draft_logits, draft_tokens, temperature, gumbe
     _check(ess, "ess", f32, (R,), dev)
     _check(resampled, "resampled", i32, (R,), dev)
     _check(ancestors, "ancestors", i32, (R, N), dev)
-    _check(bonus, "bonus", i32, (R, N), dev)
+    if bonus is not None or gumbel is not None:
+        _check(bonus, "bonus", i32, (R, N), dev)
     _check(workspace, "workspace", torch.uint8, None, dev)
     if out_tokens is not None:
         _check(out_tokens, "out_tokens", i32, (R, N, K + 1), dev)
@@ -360,6 +367,42 @@ def smcsd_remap_pages(*, ancestors, page_table_in, page_table_out, refcount, err
         raise SmcsdError(st, "smcsd_remap_pages")
 
 
+def smcsd_bonus_workspace_size(R: int, N: int, V: int, dtype: int) -> int:
+    return int(_lib.smcsd_bonus_workspace_size(R, N, V, dtype))
+
+
+def smcsd_bonus_resampled(*, target_logits, temperature, ancestors, gumbel, bonus, workspace,
+                          out_tokens=None, error_flags=None, V: int | None = None,
+                          stream=None) -> None:
+    """Enqueue the bonus draw after resampling (smcsd_bonus_resampled): slot j of request r
+    takes the Gumbel-max of its ancestor's target row K with noise row gumbel[r, j]. Shapes:
+    target [R,N,K+1,ld], temperature [R], ancestors [R,N], gumbel [R,N,ld], bonus [R,N],
+    out_tokens None or [R,N,K+1] (column K receives the bonus)."""
+    dev = target_logits.device
+    if target_logits.dtype not in (torch.float32, torch.bfloat16) or target_logits.dim() != 4:
+        raise ValueError("target_logits must be float32 or bfloat16 [R, N, K+1, ld]")
+    R, N, K1, ld = target_logits.shape
+    V = ld if V is None else int(V)
+    f32, i32 = torch.float32, torch.int32
+    _check(target_logits, "target_logits", None, None, dev)
+    _check(temperature, "temperature", f32, (R,), dev)
+    _check(ancestors, "ancestors", i32, (R, N), dev)
+    _check(gumbel, "gumbel", f32, (R, N, ld), dev)
+    _check(bonus, "bonus", i32, (R, N), dev)
+    _check(workspace, "workspace", torch.uint8, None, dev)
+    if out_tokens is not None:
+        _check(out_tokens, "out_tokens", i32, (R, N, K1), dev)
+    if error_flags is not None:
+        _check(error_flags, "error_flags", i32, None, dev)
+    dt = BF16 if target_logits.dtype == torch.bfloat16 else F32
+    st = _lib.smcsd_bonus_resampled(R, N, K1 - 1, V, ld, dt, _ptr(target_logits),
+                                    _ptr(temperature), _ptr(ancestors), _ptr(gumbel),
+                                    _ptr(bonus), _ptr(out_tokens), _ptr(workspace),
+                                    workspace.numel(), _ptr(error_flags), _stream(dev, stream))
+    if st != OK:
+        raise SmcsdError(st, "smcsd_bonus_resampled")
+
+
 def smcsd_pages_workspace_size(R: int, N: int, P: int, num_pages: int) -> int:
     return int(_lib.smcsd_pages_workspace_size(R, N, P, num_pages))
 
@@ -443,9 +486,11 @@ def alloc_outputs(R: int, N: int, K: int, device, tv: bool = False, out_tokens: 
 
 
 def run_round(inputs: dict, *, mode="always", ess_frac=0.5, tv=False, pages=True, outputs=None,
-              timing_events=None, stream=None) -> dict:
+              timing_events=None, bonus_noise=None, stream=None) -> dict:
     """smcsd_round on a dict from ``synth.make_inputs`` (log_weights, page tables and refcount
-    are updated in place / swapped like a caller would). Returns the output tensors."""
+    are updated in place / swapped like a caller would). Returns the output tensors.
+    With ``bonus_noise`` ([R,N,ld] float32) the round draws no bonus itself; the bonus is
+    drawn after resampling, per new slot, with that noise (smcsd_bonus_resampled)."""
     tgt = inputs["target"]
     R, N, K1, ld = tgt.shape
     K = K1 - 1
@@ -454,8 +499,9 @@ def run_round(inputs: dict, *, mode="always", ess_frac=0.5, tv=False, pages=True
     pt_in = inputs.get("page_table") if pages else None
     if pt_in is not None and "page_table_out" not in out:
         out["page_table_out"] = torch.empty_like(pt_in)
+    after = bonus_noise is not None
     smcsd_round(target_logits=tgt, draft_logits=inputs["draft"], draft_tokens=inputs["tokens"],
-                temperature=inputs["temperature"], gumbel=inputs["gumbel"],
+                temperature=inputs["temperature"], gumbel=None if after else inputs["gumbel"],
                 uniform=inputs["uniform"], log_weights=inputs["log_weights"],
                 log_w_incr=out["log_w_incr"], log_norm=out["log_norm"], ess=out["ess"],
                 resampled=out["resampled"], ancestors=out["ancestors"], bonus=out["bonus"],
@@ -465,6 +511,16 @@ def run_round(inputs: dict, *, mode="always", ess_frac=0.5, tv=False, pages=True
                 error_flags=out["error_flags"], workspace=out["workspace"],
                 log_potential=inputs.get("log_potential"), V=inputs["V"],
                 mode=mode, ess_frac=ess_frac, timing_events=timing_events, stream=stream)
+    if after:
+        if "bonus_workspace" not in out:
+            ws = smcsd_bonus_workspace_size(R, N, inputs["V"], dt)
+            out["bonus_workspace"] = torch.empty((max(ws, 256),), dtype=torch.uint8,
+                                                 device=tgt.device)
+        smcsd_bonus_resampled(target_logits=tgt, temperature=inputs["temperature"],
+                              ancestors=out["ancestors"], gumbel=bonus_noise,
+                              bonus=out["bonus"], out_tokens=out.get("out_tokens"),
+                              workspace=out["bonus_workspace"], error_flags=out["error_flags"],
+                              V=inputs["V"], stream=stream)
     return out
 
 

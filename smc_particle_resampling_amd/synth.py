@@ -38,7 +38,8 @@ import math
 import torch
 
 STREAMS = dict(target=1, peaks=2, draft=3, tokens=4, gumbel=5, uniform=6, temp=7, pages=8,
-               ragged=9, zipf_q=10, potential=11, accept=12, residual=13, pool=14, kv=15)
+               ragged=9, zipf_q=10, potential=11, accept=12, residual=13, pool=14, kv=15,
+               ancestors=16, noise=17)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -203,6 +204,28 @@ def make_page_table(R: int, N: int, P: int, seed: int, ragged: bool = False):
     valid = table[table >= 0].to(torch.int64)
     refcount = torch.bincount(valid, minlength=num_pages).to(torch.int32)
     return table.contiguous(), refcount.contiguous(), int(num_pages)
+
+
+def make_gumbel(w: Workload, seed: int, device="cpu", pad_value: float = 8192.0) -> torch.Tensor:
+    """[R,N,ld] float32 standard Gumbel noise alone (say, the fresh noise of a bonus drawn
+    after resampling), drawn as the round's noise from its own stream; padding pad_value."""
+    R, N, V, ld = w.R, w.N, w.V, w.row_stride
+    dev = torch.device(device)
+    out = torch.full((R, N, ld), pad_value, dtype=torch.float32, device=dev)
+    g = _gen(seed, "noise", dev)
+    tiny = torch.finfo(torch.float32).tiny
+    for r in range(R):
+        u = torch.rand(N, V, generator=g, device=dev).clamp_(tiny, 1.0 - 2.0 ** -24)
+        out[r, :, :V] = -torch.log(-torch.log(u))
+    return out
+
+
+def make_ancestors(R: int, N: int, seed: int, device="cpu") -> torch.Tensor:
+    """[R,N] int32 ancestor indices as a resampling step leaves them: N uniform draws from
+    [0, N) per request, sorted."""
+    g = _gen(seed, "ancestors", "cpu")
+    a = torch.sort(torch.randint(0, N, (R, N), generator=g), dim=1).values
+    return a.to(torch.int32).to(device)
 
 
 def make_page_pool(R: int, N: int, P: int, page_size: int, seed: int, steps=None,

@@ -29,7 +29,8 @@ def test_every_declared_symbol_is_exported():
             "smcsd_status_string", "smcsd_round_args_size", "smcsd_bench_stream_read",
             "smcsd_bench_copy", "smcsd_sd_verify", "smcsd_verify_workspace_size",
             "smcsd_verify_args_size", "smcsd_gumbel_topk", "smcsd_topk_workspace_size",
-            "smcsd_pages_advance", "smcsd_pages_workspace_size"} <= names
+            "smcsd_pages_advance", "smcsd_pages_workspace_size", "smcsd_bonus_resampled",
+            "smcsd_bonus_workspace_size"} <= names
     lib = ctypes.CDLL(S.library_path())
     for n in sorted(names):
         assert hasattr(lib, n), n
@@ -86,7 +87,8 @@ def _round(a):
     ("mode", 3, S.ERR_ARG), ("reserved0", 1, S.ERR_ARG),
     ("N", S.MAX_N + 1, S.ERR_UNSUPPORTED), ("K", S.MAX_K + 1, S.ERR_UNSUPPORTED),
     ("target_logits", None, S.ERR_ARG), ("draft_logits", None, S.ERR_ARG),
-    ("draft_tokens", None, S.ERR_ARG), ("gumbel", None, S.ERR_ARG), ("uniform", None, S.ERR_ARG),
+    ("draft_tokens", None, S.ERR_ARG), ("gumbel", 0x10000008, S.ERR_ARG),  # misaligned
+    ("uniform", None, S.ERR_ARG),
     ("log_weights", None, S.ERR_ARG), ("ancestors", None, S.ERR_ARG), ("bonus", None, S.ERR_ARG),
     ("target_logits", 0x10000008, S.ERR_ARG),                # not 16-byte aligned
     ("workspace", None, S.ERR_WORKSPACE), ("workspace_bytes", 100, S.ERR_WORKSPACE),
@@ -265,3 +267,61 @@ def _pages(**kw):
 ])
 def test_pages_validation(kw, status):
     assert _pages(**kw) == status
+
+
+def test_bonus_workspace_size():
+    a = S.smcsd_bonus_workspace_size(64, 32, 128256, S.BF16)
+    assert a > 0 and a % 256 == 0
+    assert a == S.smcsd_topk_workspace_size(64 * 32, 128256, S.BF16, 1)
+    assert S.smcsd_bonus_workspace_size(1, 0, 100, S.BF16) == 0
+    assert S.smcsd_bonus_workspace_size(1, S.MAX_N + 1, 100, S.BF16) == 0
+    assert S.smcsd_bonus_workspace_size(1, 8, 100, 7) == 0
+
+
+def _bonus(**kw):
+    base = 0x10000000
+    a = dict(R=2, N=8, K=4, V=1000, ld=1000, dtype=S.BF16, target=base, temperature=base + 0x100000,
+             ancestors=base + 0x200000, gumbel=base + 0x300000, bonus=base + 0x400000,
+             out_tokens=None, workspace=base + 0x500000, workspace_bytes=1 << 20,
+             error_flags=None)
+    a.update(kw)
+    return S.raw_library().smcsd_bonus_resampled(
+        a["R"], a["N"], a["K"], a["V"], a["ld"], a["dtype"], a["target"], a["temperature"],
+        a["ancestors"], a["gumbel"], a["bonus"], a["out_tokens"], a["workspace"],
+        a["workspace_bytes"], a["error_flags"], None)
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(N=0), S.ERR_ARG),
+    (dict(K=0), S.ERR_ARG),
+    (dict(V=0), S.ERR_ARG),
+    (dict(R=-1), S.ERR_ARG),
+    (dict(ld=999), S.ERR_ARG),
+    (dict(ld=1004), S.ERR_ARG),                 # not a multiple of 8 for bf16
+    (dict(dtype=2), S.ERR_ARG),
+    (dict(N=S.MAX_N + 1), S.ERR_UNSUPPORTED),
+    (dict(K=S.MAX_K + 1), S.ERR_UNSUPPORTED),
+    (dict(target=None), S.ERR_ARG),
+    (dict(ancestors=None), S.ERR_ARG),
+    (dict(gumbel=None), S.ERR_ARG),
+    (dict(bonus=None), S.ERR_ARG),
+    (dict(gumbel=0x10300008), S.ERR_ARG),       # misaligned
+    (dict(workspace=None), S.ERR_WORKSPACE),
+    (dict(workspace_bytes=16), S.ERR_WORKSPACE),
+    (dict(workspace=0x10500010), S.ERR_WORKSPACE),
+])
+def test_bonus_validation(kw, status):
+    assert _bonus(**kw) == status
+
+
+def test_empty_bonus_call_is_a_no_op():
+    assert _bonus(R=0, target=None, temperature=None, ancestors=None, gumbel=None, bonus=None,
+                  workspace=None) == S.OK
+
+
+def test_round_without_noise_is_still_validated():
+    # gumbel NULL (no bonus in the round) is valid, so these calls must fail on another
+    # argument before anything is launched.
+    assert _round(_args(gumbel=None, bonus=None, uniform=None)) == S.ERR_ARG
+    assert _round(_args(gumbel=None, workspace_bytes=100)) == S.ERR_WORKSPACE
+    assert _round(_args(gumbel=None, N=S.MAX_N + 1)) == S.ERR_UNSUPPORTED
