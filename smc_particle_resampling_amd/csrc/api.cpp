@@ -126,6 +126,39 @@ static smcsd_status check_verify(const smcsd_verify_args* a, Plan* plan) {
     return SMCSD_OK;
 }
 
+// The logits pass. With TV the row pairs run in the cooperative exchange kernel and the
+// bonus rows (if any) in the Gumbel-Top-K slice kernel with k = 1, whose (key, index) per
+// (row, slice) lands in the same BonusPart layout (its slicing equals the TV plan's).
+// A persistent grid's share of the bonus rows ran slower than this ordinary grid.
+static_assert(kTvCPL == kTopkCPL, "bonus slices of the TV plan are Gumbel-Top-K slices");
+
+static hipError_t launch_logits_pass(const Plan& plan, const LogitsArgs& la, hipStream_t s) {
+    if (!plan.tv || plan.bonus_rows == 0) return launch_logits(plan, la, s);
+    Plan pairs = plan;
+    pairs.bonus_rows = 0;
+    pairs.total_wgs = plan.pair_wgs;
+    LogitsArgs lp = la;
+    lp.total_wgs = la.pair_wgs;
+    hipError_t e = launch_logits(pairs, lp, s);
+    if (e != hipSuccess) return e;
+    TopkArgs t{};
+    t.logits = la.target;
+    t.temperature = la.temperature;
+    t.gumbel = la.gumbel;
+    t.cand = la.bp;
+    t.out_tokens = nullptr;
+    t.row_mode = kTopkBonusRows;
+    t.ld = la.ld;
+    t.V = la.V;
+    t.k = 1;
+    t.chunks = plan.chunks;
+    t.S = plan.S;
+    t.cps = plan.cps;
+    t.N = la.N;
+    t.K = la.K;
+    return launch_topk_slices(plan.bonus_rows, plan.dtype, t, s);
+}
+
 // The TV pass of the round over the given logits: exchange slots filled, then the pass,
 // bracketed by the optional timing events.
 static hipError_t run_tv_pass(const Plan& plan, const LogitsArgs& la, char* ws,
@@ -137,7 +170,7 @@ static hipError_t run_tv_pass(const Plan& plan, const LogitsArgs& la, char* ws,
                               (int64_t)(plan.pair_wgs * sizeof(PairPart) / 4), ~0u, s);
     if (e != hipSuccess) return e;
     if (begin && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(begin), s)) != hipSuccess) return e;
-    if ((e = launch_logits(plan, la, s)) != hipSuccess) return e;
+    if ((e = launch_logits_pass(plan, la, s)) != hipSuccess) return e;
     if (end && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(end), s)) != hipSuccess) return e;
     return hipSuccess;
 }
@@ -232,7 +265,7 @@ smcsd_status smcsd_round(const smcsd_round_args* args, smcsd_stream stream) {
     }
     if (a.timing_begin && hipEventRecord(reinterpret_cast<hipEvent_t>(a.timing_begin), s) != hipSuccess)
         return SMCSD_ERR_DEVICE;
-    e = launch_logits(plan, la, s);
+    e = launch_logits_pass(plan, la, s);
     if (e != hipSuccess) return SMCSD_ERR_DEVICE;
     if (a.timing_end && hipEventRecord(reinterpret_cast<hipEvent_t>(a.timing_end), s) != hipSuccess)
         return SMCSD_ERR_DEVICE;
@@ -553,6 +586,7 @@ smcsd_status smcsd_bonus_resampled(int32_t R, int32_t N, int32_t K, int32_t V, i
     a.gumbel = gumbel;
     a.cand = static_cast<BonusPart*>(workspace);
     a.out_tokens = bonus;
+    a.row_mode = kTopkResampled;
     a.ancestors = ancestors;
     a.slot_tokens = out_tokens;
     a.error_flags = error_flags;

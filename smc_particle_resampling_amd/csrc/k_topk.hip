@@ -105,11 +105,15 @@ __global__ __launch_bounds__(kThreads) void k_topk_slice(TopkArgs a) {
     const int s = (int)(blockIdx.x % (unsigned)a.S);
     const int tid = threadIdx.x;
     int64_t lrow = row, trow = row;
-    if (a.ancestors) {
-        const int32_t x = a.ancestors[row];
-        if (x < 0 || x >= a.N) return;       // the merge writes -1 for this row
+    if (a.row_mode != kTopkRows) {
         trow = row / a.N;
-        lrow = (trow * a.N + x) * (a.K + 1) + a.K;
+        int64_t src = row;
+        if (a.row_mode == kTopkResampled) {
+            const int32_t x = a.ancestors[row];
+            if (x < 0 || x >= a.N) return;   // the merge writes -1 for this row
+            src = trow * a.N + x;
+        }
+        lrow = src * (a.K + 1) + a.K;
     }
     const char* zrow = static_cast<const char*>(a.logits) + (size_t)(lrow * a.ld) * ESZ;
     const float* grow = a.gumbel + (size_t)row * a.ld;
@@ -168,7 +172,7 @@ __global__ __launch_bounds__(kThreads) void k_topk_merge(TopkArgs a) {
     __shared__ BonusPart res[kMaxTopk];
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x;
-    if (a.ancestors) {
+    if (a.row_mode == kTopkResampled) {
         const int32_t x = a.ancestors[row];
         if (x < 0 || x >= a.N) {
             if (tid == 0) {
@@ -209,6 +213,14 @@ hipError_t launch_topk(int64_t rows, int32_t dtype, const TopkArgs& a, hipStream
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     k_topk_merge<<<dim3((unsigned)rows), block, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk_slices(int64_t rows, int32_t dtype, const TopkArgs& a, hipStream_t s) {
+    if (rows <= 0) return hipSuccess;
+    const dim3 block(kThreads), grid((unsigned)(rows * a.S));
+    if (dtype == SMCSD_BF16) k_topk_slice<SMCSD_BF16><<<grid, block, 0, s>>>(a);
+    else k_topk_slice<SMCSD_F32><<<grid, block, 0, s>>>(a);
     return hipGetLastError();
 }
 

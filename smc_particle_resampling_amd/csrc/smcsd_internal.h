@@ -136,6 +136,7 @@ struct VerifyArgs {
 
 // Gumbel-Top-K. Slices as in the TV pass (4 chunks a lane); every slice keeps its k best
 // (key, index) pairs, and one workgroup per row merges the S * k candidates.
+constexpr int kTopkRows = 0, kTopkBonusRows = 1, kTopkResampled = 2;
 constexpr int kTopkCPL = 4;
 constexpr int kMaxTopk = 64;           // == SMCSD_MAX_TOPK
 constexpr int kMaxTopkSlices = 64;     // S * k candidates, at most 8 per lane of the merge
@@ -147,8 +148,10 @@ struct TopkArgs {
     BonusPart* cand;       // [rows][S][k] workspace
     int32_t* out_tokens;
     float* out_keys;
-    // Bonus after resampling: row i = (r, j) reads target row ((r*N + ancestors[i])*(K+1) + K)
-    // and temperature[r]; nullptr ancestors = logits row i and temperature[i].
+    // Row map. kTopkRows: logits row i, temperature[i]. kTopkBonusRows: the round's bonus
+    // rows, row i = (r, j) reads target row i*(K+1) + K and temperature[r]. kTopkResampled:
+    // the bonus after resampling, target row ((r*N + ancestors[i])*(K+1) + K).
+    int32_t row_mode;
     const int32_t* ancestors;
     int32_t* slot_tokens;  // optional [rows][K+1]: column K receives the token
     int32_t* error_flags;
@@ -204,6 +207,8 @@ hipError_t launch_finalize(int32_t R, bool from_partials, int32_t dtype, const F
 hipError_t launch_remap(int32_t R, const RemapArgs& a, hipStream_t s);
 hipError_t launch_verify(int32_t R, int32_t dtype, const VerifyArgs& a, hipStream_t s);
 hipError_t launch_topk(int64_t rows, int32_t dtype, const TopkArgs& a, hipStream_t s);
+// The slice pass alone (k = 1 candidates per (row, slice) in a.cand), for the round's bonus.
+hipError_t launch_topk_slices(int64_t rows, int32_t dtype, const TopkArgs& a, hipStream_t s);
 hipError_t launch_pages(const PagesArgs& a, int32_t copy_grid, hipStream_t s);
 hipError_t launch_bench_read(const void* src, size_t bytes, uint32_t* sink, int32_t grid,
                              hipStream_t s);
