@@ -34,6 +34,7 @@ sys.path.insert(0, ROOT)
 PEAK_HBM_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["smc_particle_resampling_amd/csrc/k_logits.hip",
+                  "smc_particle_resampling_amd/csrc/k_topk.hip",
                   "smc_particle_resampling_amd/csrc/smcsd_internal.h"]
 
 
@@ -342,6 +343,8 @@ def main():
     ms_per_step = elapsed * 1e3 / args.steps
     alg = w.algorithmic_bytes()
     logits_bytes = alg["target"] + alg["draft"] + alg["noise"]
+    if after:       # the timed pass reads the row pairs only; the bonus is drawn afterwards
+        logits_bytes = alg["target"] * w.K // (w.K + 1) + alg["draft"]
     if topk:        # one logits row and one noise row per particle
         e = 2 if w.dtype == "bf16" else 4
         logits_bytes = w.R * w.N * w.V * (e + 4)
@@ -425,8 +428,11 @@ def main():
                    "round_GBps": (logits_bytes + table_bytes) / (ms_per_step * 1e-3) / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": None if topk else stored_traffic(name),
-                     "kernel": "k_topk_slice+k_topk_merge" if topk else "k_logits",
+                     "traffic": None if (topk or after) else stored_traffic(name),
+                     "kernel": ("k_topk_slice+k_topk_merge" if topk else
+                                "k_logits_tv" if after and w.tv else
+                                "k_logits_tv+k_topk_slice (bonus rows)" if w.tv else
+                                "k_logits_stream"),
                      "kernel_ms": k_mean_ms,
                      "algorithmic_bytes_per_launch": logits_bytes,
                      "attainable_read_GBps": rr},
