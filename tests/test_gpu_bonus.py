@@ -56,6 +56,7 @@ CASES = [
     W["r1-n8-k4-v32000-f32"].scaled(R=2),
     W["r16-n16-k4-v128256-bf16"].scaled(R=3, V=40001),           # ragged last chunk
     W["r64-n32-k8-v128256-bf16-tv"].scaled(R=4),                 # full vocabulary
+    W["r64-n32-k8-v128256-bf16-tv"],                             # the headline shape
     W["r32-n32-k8-v256000-bf16-tv-mixT"].scaled(R=3, V=70000),   # mixed temperatures
     W["r16-n16-k4-v128256-bf16"].scaled(R=2, N=1024, K=1, V=3000),
     W["r1-n8-k4-v32000-f32"].scaled(R=3, N=5, K=2, V=1),
@@ -67,7 +68,7 @@ CASES = [
 def test_bonus_resampled_matches_oracle(w, dev):
     _say("case", w.name, "R N K V", w.R, w.N, w.K, w.V)
     inp = synth.make_inputs(w, 5, device=dev, pages=False)
-    noise = synth.make_inputs(w, 6, device=dev, pages=False)["gumbel"]
+    noise = synth.make_gumbel(w, 6, device=dev)
     anc = synth.make_ancestors(w.R, w.N, 7, device=dev)
     out_tok = torch.full((w.R, w.N, w.K + 1), -5, dtype=torch.int32, device=dev)
     g, flags = _bonus_gpu(inp, anc, noise, dev, out_tokens=out_tok)
@@ -139,7 +140,7 @@ def test_round_then_bonus_after_resampling(mode, dev):
     oracle's own ancestors."""
     w = W["r64-n32-k8-v128256-bf16-tv"].scaled(R=3, V=20000, ctx=256, mode=mode)
     inp = synth.make_inputs(w, 9, device=dev)
-    noise = synth.make_inputs(w, 10, device=dev, pages=False)["gumbel"]
+    noise = synth.make_gumbel(w, 10, device=dev)
     host = synth.to_host(inp)
     out = smcsd.run_round(inp, mode=mode, ess_frac=w.ess_frac, tv=w.tv, bonus_noise=noise)
     torch.cuda.synchronize()

@@ -129,6 +129,7 @@ CASES = [
     (2, 1024, 3, 8, 7, 2048, 1, 16, 8),          # particle maximum
     (4, 64, 20, 8, 8, 3000, 0, 0, 9),            # > 4096 pages: several ragged chunks
     (6, 24, 10, 4, None, 0, 1, 32, 10),          # empty free list at entry
+    (64, 32, 30, 16, 9, 65536, 2, 64, 14),       # the driver bench's shape: 64 x 32, page 16
 ]
 
 
