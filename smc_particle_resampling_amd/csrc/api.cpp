@@ -298,10 +298,21 @@ smcsd_status smcsd_round(const smcsd_round_args* args, smcsd_stream stream) {
     fa.S = plan.S;
     fa.mode = a.mode;
     fa.ess_frac = a.ess_frac;
+    // Small tables are remapped by the finalize workgroup of their request, which saves a
+    // launch; larger ones (more than 16 entries a thread) keep the separate remap kernel,
+    // which spreads a request's table over several workgroups.
+    const int64_t table_entries = (int64_t)a.N * a.P;
+    const bool fused_remap = a.page_table_in && table_entries <= 16 * kThreads;
+    if (fused_remap) {
+        fa.pt_in = a.page_table_in;
+        fa.pt_out = a.page_table_out;
+        fa.refcount = a.refcount;
+        fa.P = a.P;
+        fa.num_pages = a.num_pages;
+    }
     e = launch_finalize(a.R, true, a.dtype, fa, s);
     if (e != hipSuccess) return SMCSD_ERR_DEVICE;
-
-    if (a.page_table_in) {
+    if (a.page_table_in && !fused_remap) {
         RemapArgs ra{};
         ra.ancestors = a.ancestors;
         ra.pt_in = a.page_table_in;
@@ -311,7 +322,7 @@ smcsd_status smcsd_round(const smcsd_round_args* args, smcsd_stream stream) {
         ra.N = a.N;
         ra.P = a.P;
         ra.num_pages = a.num_pages;
-        ra.blocks_per_request = (int32_t)std::max<int64_t>(1, ((int64_t)a.N * a.P + 2047) / 2048);
+        ra.blocks_per_request = (int32_t)std::max<int64_t>(1, (table_entries + 2047) / 2048);
         e = launch_remap(a.R, ra, s);
         if (e != hipSuccess) return SMCSD_ERR_DEVICE;
     }

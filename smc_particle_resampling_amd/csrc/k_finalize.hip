@@ -7,7 +7,9 @@
 // token. One workgroup handles one request. The slice partials of the logits pass are
 // combined in fixed slice order, and everything per request runs in double precision: the
 // log-weights, logsumexp, ESS and the inclusive prefix sum of the weights. A boundary tie
-// U_j == C_i therefore resolves the same way on every run.
+// U_j == C_i therefore resolves the same way on every run. When the round carries a page
+// table, the same workgroup then remaps its request's table rows through the ancestors
+// (pointer exchange, as k_remap does), which saves the round a launch.
 #include "smcsd_internal.h"
 
 namespace smcsd {
@@ -20,6 +22,8 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
     __shared__ double s_l[SMCSD_MAX_N];    // l_i = log_weights_i + log_w_incr_i
     __shared__ double s_c[SMCSD_MAX_N];    // W_i, then C_i
     __shared__ int32_t s_bonus[SMCSD_MAX_N];
+    __shared__ int32_t s_anc[SMCSD_MAX_N];   // ancestors, for the page-table remap
+    __shared__ int32_t s_off[SMCSD_MAX_N];   // offspring counts o_i
     __shared__ double s_logZ;
     __shared__ int32_t s_rs;
     const int tid = threadIdx.x;
@@ -87,6 +91,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
         for (int32_t i = tid; i < N; i += kThreads)
             s_l[i] = (double)a.log_weights[r * N + i] + (double)a.log_w_incr[r * N + i];
     }
+    for (int32_t i = tid; i < N; i += kThreads) s_off[i] = 0;
     __syncthreads();
 
     if (tid == 0) {
@@ -138,6 +143,8 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
             anc = lo;
         }
         a.ancestors[r * N + j] = anc;
+        s_anc[j] = anc;
+        if (a.pt_in) atomicAdd(&s_off[anc], 1);
         a.log_weights[r * N + j] = rs ? (float)(-log((double)N)) : (float)(s_l[j] - logZ);
         if constexpr (FROM_PARTIALS) {
             if (a.out_tokens) {
@@ -145,6 +152,32 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
                 const int32_t* src = a.tokens + (r * N + anc) * K;
                 for (int32_t k = 0; k < K; ++k) dst[k] = src[k];
                 dst[K] = s_bonus[anc];
+            }
+        }
+    }
+
+    // Page-table remap: pt_out[j] = pt_in[anc_j]; every valid entry of old row i with
+    // o_i != 1 moves its page's refcount by o_i - 1 (integer atomics commute, so the result
+    // does not depend on the order).
+    if (a.pt_in) {
+        __syncthreads();
+        const int32_t P = a.P;
+        const int64_t NP = (int64_t)N * P;
+        const int32_t* in = a.pt_in + r * NP;
+        int32_t* out = a.pt_out + r * NP;
+        for (int64_t e = tid; e < NP; e += kThreads) {
+            const int32_t j = (int32_t)(e / P);
+            const int32_t col = (int32_t)(e - (int64_t)j * P);
+            out[e] = in[(int64_t)s_anc[j] * P + col];
+            const int32_t page = in[e];
+            const int32_t o = s_off[j];
+            if (page >= 0 && o != 1) {
+                if (page >= a.num_pages) {
+                    flag_error(a.error_flags, SMCSD_DEVERR_PAGE);
+                } else {
+                    const int32_t old = atomicAdd(&a.refcount[page], o - 1);
+                    if (old + (o - 1) < 0) flag_error(a.error_flags, SMCSD_DEVERR_REFCOUNT);
+                }
             }
         }
     }

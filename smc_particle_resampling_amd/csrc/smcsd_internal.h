@@ -97,6 +97,11 @@ struct FinalizeArgs {
     int32_t* out_tokens;
     float* tv;
     int32_t* error_flags;
+    // page-table remap in the same launch (pt_in == nullptr: none)
+    const int32_t* pt_in;
+    int32_t* pt_out;
+    int32_t* refcount;
+    int32_t P, num_pages;
     int64_t ld;
     int32_t N, K, V, S;
     int32_t mode;
