@@ -275,6 +275,11 @@ def main():
         pool = synth.make_page_pool(w.R, w.N, P, ps, 0, steps=total * (w.K + 1),
                                     spare=w.R * w.N * grow)
         num_pages = pool["refcount"].numel()
+        pool_gib = num_pages * args.kv_tensors * args.kv_page_bytes / 2**30
+        if pool_gib > 160:
+            raise SystemExit("page pool of %.0f GiB for %d steps does not fit beside the logits; "
+                             "use fewer --steps or smaller --kv-tensors / --kv-page-bytes"
+                             % (pool_gib, total))
         print("# page pool: %d pages x %d KV tensors x %d B = %.1f GiB" % (
             num_pages, args.kv_tensors, args.kv_page_bytes,
             num_pages * args.kv_tensors * args.kv_page_bytes / 2**30), file=sys.stderr, flush=True)

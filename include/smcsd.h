@@ -221,7 +221,7 @@ smcsd_status smcsd_remap_pages(int32_t R, int32_t N, int32_t P, const int32_t *a
  *  kv: NULL (tables only) or kv_count KV tensors, tensor t's page p at byte
  *    kv + t * kv_stride + p * page_bytes; kv, page_bytes and kv_stride multiples of 16,
  *    kv_stride >= num_pages * page_bytes when kv_count > 1;
- *  workspace of smcsd_pages_workspace_size(R, N, P, num_pages) bytes;
+ *  workspace of smcsd_pages_workspace_size(R, N, P, num_pages) bytes, 256-byte aligned;
  *  stats: NULL or [4] int32 out: pages released, pops served, pages copied, pops that found
  *    the free list empty; error_flags optional.
  * A page must not be named by two requests' tables. If the free list runs dry, the

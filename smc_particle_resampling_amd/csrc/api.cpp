@@ -437,6 +437,7 @@ smcsd_status smcsd_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_s
         max_units = (int64_t)R * N * kv_count * tiles;
     }
     if (!workspace || workspace_bytes < L.bytes) return SMCSD_ERR_WORKSPACE;
+    if (reinterpret_cast<uintptr_t>(workspace) & 255u) return SMCSD_ERR_WORKSPACE;
     const size_t pb = sizeof(int32_t) * (size_t)num_pages;
     const size_t tb = sizeof(int32_t) * (size_t)R * N * P;
     const void* bufs[6] = {page_table, refcount, free_ids, n_free, workspace, stats};

@@ -264,6 +264,7 @@ def _pages(**kw):
     (dict(free_ids=0x10010100), S.ERR_ARG),                              # overlaps refcount
     (dict(n_free=0x10040010), S.ERR_ARG),                                # inside the workspace
     (dict(stats=0x10030000), S.ERR_ARG),                                 # overlaps n_free
+    (dict(workspace=0x10040010), S.ERR_WORKSPACE),                       # not 256-byte aligned
 ])
 def test_pages_validation(kw, status):
     assert _pages(**kw) == status
