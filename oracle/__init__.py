@@ -70,7 +70,8 @@ def lib() -> ctypes.CDLL:
             L.orc_bonus_resampled.restype = i32
             L.orc_bonus_resampled.argtypes = [i32, i32, i32, i64, i64, i32, p, p, p, p, p, p]
             L.orc_pages_advance.restype = i32
-            L.orc_pages_advance.argtypes = [i32, i32, i32, i32, p, p, p, i32, p, p, p, p, i64, i32]
+            L.orc_pages_advance.argtypes = [i32, i32, i32, i32, p, p, p, i32, p, p, p, p, i64, i32,
+                                            i32]
             L.orc_num_threads.restype = i32
             L.orc_num_threads.argtypes = []
             _lib = L
@@ -281,12 +282,15 @@ def bonus_resampled(target: np.ndarray, temperature: np.ndarray, ancestors: np.n
 
 def pages_advance(page_table: np.ndarray, refcount: np.ndarray, free_ids: np.ndarray,
                   n_free: int, len_before, len_after, page_size: int,
-                  kv: np.ndarray | None = None, kv_inplace: bool = False) -> dict:
+                  kv: np.ndarray | None = None, kv_inplace: bool = False,
+                  token_rows: bool = False) -> dict:
     """Page lifecycle between rounds (release at refcount 0, copy-on-write of shared tail
     pages, fresh pages for new columns) on copies of the given host arrays. page_table
     [R,N,P] int32, refcount and free_ids [num_pages] int32, kv uint8 [num_pages, page_bytes]
     or [kv_count, num_pages, page_bytes] (one tensor per layer and K / V) or None; with
-    kv_inplace the (C-contiguous uint8) kv array itself receives the copies.
+    kv_inplace the (C-contiguous uint8) kv array itself receives the copies. token_rows: a
+    page is page_size token rows in token order, and a copy moves only the rows the tail
+    holds.
     Lengths satisfy 0 <= len_before <= len_after <= P * page_size.
     Returns dict(page_table, refcount, free_ids, n_free, kv, status)."""
     pt = np.array(page_table, dtype=np.int32, copy=True)
@@ -309,10 +313,11 @@ def pages_advance(page_table: np.ndarray, refcount: np.ndarray, free_ids: np.nda
         if kvc.ndim == 2:
             kvc = kvc[None]
         assert kvc.ndim == 3 and kvc.shape[1] == rc.size
+        assert not token_rows or kvc.shape[2] % page_size == 0
     nf = np.array([n_free], np.int32)
     st = lib().orc_pages_advance(R, N, P, int(page_size), _ptr(lb), _ptr(la), _ptr(pt), rc.size,
                                  _ptr(rc), _ptr(fl), _ptr(nf), _ptr(kvc), kvc.shape[2],
-                                 kvc.shape[0])
+                                 kvc.shape[0], int(bool(token_rows)))
     if kv is not None and np.ndim(kv) == 2:
         kvc = kvc[0]
     return dict(page_table=pt, refcount=rc, free_ids=fl, n_free=int(nf[0]),

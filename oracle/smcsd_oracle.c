@@ -564,12 +564,16 @@ int32_t orc_bonus_resampled(int32_t R, int32_t N, int32_t K, int64_t V, int64_t 
  * and -3 is returned.
  * Layouts: pt [R][N][P] int32, refcount / free_ids [num_pages], kv [kv_count][num_pages]
  * [page_bytes]: a page id names the same page in every one of the kv_count KV tensors (one
- * per layer and per K / V), and a copy copies it in all of them.
+ * per layer and per K / V), and a copy copies it in all of them. With token_rows (a token
+ * pool's layout: a page is page_size rows of page_bytes / page_size bytes, in token order)
+ * a copy moves only the rows the tail holds, len_before mod page_size of them; the rest of
+ * the destination page keeps its bytes (the next round writes them).
  */
 int32_t orc_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_size,
                           const int32_t *len_before, const int32_t *len_after, int32_t *pt,
                           int32_t num_pages, int32_t *refcount, int32_t *free_ids,
-                          int32_t *n_free, uint8_t *kv, int64_t page_bytes, int32_t kv_count)
+                          int32_t *n_free, uint8_t *kv, int64_t page_bytes, int32_t kv_count,
+                          int32_t token_rows)
 {
     const size_t tensor_bytes = (size_t)num_pages * (size_t)page_bytes;
     int32_t err = 0;
@@ -586,6 +590,8 @@ int32_t orc_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_size,
         int32_t lb = len_before[r];
         if (lb > 0 && lb % page_size != 0) {
             int32_t c = (lb - 1) / page_size;
+            size_t copy_bytes = token_rows ? (size_t)(lb % page_size) * (size_t)(page_bytes / page_size)
+                                           : (size_t)page_bytes;
             for (int32_t j = 0; j < N; ++j) {
                 int32_t p = row0[(size_t)j * P + c];
                 if (p < 0)
@@ -605,8 +611,7 @@ int32_t orc_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_size,
                 int32_t q = free_ids[--(*n_free)];
                 for (int32_t t = 0; t < kv_count; ++t)
                     memcpy(kv + t * tensor_bytes + (size_t)q * (size_t)page_bytes,
-                           kv + t * tensor_bytes + (size_t)p * (size_t)page_bytes,
-                           (size_t)page_bytes);
+                           kv + t * tensor_bytes + (size_t)p * (size_t)page_bytes, copy_bytes);
                 row0[(size_t)j * P + c] = q;
                 refcount[p] -= 1;
                 refcount[q] = 1;

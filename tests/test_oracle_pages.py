@@ -138,3 +138,34 @@ def test_layered_kv_copies_every_tensor():
     want[:, 13] = kv[:, 11]
     assert np.array_equal(out["kv"], want)
     assert np.array_equal(kv, np.random.default_rng(5).integers(0, 256, kv.shape, dtype=np.uint8))
+
+
+def test_token_rows_copy_only_the_filled_tokens():
+    # Page size 4, page_bytes 8: two bytes per token row. Length 6 leaves 2 tokens in the
+    # tail page (column 1), so the copy of page 11 into the popped page 13 moves 2 rows
+    # (4 bytes) and the other 4 bytes of page 13 stay as they were, in every tensor.
+    num_pages, page_bytes, T = 16, 8, 2
+    rc = np.full(num_pages, -1, np.int32)
+    free = np.zeros(num_pages, np.int32)
+    free[:12] = list(range(10)) + [14, 15]
+    pt = np.array([[[10, 11, -1], [10, 11, -1], [10, 12, -1]]], np.int32)
+    rc[10], rc[11], rc[12], rc[13] = 3, 2, 1, 0
+    kv = np.random.default_rng(6).integers(0, 256, (T, num_pages, page_bytes), dtype=np.uint8)
+    full = oracle.pages_advance(pt, rc, free, 12, [6], [9], 4, kv)
+    rows = oracle.pages_advance(pt, rc, free, 12, [6], [9], 4, kv, token_rows=True)
+    for k in ("page_table", "refcount", "free_ids", "n_free", "status"):
+        assert np.array_equal(np.asarray(full[k]), np.asarray(rows[k])), k
+    want = kv.copy()
+    want[:, 13, :4] = kv[:, 11, :4]
+    assert np.array_equal(rows["kv"], want)
+    assert not np.array_equal(full["kv"], rows["kv"])          # the full copy moved all 8
+
+
+def test_token_rows_with_a_full_tail_copy_nothing():
+    pt = np.array([[[3, -1], [3, -1]]], np.int32)
+    rc = np.array([0, -1, 0, 2, -1, 0, -1, -1], np.int32)
+    free = np.array([1, 4, 6, 7, 0, 0, 0, 0], np.int32)
+    kv = np.arange(8 * 16, dtype=np.uint8).reshape(8, 16)
+    out = oracle.pages_advance(pt, rc, free, 4, [4], [5], 4, kv, token_rows=True)
+    assert np.array_equal(out["kv"], kv)
+    assert out["page_table"][0, :, 1].tolist() == [5, 2]      # appends only
