@@ -120,7 +120,7 @@ def cpu_baseline_driver(w, pool_args, target_s=12.0, sample_requests=2):
     rs = min(w.R, sample_requests)
     small = w.scaled(R=rs)
     host = synth.to_host(synth.make_inputs(small, 11, device="cpu", pages=False))
-    ps, P, kv_tensors, page_bytes = pool_args
+    ps, P, kv_tensors, page_bytes, token_rows = pool_args
     pool = synth.make_page_pool(rs, w.N, P, ps, 11, steps=w.K + 1, spare=256)
     num_pages = pool["refcount"].numel()
     kv = np.zeros((kv_tensors, num_pages, page_bytes), np.uint8)
@@ -131,7 +131,8 @@ def cpu_baseline_driver(w, pool_args, target_s=12.0, sample_requests=2):
         ora = oracle.round(host, V=w.V, mode=w.mode, ess_frac=w.ess_frac, tv=w.tv)
         oracle.pages_advance(ora["page_table"], ora["refcount"], pool["free_ids"].numpy(),
                              pool["n_free"], pool["len_before"].numpy(),
-                             pool["len_after"].numpy(), ps, kv, kv_inplace=True)
+                             pool["len_after"].numpy(), ps, kv, kv_inplace=True,
+                             token_rows=token_rows)
         times.append(time.perf_counter() - t)
     per_request = sum(times) / (len(times) * rs)
     return {"value": 1.0 / (w.R * per_request), "unit": "driver steps/s",
@@ -211,6 +212,9 @@ def main():
                          "(after: smcsd_round without noise, then smcsd_bonus_resampled)")
     ap.add_argument("--kv-tensors", type=int, default=64,
                     help="driver: KV tensors sharing the page ids (32 layers x K and V)")
+    ap.add_argument("--kv-token-rows", action="store_true",
+                    help="driver: token-major KV pages (a token pool's layout); copy-on-write "
+                         "moves only the tail's filled token rows")
     ap.add_argument("--kv-page-bytes", type=int, default=32768,
                     help="driver: bytes of one page in one KV tensor (16 tokens x 8 KV heads x "
                          "128 dims x bf16)")
@@ -291,7 +295,7 @@ def main():
         n_free = torch.tensor([pool["n_free"]], dtype=torch.int32, device=dev)
         lens = torch.stack([pool["len_before"] + t * (w.K + 1) for t in range(total + 1)])
         lens = lens.to(torch.int32).to(dev)
-        stats = torch.zeros((total, 4), dtype=torch.int32, device=dev)
+        stats = torch.zeros((total, 5), dtype=torch.int32, device=dev)
         pws = torch.empty(smcsd.smcsd_pages_workspace_size(w.R, w.N, P, num_pages),
                           dtype=torch.uint8, device=dev)
         out = smcsd.alloc_outputs(w.R, w.N, w.K, dev, tv=w.tv, V=w.V,
@@ -313,7 +317,8 @@ def main():
                                       page_table=out["page_table_out"],
                                       refcount=inp["refcount"], free_ids=free_ids,
                                       n_free=n_free, page_size=ps, workspace=pws, kv=kv,
-                                      stats=stats[t], error_flags=out["error_flags"])
+                                      token_rows=args.kv_token_rows, stats=stats[t],
+                                      error_flags=out["error_flags"])
             if lt:
                 ev.record(lt[1], cur)
     else:
@@ -362,11 +367,13 @@ def main():
         lms = [ev.elapsed_ms(a, b) for a, b in life]
         st = stats[args.warmup:].cpu().numpy()
         copied = float(st[:, 2].mean())
-        moved = 2.0 * copied * args.kv_tensors * args.kv_page_bytes    # read + write per copy
+        # read + write of every copied token row in every tensor
+        moved = 2.0 * float(st[:, 4].mean()) * (args.kv_page_bytes // ps) * args.kv_tensors
         lifecycle = {"ms_mean": sum(lms) / len(lms), "ms_min": min(lms), "ms_max": max(lms),
                      "released_per_step": float(st[:, 0].mean()),
                      "pops_per_step": float(st[:, 1].mean()),
                      "pages_copied_per_step": copied,
+                     "token_rows_copied_per_step": float(st[:, 4].mean()),
                      "pops_unserved": int(st[:, 3].sum()),
                      "kv_copy_bytes_per_step": moved,
                      "kv_copy_GBps_over_lifecycle": moved / (sum(lms) / len(lms) * 1e-3) / 1e9}
@@ -386,7 +393,8 @@ def main():
     if args.no_cpu_baseline:
         cpu = None
     elif driver:
-        cpu = cpu_baseline_driver(w, (ps, P, args.kv_tensors, args.kv_page_bytes))
+        cpu = cpu_baseline_driver(w, (ps, P, args.kv_tensors, args.kv_page_bytes,
+                                      args.kv_token_rows))
     else:
         cpu = cpu_baseline(w, path=args.path, k=args.topk)
     if driver:
@@ -427,7 +435,9 @@ def main():
                    "pages_per_particle": (w.P if args.path == "round" else
                                           P if driver else None),
                    "kv_cache": ({"tensors": args.kv_tensors, "page_bytes": args.kv_page_bytes,
-                                 "page_tokens": ps, "pages": num_pages} if driver else None),
+                                 "page_tokens": ps, "pages": num_pages,
+                                 "copy": "filled token rows" if args.kv_token_rows else "whole pages"}
+                                if driver else None),
                    "topk": args.topk if topk else None,
                    "bonus": (args.bonus if args.path in ("round", "driver") else None),
                    "round_GBps": (logits_bytes + table_bytes) / (ms_per_step * 1e-3) / 1e9},

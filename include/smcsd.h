@@ -220,10 +220,15 @@ smcsd_status smcsd_remap_pages(int32_t R, int32_t N, int32_t P, const int32_t *a
  *  refcount, free_ids [num_pages] int32, in/out; n_free [1] int32, in/out;
  *  kv: NULL (tables only) or kv_count KV tensors, tensor t's page p at byte
  *    kv + t * kv_stride + p * page_bytes; kv, page_bytes and kv_stride multiples of 16,
- *    kv_stride >= num_pages * page_bytes when kv_count > 1;
+ *    kv_stride >= num_pages * page_bytes when kv_count > 1, page_bytes <= INT32_MAX;
+ *  token_rows: 0 copies whole pages; nonzero declares token-major pages (page_size rows of
+ *    page_bytes / page_size bytes, a multiple of 16, in token order, the layout of a token
+ *    pool) and copies only the len_before mod page_size rows the tail holds; the other rows
+ *    of the new page keep their bytes until the next round writes them;
  *  workspace of smcsd_pages_workspace_size(R, N, P, num_pages) bytes, 256-byte aligned;
- *  stats: NULL or [4] int32 out: pages released, pops served, pages copied, pops that found
- *    the free list empty; error_flags optional.
+ *  stats: NULL or [5] int32 out: pages released, pops served, pages copied, pops that found
+ *    the free list empty, token rows the copies cover in each KV tensor (page_size per copy
+ *    unless token_rows); error_flags optional.
  * A page must not be named by two requests' tables. If the free list runs dry, the
  * entries it cannot fill stay -1 and SMCSD_DEVERR_POOL is set.
  */
@@ -232,7 +237,8 @@ smcsd_status smcsd_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_s
                                  int32_t *page_table, int32_t num_pages, int32_t *refcount,
                                  int32_t *free_ids, int32_t *n_free, void *kv,
                                  int64_t page_bytes, int32_t kv_count, int64_t kv_stride,
-                                 void *workspace, size_t workspace_bytes, int32_t *stats,
+                                 int32_t token_rows, void *workspace, size_t workspace_bytes,
+                                 int32_t *stats,
                                  int32_t *error_flags, smcsd_stream stream);
 
 /* Workspace bytes smcsd_pages_advance needs (0 if the sizes are invalid). */

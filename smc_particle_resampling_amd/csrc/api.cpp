@@ -404,7 +404,7 @@ static bool pages_layout(int32_t R, int32_t N, int32_t P, int32_t num_pages, Pag
     L->off_chunk = o;                                 // chunk_cnt, chunk_off
     o = align256(o + 2 * sizeof(int32_t) * (size_t)L->chunks);
     L->off_copies = o;
-    o = align256(o + sizeof(int2) * (size_t)R * N);
+    o = align256(o + sizeof(PageCopy) * (size_t)R * N);
     L->bytes = o;
     return true;
 }
@@ -419,7 +419,8 @@ smcsd_status smcsd_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_s
                                  int32_t* page_table, int32_t num_pages, int32_t* refcount,
                                  int32_t* free_ids, int32_t* n_free, void* kv,
                                  int64_t page_bytes, int32_t kv_count, int64_t kv_stride,
-                                 void* workspace, size_t workspace_bytes, int32_t* stats,
+                                 int32_t token_rows, void* workspace, size_t workspace_bytes,
+                                 int32_t* stats,
                                  int32_t* error_flags, smcsd_stream stream) {
     if (R < 0 || N < 1 || P < 1 || page_size < 1 || num_pages < 1) return SMCSD_ERR_ARG;
     PagesLayout L;
@@ -429,6 +430,10 @@ smcsd_status smcsd_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_s
     int64_t max_units = 0;
     if (kv) {
         if (page_bytes < 16 || page_bytes % 16 != 0 || !aligned16(kv) || kv_count < 1)
+            return SMCSD_ERR_ARG;
+        if (page_bytes > INT32_MAX) return SMCSD_ERR_UNSUPPORTED;
+        // token rows: page_size rows of page_bytes / page_size bytes, each a multiple of 16
+        if (token_rows && (page_bytes % page_size != 0 || (page_bytes / page_size) % 16 != 0))
             return SMCSD_ERR_ARG;
         if (page_bytes > INT64_MAX / num_pages) return SMCSD_ERR_ARG;
         if (kv_count > 1 && (kv_stride % 16 != 0 || kv_stride < page_bytes * num_pages))
@@ -441,7 +446,7 @@ smcsd_status smcsd_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_s
     const size_t pb = sizeof(int32_t) * (size_t)num_pages;
     const size_t tb = sizeof(int32_t) * (size_t)R * N * P;
     const void* bufs[6] = {page_table, refcount, free_ids, n_free, workspace, stats};
-    const size_t sizes[6] = {tb, pb, pb, sizeof(int32_t), L.bytes, 4 * sizeof(int32_t)};
+    const size_t sizes[6] = {tb, pb, pb, sizeof(int32_t), L.bytes, 5 * sizeof(int32_t)};
     for (int i = 0; i < 6; ++i)
         for (int k = i + 1; k < 6; ++k)
             if (bufs[i] && bufs[k] && overlap(bufs[i], sizes[i], bufs[k], sizes[k]))
@@ -458,6 +463,7 @@ smcsd_status smcsd_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_s
     a.page_bytes = page_bytes;
     a.kv_stride = kv_stride;
     a.kv_count = kv ? kv_count : 0;
+    a.token_rows = token_rows != 0;
     int32_t* req = reinterpret_cast<int32_t*>(ws + L.off_req);
     a.hdr = reinterpret_cast<int32_t*>(ws + L.off_hdr);
     a.req_cow = req;
@@ -467,7 +473,7 @@ smcsd_status smcsd_pages_advance(int32_t R, int32_t N, int32_t P, int32_t page_s
     a.cow_rank = reinterpret_cast<int32_t*>(ws + L.off_rank);
     a.chunk_cnt = reinterpret_cast<int32_t*>(ws + L.off_chunk);
     a.chunk_off = a.chunk_cnt + L.chunks;
-    a.copies = reinterpret_cast<int2*>(ws + L.off_copies);
+    a.copies = reinterpret_cast<PageCopy*>(ws + L.off_copies);
     a.stats = stats;
     a.error_flags = error_flags;
     a.R = R;

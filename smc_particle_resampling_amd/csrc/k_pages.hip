@@ -28,7 +28,8 @@
 //   k_pages_apply    one workgroup per request: pop number i (over all requests) takes
 //                    free_ids[F - 1 - i], F = free count after release; writes the table,
 //                    the refcounts and the (source, destination) list of copies.
-//   k_pages_copy     a grid-stride pass over (copy, KV tensor, 32 KiB tile): HBM-bound copy.
+//   k_pages_copy     a grid-stride pass over (copy, KV tensor, 32 KiB tile): HBM-bound copy,
+//                    of the whole page or (token-major pages) of the tail's filled rows.
 // Integer atomics commute and every pop index is fixed by the sums, so the result is the
 // same as the sequential one on every run.
 #include "smcsd_internal.h"
@@ -185,17 +186,24 @@ __global__ __launch_bounds__(kThreads) void k_pages_scan(PagesArgs a) {
     __syncthreads();
     if (a.stats) {
         // Copies served: request r's copies are pops req_base[r] .. req_base[r] + req_cow[r] - 1.
+        // Each copies `rows` token rows: the tail's filled rows with token-major pages, else all.
         const int32_t F = s_F;
-        int mine = 0;
-        for (int64_t i = threadIdx.x; i < a.R; i += kThreads)
-            mine += max(0, min(a.req_cow[i], F - a.req_base[i]));
-        int copied;
+        int mine = 0, mine_rows = 0;
+        for (int64_t i = threadIdx.x; i < a.R; i += kThreads) {
+            const int served = max(0, min(a.req_cow[i], F - a.req_base[i]));
+            const int rows = a.token_rows ? a.len_before[i] % a.page_size : a.page_size;
+            mine += served;
+            mine_rows += served * rows;
+        }
+        int copied, rows_copied;
         block_excl_scan(mine, s_scan, &copied);
+        block_excl_scan(mine_rows, s_scan, &rows_copied);
         if (threadIdx.x == 0) {
             a.stats[0] = F - a.hdr[0];
             a.stats[1] = min(pops, F);
             a.stats[2] = copied;
             a.stats[3] = max(0, pops - F);
+            a.stats[4] = rows_copied;
         }
     }
 }
@@ -250,6 +258,8 @@ __global__ __launch_bounds__(kThreads) void k_pages_apply(PagesArgs a) {
     const int64_t cb = a.cow_base[r];
     int32_t* row0 = a.page_table + (int64_t)r * N * P;
     const int32_t c = tail_col(lb, a.page_size);
+    const int32_t copy_bytes =
+        a.token_rows ? (int32_t)((lb % a.page_size) * (a.page_bytes / a.page_size)) : (int32_t)a.page_bytes;
     if (c >= 0) {
         for (int32_t j = threadIdx.x; j < N; j += kThreads) {
             const int32_t rank = a.cow_rank[(int64_t)r * N + j];
@@ -261,7 +271,7 @@ __global__ __launch_bounds__(kThreads) void k_pages_apply(PagesArgs a) {
             if (q >= 0) a.refcount[q] = 1;
             const int32_t old = atomicSub(&a.refcount[p], 1);
             if (old < 1) flag_error(a.error_flags, SMCSD_DEVERR_REFCOUNT);
-            a.copies[cb + rank] = make_int2(p, q);
+            a.copies[cb + rank] = PageCopy{p, q, copy_bytes, 0};
         }
     }
     const int32_t c0 = ceil_div(lb, a.page_size);
@@ -288,12 +298,12 @@ __global__ __launch_bounds__(kThreads) void k_pages_copy(PagesArgs a) {
         const int64_t rem = u - ci * per_copy;
         const int64_t t = rem / tiles;
         const int64_t tile = rem - t * tiles;
-        const int2 pq = a.copies[ci];
-        if (pq.y < 0) continue;
+        const PageCopy pc = a.copies[ci];
         const int64_t off = tile * kCopyTile;
-        const int64_t n16 = (min((int64_t)kCopyTile, a.page_bytes - off)) / 16;
-        const u32x4* src = reinterpret_cast<const u32x4*>(kv + t * a.kv_stride + pq.x * a.page_bytes + off);
-        u32x4* dst = reinterpret_cast<u32x4*>(kv + t * a.kv_stride + pq.y * a.page_bytes + off);
+        if (pc.dst < 0 || off >= pc.bytes) continue;
+        const int64_t n16 = (min((int64_t)kCopyTile, (int64_t)pc.bytes - off)) / 16;
+        const u32x4* src = reinterpret_cast<const u32x4*>(kv + t * a.kv_stride + pc.src * a.page_bytes + off);
+        u32x4* dst = reinterpret_cast<u32x4*>(kv + t * a.kv_stride + pc.dst * a.page_bytes + off);
         constexpr int kPer = kCopyTile / 16 / kThreads;
         u32x4 v[kPer];
 #pragma unroll

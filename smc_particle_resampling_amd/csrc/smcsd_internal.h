@@ -171,6 +171,13 @@ struct TopkArgs {
 constexpr int kPageChunk = 4096;       // pages per workgroup of the release count / push
 constexpr int kCopyTile = 32768;       // bytes per workgroup step of the KV page copy
 
+// One copy-on-write: source and destination page, bytes to copy in each KV tensor (-1
+// destination: the pop found the list empty, nothing to copy).
+struct PageCopy {
+    int32_t src, dst;
+    int32_t bytes, pad;
+};
+
 struct PagesArgs {
     const int32_t* len_before;
     const int32_t* len_after;
@@ -181,6 +188,7 @@ struct PagesArgs {
     void* kv;
     int64_t page_bytes, kv_stride;
     int32_t kv_count;
+    int32_t token_rows;    // nonzero: copy only the tail's filled token rows
     int32_t* hdr;          // [4]: free count before release, after release, pops, copies
     int32_t* req_cow;      // [R]
     int32_t* req_pops;     // [R]
@@ -189,8 +197,9 @@ struct PagesArgs {
     int32_t* cow_rank;     // [R][N] copy rank within the request, -1 = no copy
     int32_t* chunk_cnt;    // [chunks]
     int32_t* chunk_off;    // [chunks]
-    int2* copies;          // [R*N] (source page, destination page or -1)
-    int32_t* stats;        // optional [4]: released, pops served, copies served, pops unserved
+    PageCopy* copies;      // [R*N]
+    int32_t* stats;        // optional [5]: released, pops served, copies served, pops unserved,
+                           // token rows the served copies cover (per KV tensor)
     int32_t* error_flags;
     int32_t R, N, P, page_size, num_pages, chunks;
 };

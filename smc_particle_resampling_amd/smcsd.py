@@ -86,7 +86,7 @@ _lib.smcsd_bonus_workspace_size.restype = _sz
 _lib.smcsd_bonus_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
 _lib.smcsd_pages_advance.restype = _i32
 _lib.smcsd_pages_advance.argtypes = [_i32, _i32, _i32, _i32, _p, _p, _p, _i32, _p, _p, _p, _p,
-                                     _i64, _i32, _i64, _p, _sz, _p, _p, _p]
+                                     _i64, _i32, _i64, _i32, _p, _sz, _p, _p, _p]
 _lib.smcsd_pages_workspace_size.restype = _sz
 _lib.smcsd_pages_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
 _lib.smcsd_bench_stream_read.argtypes = [_p, _sz, _p, _i32, _p]
@@ -408,11 +408,12 @@ def smcsd_pages_workspace_size(R: int, N: int, P: int, num_pages: int) -> int:
 
 
 def smcsd_pages_advance(*, len_before, len_after, page_table, refcount, free_ids, n_free,
-                        page_size: int, workspace, kv=None, stats=None, error_flags=None,
-                        stream=None) -> None:
+                        page_size: int, workspace, kv=None, token_rows: bool = False,
+                        stats=None, error_flags=None, stream=None) -> None:
     """Enqueue the page lifecycle between rounds (smcsd_pages_advance). page_table [R,N,P],
     len_before / len_after [R], refcount / free_ids [num_pages], n_free [1], all int32; kv
-    None or a uint8 tensor [num_pages, page_bytes] or [kv_count, num_pages, page_bytes]."""
+    None or a uint8 tensor [num_pages, page_bytes] or [kv_count, num_pages, page_bytes];
+    token_rows: token-major pages, copy only the tail's filled rows."""
     dev = page_table.device
     R, N, P = page_table.shape
     i32 = torch.int32
@@ -437,13 +438,14 @@ def smcsd_pages_advance(*, len_before, len_after, page_table, refcount, free_ids
             raise ValueError("kv holds %d pages, refcount %d" % (kv.shape[-2], num_pages))
         kv_stride = num_pages * page_bytes
     if stats is not None:
-        _check(stats, "stats", i32, (4,), dev)
+        _check(stats, "stats", i32, (5,), dev)
     if error_flags is not None:
         _check(error_flags, "error_flags", i32, None, dev)
     st = _lib.smcsd_pages_advance(R, N, P, int(page_size), _ptr(len_before), _ptr(len_after),
                                   _ptr(page_table), num_pages, _ptr(refcount), _ptr(free_ids),
                                   _ptr(n_free), _ptr(kv), page_bytes, kv_count, kv_stride,
-                                  _ptr(workspace), workspace.numel(), _ptr(stats),
+                                  int(bool(token_rows)), _ptr(workspace), workspace.numel(),
+                                  _ptr(stats),
                                   _ptr(error_flags), _stream(dev, stream))
     if st != OK:
         raise SmcsdError(st, "smcsd_pages_advance")

@@ -232,13 +232,15 @@ def _pages(**kw):
     a = dict(R=2, N=4, P=8, page_size=16, len_before=base, len_after=base + 0x1000,
              page_table=base + 0x2000, num_pages=100, refcount=base + 0x10000,
              free_ids=base + 0x20000, n_free=base + 0x30000, kv=None, page_bytes=0,
-             kv_count=0, kv_stride=0, workspace=base + 0x40000, workspace_bytes=1 << 20,
+             kv_count=0, kv_stride=0, token_rows=0, workspace=base + 0x40000,
+             workspace_bytes=1 << 20,
              stats=None, error_flags=None)
     a.update(kw)
     return S.raw_library().smcsd_pages_advance(
         a["R"], a["N"], a["P"], a["page_size"], a["len_before"], a["len_after"],
         a["page_table"], a["num_pages"], a["refcount"], a["free_ids"], a["n_free"], a["kv"],
-        a["page_bytes"], a["kv_count"], a["kv_stride"], a["workspace"], a["workspace_bytes"],
+        a["page_bytes"], a["kv_count"], a["kv_stride"], a["token_rows"], a["workspace"],
+        a["workspace_bytes"],
         a["stats"], a["error_flags"], None)
 
 
@@ -265,6 +267,8 @@ def _pages(**kw):
     (dict(n_free=0x10040010), S.ERR_ARG),                                # inside the workspace
     (dict(stats=0x10030000), S.ERR_ARG),                                 # overlaps n_free
     (dict(workspace=0x10040010), S.ERR_WORKSPACE),                       # not 256-byte aligned
+    (dict(kv=0x50000000, page_bytes=48, kv_count=1, token_rows=1), S.ERR_ARG),   # 3 B a row
+    (dict(kv=0x50000000, page_bytes=16 * 24, kv_count=1, token_rows=1), S.ERR_ARG),  # 24 B rows
 ])
 def test_pages_validation(kw, status):
     assert _pages(**kw) == status

@@ -39,7 +39,7 @@ def test_driver_step_replays_in_a_graph(tv, dev):
     out["page_table_out"] = torch.empty_like(st["page_table"])
     pws = torch.empty(smcsd.smcsd_pages_workspace_size(w.R, w.N, P, st["refcount"].numel()),
                       dtype=torch.uint8, device=dev)
-    stats = torch.zeros(4, dtype=torch.int32, device=dev)
+    stats = torch.zeros(5, dtype=torch.int32, device=dev)
 
     def step():
         smcsd.run_round(inp, mode=w.mode, ess_frac=w.ess_frac, tv=tv, outputs=out)

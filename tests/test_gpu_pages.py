@@ -33,7 +33,7 @@ def _say(*a):
     sys.stdout.flush()
 
 
-def _gpu_advance(pool, dev, lens=None):
+def _gpu_advance(pool, dev, lens=None, token_rows=False):
     """Copies the pool to the device, runs smcsd_pages_advance, returns host arrays."""
     R, N, P = pool["page_table"].shape
     lb, la = lens if lens is not None else (pool["len_before"], pool["len_after"])
@@ -47,9 +47,9 @@ def _gpu_advance(pool, dev, lens=None):
     ws = torch.empty(max(256, smcsd.smcsd_pages_workspace_size(R, N, P, num_pages)),
                      dtype=torch.uint8, device=dev)
     flags = torch.zeros(1, dtype=torch.int32, device=dev)
-    stats = torch.full((4,), -5, dtype=torch.int32, device=dev)
+    stats = torch.full((5,), -5, dtype=torch.int32, device=dev)
     smcsd.smcsd_pages_advance(page_size=pool["page_size"], workspace=ws, error_flags=flags,
-                              stats=stats, **t)
+                              stats=stats, token_rows=token_rows, **t)
     torch.cuda.synchronize()
     out = {k: (None if v is None else v.cpu().numpy()) for k, v in t.items()}
     out["n_free"] = int(out["n_free"][0])
@@ -58,33 +58,36 @@ def _gpu_advance(pool, dev, lens=None):
     return out
 
 
-def _expected_stats(pool, o, lens=None):
-    """[released, pops served, pages copied, pops unserved] read off the oracle's result."""
+def _expected_stats(pool, o, lens=None, token_rows=False):
+    """[released, pops served, pages copied, pops unserved, token rows copied] read off the
+    oracle's result."""
     lb, la = lens if lens is not None else (pool["len_before"], pool["len_after"])
     lb, la = np.asarray(lb, np.int64), np.asarray(la, np.int64)
     ps = pool["page_size"]
     pt0, pt1 = pool["page_table"].numpy(), o["page_table"]
     released = int((pool["refcount"].numpy() == 0).sum())
     served = pool["n_free"] + released - o["n_free"]
-    copied = unserved = 0
+    copied = unserved = rows = 0
     for r in range(pt0.shape[0]):
         if lb[r] > 0 and lb[r] % ps:
             c = (lb[r] - 1) // ps
             changed = pt1[r, :, c] != pt0[r, :, c]
-            copied += int((changed & (pt1[r, :, c] >= 0)).sum())
+            n = int((changed & (pt1[r, :, c] >= 0)).sum())
+            copied += n
+            rows += n * (int(lb[r] % ps) if token_rows else ps)
             unserved += int((changed & (pt1[r, :, c] < 0)).sum())
         c0, c1 = -(-lb[r] // ps), -(-la[r] // ps)
         unserved += int((pt1[r, :, c0:c1] < 0).sum())
-    return [released, served, copied, unserved]
+    return [released, served, copied, unserved, rows]
 
 
-def _oracle_advance(pool, lens=None):
+def _oracle_advance(pool, lens=None, token_rows=False):
     lb, la = lens if lens is not None else (pool["len_before"], pool["len_after"])
     kv = pool.get("kv")
     return oracle.pages_advance(pool["page_table"].numpy(), pool["refcount"].numpy(),
                                 pool["free_ids"].numpy(), pool["n_free"], np.asarray(lb),
                                 np.asarray(la), pool["page_size"],
-                                None if kv is None else kv.numpy())
+                                None if kv is None else kv.numpy(), token_rows=token_rows)
 
 
 def _compare(g, o, expect_flags=0):
@@ -146,6 +149,34 @@ def test_advance_matches_oracle(case, dev):
     _say("  ok: status", o["status"], "free", pool["n_free"], "->", o["n_free"], "stats", g["stats"])
 
 
+# token-major pages: (R, N, P, page_size, steps, spare, kv_count, page_bytes, seed), rows of
+# page_bytes / page_size = 16, 16, 16 and 32 bytes
+TOKEN_ROW_CASES = [
+    (3, 8, 6, 4, None, 40, 2, 64, 1),
+    (2, 37, 9, 5, None, 300, 1, 80, 7),
+    (6, 24, 10, 4, None, 0, 1, 64, 10),
+    (64, 32, 30, 16, 9, 65536, 2, 512, 14),
+]
+
+
+@pytest.mark.parametrize("case", TOKEN_ROW_CASES,
+                         ids=["R%d-N%d-P%d-ps%d-s%s-sp%d-kv%d" % c[:7] for c in TOKEN_ROW_CASES])
+def test_token_rows_match_oracle(case, dev):
+    R, N, P, ps, steps, spare, kvc, pb, seed = case
+    _say("case", case)
+    pool = synth.make_page_pool(R, N, P, ps, seed, steps=steps, spare=spare, kv_count=kvc,
+                                page_bytes=pb)
+    o = _oracle_advance(pool, token_rows=True)
+    g = _gpu_advance(pool, dev, token_rows=True)
+    _compare(g, o, expect_flags=smcsd.DEVERR_POOL if o["status"] == -3 else 0)
+    assert g["stats"] == _expected_stats(pool, o, token_rows=True)
+    full = _oracle_advance(pool)
+    assert np.array_equal(full["page_table"], o["page_table"])
+    if g["stats"][2] > 0:
+        assert not np.array_equal(full["kv"], o["kv"])      # fewer bytes were copied
+    _say("  ok: stats", g["stats"])
+
+
 def test_free_list_runs_dry(dev):
     # Spare pages cover only part of the pops: the GPU leaves the same entries -1 as the
     # oracle, and flags it.
@@ -205,8 +236,10 @@ def _host(t):
     return t.numpy()
 
 
-@pytest.mark.parametrize("mode,rounds,seed", [("ess", 6, 21), ("always", 4, 22)])
-def test_multi_round_driver(mode, rounds, seed, dev):
+@pytest.mark.parametrize("mode,rounds,seed,token_rows", [("ess", 6, 21, False),
+                                                        ("always", 4, 22, False),
+                                                        ("ess", 5, 23, True)])
+def test_multi_round_driver(mode, rounds, seed, token_rows, dev):
     """Rounds of propose -> weight -> resample (ESS-adaptive) -> remap -> page lifecycle.
     The GPU chain and the oracle chain start from the same seeded state and each carries its
     own log-weights, page table, refcounts, free list and KV bytes; every round compares them."""
@@ -214,7 +247,7 @@ def test_multi_round_driver(mode, rounds, seed, dev):
         name="driver", R=3, N=16, K=3, V=6000, mode=mode, ess_frac=0.5)
     K, ps, P = w.K, 4, 16
     pool = synth.make_page_pool(w.R, w.N, P, ps, seed, steps=rounds * (K + 1), spare=400,
-                                kv_count=2, page_bytes=32, min_len=2)
+                                kv_count=2, page_bytes=64, min_len=2)
     base = synth.make_inputs(w, seed, device=dev, pages=False)
     # GPU state
     g_lw = base["log_weights"].clone()
@@ -242,7 +275,7 @@ def test_multi_round_driver(mode, rounds, seed, dev):
         smcsd.smcsd_pages_advance(len_before=lb.to(dev), len_after=la.to(dev),
                                   page_table=out["page_table_out"], refcount=g_rc,
                                   free_ids=g_free, n_free=g_nfree, page_size=ps, workspace=ws,
-                                  kv=g_kv, error_flags=out["error_flags"])
+                                  kv=g_kv, token_rows=token_rows, error_flags=out["error_flags"])
         torch.cuda.synchronize()
         assert int(out["error_flags"].item()) == 0
 
@@ -264,7 +297,7 @@ def test_multi_round_driver(mode, rounds, seed, dev):
         resampled_rounds += int(ora["resampled"].sum())
 
         adv = oracle.pages_advance(ora["page_table"], ora["refcount"], o_free, o_nfree,
-                                   lb.numpy(), la.numpy(), ps, o_kv)
+                                   lb.numpy(), la.numpy(), ps, o_kv, token_rows=token_rows)
         assert adv["status"] == 0
         g = dict(page_table=out["page_table_out"].cpu().numpy(), refcount=g_rc.cpu().numpy(),
                  free_ids=g_free.cpu().numpy(), n_free=int(g_nfree.item()),
