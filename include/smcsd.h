@@ -65,7 +65,11 @@ typedef enum smcsd_resample_mode {
 #define SMCSD_DEVERR_ANCESTOR 2u  /* ancestor outside [0,N) given to remap; its row is skipped */
 #define SMCSD_DEVERR_PAGE 4u      /* page id >= num_pages; its refcount update is skipped */
 #define SMCSD_DEVERR_REFCOUNT 8u  /* a refcount went below zero (inconsistent input table) */
-#define SMCSD_DEVERR_EXCHANGE 16u /* a TV slice exchange exceeded its time limit (results void) */
+#define SMCSD_DEVERR_EXCHANGE 16u /* a TV slice exchange exceeded its time limit (results void).
+                                     The limit is 4 s; the environment variable
+                                     SMCSD_EXCHANGE_TIMEOUT_TICKS (ticks of the 100 MHz
+                                     constant clock, read at each call) overrides it, e.g. to
+                                     exercise this path */
 #define SMCSD_DEVERR_POOL 32u     /* page free list ran dry (or its count was out of range): the
                                      entries it could not fill are left -1 */
 #define SMCSD_DEVERR_LENGTH 64u   /* a request's lengths are not 0 <= before <= after <=

@@ -6,6 +6,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <cstdlib>
 #include <cstdint>
 #include <cstring>
 
@@ -16,6 +17,16 @@
 namespace smcsd {
 
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
+
+uint32_t exchange_timeout_ticks() {
+    const char* v = std::getenv("SMCSD_EXCHANGE_TIMEOUT_TICKS");
+    if (v && *v) {
+        char* end = nullptr;
+        const unsigned long long t = std::strtoull(v, &end, 10);
+        if (end && *end == '\0') return (uint32_t)std::min<unsigned long long>(t, UINT32_MAX);
+    }
+    return 400000000u;
+}
 
 bool make_plan(int32_t R, int32_t N, int32_t K, int32_t V, int64_t ld, int32_t dtype, bool tv,
                Plan* p) {
@@ -163,8 +174,8 @@ static hipError_t launch_logits_pass(const Plan& plan, const LogitsArgs& la, hip
 // bracketed by the optional timing events.
 static hipError_t run_tv_pass(const Plan& plan, const LogitsArgs& la, char* ws,
                               smcsd_event begin, smcsd_event end, hipStream_t s) {
-    hipError_t e = launch_fill_words(reinterpret_cast<uint32_t*>(ws + plan.off_ctrl),
-                                     (int64_t)sizeof(Ctrl) / 4, 0u, s);
+    hipError_t e = launch_fill_ctrl(reinterpret_cast<Ctrl*>(ws + plan.off_ctrl),
+                                    exchange_timeout_ticks(), s);
     if (e == hipSuccess)
         e = launch_fill_words(reinterpret_cast<uint32_t*>(la.pp),
                               (int64_t)(plan.pair_wgs * sizeof(PairPart) / 4), ~0u, s);
@@ -254,10 +265,10 @@ smcsd_status smcsd_round(const smcsd_round_args* args, smcsd_stream stream) {
 
     hipError_t e = hipSuccess;
     if (plan.tv) {
-        // the abort flag starts at 0 and every exchange word at the all-ones "empty" pattern
-        // (fill kernels, not memset nodes, so the sequence can be captured in a graph)
-        e = launch_fill_words(reinterpret_cast<uint32_t*>(ws + plan.off_ctrl),
-                              (int64_t)sizeof(Ctrl) / 4, 0u, s);
+        // the control word starts with abort 0 and the wait limit, every exchange word at the
+        // all-ones "empty" pattern (fill kernels, not memset nodes, so the sequence can be
+        // captured in a graph)
+        e = launch_fill_ctrl(reinterpret_cast<Ctrl*>(ws + plan.off_ctrl), exchange_timeout_ticks(), s);
         if (e == hipSuccess)
             e = launch_fill_words(reinterpret_cast<uint32_t*>(la.pp),
                                   (int64_t)(plan.pair_wgs * sizeof(PairPart) / 4), ~0u, s);

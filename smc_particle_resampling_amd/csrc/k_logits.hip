@@ -44,8 +44,6 @@ namespace smcsd {
 namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
-// 4e8 ticks of the 100 MHz constant clock: 4 s, ~10^4 times the longest expected wait.
-constexpr uint64_t kExchangeTimeoutTicks = 400000000ull;
 
 template <int DT>
 struct Elem {
@@ -285,11 +283,14 @@ __device__ bool poll_slices(const uint64_t* words, int nwords, Ctrl* ctrl, int32
     const uint64_t v1 = lane + 64 < nwords
                             ? __hip_atomic_load(words + lane + 64, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
                             : 0ull;
-    const uint32_t abort = __hip_atomic_load(&ctrl->abort, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    bool done = !__any(v0 == kEmpty || v1 == kEmpty) || abort != 0;
-    if (!done && wall_clock64() - t0 > kExchangeTimeoutTicks) {
+    // the control word: abort flag (low half) and wait limit (high half)
+    uint64_t* cw = reinterpret_cast<uint64_t*>(ctrl);
+    const uint64_t c = __hip_atomic_load(cw, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    bool done = !__any(v0 == kEmpty || v1 == kEmpty) || (uint32_t)c != 0;
+    if (!done && wall_clock64() - t0 > (c >> 32)) {
         if (lane == 0) {
-            __hip_atomic_store(&ctrl->abort, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(cw, (c & 0xFFFFFFFF00000000ull) | 1ull, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
             flag_error(error_flags, SMCSD_DEVERR_EXCHANGE);
         }
         done = true;
@@ -572,6 +573,15 @@ __global__ void k_fill_words(uint32_t* p, int64_t n, uint32_t value) {
 }
 
 }  // namespace
+
+__global__ void k_fill_ctrl(Ctrl* ctrl, uint32_t timeout) {
+    if (threadIdx.x == 0) *ctrl = Ctrl{0u, timeout};
+}
+
+hipError_t launch_fill_ctrl(Ctrl* ctrl, uint32_t timeout, hipStream_t s) {
+    k_fill_ctrl<<<dim3(1), dim3(64), 0, s>>>(ctrl, timeout);
+    return hipGetLastError();
+}
 
 hipError_t launch_fill_words(uint32_t* p, int64_t n, uint32_t value, hipStream_t s) {
     if (n <= 0) return hipSuccess;

@@ -38,8 +38,8 @@ struct Plan {
 
 // Control block at the start of the workspace (zeroed before each TV launch).
 struct Ctrl {
-    uint32_t abort;   // set when a slice exchange timed out; later waits return at once
-    uint32_t pad;
+    uint32_t abort;     // set when a slice exchange timed out; later waits return at once
+    uint32_t timeout;   // the wait limit, in ticks of the 100 MHz constant clock
 };
 
 // Per (row pair, slice): max and sum of exp2((z - max) * log2e/T) of target and draft.
@@ -73,6 +73,10 @@ struct LogitsArgs {
     int32_t N, K, V;
     int32_t chunks, S, cps;
 };
+
+// The TV exchange wait limit: 4e8 ticks (4 s, ~10^4 times the longest expected wait), or
+// the value of SMCSD_EXCHANGE_TIMEOUT_TICKS, which lets a test drive the abort path.
+uint32_t exchange_timeout_ticks();
 
 struct FinalizeArgs {
     // from the logits pass (nullptr when log_w_incr is an input)
@@ -215,6 +219,8 @@ struct RemapArgs {
 
 // Host launchers (defined next to their kernels). Return hipSuccess or the launch error.
 hipError_t launch_fill_words(uint32_t* p, int64_t n, uint32_t value, hipStream_t s);
+// Ctrl of a TV pass: abort 0 and the wait limit (one small kernel, graph-capturable).
+hipError_t launch_fill_ctrl(Ctrl* ctrl, uint32_t timeout, hipStream_t s);
 hipError_t launch_logits(const Plan& plan, const LogitsArgs& a, hipStream_t s);
 hipError_t launch_finalize(int32_t R, bool from_partials, int32_t dtype, const FinalizeArgs& a,
                            hipStream_t s);

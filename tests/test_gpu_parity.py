@@ -284,3 +284,35 @@ def test_out_of_range_token_is_flagged(dev):
     torch.cuda.synchronize()
     assert int(out["error_flags"].item()) & smcsd.DEVERR_TOKEN
     assert torch.isfinite(out["log_w_incr"]).all()
+
+
+# ---------------------------------------------------------------- failure handling
+def test_exchange_time_limit_aborts_and_drains(dev, monkeypatch):
+    """A wait limit of 0 ticks, set from the host, makes every exchange that is not complete
+    at its first poll time out. The workgroup that times out raises the abort flag and
+    SMCSD_DEVERR_EXCHANGE, every later wait returns at once, and the kernel drains. The next
+    call, with the normal limit, is correct again on the same workspace."""
+    w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="abort", R=2, N=8, K=4, ctx=256)
+    inp = synth.make_inputs(w, 4, device=dev)
+    out = smcsd.alloc_outputs(w.R, w.N, w.K, dev, tv=True, V=w.V)
+    monkeypatch.setenv("SMCSD_EXCHANGE_TIMEOUT_TICKS", "0")
+    _say("case abort: time limit 0")
+    smcsd.run_round({k: (v.clone() if torch.is_tensor(v) else v) for k, v in inp.items()},
+                    mode=w.mode, tv=True, outputs=out)
+    torch.cuda.synchronize()
+    flags = int(out["error_flags"].item())
+    assert flags & smcsd.DEVERR_EXCHANGE, flags
+    monkeypatch.delenv("SMCSD_EXCHANGE_TIMEOUT_TICKS")
+    out["error_flags"].zero_()
+    out["page_table_out"] = torch.empty_like(inp["page_table"])
+    _say("case abort: normal limit on the same workspace")
+    host = synth.to_host(inp)
+    rc_before = inp["refcount"].cpu().numpy().copy()
+    smcsd.run_round(inp, mode=w.mode, tv=True, outputs=out)
+    torch.cuda.synchronize()
+    assert int(out["error_flags"].item()) == 0
+    gpu = parity.to_numpy(out)
+    gpu["log_weights"] = inp["log_weights"].cpu().numpy()
+    ora = oracle.round(host, V=w.V, mode=w.mode, tv=True)
+    parity.check_round(host, ora, gpu, N=w.N, mode=w.mode, tv=True, rc_before=rc_before,
+                       rc_after=inp["refcount"].cpu().numpy())
