@@ -144,14 +144,14 @@ static smcsd_status check_verify(const smcsd_verify_args* a, Plan* plan) {
 static_assert(kTvCPL == kTopkCPL, "bonus slices of the TV plan are Gumbel-Top-K slices");
 
 static hipError_t launch_logits_pass(const Plan& plan, const LogitsArgs& la, hipStream_t s) {
-    if (!plan.tv || plan.bonus_rows == 0) return launch_logits(plan, la, s);
+    if (!plan.tv) return launch_logits(plan, la, s);
     Plan pairs = plan;
     pairs.bonus_rows = 0;
     pairs.total_wgs = plan.pair_wgs;
     LogitsArgs lp = la;
     lp.total_wgs = la.pair_wgs;
     hipError_t e = launch_logits(pairs, lp, s);
-    if (e != hipSuccess) return e;
+    if (e != hipSuccess || plan.bonus_rows == 0) return e;
     TopkArgs t{};
     t.logits = la.target;
     t.temperature = la.temperature;

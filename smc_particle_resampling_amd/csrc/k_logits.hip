@@ -5,8 +5,10 @@
 // vocabulary. It produces their temperature log-softmax normalisers, which the importance
 // weights of "Faster LLM Inference via Sequential Monte Carlo" (section 2) need, and, when
 // asked, the total-variation distance between the two distributions (the block-divergence
-// signal of the METASD page, section 2). For every particle it also reduces the bonus row
-// with its precomputed Gumbel noise to the Gumbel-max token (STAND page, method item 2).
+// signal of the METASD page, section 2). It can also reduce every particle's bonus row with
+// its precomputed Gumbel noise to the Gumbel-max token (STAND page, method item 2): the round
+// does so here without TV, and with TV hands those rows to the Gumbel-Top-K slice kernel
+// (k = 1), which ran them faster than this grid's tail.
 //
 // Work decomposition. A row is cut into 16-byte chunks and the chunks into S slices. One
 // 512-thread workgroup (8 wave64) handles one slice of one row pair (target row k, draft row
