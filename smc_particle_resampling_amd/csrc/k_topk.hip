@@ -94,26 +94,31 @@ __device__ __forceinline__ int lane_best_pos(const float (&key)[n], float& bk) {
     return m == -INFINITY ? -1 : pos;
 }
 
-template <int DT>
-__global__ __launch_bounds__(kThreads) void k_topk_slice(TopkArgs a) {
+// MODE is TopkArgs::row_mode as a template parameter, so the plain kernel carries none of the
+// row-map arithmetic. 8 waves per SIMD (4 workgroups per CU) are asked for explicitly: the
+// row map had raised the SGPR count enough to cost one, and the pass 10%.
+template <int DT, int MODE>
+__global__ __launch_bounds__(kThreads, 8) void k_topk_slice(TopkArgs a) {
     constexpr int EPC = DT == SMCSD_F32 ? 4 : 8;
     constexpr size_t ESZ = DT == SMCSD_F32 ? 4 : 2;
     constexpr int n = kTopkCPL * EPC;
     __shared__ float lk[2 * kWaves];
     __shared__ int32_t li[2 * kWaves];
-    const int64_t row = blockIdx.x / (unsigned)a.S;
+    const uint32_t row32 = blockIdx.x / (unsigned)a.S;   // rows * S < 2^31
+    const int64_t row = row32;
     const int s = (int)(blockIdx.x % (unsigned)a.S);
     const int tid = threadIdx.x;
     int64_t lrow = row, trow = row;
-    if (a.row_mode != kTopkRows) {
-        trow = row / a.N;
-        int64_t src = row;
-        if (a.row_mode == kTopkResampled) {
+    if constexpr (MODE != kTopkRows) {
+        const uint32_t r = row32 / (uint32_t)a.N;         // the request
+        uint32_t src = row32;                              // its particle row
+        if constexpr (MODE == kTopkResampled) {
             const int32_t x = a.ancestors[row];
             if (x < 0 || x >= a.N) return;   // the merge writes -1 for this row
-            src = trow * a.N + x;
+            src = r * (uint32_t)a.N + (uint32_t)x;
         }
-        lrow = src * (a.K + 1) + a.K;
+        trow = r;
+        lrow = (int64_t)src * (a.K + 1) + a.K;
     }
     const char* zrow = static_cast<const char*>(a.logits) + (size_t)(lrow * a.ld) * ESZ;
     const float* grow = a.gumbel + (size_t)row * a.ld;
@@ -165,6 +170,7 @@ __global__ __launch_bounds__(kThreads) void k_topk_slice(TopkArgs a) {
     }
 }
 
+template <int MODE>
 __global__ __launch_bounds__(kThreads) void k_topk_merge(TopkArgs a) {
     constexpr int n = kMaxTopk * kMaxTopkSlices / kThreads;   // 8 candidates a lane at most
     __shared__ float lk[2 * kWaves];
@@ -172,7 +178,7 @@ __global__ __launch_bounds__(kThreads) void k_topk_merge(TopkArgs a) {
     __shared__ BonusPart res[kMaxTopk];
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x;
-    if (a.row_mode == kTopkResampled) {
+    if constexpr (MODE == kTopkResampled) {
         const int32_t x = a.ancestors[row];
         if (x < 0 || x >= a.N) {
             if (tid == 0) {
@@ -208,19 +214,25 @@ hipError_t launch_topk(int64_t rows, int32_t dtype, const TopkArgs& a, hipStream
     if (rows <= 0) return hipSuccess;
     const dim3 block(kThreads);
     const dim3 g1((unsigned)(rows * a.S));
-    if (dtype == SMCSD_BF16) k_topk_slice<SMCSD_BF16><<<g1, block, 0, s>>>(a);
-    else k_topk_slice<SMCSD_F32><<<g1, block, 0, s>>>(a);
+    if (a.row_mode == kTopkResampled) {
+        if (dtype == SMCSD_BF16) k_topk_slice<SMCSD_BF16, kTopkResampled><<<g1, block, 0, s>>>(a);
+        else k_topk_slice<SMCSD_F32, kTopkResampled><<<g1, block, 0, s>>>(a);
+    } else {
+        if (dtype == SMCSD_BF16) k_topk_slice<SMCSD_BF16, kTopkRows><<<g1, block, 0, s>>>(a);
+        else k_topk_slice<SMCSD_F32, kTopkRows><<<g1, block, 0, s>>>(a);
+    }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    k_topk_merge<<<dim3((unsigned)rows), block, 0, s>>>(a);
+    if (a.row_mode == kTopkResampled) k_topk_merge<kTopkResampled><<<dim3((unsigned)rows), block, 0, s>>>(a);
+    else k_topk_merge<kTopkRows><<<dim3((unsigned)rows), block, 0, s>>>(a);
     return hipGetLastError();
 }
 
 hipError_t launch_topk_slices(int64_t rows, int32_t dtype, const TopkArgs& a, hipStream_t s) {
     if (rows <= 0) return hipSuccess;
     const dim3 block(kThreads), grid((unsigned)(rows * a.S));
-    if (dtype == SMCSD_BF16) k_topk_slice<SMCSD_BF16><<<grid, block, 0, s>>>(a);
-    else k_topk_slice<SMCSD_F32><<<grid, block, 0, s>>>(a);
+    if (dtype == SMCSD_BF16) k_topk_slice<SMCSD_BF16, kTopkBonusRows><<<grid, block, 0, s>>>(a);
+    else k_topk_slice<SMCSD_F32, kTopkBonusRows><<<grid, block, 0, s>>>(a);
     return hipGetLastError();
 }
 
