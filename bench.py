@@ -109,6 +109,18 @@ def stored_traffic(workload: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (for the CPU baseline's record), or "unknown"."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline_driver(w, pool_args, target_s=12.0, sample_requests=2):
     """The oracle's round plus its page lifecycle on a bounded sample: the first requests of
     the workload with a page pool of the same geometry (KV tensors zero-filled), each pass
@@ -136,7 +148,7 @@ def cpu_baseline_driver(w, pool_args, target_s=12.0, sample_requests=2):
         times.append(time.perf_counter() - t)
     per_request = sum(times) / (len(times) * rs)
     return {"value": 1.0 / (w.R * per_request), "unit": "driver steps/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
+            "cores": oracle.num_threads(), "kind": "oracle", "cpu": cpu_model(),
             "sample": "%d of %d requests (N=%d, K=%d, V=%d, TV %s, %s resampling) with a pool of "
                       "%d pages x %d KV tensors x %d B: fp64 oracle round then the oracle's "
                       "page lifecycle (its KV copies included), repeated %d times (%.1f s in "
@@ -179,7 +191,7 @@ def cpu_baseline(w, target_s=12.0, sample_requests=4, path="round", k=8):
     what = {"round": "round", "sd_verify": "SD verification",
             "gumbel_topk": "Gumbel-Top-K (k=%d) of every particle row" % k}[path]
     return {"value": 1.0 / (w.R * per_request), "unit": unit, "cores": oracle.num_threads(),
-            "kind": "oracle",
+            "kind": "oracle", "cpu": cpu_model(),
             "sample": "%d of %d requests (N=%d, K=%d, V=%d, TV %s), fp64 oracle %s over them "
                       "repeated %d times (%.1f s in all), %.4f s per request; %s = "
                       "1/(%d * that)" % (rs, w.R, w.N, w.K, w.V, "on" if w.tv else "off", what,
