@@ -10,6 +10,7 @@
 // U_j == C_i therefore resolves the same way on every run. When the round carries a page
 // table, the same workgroup then remaps its request's table rows through the ancestors
 // (pointer exchange, as k_remap does), which saves the round a launch.
+#include "remap_rows.h"
 #include "smcsd_internal.h"
 
 namespace smcsd {
@@ -156,30 +157,12 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
         }
     }
 
-    // Page-table remap: pt_out[j] = pt_in[anc_j]; every valid entry of old row i with
-    // o_i != 1 moves its page's refcount by o_i - 1 (integer atomics commute, so the result
-    // does not depend on the order).
+    // the request's page-table remap, when the round carries a small table
     if (a.pt_in) {
         __syncthreads();
-        const int32_t P = a.P;
-        const int64_t NP = (int64_t)N * P;
-        const int32_t* in = a.pt_in + r * NP;
-        int32_t* out = a.pt_out + r * NP;
-        for (int64_t e = tid; e < NP; e += kThreads) {
-            const int32_t j = (int32_t)(e / P);
-            const int32_t col = (int32_t)(e - (int64_t)j * P);
-            out[e] = in[(int64_t)s_anc[j] * P + col];
-            const int32_t page = in[e];
-            const int32_t o = s_off[j];
-            if (page >= 0 && o != 1) {
-                if (page >= a.num_pages) {
-                    flag_error(a.error_flags, SMCSD_DEVERR_PAGE);
-                } else {
-                    const int32_t old = atomicAdd(&a.refcount[page], o - 1);
-                    if (old + (o - 1) < 0) flag_error(a.error_flags, SMCSD_DEVERR_REFCOUNT);
-                }
-            }
-        }
+        const int64_t NP = (int64_t)N * a.P;
+        remap_rows(a.pt_in + r * NP, a.pt_out + r * NP, s_anc, s_off, a.P, 0, NP, a.refcount,
+                   a.num_pages, a.error_flags);
     }
 }
 

@@ -9,6 +9,7 @@
 //   old row i with o_i != 1.
 // Rows with o_i == 1 (kept once) cost one copy and no atomic. Integer atomics commute, so
 // the resulting refcounts do not depend on scheduling.
+#include "remap_rows.h"
 #include "smcsd_internal.h"
 
 namespace smcsd {
@@ -37,24 +38,8 @@ __global__ __launch_bounds__(kThreads) void k_remap(RemapArgs a) {
     const int64_t per = (NP + a.blocks_per_request - 1) / a.blocks_per_request;
     const int64_t e0 = (int64_t)part * per;
     const int64_t e1 = min(NP, e0 + per);
-    const int32_t* in = a.pt_in + r * NP;
-    int32_t* out = a.pt_out + r * NP;
-    for (int64_t e = e0 + tid; e < e1; e += kThreads) {
-        const int32_t j = (int32_t)(e / P);
-        const int32_t col = (int32_t)(e - (int64_t)j * P);
-        const int32_t src = s_anc[j];
-        out[e] = src >= 0 ? in[(int64_t)src * P + col] : -1;
-        const int32_t page = in[e];            // old row j, column col
-        const int32_t o = s_off[j];
-        if (page >= 0 && o != 1) {
-            if (page >= a.num_pages) {
-                flag_error(a.error_flags, SMCSD_DEVERR_PAGE);
-            } else {
-                const int32_t old = atomicAdd(&a.refcount[page], o - 1);
-                if (old + (o - 1) < 0) flag_error(a.error_flags, SMCSD_DEVERR_REFCOUNT);
-            }
-        }
-    }
+    remap_rows(a.pt_in + r * NP, a.pt_out + r * NP, s_anc, s_off, P, e0, e1, a.refcount,
+               a.num_pages, a.error_flags);
 }
 
 }  // namespace
