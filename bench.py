@@ -222,6 +222,9 @@ def main():
                     help="round / driver: draw the bonus inside the logits pass per original "
                          "particle (pass), or after resampling per new slot with fresh noise "
                          "(after: smcsd_round without noise, then smcsd_bonus_resampled)")
+    ap.add_argument("--vocab-shards", type=int, default=1,
+                    help="round: run one GPU's share of a vocabulary-sharded target, V/G "
+                         "columns per row (the cross-GPU combine of the partials is not built)")
     ap.add_argument("--kv-tensors", type=int, default=64,
                     help="driver: KV tensors sharing the page ids (32 layers x K and V)")
     ap.add_argument("--kv-token-rows", action="store_true",
@@ -246,6 +249,10 @@ def main():
 
     name = args.workload or synth.HEADLINE
     w = synth.WORKLOADS[name]
+    if args.vocab_shards > 1:
+        share = -(-w.V // args.vocab_shards)
+        share = -(-share // 8) * 8            # whole 16-byte rows
+        w = w.scaled(V=share, name="%s-vshard1of%d" % (name, args.vocab_shards))
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     print("# building inputs for %s" % name, file=sys.stderr, flush=True)
@@ -426,6 +433,8 @@ def main():
         table_bytes = 0
     else:
         metric = "SMC-SD rounds/s and achieved HBM GB/s (% of peak), N=32 K=8 V=128256 bf16"
+        if args.vocab_shards > 1:
+            metric += ", one GPU's vocabulary shard (1/%d, V=%d)" % (args.vocab_shards, w.V)
         unit = "rounds/s"
         table_bytes = alg["table"]
     line = {
@@ -451,11 +460,15 @@ def main():
                                  "copy": "filled token rows" if args.kv_token_rows else "whole pages"}
                                 if driver else None),
                    "topk": args.topk if topk else None,
+                   "vocab_shard": ("1/%d: V = %d of %d" % (args.vocab_shards, w.V,
+                                                          synth.WORKLOADS[name].V)
+                                   if args.vocab_shards > 1 else None),
                    "bonus": (args.bonus if args.path in ("round", "driver") else None),
                    "round_GBps": (logits_bytes + table_bytes) / (ms_per_step * 1e-3) / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": None if (topk or after) else stored_traffic(name),
+                     "traffic": (None if (topk or after or args.vocab_shards > 1)
+                                 else stored_traffic(name)),
                      "kernel": ("k_topk_slice+k_topk_merge" if topk else
                                 "k_logits_tv" if after and w.tv else
                                 "k_logits_tv+k_topk_slice (bonus rows)" if w.tv else
