@@ -448,9 +448,12 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": w.dtype,
+        # the arithmetic: logits widened exactly to f32, exponentials and sums in f32, the
+        # per-request weights in f64; the logits themselves are stored as config.logits_dtype
+        "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": name, "path": args.path, "R": w.R, "N": w.N, "K": w.K, "V": w.V,
+                   "logits_dtype": w.dtype,
                    "tv": (w.tv or verify) and not topk,
                    "resample": w.mode if args.path in ("round", "driver") else None,
                    "pages_per_particle": (w.P if args.path == "round" else
