@@ -101,7 +101,7 @@ def test_log_potential(mode, tv, dev):
         assert all(not (set(gpu["ancestors"][r].tolist()) & dead[r]) for r in range(w.R))
 
 
-@pytest.mark.parametrize("N,K", [(1, 1), (1, 4), (3, 1), (1024, 2), (40, 17)])
+@pytest.mark.parametrize("N,K", [(1, 1), (1, 4), (3, 1), (1024, 2), (40, 17), (2, 256)])
 def test_particle_and_position_extremes(N, K, dev):
     w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="extreme", R=2, N=N, K=K, V=3000, ctx=64)
     run_and_compare(w, dev, seed=3)

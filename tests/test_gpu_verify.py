@@ -107,7 +107,7 @@ def test_verify_ragged_vocabularies(V, dtype, dev):
     run_and_compare(w, dev, seed=6, max_excluded=0.2 if V < 16 else 0.05)
 
 
-@pytest.mark.parametrize("N,K", [(1, 1), (3, 1), (1024, 2), (40, 17)])
+@pytest.mark.parametrize("N,K", [(1, 1), (3, 1), (1024, 2), (40, 17), (2, 256)])
 def test_verify_particle_and_position_extremes(N, K, dev):
     w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="verify-extreme", R=2, N=N, K=K, V=3000,
                                                 ctx=64)
