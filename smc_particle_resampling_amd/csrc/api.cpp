@@ -176,9 +176,7 @@ static hipError_t run_tv_pass(const Plan& plan, const LogitsArgs& la, char* ws,
                               smcsd_event begin, smcsd_event end, hipStream_t s) {
     hipError_t e = launch_fill_ctrl(reinterpret_cast<Ctrl*>(ws + plan.off_ctrl),
                                     exchange_timeout_ticks(), s);
-    if (e == hipSuccess)
-        e = launch_fill_words(reinterpret_cast<uint32_t*>(la.pp),
-                              (int64_t)(plan.pair_wgs * sizeof(PairPart) / 4), ~0u, s);
+    if (e == hipSuccess) e = launch_tv_fill(plan, la, s);
     if (e != hipSuccess) return e;
     if (begin && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(begin), s)) != hipSuccess) return e;
     if ((e = launch_logits_pass(plan, la, s)) != hipSuccess) return e;
@@ -269,9 +267,7 @@ smcsd_status smcsd_round(const smcsd_round_args* args, smcsd_stream stream) {
         // all-ones "empty" pattern (fill kernels, not memset nodes, so the sequence can be
         // captured in a graph)
         e = launch_fill_ctrl(reinterpret_cast<Ctrl*>(ws + plan.off_ctrl), exchange_timeout_ticks(), s);
-        if (e == hipSuccess)
-            e = launch_fill_words(reinterpret_cast<uint32_t*>(la.pp),
-                                  (int64_t)(plan.pair_wgs * sizeof(PairPart) / 4), ~0u, s);
+        if (e == hipSuccess) e = launch_tv_fill(plan, la, s);
         if (e != hipSuccess) return SMCSD_ERR_DEVICE;
     }
     if (a.timing_begin && hipEventRecord(reinterpret_cast<hipEvent_t>(a.timing_begin), s) != hipSuccess)

@@ -16,13 +16,15 @@
 // rows with 16-byte non-temporal buffer loads. Chunks outside the slice and elements >= V
 // become -inf, which adds nothing to any max, sum, TV or argmax, so the arithmetic has no
 // per-element branch.
-//   phase 1: slice max m of z, then e = exp2((z - m) * log2e/T) and its sum, for p and q;
+//   phase 1: the maximum m of z over a share of the slice, then e = exp2((z - m) * log2e/T)
+//            and its sum, for p and q. TV off: the share is the slice (one workgroup max).
+//            TV on: each wave's own share, so nothing waits between loads and exponentials.
 //   phase 2 (TV only): the S workgroups of the row pair swap their (m, sum) partials and
 //            combine them in one fixed order into the row's maxima M and sums S. With
-//            f = exp2((m - M) * log2e/T) the slice's |p - q| terms are
-//            (f_p / S_p) |e_p - rho e_q|, rho = (f_q S_p) / (f_p S_q). The slice keeps
-//            its e values in fp32 registers from phase 1, so phase 2 costs one fma and one
-//            add per element and no exponential. rho is exactly 1 when the two rows are
+//            f = exp2((m - M) * log2e/T) (m of the wave that computed the e values) the
+//            |p - q| terms are (f_p / S_p) |e_p - rho e_q|, rho = (f_q S_p) / (f_p S_q).
+//            The e values stay in fp32 registers from phase 1, so phase 2 costs one fma and
+//            one add per element and no exponential. rho is exactly 1 when the two rows are
 //            equal, and then TV is exactly 0.
 // The finalize kernel combines slices (normalisers, weights, TV, argmax) in fixed order, so
 // every result is deterministic.
@@ -30,11 +32,12 @@
 // Launch shapes. Without TV, every (row, slice) is an independent workgroup of an ordinary
 // grid (8 chunks a lane). With TV, the S workgroups of a row pair must be resident together
 // to swap partials, so the pass runs as a persistent cooperative grid
-// (hipLaunchCooperativeKernel guarantees co-residency). It has C clusters of S consecutive
-// workgroups, and each cluster walks the row pairs c, c+C, c+2C, ... in lockstep, then its
-// share of the bonus rows (4 chunks a lane, so the fp32 e values fit in registers). The
-// loads of a cluster's next row pair are issued while the current one is exchanged and
-// finished. A wall-clock limit bounds every wait. A workgroup that times out raises
+// (hipLaunchCooperativeKernel guarantees co-residency) over the row pairs only. It has C
+// clusters of S consecutive workgroups (4 chunks a lane, so the fp32 e values fit in
+// registers), and each cluster walks the row pairs c, c+C, c+2C, ... in lockstep. The loads
+// of a cluster's next row pair are issued while the current one is exchanged and finished.
+// The round's bonus rows then run as an ordinary grid of the Gumbel-Top-K slice kernel.
+// A wall-clock limit bounds every wait. A workgroup that times out raises
 // SMCSD_DEVERR_EXCHANGE and an abort flag, every later wait returns at once, and the kernel
 // always drains.
 #include <algorithm>
@@ -167,25 +170,6 @@ __device__ __forceinline__ float slice_sumexp(const u32x4 (&R)[CPL], float c, fl
         for (int e = 0; e < Elem<DT>::EPC; e += 2) {
             s0 += __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(R[j], e), c, nmc));
             s1 += __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(R[j], e + 1), c, nmc));
-        }
-    }
-    return s0 + s1;
-}
-
-// Same sum, keeping every term: E[j * EPC + e] = exp2(z * c - m * c).
-template <int DT, int CPL>
-__device__ __forceinline__ float slice_exp(const u32x4 (&R)[CPL], float c, float nmc,
-                                           float (&E)[CPL * Elem<DT>::EPC]) {
-    constexpr int EPC = Elem<DT>::EPC;
-    float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-#pragma unroll
-        for (int e = 0; e < EPC; e += 2) {
-            E[j * EPC + e] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(R[j], e), c, nmc));
-            E[j * EPC + e + 1] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(R[j], e + 1), c, nmc));
-            s0 += E[j * EPC + e];
-            s1 += E[j * EPC + e + 1];
         }
     }
     return s0 + s1;
@@ -422,74 +406,159 @@ __device__ void bonus_slice(const LogitsArgs& a, int64_t b, int s, float* red, i
     bonus_finish(a, b, s, best, besti, red, redi);
 }
 
-// LDS of the TV pass. Each step of a row pair has its own buffer, so one barrier per step
-// suffices: a buffer is rewritten only after every wave has passed a later barrier.
+// Wave-wide integer max / min by DPP row steps, then the four row results.
+__device__ __forceinline__ int32_t wave_max_i32(int32_t v) {
+    v = max(v, dpp_i32<kDppXor1>(v));
+    v = max(v, dpp_i32<kDppXor2>(v));
+    v = max(v, dpp_i32<kDppRowHalfMirror>(v));
+    v = max(v, dpp_i32<kDppRowMirror>(v));
+    return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+__device__ __forceinline__ int32_t wave_min_i32(int32_t v) {
+    v = min(v, dpp_i32<kDppXor1>(v));
+    v = min(v, dpp_i32<kDppXor2>(v));
+    v = min(v, dpp_i32<kDppRowHalfMirror>(v));
+    v = min(v, dpp_i32<kDppRowMirror>(v));
+    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
+               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
+}
+
+// Maximum of this wave's share of a slice (wave-uniform). bf16: the packed int16 max alone
+// decides whenever the wave holds a non-negative value (those order like their int16 bits
+// and beat every negative); only a wave whose share is entirely negative takes the int16
+// min as well (negative values order in reverse). -inf padding (int16 -128) never wins
+// either way while a finite value is present.
+template <int DT, int CPL>
+__device__ __forceinline__ float wave_share_max(const u32x4 (&R)[CPL]) {
+    if constexpr (DT == SMCSD_F32) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+            for (int w = 0; w < 4; w += 2)
+                m = fmaxf(m, fmaxf(__uint_as_float(R[j][w]), __uint_as_float(R[j][w + 1])));
+        return wave_max(m);
+    } else {
+        i16x2 mx = {(short)-32768, (short)-32768};
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t word = R[j][w];
+                mx = __builtin_elementwise_max(mx, __builtin_bit_cast(i16x2, word));
+            }
+        const int32_t hi = wave_max_i32(mx[0] > mx[1] ? mx[0] : mx[1]);
+        if (hi >= 0) return __uint_as_float((uint32_t)hi << 16);
+        i16x2 mn = {(short)32767, (short)32767};
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+#pragma unroll
+            for (int w = 0; w < 4; ++w) {
+                const uint32_t word = R[j][w];
+                mn = __builtin_elementwise_min(mn, __builtin_bit_cast(i16x2, word));
+            }
+        const int32_t lo = wave_min_i32(mn[0] < mn[1] ? mn[0] : mn[1]);
+        return __uint_as_float(((uint32_t)lo & 0xFFFFu) << 16);
+    }
+}
+
+// LDS of the TV pass: the wave partials (max p, sum p, max q, sum q) of the current row pair
+// and its exchange words. Reuse by the next row pair needs no third barrier: wave 0 reads
+// wpart before the exchange barrier, and the next row pair rewrites it only after that
+// barrier; wave 0 rewrites xch only after the next row pair's first barrier, which every
+// wave reaches after its last read of xch.
 struct TvLds {
-    float max2[2 * kWaves];          // slice maxima of p and q
-    float sum2[2 * kWaves];          // slice sums of p and q
-    uint64_t xch[2 * kMaxTvSlices];  // the row pair's exchange words
+    float4 wpart[kWaves];
+    uint64_t xch[2 * kMaxTvSlices];
 };
 
 // TV on: partials, exchange, and this slice's share of sum |p - q|, one partial per wave.
-// P and Q hold this slice's loads, issued one row pair earlier. Once they are turned into
-// exponentials, the loads of row pair `next` (if >= 0) go into P and Q, so they are in flight
-// during the exchange and phase 2. Three barriers per row pair: slice max, slice sum,
-// exchange words in LDS. LDS reuse by the next row pair is safe without a fourth: each buffer
-// is rewritten only after every wave has passed the barrier that follows its last read.
+// Each wave shifts its exponentials by the maximum of its own share of the slice, so nothing
+// waits between the loads and the exponentials; wave 0 combines the eight wave partials into
+// the slice partial it publishes, and in phase 2 each wave scales its terms by its own
+// f = exp2((m_wave - M_row) c). P and Q hold this slice's loads, issued one row pair earlier;
+// once they are exponentials, the loads of row pair `next` (if >= 0) go into them, in flight
+// during the exchange and phase 2. Two barriers per row pair: wave partials, exchange words.
+
 template <int DT>
-__device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, int64_t next,
-                              u32x4 (&P)[kTvCPL], u32x4 (&Q)[kTvCPL], TvLds& sh) {
+__device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, int64_t next, bool ragged,
+                              int c0, int c1, u32x4 (&P)[kTvCPL], u32x4 (&Q)[kTvCPL], TvLds& sh,
+                              int64_t& r_c, float& c_r) {
     constexpr int NE = kTvCPL * Elem<DT>::EPC;
+    constexpr int EPC = Elem<DT>::EPC;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
-    const PairLoc L = pair_location<DT>(a, u, s);
-    const float c = kLog2e / load_constant(a.temperature, L.r);
+    const int w = tid >> 6;
+    // log2(e)/T, divided once per request (row pairs of one request follow each other)
+    const int64_t r = u / ((int64_t)a.N * a.K);
+    if (r != r_c) {
+        r_c = r;
+        c_r = kLog2e / load_constant(a.temperature, r);
+    }
+    const float c = c_r;
     float Ep[NE], Eq[NE];
-    float mp, mq, sp, sq;
     // Wave priority: highest until this slice's partials are published (the other slices of
     // the row pair wait for them), lowest while polling, in between after the exchange (that
-    // work delays only this slice's next publish).
+    // work delays only this slice's next publish). Without it the pass took 7% longer.
     __builtin_amdgcn_s_setprio(3);
-    {
-        mask_slice<DT, kTvCPL>(P, L.c0, L.c1, a.V);
-        mask_slice<DT, kTvCPL>(Q, L.c0, L.c1, a.V);
-        mp = slice_max<DT, kTvCPL>(P);
-        mq = slice_max<DT, kTvCPL>(Q);
-        block_reduce2<true>(mp, mq, sh.max2);
-        sp = slice_exp<DT, kTvCPL>(P, c, -mp * c, Ep);
-        sq = slice_exp<DT, kTvCPL>(Q, c, -mq * c, Eq);
+    if (ragged) {
+        mask_slice<DT, kTvCPL>(P, c0, c1, a.V);
+        mask_slice<DT, kTvCPL>(Q, c0, c1, a.V);
     }
+    const float mpw = wave_share_max<DT, kTvCPL>(P);
+    const float mqw = wave_share_max<DT, kTvCPL>(Q);
+    float s0 = 0.0f, s1 = 0.0f, q0 = 0.0f, q1 = 0.0f;
+    {
+        const float nmp = mpw == -INFINITY ? 0.0f : -mpw * c;
+        const float nmq = mqw == -INFINITY ? 0.0f : -mqw * c;
+#pragma unroll
+        for (int j = 0; j < kTvCPL; ++j) {
+#pragma unroll
+            for (int e = 0; e < EPC; e += 2) {
+                const int x = j * EPC + e;
+                Ep[x] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(P[j], e), c, nmp));
+                Ep[x + 1] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(P[j], e + 1), c, nmp));
+                Eq[x] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(Q[j], e), c, nmq));
+                Eq[x + 1] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(Q[j], e + 1), c, nmq));
+                s0 += Ep[x];
+                s1 += Ep[x + 1];
+                q0 += Eq[x];
+                q1 += Eq[x + 1];
+            }
+        }
+    }
+    __builtin_amdgcn_sched_barrier(0);
     if (next >= 0) {
         const PairLoc N = pair_location<DT>(a, next, s);
-        issue_slice<kTvCPL>(P, N.zp, N.c0, N.c1);
-        issue_slice<kTvCPL>(Q, N.zq, N.c0, N.c1);
+        issue_slice<kTvCPL>(P, N.zp, c0, c1);
+        issue_slice<kTvCPL>(Q, N.zq, c0, c1);
     }
-    block_reduce2<false>(sp, sq, sh.sum2);
-
-    uint64_t* words = reinterpret_cast<uint64_t*>(a.pp + u * a.S);
-    if (tid == 0) {
-        __hip_atomic_store(words + 2 * s, pack2(mp, sp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(words + 2 * s + 1, pack2(mq, sq), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-    __builtin_amdgcn_s_setprio(0);
-    // wave 0 waits for the other slices; the rest of the workgroup waits at the barrier
+    const float spw = wave_sum(s0 + s1), sqw = wave_sum(q0 + q1);
+    if (lane == 0) sh.wpart[w] = make_float4(mpw, spw, mqw, sqw);
+    __syncthreads();
     if (tid < 64) {
+        const float4 wpv = lane < kWaves ? sh.wpart[lane] : make_float4(-INFINITY, 0.0f, -INFINITY, 0.0f);
+        const float mp = readlane_f32(row_max(wpv.x), 0);
+        const float mq = readlane_f32(row_max(wpv.z), 0);
+        const float sp = readlane_f32(row_sum(wpv.y * __builtin_amdgcn_exp2f((wpv.x - mp) * c)), 0);
+        const float sq = readlane_f32(row_sum(wpv.w * __builtin_amdgcn_exp2f((wpv.z - mq) * c)), 0);
+        uint64_t* words = reinterpret_cast<uint64_t*>(a.pp + u * a.S);
+        if (lane == 0) {
+            __hip_atomic_store(words + 2 * s, pack2(mp, sp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            __hip_atomic_store(words + 2 * s + 1, pack2(mq, sq), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __builtin_amdgcn_s_setprio(0);
         const uint64_t t0 = wall_clock64();
         while (!poll_slices(words, 2 * a.S, a.ctrl, a.error_flags, sh.xch, t0)) __builtin_amdgcn_s_sleep(1);
     }
     __syncthreads();
     __builtin_amdgcn_s_setprio(1);
-
-    // Every wave combines the S (<= 64) slices itself: lane t holds slice t's target and
-    // draft words, and whole-wave reductions (fixed order) give the row maxima and sums.
-    // Lanes without a slice hold (-inf, 0), which adds nothing.
     const uint64_t kNone = pack2(-INFINITY, 0.0f);
     const uint64_t wp = lane < a.S ? sh.xch[2 * lane] : kNone;
     const uint64_t wq = lane < a.S ? sh.xch[2 * lane + 1] : kNone;
     float Mp, Mq, Sp, Sq;
     if (a.S <= 16) {
-        // all slices sit in the first 16-lane row; the other rows hold (-inf, 0), so the
-        // whole-wave result is the first row's result exactly
         Mp = readlane_f32(row_max(word_lo(wp)), 0);
         Mq = readlane_f32(row_max(word_lo(wq)), 0);
         Sp = readlane_f32(row_sum(word_hi(wp) * __builtin_amdgcn_exp2f((word_lo(wp) - Mp) * c)), 0);
@@ -500,17 +569,14 @@ __device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, int64_t nex
         Sp = wave_sum(word_hi(wp) * __builtin_amdgcn_exp2f((word_lo(wp) - Mp) * c));
         Sq = wave_sum(word_hi(wq) * __builtin_amdgcn_exp2f((word_lo(wq) - Mq) * c));
     }
-    // p = e_p f_p / S_p and q = e_q f_q / S_q with f = exp2((m_slice - M_row) c). Factor out
-    // the larger of f_p / S_p and f_q / S_q, so the ratio stays finite even when the other
-    // factor underflows (a slice far below its row's max). Equal rows take the first branch
-    // with rho exactly 1.
-    const float fp = __builtin_amdgcn_exp2f((mp - Mp) * c);
-    const float fq = __builtin_amdgcn_exp2f((mq - Mq) * c);
-    const bool p_major = fp * Sq >= fq * Sp;   // the same in every lane
+    const float fp = __builtin_amdgcn_exp2f((mpw - Mp) * c);
+    const float fq = __builtin_amdgcn_exp2f((mqw - Mq) * c);
+    const bool p_major = fp * Sq >= fq * Sp;
     const float num = p_major ? fq * Sp : fp * Sq;
     const float den = p_major ? fp * Sq : fq * Sp;
-    const float rho = den > 0.0f ? num / den : 0.0f;
-    const float scale = p_major ? fp / Sp : fq / Sq;
+    // equal rows: rho exactly 1, so TV is exactly 0 (a reciprocal would not give that)
+    const float rho = num == den ? 1.0f : den > 0.0f ? num * __builtin_amdgcn_rcpf(den) : 0.0f;
+    const float scale = p_major ? fp * __builtin_amdgcn_rcpf(Sp) : fq * __builtin_amdgcn_rcpf(Sq);
     float acc0 = 0.0f, acc1 = 0.0f;
     if (p_major) {
 #pragma unroll
@@ -525,11 +591,32 @@ __device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, int64_t nex
             acc1 += fabsf(fmaf(-rho, Ep[e + 1], Eq[e + 1]));
         }
     }
-    // one partial per wave, so no barrier ends the row pair
     const float acc = wave_sum(acc0 + acc1);
-    if (lane == 0) a.tvp[(u * a.S + s) * kWaves + (tid >> 6)] = acc * scale;
+    if (lane == 0) a.tvp[(u * a.S + s) * kWaves + w] = acc * scale;
 }
 
+// TV on: persistent cooperative grid, gridDim.x = C * S.
+template <int DT>
+__global__ __launch_bounds__(kThreads, 4) void k_logits_tv(LogitsArgs a) {
+    __shared__ TvLds sh;
+    const int s = (int)(blockIdx.x % (unsigned)a.S);
+    const int64_t C = gridDim.x / (unsigned)a.S;
+    const int64_t cluster = blockIdx.x / (unsigned)a.S;
+    if (cluster >= a.pairs) return;
+    const int c0 = s * a.cps;
+    const int c1 = min(c0 + a.cps, a.chunks);
+    const bool ragged = c1 - c0 < kThreads * kTvCPL || (int64_t)c1 * Elem<DT>::EPC > a.V;
+    u32x4 P[kTvCPL], Q[kTvCPL];
+    {
+        const PairLoc L0 = pair_location<DT>(a, cluster, s);
+        issue_slice<kTvCPL>(P, L0.zp, c0, c1);
+        issue_slice<kTvCPL>(Q, L0.zq, c0, c1);
+    }
+    int64_t r_c = -1;
+    float c_r = 0.0f;
+    for (int64_t it = cluster; it < a.pairs; it += C)
+        pair_slice_tv<DT>(a, it, s, it + C < a.pairs ? it + C : -1, ragged, c0, c1, P, Q, sh, r_c, c_r);
+}
 
 // TV off: one workgroup per (row, slice).
 template <int DT>
@@ -544,28 +631,6 @@ __global__ __launch_bounds__(kThreads) void k_logits_stream(LogitsArgs a) {
         const int64_t tb = t - a.pair_wgs;
         bonus_slice<DT, kStreamCPL>(a, tb / a.S, (int)(tb % a.S), red, redi);
     }
-}
-
-// TV on: persistent cooperative grid, gridDim.x = C * S.
-template <int DT>
-__global__ __launch_bounds__(kThreads, 4) void k_logits_tv(LogitsArgs a) {
-    __shared__ TvLds sh;
-    __shared__ float red[kWaves];
-    __shared__ int32_t redi[kWaves];
-    const int s = (int)(blockIdx.x % (unsigned)a.S);
-    const int64_t cluster = blockIdx.x / (unsigned)a.S;
-    const int64_t clusters = gridDim.x / (unsigned)a.S;
-    const int64_t items = a.pairs + (a.total_wgs - a.pair_wgs) / a.S;
-    int64_t it = cluster;
-    u32x4 P[kTvCPL], Q[kTvCPL];
-    if (it < a.pairs) {
-        const PairLoc L0 = pair_location<DT>(a, it, s);
-        issue_slice<kTvCPL>(P, L0.zp, L0.c0, L0.c1);
-        issue_slice<kTvCPL>(Q, L0.zq, L0.c0, L0.c1);
-    }
-    for (; it < a.pairs; it += clusters)
-        pair_slice_tv<DT>(a, it, s, it + clusters < a.pairs ? it + clusters : -1, P, Q, sh);
-    for (; it < items; it += clusters) bonus_slice<DT, kTvCPL>(a, it - a.pairs, s, red, redi);
 }
 
 __global__ void k_fill_words(uint32_t* p, int64_t n, uint32_t value) {
@@ -614,11 +679,17 @@ static int64_t coop_capacity() {
     return c;
 }
 
+// Every exchange word of the pass at the all-ones "empty" pattern.
+hipError_t launch_tv_fill(const Plan& plan, const LogitsArgs& a, hipStream_t s) {
+    return launch_fill_words(reinterpret_cast<uint32_t*>(a.pp),
+                             (int64_t)(plan.pair_wgs * sizeof(PairPart) / 4), ~0u, s);
+}
+
+// The row pairs only: the round hands the bonus rows to the Gumbel-Top-K slice kernel.
 template <int DT>
 static hipError_t launch_tv(const Plan& plan, const LogitsArgs& a, hipStream_t s) {
     const int64_t cap = coop_capacity<DT>();
-    const int64_t items = plan.pairs + plan.bonus_rows;
-    const int64_t clusters = std::min<int64_t>(cap / plan.S, items);
+    const int64_t clusters = std::min<int64_t>(cap / plan.S, plan.pairs);
     if (clusters < 1) return hipErrorCooperativeLaunchTooLarge;
     LogitsArgs copy = a;
     void* params[] = {&copy};
