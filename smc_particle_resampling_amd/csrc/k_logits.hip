@@ -463,6 +463,89 @@ __device__ __forceinline__ float wave_share_max(const u32x4 (&R)[CPL]) {
     }
 }
 
+// The -inf padding of one workgroup's slice, fixed for the whole persistent loop (every row
+// has the same length): which chunk groups run past the slice end (a uniform bit per group),
+// whether this lane's chunk of such a group lies inside, and which lane holds the row's
+// partial tail chunk, if any. Applying it is one select per word of a partial group.
+template <int DT, int CPL>
+struct SliceMask {
+    uint32_t partial;      // bit j: chunk group j has lanes past the slice end (uniform)
+    bool inside[CPL];      // this lane's chunk of group j is inside the slice
+    bool has_tail;         // the slice holds the row's last chunk and V is not a multiple of
+                           // the chunk width (uniform)
+    int tail_j;            // chunk group of that chunk if this lane holds it, else -1
+    uint32_t keep[4];      // per word of the tail chunk: bits kept (uniform)
+
+    __device__ __forceinline__ SliceMask(int c0, int c1, int V) {
+        constexpr int EPC = Elem<DT>::EPC;
+        const int tid = threadIdx.x;
+        const int n = c1 - c0;
+        partial = 0;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j) {
+            if ((j + 1) * kThreads > n) partial |= 1u << j;
+            inside[j] = j * kThreads + tid < n;
+        }
+        has_tail = (int64_t)c1 * EPC > V;
+        tail_j = -1;
+        const int nv = V - (c1 - 1) * EPC;   // valid elements of the last chunk
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+            if constexpr (DT == SMCSD_F32) keep[w] = w < nv ? 0xFFFFFFFFu : 0u;
+            else keep[w] = 2 * w + 1 < nv ? 0xFFFFFFFFu : 2 * w < nv ? 0x0000FFFFu : 0u;
+        }
+        if (has_tail) {
+            const int last = c1 - 1 - c0;
+            if (last % kThreads == tid) tail_j = last / kThreads;
+        }
+    }
+
+    // -inf bits are exactly the complement of the kept bits within each element, so the
+    // padding is (x & keep) | (kNegInf & ~keep)
+    __device__ __forceinline__ void apply(u32x4 (&R)[CPL]) const {
+        const uint32_t ni = Elem<DT>::kNegInf;
+#pragma unroll
+        for (int j = 0; j < CPL; ++j)
+            if (partial & (1u << j)) {
+#pragma unroll
+                for (int w = 0; w < 4; ++w) R[j][w] = inside[j] ? R[j][w] : ni;
+            }
+        if (has_tail) {
+#pragma unroll
+            for (int j = 0; j < CPL; ++j)
+#pragma unroll
+                for (int w = 0; w < 4; ++w) {
+                    const uint32_t m = (R[j][w] & keep[w]) | (ni & ~keep[w]);
+                    R[j][w] = tail_j == j ? m : R[j][w];
+                }
+        }
+    }
+};
+
+// The rows of row pair u: with g = u / K (request * N + particle) and k = u - g * K, the
+// target row is g * (K + 1) + k = u + g and the draft row is u. Row pairs number fewer than
+// 2^31 (the grid bound of the plan), so 32-bit division suffices.
+template <int DT>
+__device__ __forceinline__ void pair_rows(const LogitsArgs& a, uint32_t u, int c0, const char*& zp,
+                                          const char*& zq) {
+    constexpr size_t ESZ = Elem<DT>::ESZ;
+    const uint32_t g = u / (uint32_t)a.K;
+    zp = static_cast<const char*>(a.target) + ((size_t)(u + g) * a.ld + (size_t)c0 * Elem<DT>::EPC) * ESZ;
+    zq = static_cast<const char*>(a.draft) + ((size_t)u * a.ld + (size_t)c0 * Elem<DT>::EPC) * ESZ;
+}
+
+// Issue the loads of this lane's chunks of the slice that starts at `row` (c0 already
+// applied) and holds n chunks.
+template <int CPL>
+__device__ __forceinline__ void issue_at(u32x4 (&R)[CPL], const char* row, int n) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(row), 0, n * 16,
+                                                                       kRsrcWord3);
+    const int voff = (int)threadIdx.x * 16;
+#pragma unroll
+    for (int j = 0; j < CPL; ++j)
+        R[j] = __builtin_amdgcn_raw_buffer_load_b128(r, voff, j * kThreads * 16, kLoadNontemporal);
+}
+
 // LDS of the TV pass: the wave partials (max p, sum p, max q, sum q) of the current row pair
 // and its exchange words. Reuse by the next row pair needs no third barrier: wave 0 reads
 // wpart before the exchange barrier, and the next row pair rewrites it only after that
@@ -482,18 +565,20 @@ struct TvLds {
 // during the exchange and phase 2. Two barriers per row pair: wave partials, exchange words.
 
 template <int DT>
-__device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, int64_t next, bool ragged,
-                              int c0, int c1, u32x4 (&P)[kTvCPL], u32x4 (&Q)[kTvCPL], TvLds& sh,
-                              int64_t& r_c, float& c_r) {
+__device__ void pair_slice_tv(const LogitsArgs& a, uint32_t u, int s, int64_t next,
+                              const SliceMask<DT, kTvCPL>& mask, int c0, int n, u32x4 (&P)[kTvCPL],
+                              u32x4 (&Q)[kTvCPL], TvLds& sh, uint32_t& r_lo, float& c_r) {
     constexpr int NE = kTvCPL * Elem<DT>::EPC;
     constexpr int EPC = Elem<DT>::EPC;
     const int tid = threadIdx.x;
     const int lane = tid & 63;
     const int w = tid >> 6;
-    // log2(e)/T, divided once per request (row pairs of one request follow each other)
-    const int64_t r = u / ((int64_t)a.N * a.K);
-    if (r != r_c) {
-        r_c = r;
+    // log2(e)/T, divided once per request (row pairs of one request follow each other):
+    // r_lo is the first row pair of the request c_r belongs to
+    const uint32_t nk = (uint32_t)a.N * (uint32_t)a.K;
+    if (u - r_lo >= nk) {
+        const uint32_t r = u / nk;
+        r_lo = r * nk;
         c_r = kLog2e / load_constant(a.temperature, r);
     }
     const float c = c_r;
@@ -502,10 +587,8 @@ __device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, int64_t nex
     // the row pair wait for them), lowest while polling, in between after the exchange (that
     // work delays only this slice's next publish). Without it the pass took 7% longer.
     __builtin_amdgcn_s_setprio(3);
-    if (ragged) {
-        mask_slice<DT, kTvCPL>(P, c0, c1, a.V);
-        mask_slice<DT, kTvCPL>(Q, c0, c1, a.V);
-    }
+    mask.apply(P);
+    mask.apply(Q);
     const float mpw = wave_share_max<DT, kTvCPL>(P);
     const float mqw = wave_share_max<DT, kTvCPL>(Q);
     float s0 = 0.0f, s1 = 0.0f, q0 = 0.0f, q1 = 0.0f;
@@ -530,9 +613,10 @@ __device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, int64_t nex
     }
     __builtin_amdgcn_sched_barrier(0);
     if (next >= 0) {
-        const PairLoc N = pair_location<DT>(a, next, s);
-        issue_slice<kTvCPL>(P, N.zp, c0, c1);
-        issue_slice<kTvCPL>(Q, N.zq, c0, c1);
+        const char *zp, *zq;
+        pair_rows<DT>(a, (uint32_t)next, c0, zp, zq);
+        issue_at<kTvCPL>(P, zp, n);
+        issue_at<kTvCPL>(Q, zq, n);
     }
     const float spw = wave_sum(s0 + s1), sqw = wave_sum(q0 + q1);
     if (lane == 0) sh.wpart[w] = make_float4(mpw, spw, mqw, sqw);
@@ -543,7 +627,7 @@ __device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, int64_t nex
         const float mq = readlane_f32(row_max(wpv.z), 0);
         const float sp = readlane_f32(row_sum(wpv.y * __builtin_amdgcn_exp2f((wpv.x - mp) * c)), 0);
         const float sq = readlane_f32(row_sum(wpv.w * __builtin_amdgcn_exp2f((wpv.z - mq) * c)), 0);
-        uint64_t* words = reinterpret_cast<uint64_t*>(a.pp + u * a.S);
+        uint64_t* words = reinterpret_cast<uint64_t*>(a.pp + (size_t)u * a.S);
         if (lane == 0) {
             __hip_atomic_store(words + 2 * s, pack2(mp, sp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
             __hip_atomic_store(words + 2 * s + 1, pack2(mq, sq), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -592,7 +676,7 @@ __device__ void pair_slice_tv(const LogitsArgs& a, int64_t u, int s, int64_t nex
         }
     }
     const float acc = wave_sum(acc0 + acc1);
-    if (lane == 0) a.tvp[(u * a.S + s) * kWaves + w] = acc * scale;
+    if (lane == 0) a.tvp[((size_t)u * a.S + s) * kWaves + w] = acc * scale;
 }
 
 // TV on: persistent cooperative grid, gridDim.x = C * S.
@@ -605,17 +689,20 @@ __global__ __launch_bounds__(kThreads, 4) void k_logits_tv(LogitsArgs a) {
     if (cluster >= a.pairs) return;
     const int c0 = s * a.cps;
     const int c1 = min(c0 + a.cps, a.chunks);
-    const bool ragged = c1 - c0 < kThreads * kTvCPL || (int64_t)c1 * Elem<DT>::EPC > a.V;
+    const SliceMask<DT, kTvCPL> mask(c0, c1, a.V);
     u32x4 P[kTvCPL], Q[kTvCPL];
     {
-        const PairLoc L0 = pair_location<DT>(a, cluster, s);
-        issue_slice<kTvCPL>(P, L0.zp, c0, c1);
-        issue_slice<kTvCPL>(Q, L0.zq, c0, c1);
+        const char *zp, *zq;
+        pair_rows<DT>(a, (uint32_t)cluster, c0, zp, zq);
+        issue_at<kTvCPL>(P, zp, c1 - c0);
+        issue_at<kTvCPL>(Q, zq, c1 - c0);
     }
-    int64_t r_c = -1;
-    float c_r = 0.0f;
+    const uint32_t nk = (uint32_t)a.N * (uint32_t)a.K;
+    uint32_t r_lo = (uint32_t)cluster / nk * nk;   // first row pair of the current request
+    float c_r = kLog2e / load_constant(a.temperature, (uint32_t)cluster / nk);
     for (int64_t it = cluster; it < a.pairs; it += C)
-        pair_slice_tv<DT>(a, it, s, it + C < a.pairs ? it + C : -1, ragged, c0, c1, P, Q, sh, r_c, c_r);
+        pair_slice_tv<DT>(a, (uint32_t)it, s, it + C < a.pairs ? it + C : -1, mask, c0, c1 - c0, P,
+                          Q, sh, r_lo, c_r);
 }
 
 // TV off: one workgroup per (row, slice).
