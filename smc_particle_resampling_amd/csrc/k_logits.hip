@@ -124,42 +124,6 @@ __device__ __forceinline__ void mask_slice(u32x4 (&R)[CPL], int c0, int c1, int 
 
 typedef short i16x2 __attribute__((ext_vector_type(2)));
 
-// Slice max. For bf16 it works on the raw bit patterns with packed 16-bit integer max and
-// min: read as int16, non-negative bf16 values order like their floats and negative ones
-// in reverse. So the float max is the int16 max when that is >= 0 (some element is
-// non-negative), and otherwise the int16 min (the negative value of least magnitude). -inf
-// (0xFF80) is the int16 -128, above every finite negative, so masked elements never win.
-template <int DT, int CPL>
-__device__ __forceinline__ float slice_max(const u32x4 (&R)[CPL]) {
-    if constexpr (DT == SMCSD_F32) {
-        float m = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j)
-#pragma unroll
-            for (int w = 0; w < 4; w += 2)
-                m = fmaxf(m, fmaxf(__uint_as_float(R[j][w]), __uint_as_float(R[j][w + 1])));
-        return m;
-    } else {
-        i16x2 mx = {(short)-32768, (short)-32768}, mn = {(short)32767, (short)32767};
-#pragma unroll
-        for (int j = 0; j < CPL; ++j)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t word = R[j][w];
-                // copy the element first: a bit cast applied to a vector element directly
-                // reads the vector's first element instead (clang lowers it as a load from
-                // the vector's address)
-                const i16x2 x = __builtin_bit_cast(i16x2, word);
-                mx = __builtin_elementwise_max(mx, x);
-                mn = __builtin_elementwise_min(mn, x);
-            }
-        const short hi = mx[0] > mx[1] ? mx[0] : mx[1];
-        const short lo = mn[0] < mn[1] ? mn[0] : mn[1];
-        const uint32_t bits = (uint32_t)(uint16_t)(hi >= 0 ? hi : lo);
-        return __uint_as_float(bits << 16);
-    }
-}
-
 // sum over the slice of exp2(z * c - m * c)
 template <int DT, int CPL>
 __device__ __forceinline__ float slice_sumexp(const u32x4 (&R)[CPL], float c, float nmc) {
@@ -197,48 +161,6 @@ __device__ __forceinline__ PairLoc pair_location(const LogitsArgs& a, int64_t u,
     L.c0 = s * a.cps;
     L.c1 = min(L.c0 + a.cps, a.chunks);
     return L;
-}
-
-// Two block-wide reductions at once (max or sum), in a fixed order: within each wave as in
-// wave_max / wave_sum, then waves 0..3. lds holds 2 * kWaves floats. One barrier: a later
-// call must use other lds (or come after another barrier) so that no wave overwrites values
-// still being read.
-template <bool kMax>
-__device__ __forceinline__ void block_reduce2(float& a, float& b, float* lds) {
-    a = kMax ? wave_max(a) : wave_sum(a);
-    b = kMax ? wave_max(b) : wave_sum(b);
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) {
-        lds[2 * w] = a;
-        lds[2 * w + 1] = b;
-    }
-    __syncthreads();
-    a = lds[0];
-    b = lds[1];
-#pragma unroll
-    for (int i = 1; i < kWaves; ++i) {
-        a = kMax ? fmaxf(a, lds[2 * i]) : a + lds[2 * i];
-        b = kMax ? fmaxf(b, lds[2 * i + 1]) : b + lds[2 * i + 1];
-    }
-}
-
-// TV off: slice partials only.
-template <int DT>
-__device__ void pair_slice_stream(const LogitsArgs& a, int64_t u, int s, float* red2a,
-                                  float* red2b) {
-    const PairLoc L = pair_location<DT>(a, u, s);
-    const float c = kLog2e / load_constant(a.temperature, L.r);   // exp(z/T) = exp2(z * c)
-    u32x4 P[kStreamCPL], Q[kStreamCPL];
-    issue_slice<kStreamCPL>(P, L.zp, L.c0, L.c1);
-    issue_slice<kStreamCPL>(Q, L.zq, L.c0, L.c1);
-    mask_slice<DT, kStreamCPL>(P, L.c0, L.c1, a.V);
-    mask_slice<DT, kStreamCPL>(Q, L.c0, L.c1, a.V);
-    float mp = slice_max<DT, kStreamCPL>(P), mq = slice_max<DT, kStreamCPL>(Q);
-    block_reduce2<true>(mp, mq, red2a);
-    float sp = slice_sumexp<DT, kStreamCPL>(P, c, -mp * c);
-    float sq = slice_sumexp<DT, kStreamCPL>(Q, c, -mq * c);
-    block_reduce2<false>(sp, sq, red2b);
-    if (threadIdx.x == 0) a.pp[u * a.S + s] = PairPart{mp, sp, mq, sq};
 }
 
 // Slice exchange of the TV pass. Every (row pair, slice) partial is two 64-bit words, (max,
@@ -705,15 +627,45 @@ __global__ __launch_bounds__(kThreads, 4) void k_logits_tv(LogitsArgs a) {
                           Q, sh, r_lo, c_r);
 }
 
+// TV off: slice partials only. Each wave shifts its exponentials by the maximum of its own
+// share (no barrier between the loads and the exponentials); wave 0 combines the eight wave
+// partials into the slice partial after the one barrier.
+template <int DT>
+__device__ void pair_slice_stream(const LogitsArgs& a, int64_t u, int s, float4* wpart) {
+    const PairLoc L = pair_location<DT>(a, u, s);
+    const float c = kLog2e / load_constant(a.temperature, L.r);   // exp(z/T) = exp2(z * c)
+    const int lane = threadIdx.x & 63;
+    u32x4 P[kStreamCPL], Q[kStreamCPL];
+    issue_slice<kStreamCPL>(P, L.zp, L.c0, L.c1);
+    issue_slice<kStreamCPL>(Q, L.zq, L.c0, L.c1);
+    mask_slice<DT, kStreamCPL>(P, L.c0, L.c1, a.V);
+    mask_slice<DT, kStreamCPL>(Q, L.c0, L.c1, a.V);
+    const float mpw = wave_share_max<DT, kStreamCPL>(P);
+    const float mqw = wave_share_max<DT, kStreamCPL>(Q);
+    // a wave whose share is all padding has maximum -inf: shift 0, so its terms are 0
+    const float spw = wave_sum(slice_sumexp<DT, kStreamCPL>(P, c, mpw == -INFINITY ? 0.0f : -mpw * c));
+    const float sqw = wave_sum(slice_sumexp<DT, kStreamCPL>(Q, c, mqw == -INFINITY ? 0.0f : -mqw * c));
+    if (lane == 0) wpart[threadIdx.x >> 6] = make_float4(mpw, spw, mqw, sqw);
+    __syncthreads();
+    if (threadIdx.x < 64) {
+        const float4 wpv = lane < kWaves ? wpart[lane] : make_float4(-INFINITY, 0.0f, -INFINITY, 0.0f);
+        const float mp = readlane_f32(row_max(wpv.x), 0);
+        const float mq = readlane_f32(row_max(wpv.z), 0);
+        const float sp = readlane_f32(row_sum(wpv.y * __builtin_amdgcn_exp2f((wpv.x - mp) * c)), 0);
+        const float sq = readlane_f32(row_sum(wpv.w * __builtin_amdgcn_exp2f((wpv.z - mq) * c)), 0);
+        if (lane == 0) a.pp[u * a.S + s] = PairPart{mp, sp, mq, sq};
+    }
+}
+
 // TV off: one workgroup per (row, slice).
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_logits_stream(LogitsArgs a) {
     __shared__ float red[kWaves];
     __shared__ int32_t redi[kWaves];
-    __shared__ float red2a[2 * kWaves], red2b[2 * kWaves];
+    __shared__ float4 wpart[kWaves];
     const int64_t t = blockIdx.x;
     if (t < a.pair_wgs) {
-        pair_slice_stream<DT>(a, t / a.S, (int)(t % a.S), red2a, red2b);
+        pair_slice_stream<DT>(a, t / a.S, (int)(t % a.S), wpart);
     } else if (t < a.total_wgs) {
         const int64_t tb = t - a.pair_wgs;
         bonus_slice<DT, kStreamCPL>(a, tb / a.S, (int)(tb % a.S), red, redi);
