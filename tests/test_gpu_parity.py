@@ -145,6 +145,22 @@ def test_extreme_logit_ranges(dev):
 
 
 @pytest.mark.parametrize("tv", [True, False])
+def test_all_negative_logits(tv, dev):
+    # every logit below -20: each wave's share of each slice is negative, so its maximum comes
+    # from the int16-min branch of the packed bf16 max (a constant shift leaves the softmax,
+    # and so the drafted tokens, as they were)
+    w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="all-negative", R=2, N=4, K=3, V=20000,
+                                               ctx=64, tv=tv)
+
+    def shift(inp):
+        inp["target"].sub_(48.0)
+        inp["draft"].sub_(48.0)
+        assert float(inp["target"].float().max()) < 0 and float(inp["draft"].float().max()) < 0
+
+    run_and_compare(w, dev, seed=11, modify=shift)
+
+
+@pytest.mark.parametrize("tv", [True, False])
 def test_row_max_at_every_chunk_position(tv, dev):
     # a +200 spike (its exp overflows unless the slice max sees it) at each of the 8 element
     # positions of a 16-byte chunk, in different rows, plus one at the row's last element
