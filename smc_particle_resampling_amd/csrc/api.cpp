@@ -172,11 +172,9 @@ static hipError_t launch_logits_pass(const Plan& plan, const LogitsArgs& la, hip
 
 // The TV pass of the round over the given logits: exchange slots filled, then the pass,
 // bracketed by the optional timing events.
-static hipError_t run_tv_pass(const Plan& plan, const LogitsArgs& la, char* ws,
-                              smcsd_event begin, smcsd_event end, hipStream_t s) {
-    hipError_t e = launch_fill_ctrl(reinterpret_cast<Ctrl*>(ws + plan.off_ctrl),
-                                    exchange_timeout_ticks(), s);
-    if (e == hipSuccess) e = launch_tv_fill(plan, la, s);
+static hipError_t run_tv_pass(const Plan& plan, const LogitsArgs& la, smcsd_event begin,
+                              smcsd_event end, hipStream_t s) {
+    hipError_t e = launch_tv_fill(plan, la, exchange_timeout_ticks(), s);
     if (e != hipSuccess) return e;
     if (begin && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(begin), s)) != hipSuccess) return e;
     if ((e = launch_logits_pass(plan, la, s)) != hipSuccess) return e;
@@ -264,10 +262,9 @@ smcsd_status smcsd_round(const smcsd_round_args* args, smcsd_stream stream) {
     hipError_t e = hipSuccess;
     if (plan.tv) {
         // the control word starts with abort 0 and the wait limit, every exchange word at the
-        // all-ones "empty" pattern (fill kernels, not memset nodes, so the sequence can be
+        // all-ones "empty" pattern (a fill kernel, not memset nodes, so the sequence can be
         // captured in a graph)
-        e = launch_fill_ctrl(reinterpret_cast<Ctrl*>(ws + plan.off_ctrl), exchange_timeout_ticks(), s);
-        if (e == hipSuccess) e = launch_tv_fill(plan, la, s);
+        e = launch_tv_fill(plan, la, exchange_timeout_ticks(), s);
         if (e != hipSuccess) return SMCSD_ERR_DEVICE;
     }
     if (a.timing_begin && hipEventRecord(reinterpret_cast<hipEvent_t>(a.timing_begin), s) != hipSuccess)
@@ -547,7 +544,7 @@ smcsd_status smcsd_sd_verify(const smcsd_verify_args* args, smcsd_stream stream)
     la.chunks = plan.chunks;
     la.S = plan.S;
     la.cps = plan.cps;
-    if (run_tv_pass(plan, la, ws, a.timing_begin, a.timing_end, s) != hipSuccess)
+    if (run_tv_pass(plan, la, a.timing_begin, a.timing_end, s) != hipSuccess)
         return SMCSD_ERR_DEVICE;
 
     VerifyArgs va{};

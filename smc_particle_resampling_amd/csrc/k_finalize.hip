@@ -55,8 +55,17 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
             }
             a.terms[u] = term;
             if (a.tv) {
+                // the S * kWaves partials of this position, 16 bytes a load (the block of a
+                // position starts at a multiple of 32 floats)
+                const float4* tp = reinterpret_cast<const float4*>(a.tvp + u * a.S * kWaves);
                 double t2 = 0.0;
-                for (int t = 0; t < a.S * kWaves; ++t) t2 += (double)a.tvp[u * a.S * kWaves + t];
+                for (int t = 0; t < a.S * kWaves / 4; ++t) {
+                    const float4 v = tp[t];
+                    t2 += (double)v.x;
+                    t2 += (double)v.y;
+                    t2 += (double)v.z;
+                    t2 += (double)v.w;
+                }
                 a.tv[u] = (float)fmin(fmax(0.5 * t2, 0.0), 1.0);
             }
         }
@@ -95,7 +104,43 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
     for (int32_t i = tid; i < N; i += kThreads) s_off[i] = 0;
     __syncthreads();
 
-    if (tid == 0) {
+    if (N <= 64) {
+        // one wave, lane i = particle i: butterfly reductions (every lane ends with the same
+        // bits) and an inclusive prefix scan of the weights, all in double precision
+        if (tid < 64) {
+            const int i = tid;
+            const double l = i < N ? s_l[i] : -INFINITY;
+            double m = l;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) m = fmax(m, __shfl_xor(m, d));
+            const double e = i < N ? exp(l - m) : 0.0;
+            double se = e;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) se += __shfl_xor(se, d);
+            const double w = e / se;
+            double s2 = w * w;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) s2 += __shfl_xor(s2, d);
+            const double logZ = m + log(se);
+            const double ess = 1.0 / s2;
+            const int32_t rs = a.mode == SMCSD_RESAMPLE_ALWAYS ||
+                               (a.mode == SMCSD_RESAMPLE_ESS && ess < (double)a.ess_frac * (double)N);
+            double acc = w;
+#pragma unroll
+            for (int d = 1; d < 64; d <<= 1) {
+                const double o = __shfl_up(acc, d);
+                if (i >= d) acc += o;
+            }
+            if (i < N) s_c[i] = rs ? acc : w;
+            if (i == 0) {
+                a.log_norm[r] = (float)logZ;
+                a.ess[r] = (float)ess;
+                a.resampled[r] = rs;
+                s_logZ = logZ;
+                s_rs = rs;
+            }
+        }
+    } else if (tid == 0) {
         double m = -INFINITY;
         for (int32_t i = 0; i < N; ++i) m = fmax(m, s_l[i]);
         double se = 0.0;

@@ -678,16 +678,16 @@ __global__ void k_fill_words(uint32_t* p, int64_t n, uint32_t value) {
         p[i] = value;
 }
 
+// Before a TV pass: the control word (abort flag 0, the wait limit) and every exchange word
+// at the all-ones "empty" pattern, in one launch.
+__global__ void k_fill_tv(Ctrl* ctrl, uint32_t timeout, uint32_t* words, int64_t n) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) *ctrl = Ctrl{0u, timeout};
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (int64_t)gridDim.x * blockDim.x)
+        words[i] = ~0u;
+}
+
 }  // namespace
-
-__global__ void k_fill_ctrl(Ctrl* ctrl, uint32_t timeout) {
-    if (threadIdx.x == 0) *ctrl = Ctrl{0u, timeout};
-}
-
-hipError_t launch_fill_ctrl(Ctrl* ctrl, uint32_t timeout, hipStream_t s) {
-    k_fill_ctrl<<<dim3(1), dim3(64), 0, s>>>(ctrl, timeout);
-    return hipGetLastError();
-}
 
 hipError_t launch_fill_words(uint32_t* p, int64_t n, uint32_t value, hipStream_t s) {
     if (n <= 0) return hipSuccess;
@@ -718,10 +718,12 @@ static int64_t coop_capacity() {
     return c;
 }
 
-// Every exchange word of the pass at the all-ones "empty" pattern.
-hipError_t launch_tv_fill(const Plan& plan, const LogitsArgs& a, hipStream_t s) {
-    return launch_fill_words(reinterpret_cast<uint32_t*>(a.pp),
-                             (int64_t)(plan.pair_wgs * sizeof(PairPart) / 4), ~0u, s);
+hipError_t launch_tv_fill(const Plan& plan, const LogitsArgs& a, uint32_t timeout, hipStream_t s) {
+    const int64_t n = (int64_t)(plan.pair_wgs * sizeof(PairPart) / 4);
+    const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n + kThreads - 1) / kThreads, 1024));
+    k_fill_tv<<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(a.ctrl, timeout,
+                                                               reinterpret_cast<uint32_t*>(a.pp), n);
+    return hipGetLastError();
 }
 
 // The row pairs only: the round hands the bonus rows to the Gumbel-Top-K slice kernel.
