@@ -672,12 +672,6 @@ __global__ __launch_bounds__(kThreads) void k_logits_stream(LogitsArgs a) {
     }
 }
 
-__global__ void k_fill_words(uint32_t* p, int64_t n, uint32_t value) {
-    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
-         i += (int64_t)gridDim.x * blockDim.x)
-        p[i] = value;
-}
-
 // Before a TV pass: the control word (abort flag 0, the wait limit) and every exchange word
 // at the all-ones "empty" pattern, in one launch.
 __global__ void k_fill_tv(Ctrl* ctrl, uint32_t timeout, uint32_t* words, int64_t n) {
@@ -688,13 +682,6 @@ __global__ void k_fill_tv(Ctrl* ctrl, uint32_t timeout, uint32_t* words, int64_t
 }
 
 }  // namespace
-
-hipError_t launch_fill_words(uint32_t* p, int64_t n, uint32_t value, hipStream_t s) {
-    if (n <= 0) return hipSuccess;
-    const int64_t blocks = std::min<int64_t>((n + kThreads - 1) / kThreads, 1024);
-    k_fill_words<<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(p, n, value);
-    return hipGetLastError();
-}
 
 // Workgroups of k_logits_tv<DT> that fit on the current device at once (cached per device).
 template <int DT>

@@ -218,7 +218,6 @@ struct RemapArgs {
 };
 
 // Host launchers (defined next to their kernels). Return hipSuccess or the launch error.
-hipError_t launch_fill_words(uint32_t* p, int64_t n, uint32_t value, hipStream_t s);
 // Ctrl of a TV pass: abort 0 and the wait limit (one small kernel, graph-capturable).
 hipError_t launch_logits(const Plan& plan, const LogitsArgs& a, hipStream_t s);
 hipError_t launch_tv_fill(const Plan& plan, const LogitsArgs& a, uint32_t timeout, hipStream_t s);
