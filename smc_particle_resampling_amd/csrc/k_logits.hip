@@ -468,14 +468,15 @@ __device__ __forceinline__ void issue_at(u32x4 (&R)[CPL], const char* row, int n
         R[j] = __builtin_amdgcn_raw_buffer_load_b128(r, voff, j * kThreads * 16, kLoadNontemporal);
 }
 
-// LDS of the TV pass: the wave partials (max p, sum p, max q, sum q) of the current row pair
-// and its exchange words. Reuse by the next row pair needs no third barrier: wave 0 reads
-// wpart before the exchange barrier, and the next row pair rewrites it only after that
-// barrier; wave 0 rewrites xch only after the next row pair's first barrier, which every
-// wave reaches after its last read of xch.
+// LDS of the TV pass: the wave partials (max p, sum p, max q, sum q) of the current row pair,
+// its exchange words and the row sums wave 0 makes of them. Reuse by the next row pair needs
+// no third barrier: wave 0 reads wpart and xch before the exchange barrier, and the next row
+// pair rewrites them only after that barrier; wave 0 rewrites norm only after the next row
+// pair's first barrier, which every wave reaches after its last read of norm.
 struct TvLds {
     float4 wpart[kWaves];
     uint64_t xch[2 * kMaxTvSlices];
+    float4 norm;   // the row pair's (max p, sum p, max q, sum q), from wave 0
 };
 
 // TV on: partials, exchange, and this slice's share of sum |p - q|, one partial per wave.
@@ -557,24 +558,29 @@ __device__ void pair_slice_tv(const LogitsArgs& a, uint32_t u, int s, int64_t ne
         __builtin_amdgcn_s_setprio(0);
         const uint64_t t0 = wall_clock64();
         while (!poll_slices(words, 2 * a.S, a.ctrl, a.error_flags, sh.xch, t0)) __builtin_amdgcn_s_sleep(1);
+        // the row maxima and sums from the S slice partials, once for the workgroup: lane t
+        // holds slice t (lanes without a slice hold (-inf, 0), which adds nothing)
+        const uint64_t kNone = pack2(-INFINITY, 0.0f);
+        const uint64_t wp = lane < a.S ? sh.xch[2 * lane] : kNone;
+        const uint64_t wq = lane < a.S ? sh.xch[2 * lane + 1] : kNone;
+        float Mp, Mq, Sp, Sq;
+        if (a.S <= 16) {
+            Mp = readlane_f32(row_max(word_lo(wp)), 0);
+            Mq = readlane_f32(row_max(word_lo(wq)), 0);
+            Sp = readlane_f32(row_sum(word_hi(wp) * __builtin_amdgcn_exp2f((word_lo(wp) - Mp) * c)), 0);
+            Sq = readlane_f32(row_sum(word_hi(wq) * __builtin_amdgcn_exp2f((word_lo(wq) - Mq) * c)), 0);
+        } else {
+            Mp = wave_max(word_lo(wp));
+            Mq = wave_max(word_lo(wq));
+            Sp = wave_sum(word_hi(wp) * __builtin_amdgcn_exp2f((word_lo(wp) - Mp) * c));
+            Sq = wave_sum(word_hi(wq) * __builtin_amdgcn_exp2f((word_lo(wq) - Mq) * c));
+        }
+        if (lane == 0) sh.norm = make_float4(Mp, Sp, Mq, Sq);
     }
     __syncthreads();
     __builtin_amdgcn_s_setprio(1);
-    const uint64_t kNone = pack2(-INFINITY, 0.0f);
-    const uint64_t wp = lane < a.S ? sh.xch[2 * lane] : kNone;
-    const uint64_t wq = lane < a.S ? sh.xch[2 * lane + 1] : kNone;
-    float Mp, Mq, Sp, Sq;
-    if (a.S <= 16) {
-        Mp = readlane_f32(row_max(word_lo(wp)), 0);
-        Mq = readlane_f32(row_max(word_lo(wq)), 0);
-        Sp = readlane_f32(row_sum(word_hi(wp) * __builtin_amdgcn_exp2f((word_lo(wp) - Mp) * c)), 0);
-        Sq = readlane_f32(row_sum(word_hi(wq) * __builtin_amdgcn_exp2f((word_lo(wq) - Mq) * c)), 0);
-    } else {
-        Mp = wave_max(word_lo(wp));
-        Mq = wave_max(word_lo(wq));
-        Sp = wave_sum(word_hi(wp) * __builtin_amdgcn_exp2f((word_lo(wp) - Mp) * c));
-        Sq = wave_sum(word_hi(wq) * __builtin_amdgcn_exp2f((word_lo(wq) - Mq) * c));
-    }
+    const float4 nrm = sh.norm;
+    const float Mp = nrm.x, Sp = nrm.y, Mq = nrm.z, Sq = nrm.w;
     const float fp = __builtin_amdgcn_exp2f((mpw - Mp) * c);
     const float fq = __builtin_amdgcn_exp2f((mqw - Mq) * c);
     const bool p_major = fp * Sq >= fq * Sp;
