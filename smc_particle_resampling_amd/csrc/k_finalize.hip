@@ -206,8 +206,14 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
     if (a.pt_in) {
         __syncthreads();
         const int64_t NP = (int64_t)N * a.P;
-        remap_rows(a.pt_in + r * NP, a.pt_out + r * NP, s_anc, s_off, a.P, 0, NP, a.refcount,
-                   a.num_pages, a.error_flags);
+        // up to 64 particles: one atomic per run of equal pages in a column; more particles
+        // would make each column's walk long, so one atomic per entry there
+        if (N <= 64)
+            remap_request_runs(a.pt_in + r * NP, a.pt_out + r * NP, s_anc, s_off, N, a.P, a.refcount,
+                               a.num_pages, a.error_flags);
+        else
+            remap_rows(a.pt_in + r * NP, a.pt_out + r * NP, s_anc, s_off, a.P, 0, NP, a.refcount,
+                       a.num_pages, a.error_flags);
     }
 }
 

@@ -35,4 +35,60 @@ __device__ __forceinline__ void remap_rows(const int32_t* in, int32_t* out, cons
     }
 }
 
+// The same remap for a whole request in one workgroup, with fewer refcount atomics: the
+// table copy as above, then per column the rows are walked in order and consecutive rows
+// naming the same page form a run whose net change, the sum of o_j - 1 over the run, goes to
+// the page with one atomic, none when it is 0 (a prompt page kept by every row, say). Each
+// page still gets the sum of o_i - 1 over every entry naming it, so the refcounts are those
+// of remap_rows exactly; only the checks (a page id out of range among entries that change
+// it, a refcount taken below zero) are made per run instead of per entry.
+__device__ __forceinline__ void remap_request_runs(const int32_t* in, int32_t* out, const int32_t* anc,
+                                                   const int32_t* off, int32_t N, int32_t P,
+                                                   int32_t* refcount, int32_t num_pages,
+                                                   int32_t* error_flags) {
+    const int64_t NP = (int64_t)N * P;
+    for (int64_t e = threadIdx.x; e < NP; e += blockDim.x) {
+        const int32_t j = (int32_t)(e / P);
+        const int32_t col = (int32_t)(e - (int64_t)j * P);
+        const int32_t src = anc[j];
+        out[e] = src >= 0 ? in[(int64_t)src * P + col] : -1;
+    }
+    constexpr int kRows = 8;   // loads of a column issued together
+    for (int32_t c = threadIdx.x; c < P; c += blockDim.x) {
+        int32_t run_page = -1, run_delta = 0;
+        bool run_moves = false, bad = false, neg = false;
+        auto flush = [&]() {
+            if (run_page >= 0 && run_moves) {
+                if (run_page >= num_pages) {
+                    bad = true;
+                } else if (run_delta != 0) {
+                    const int32_t old = atomicAdd(&refcount[run_page], run_delta);
+                    if (old + run_delta < 0) neg = true;
+                }
+            }
+        };
+        for (int32_t j0 = 0; j0 < N; j0 += kRows) {
+            int32_t pg[kRows];
+#pragma unroll
+            for (int b = 0; b < kRows; ++b) pg[b] = j0 + b < N ? in[(int64_t)(j0 + b) * P + c] : -1;
+#pragma unroll
+            for (int b = 0; b < kRows; ++b) {
+                if (j0 + b >= N) break;
+                if (pg[b] != run_page) {
+                    flush();
+                    run_page = pg[b];
+                    run_delta = 0;
+                    run_moves = false;
+                }
+                const int32_t d = off[j0 + b] - 1;
+                run_delta += d;
+                run_moves = run_moves || d != 0;
+            }
+        }
+        flush();
+        if (bad) flag_error(error_flags, SMCSD_DEVERR_PAGE);
+        if (neg) flag_error(error_flags, SMCSD_DEVERR_REFCOUNT);
+    }
+}
+
 }  // namespace smcsd
