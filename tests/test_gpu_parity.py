@@ -260,6 +260,29 @@ def test_smcsd_resample(N, mode, dev):
                                    rtol=1e-6, atol=1e-6)
 
 
+@pytest.mark.parametrize("N", [16, 128])
+def test_round_remap_with_repeated_pages(N, dev):
+    # Page ids repeated across rows in any order and across columns, some columns one page for
+    # every row. The round's fused remap (one atomic per run of equal pages in a column up to
+    # 64 particles, one per entry above) must still give every page the sum over its entries.
+    w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="repeated-pages", R=3, N=N, K=2, V=3000,
+                                               ctx=1024)
+
+    def tables(inp):
+        R, n, P = inp["page_table"].shape
+        g = torch.Generator().manual_seed(12)
+        pool = 40
+        pt = torch.randint(0, pool, (R, n, P), generator=g, dtype=torch.int32)
+        pt[:, :, :4] = pt[:, :1, :4]                                   # kept by every row
+        pt[torch.rand(R, n, P, generator=g) < 0.1] = -1                # unused entries
+        pt = torch.where(pt >= 0, pt + pool * torch.arange(R, dtype=torch.int32).view(R, 1, 1), pt)
+        rc = torch.bincount(pt[pt >= 0].long(), minlength=R * pool).to(torch.int32)
+        inp["page_table"] = pt.to(dev).contiguous()
+        inp["refcount"] = rc.to(dev).contiguous()
+
+    run_and_compare(w, dev, seed=12, modify=tables)
+
+
 def test_smcsd_remap_pages_and_error_flags(dev):
     R, N, P = 3, 16, 40
     pt, rc, npg = synth.make_page_table(R, N, P, seed=8, ragged=True)
