@@ -209,8 +209,8 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
         // up to 64 particles: one atomic per run of equal pages in a column; more particles
         // would make each column's walk long, so one atomic per entry there
         if (N <= 64)
-            remap_request_runs(a.pt_in + r * NP, a.pt_out + r * NP, s_anc, s_off, N, a.P, a.refcount,
-                               a.num_pages, a.error_flags);
+            remap_columns_runs(a.pt_in + r * NP, a.pt_out + r * NP, s_anc, s_off, N, a.P, 0, a.P,
+                               a.refcount, a.num_pages, a.error_flags);
         else
             remap_rows(a.pt_in + r * NP, a.pt_out + r * NP, s_anc, s_off, a.P, 0, NP, a.refcount,
                        a.num_pages, a.error_flags);

@@ -7,8 +7,9 @@
 //   page_table_out[r][j] = page_table_in[r][ancestors[r][j]]
 //   o_i = #{j : ancestors[r][j] = i};  refcount[page] += o_i - 1 for every valid entry of
 //   old row i with o_i != 1.
-// Rows with o_i == 1 (kept once) cost one copy and no atomic. Integer atomics commute, so
-// the resulting refcounts do not depend on scheduling.
+// Rows with o_i == 1 (kept once) cost one copy and no atomic; up to 64 particles, equal pages
+// in consecutive rows of a column share one atomic. Integer atomics commute, so the
+// resulting refcounts do not depend on scheduling.
 #include "remap_rows.h"
 #include "smcsd_internal.h"
 
@@ -35,6 +36,16 @@ __global__ __launch_bounds__(kThreads) void k_remap(RemapArgs a) {
     __syncthreads();
 
     const int64_t NP = (int64_t)N * P;
+    if (N <= 64) {
+        // up to 64 particles: the request's columns split between its workgroups, one
+        // refcount atomic per run of equal pages in a column (remap_columns_runs)
+        const int32_t per = (P + a.blocks_per_request - 1) / a.blocks_per_request;
+        const int32_t p0 = min(P, part * per);
+        const int32_t p1 = min(P, p0 + per);
+        remap_columns_runs(a.pt_in + r * NP, a.pt_out + r * NP, s_anc, s_off, N, P, p0, p1,
+                           a.refcount, a.num_pages, a.error_flags);
+        return;
+    }
     const int64_t per = (NP + a.blocks_per_request - 1) / a.blocks_per_request;
     const int64_t e0 = (int64_t)part * per;
     const int64_t e1 = min(NP, e0 + per);

@@ -42,19 +42,21 @@ __device__ __forceinline__ void remap_rows(const int32_t* in, int32_t* out, cons
 // page still gets the sum of o_i - 1 over every entry naming it, so the refcounts are those
 // of remap_rows exactly; only the checks (a page id out of range among entries that change
 // it, a refcount taken below zero) are made per run instead of per entry.
-__device__ __forceinline__ void remap_request_runs(const int32_t* in, int32_t* out, const int32_t* anc,
+// Columns [p0, p1) of every row; a request's workgroups can split its columns between them.
+__device__ __forceinline__ void remap_columns_runs(const int32_t* in, int32_t* out, const int32_t* anc,
                                                    const int32_t* off, int32_t N, int32_t P,
-                                                   int32_t* refcount, int32_t num_pages,
-                                                   int32_t* error_flags) {
-    const int64_t NP = (int64_t)N * P;
-    for (int64_t e = threadIdx.x; e < NP; e += blockDim.x) {
-        const int32_t j = (int32_t)(e / P);
-        const int32_t col = (int32_t)(e - (int64_t)j * P);
+                                                   int32_t p0, int32_t p1, int32_t* refcount,
+                                                   int32_t num_pages, int32_t* error_flags) {
+    const int32_t W = p1 - p0;
+    const int64_t NW = (int64_t)N * W;
+    for (int64_t e = threadIdx.x; e < NW; e += blockDim.x) {
+        const int32_t j = (int32_t)(e / W);
+        const int32_t col = p0 + (int32_t)(e - (int64_t)j * W);
         const int32_t src = anc[j];
-        out[e] = src >= 0 ? in[(int64_t)src * P + col] : -1;
+        out[(int64_t)j * P + col] = src >= 0 ? in[(int64_t)src * P + col] : -1;
     }
     constexpr int kRows = 8;   // loads of a column issued together
-    for (int32_t c = threadIdx.x; c < P; c += blockDim.x) {
+    for (int32_t c = p0 + (int32_t)threadIdx.x; c < p1; c += blockDim.x) {
         int32_t run_page = -1, run_delta = 0;
         bool run_moves = false, bad = false, neg = false;
         auto flush = [&]() {
