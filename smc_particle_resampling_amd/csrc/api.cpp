@@ -306,7 +306,7 @@ smcsd_status smcsd_round(const smcsd_round_args* args, smcsd_stream stream) {
     // launch; larger ones (more than 16 entries a thread) keep the separate remap kernel,
     // which spreads a request's table over several workgroups.
     const int64_t table_entries = (int64_t)a.N * a.P;
-    const bool fused_remap = a.page_table_in && table_entries <= 16 * kThreads;
+    const bool fused_remap = a.page_table_in && table_entries <= kFusedRemapEntries;
     if (fused_remap) {
         fa.pt_in = a.page_table_in;
         fa.pt_out = a.page_table_out;

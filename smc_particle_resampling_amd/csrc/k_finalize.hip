@@ -27,24 +27,54 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
     __shared__ int32_t s_off[SMCSD_MAX_N];   // offspring counts o_i
     __shared__ double s_logZ;
     __shared__ int32_t s_rs;
+    __shared__ int32_t s_pt[kFusedRemapEntries];   // the request's input page table
     const int tid = threadIdx.x;
     const int64_t r = blockIdx.x;
     const int32_t N = a.N, K = a.K;
+
+    // The input page table does not depend on this round's ancestors, so its loads (16 a
+    // thread at most) are issued first; they arrive while the weights are computed and go to
+    // LDS, from where the remap at the end reads them instead of waiting on global memory.
+    constexpr int kPtRegs = kFusedRemapEntries / kThreads;
+    const int64_t NP = a.pt_in ? (int64_t)N * a.P : 0;
+    const bool staged = NP > 0 && NP <= kFusedRemapEntries;
+    int32_t ptv[kPtRegs];
+    if (staged) {
+#pragma unroll
+        for (int b = 0; b < kPtRegs; ++b) {
+            const int64_t e = (int64_t)b * kThreads + tid;
+            if (e < NP) ptv[b] = a.pt_in[r * NP + e];
+        }
+    }
 
     if constexpr (FROM_PARTIALS) {
         const float T = a.temperature[r];
         const float c = kLog2e / T;             // the scale the logits pass used
         const double invT = 1.0 / (double)T;
-        // one thread per (particle, position): the position's log p(x) - log q(x) and TV
+        // one thread per (particle, position): the position's log p(x) - log q(x) and TV.
+        // The token, the S slice parts and (with TV) the first 16 float4 of the position's
+        // S * kWaves partials are all loaded before any of them is used, so a thread waits
+        // for memory a few times rather than once per load. Every sum keeps its order.
+        constexpr int kTvRegs = 16;
         for (int32_t ik = tid; ik < N * K; ik += kThreads) {
             const int32_t i = ik / K, k = ik - i * K;
             const int64_t ri = r * N + i;
             const int64_t u = ri * K + k;
+            const int32_t x = a.tokens[u];
+            const PairPart* part = a.pp + u * a.S;
+            PairPart v[kPartRegs];
+            load_parts(part, a.S, v);
+            // the position's block of partials starts at a multiple of 32 floats
+            const float4* tp = reinterpret_cast<const float4*>(a.tvp + u * a.S * kWaves);
+            const int n4 = a.tv ? a.S * kWaves / 4 : 0;
+            float4 tv4[kTvRegs];
+#pragma unroll
+            for (int t = 0; t < kTvRegs; ++t)
+                if (t < n4) tv4[t] = tp[t];
             float Mp, Mq;
             double Sp, Sq;
-            pair_norms(a.pp + u * a.S, a.S, c, Mp, Mq, Sp, Sq);
+            pair_norms_from(part, v, a.S, c, Mp, Mq, Sp, Sq);
             double term = 0.0;
-            const int32_t x = a.tokens[u];
             if (x < 0 || x >= a.V) {
                 flag_error(a.error_flags, SMCSD_DEVERR_TOKEN);
             } else {
@@ -55,35 +85,57 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
             }
             a.terms[u] = term;
             if (a.tv) {
-                // the S * kWaves partials of this position, 16 bytes a load (the block of a
-                // position starts at a multiple of 32 floats)
-                const float4* tp = reinterpret_cast<const float4*>(a.tvp + u * a.S * kWaves);
                 double t2 = 0.0;
-                for (int t = 0; t < a.S * kWaves / 4; ++t) {
-                    const float4 v = tp[t];
-                    t2 += (double)v.x;
-                    t2 += (double)v.y;
-                    t2 += (double)v.z;
-                    t2 += (double)v.w;
+                auto add4 = [&](const float4& f) {
+                    t2 += (double)f.x;
+                    t2 += (double)f.y;
+                    t2 += (double)f.z;
+                    t2 += (double)f.w;
+                };
+#pragma unroll
+                for (int t = 0; t < kTvRegs; ++t)
+                    if (t < n4) add4(tv4[t]);
+                for (int t0 = kTvRegs; t0 < n4; t0 += 8) {
+                    float4 w[8];
+#pragma unroll
+                    for (int b = 0; b < 8; ++b)
+                        if (t0 + b < n4) w[b] = tp[t0 + b];
+#pragma unroll
+                    for (int b = 0; b < 8; ++b)
+                        if (t0 + b < n4) add4(w[b]);
                 }
                 a.tv[u] = (float)fmin(fmax(0.5 * t2, 0.0), 1.0);
             }
         }
+        if (staged) {
+#pragma unroll
+            for (int b = 0; b < kPtRegs; ++b) {
+                const int64_t e = (int64_t)b * kThreads + tid;
+                if (e < NP) s_pt[e] = ptv[b];
+            }
+        }
         // one thread per particle: its bonus token, the best (key, index) over the slices
-        // (none without noise: out_tokens then get -1 in column K)
+        // (none without noise: out_tokens then get -1 in column K); slices in batches of 8
         for (int32_t i = tid; i < N; i += kThreads) {
             if (!a.bp) {
                 s_bonus[i] = -1;
                 continue;
             }
             const BonusPart* bpart = a.bp + (r * N + i) * a.S;
-            float best = bpart[0].key;
-            int32_t besti = bpart[0].idx;
-            for (int t = 1; t < a.S; ++t)
-                if (better(bpart[t].key, bpart[t].idx, best, besti)) {
-                    best = bpart[t].key;
-                    besti = bpart[t].idx;
-                }
+            float best = -INFINITY;
+            int32_t besti = INT32_MAX;
+            for (int t0 = 0; t0 < a.S; t0 += 8) {
+                BonusPart w[8];
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+                    if (t0 + b < a.S) w[b] = bpart[t0 + b];
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+                    if (t0 + b < a.S && (t0 + b == 0 || better(w[b].key, w[b].idx, best, besti))) {
+                        best = w[b].key;
+                        besti = w[b].idx;
+                    }
+            }
             if (besti < 0 || besti >= a.V) besti = 0;   // only if every key was NaN
             a.bonus[r * N + i] = besti;
             s_bonus[i] = besti;
@@ -92,12 +144,27 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
         for (int32_t i = tid; i < N; i += kThreads) {
             const int64_t ri = r * N + i;
             double lw = 0.0;
-            for (int32_t k = 0; k < K; ++k) lw += a.terms[ri * K + k];   // k in order
+            for (int32_t k0 = 0; k0 < K; k0 += 8) {   // k in order, loads in batches of 8
+                double w[8];
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+                    if (k0 + b < K) w[b] = a.terms[ri * K + k0 + b];
+#pragma unroll
+                for (int b = 0; b < 8; ++b)
+                    if (k0 + b < K) lw += w[b];
+            }
             if (a.log_potential) lw += (double)a.log_potential[ri];
             a.log_w_incr[ri] = (float)lw;
             s_l[i] = (double)a.log_weights[ri] + lw;
         }
     } else {
+        if (staged) {
+#pragma unroll
+            for (int b = 0; b < kPtRegs; ++b) {
+                const int64_t e = (int64_t)b * kThreads + tid;
+                if (e < NP) s_pt[e] = ptv[b];
+            }
+        }
         for (int32_t i = tid; i < N; i += kThreads)
             s_l[i] = (double)a.log_weights[r * N + i] + (double)a.log_w_incr[r * N + i];
     }
@@ -196,24 +263,43 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
             if (a.out_tokens) {
                 int32_t* dst = a.out_tokens + (r * N + j) * (K + 1);
                 const int32_t* src = a.tokens + (r * N + anc) * K;
-                for (int32_t k = 0; k < K; ++k) dst[k] = src[k];
+                for (int32_t k0 = 0; k0 < K; k0 += 8) {   // loads of a batch before its stores
+                    int32_t t[8];
+#pragma unroll
+                    for (int b = 0; b < 8; ++b)
+                        if (k0 + b < K) t[b] = src[k0 + b];
+#pragma unroll
+                    for (int b = 0; b < 8; ++b)
+                        if (k0 + b < K) dst[k0 + b] = t[b];
+                }
                 dst[K] = s_bonus[anc];
             }
         }
     }
 
-    // the request's page-table remap, when the round carries a small table
+    // the request's page-table remap, when the round carries a small table (read from LDS
+    // when staged above)
     if (a.pt_in) {
         __syncthreads();
-        const int64_t NP = (int64_t)N * a.P;
+        int32_t* out = a.pt_out + r * NP;
         // up to 64 particles: one atomic per run of equal pages in a column; more particles
         // would make each column's walk long, so one atomic per entry there
-        if (N <= 64)
-            remap_columns_runs(a.pt_in + r * NP, a.pt_out + r * NP, s_anc, s_off, N, a.P, 0, a.P,
-                               a.refcount, a.num_pages, a.error_flags);
-        else
-            remap_rows(a.pt_in + r * NP, a.pt_out + r * NP, s_anc, s_off, a.P, 0, NP, a.refcount,
-                       a.num_pages, a.error_flags);
+        if (staged) {
+            if (N <= 64)
+                remap_columns_runs(s_pt, out, s_anc, s_off, N, a.P, 0, a.P, a.refcount, a.num_pages,
+                                   a.error_flags);
+            else
+                remap_rows(s_pt, out, s_anc, s_off, a.P, 0, NP, a.refcount, a.num_pages,
+                           a.error_flags);
+        } else {
+            const int32_t* in = a.pt_in + r * NP;
+            if (N <= 64)
+                remap_columns_runs(in, out, s_anc, s_off, N, a.P, 0, a.P, a.refcount, a.num_pages,
+                                   a.error_flags);
+            else
+                remap_rows(in, out, s_anc, s_off, a.P, 0, NP, a.refcount, a.num_pages,
+                           a.error_flags);
+        }
     }
 }
 

@@ -13,13 +13,29 @@
 
 namespace smcsd {
 
+// Advances a (row, column) position by one workgroup stride over a table with P columns:
+// dj = stride / P and dc = stride % P, computed once, so no entry needs a 64-bit division.
+__device__ __forceinline__ void step_entry(int32_t& j, int32_t& col, int32_t dj, int32_t dc,
+                                           int32_t P) {
+    j += dj;
+    col += dc;
+    if (col >= P) {
+        col -= P;
+        ++j;
+    }
+}
+
 __device__ __forceinline__ void remap_rows(const int32_t* in, int32_t* out, const int32_t* anc,
                                            const int32_t* off, int32_t P, int64_t e0, int64_t e1,
                                            int32_t* refcount, int32_t num_pages,
                                            int32_t* error_flags) {
-    for (int64_t e = e0 + threadIdx.x; e < e1; e += blockDim.x) {
-        const int32_t j = (int32_t)(e / P);
-        const int32_t col = (int32_t)(e - (int64_t)j * P);
+    if (e0 + threadIdx.x >= e1) return;
+    const int64_t first = e0 + threadIdx.x;
+    int32_t j = (int32_t)(first / P);                 // the only 64-bit division
+    int32_t col = (int32_t)(first - (int64_t)j * P);
+    const int32_t dj = (int32_t)(blockDim.x / (uint32_t)P);
+    const int32_t dc = (int32_t)(blockDim.x - (uint32_t)dj * (uint32_t)P);
+    for (int64_t e = first; e < e1; e += blockDim.x) {
         const int32_t src = anc[j];
         out[e] = src >= 0 ? in[(int64_t)src * P + col] : -1;
         const int32_t page = in[e];            // old row j, column col
@@ -32,6 +48,7 @@ __device__ __forceinline__ void remap_rows(const int32_t* in, int32_t* out, cons
                 if (old + (o - 1) < 0) flag_error(error_flags, SMCSD_DEVERR_REFCOUNT);
             }
         }
+        step_entry(j, col, dj, dc, P);
     }
 }
 
@@ -48,12 +65,31 @@ __device__ __forceinline__ void remap_columns_runs(const int32_t* in, int32_t* o
                                                    int32_t p0, int32_t p1, int32_t* refcount,
                                                    int32_t num_pages, int32_t* error_flags) {
     const int32_t W = p1 - p0;
-    const int64_t NW = (int64_t)N * W;
-    for (int64_t e = threadIdx.x; e < NW; e += blockDim.x) {
-        const int32_t j = (int32_t)(e / W);
-        const int32_t col = p0 + (int32_t)(e - (int64_t)j * W);
-        const int32_t src = anc[j];
-        out[(int64_t)j * P + col] = src >= 0 ? in[(int64_t)src * P + col] : -1;
+    // the table copy, 8 entries a thread at a time: all 8 loads are issued before the stores
+    // (the tables may alias as far as the compiler knows, so it would not reorder them)
+    constexpr int kCopy = 8;
+    if (W > 0) {
+        int32_t j = (int32_t)(threadIdx.x / (uint32_t)W);
+        int32_t col = (int32_t)(threadIdx.x - (uint32_t)j * (uint32_t)W);
+        const int32_t dj = (int32_t)(blockDim.x / (uint32_t)W);
+        const int32_t dc = (int32_t)(blockDim.x - (uint32_t)dj * (uint32_t)W);
+        while (j < N) {
+            int32_t v[kCopy];
+            int64_t at[kCopy];
+#pragma unroll
+            for (int b = 0; b < kCopy; ++b) {
+                at[b] = -1;
+                if (j < N) {
+                    const int32_t src = anc[j];
+                    v[b] = src >= 0 ? in[(int64_t)src * P + p0 + col] : -1;
+                    at[b] = (int64_t)j * P + p0 + col;
+                }
+                step_entry(j, col, dj, dc, W);
+            }
+#pragma unroll
+            for (int b = 0; b < kCopy; ++b)
+                if (at[b] >= 0) out[at[b]] = v[b];
+        }
     }
     constexpr int kRows = 8;   // loads of a column issued together
     for (int32_t c = p0 + (int32_t)threadIdx.x; c < p1; c += blockDim.x) {

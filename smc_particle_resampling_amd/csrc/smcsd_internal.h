@@ -16,6 +16,7 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kStreamCPL = 8;        // 16-byte chunks a lane holds per row of a slice, TV off
 constexpr int kTvCPL = 4;            // ... TV on (its fp32 exponentials stay in registers)
 constexpr int kMaxTvSlices = 64;     // TV exchange: wave 0 reads the 2*S partial words
+constexpr int kFusedRemapEntries = 16 * kThreads;   // tables the finalize kernel remaps
 
 // How one logits row is cut into 16-byte chunks and the chunks into slices, one workgroup
 // per slice. Every slice is non-empty and every chunk has at least one element < V.
@@ -316,20 +317,68 @@ __device__ __forceinline__ double logit_at(const void* base, int64_t row, int64_
 
 // Row maxima and softmax denominators of one row pair from its S slice partials, in slice
 // order: M = max_t m_t, S = sum_t s_t * exp2((m_t - M) * c) accumulated in double.
-__device__ __forceinline__ void pair_norms(const PairPart* part, int S, float c, float& Mp,
-                                           float& Mq, double& Sp, double& Sq) {
+// The first kPartRegs slice parts of a position are loaded together into registers, so a
+// thread has them all in flight at once; slices beyond those are loaded in batches of 8.
+constexpr int kPartRegs = 16;
+
+__device__ __forceinline__ void load_parts(const PairPart* part, int S, PairPart (&v)[kPartRegs]) {
+#pragma unroll
+    for (int t = 0; t < kPartRegs; ++t)
+        if (t < S) v[t] = part[t];
+}
+
+// Row maxima and sums of one position from its S slice parts; v holds the first kPartRegs
+// of them (load_parts). The sums take the slices in order 0..S-1.
+__device__ __forceinline__ void pair_norms_from(const PairPart* part, const PairPart (&v)[kPartRegs],
+                                                int S, float c, float& Mp, float& Mq, double& Sp,
+                                                double& Sq) {
     Mp = -INFINITY;
     Mq = -INFINITY;
-    for (int t = 0; t < S; ++t) {
-        Mp = fmaxf(Mp, part[t].mp);
-        Mq = fmaxf(Mq, part[t].mq);
+#pragma unroll
+    for (int t = 0; t < kPartRegs; ++t)
+        if (t < S) {
+            Mp = fmaxf(Mp, v[t].mp);
+            Mq = fmaxf(Mq, v[t].mq);
+        }
+    for (int t0 = kPartRegs; t0 < S; t0 += 8) {
+        PairPart w[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+            if (t0 + b < S) w[b] = part[t0 + b];
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+            if (t0 + b < S) {
+                Mp = fmaxf(Mp, w[b].mp);
+                Mq = fmaxf(Mq, w[b].mq);
+            }
     }
     Sp = 0.0;
     Sq = 0.0;
-    for (int t = 0; t < S; ++t) {
-        Sp += (double)(part[t].sp * __builtin_amdgcn_exp2f((part[t].mp - Mp) * c));
-        Sq += (double)(part[t].sq * __builtin_amdgcn_exp2f((part[t].mq - Mq) * c));
+#pragma unroll
+    for (int t = 0; t < kPartRegs; ++t)
+        if (t < S) {
+            Sp += (double)(v[t].sp * __builtin_amdgcn_exp2f((v[t].mp - Mp) * c));
+            Sq += (double)(v[t].sq * __builtin_amdgcn_exp2f((v[t].mq - Mq) * c));
+        }
+    for (int t0 = kPartRegs; t0 < S; t0 += 8) {
+        PairPart w[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+            if (t0 + b < S) w[b] = part[t0 + b];
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+            if (t0 + b < S) {
+                Sp += (double)(w[b].sp * __builtin_amdgcn_exp2f((w[b].mp - Mp) * c));
+                Sq += (double)(w[b].sq * __builtin_amdgcn_exp2f((w[b].mq - Mq) * c));
+            }
     }
+}
+
+__device__ __forceinline__ void pair_norms(const PairPart* part, int S, float c, float& Mp,
+                                           float& Mq, double& Sp, double& Sq) {
+    PairPart v[kPartRegs];
+    load_parts(part, S, v);
+    pair_norms_from(part, v, S, c, Mp, Mq, Sp, Sq);
 }
 
 // (key, index) argmax: the larger key wins, the lower index wins on equal keys.
