@@ -33,11 +33,12 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
     const int32_t N = a.N, K = a.K;
 
     // The input page table does not depend on this round's ancestors, so its loads (16 a
-    // thread at most) are issued first; they arrive while the weights are computed and go to
-    // LDS, from where the remap at the end reads them instead of waiting on global memory.
+    // thread at most; launch_finalize takes no larger table) are issued first; they arrive
+    // while the weights are computed and go to LDS, from where the remap at the end reads
+    // them instead of waiting on global memory.
     constexpr int kPtRegs = kFusedRemapEntries / kThreads;
     const int64_t NP = a.pt_in ? (int64_t)N * a.P : 0;
-    const bool staged = NP > 0 && NP <= kFusedRemapEntries;
+    const bool staged = NP > 0;
     int32_t ptv[kPtRegs];
     if (staged) {
 #pragma unroll
@@ -277,29 +278,17 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
         }
     }
 
-    // the request's page-table remap, when the round carries a small table (read from LDS
-    // when staged above)
+    // the request's page-table remap, when the round carries a small table, read from LDS
     if (a.pt_in) {
         __syncthreads();
         int32_t* out = a.pt_out + r * NP;
         // up to 64 particles: one atomic per run of equal pages in a column; more particles
         // would make each column's walk long, so one atomic per entry there
-        if (staged) {
-            if (N <= 64)
-                remap_columns_runs(s_pt, out, s_anc, s_off, N, a.P, 0, a.P, a.refcount, a.num_pages,
-                                   a.error_flags);
-            else
-                remap_rows(s_pt, out, s_anc, s_off, a.P, 0, NP, a.refcount, a.num_pages,
-                           a.error_flags);
-        } else {
-            const int32_t* in = a.pt_in + r * NP;
-            if (N <= 64)
-                remap_columns_runs(in, out, s_anc, s_off, N, a.P, 0, a.P, a.refcount, a.num_pages,
-                                   a.error_flags);
-            else
-                remap_rows(in, out, s_anc, s_off, a.P, 0, NP, a.refcount, a.num_pages,
-                           a.error_flags);
-        }
+        if (N <= 64)
+            remap_columns_runs(s_pt, out, s_anc, s_off, N, a.P, 0, a.P, a.refcount, a.num_pages,
+                               a.error_flags);
+        else
+            remap_rows(s_pt, out, s_anc, s_off, a.P, 0, NP, a.refcount, a.num_pages, a.error_flags);
     }
 }
 
@@ -307,6 +296,8 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
 
 hipError_t launch_finalize(int32_t R, bool from_partials, int32_t dtype, const FinalizeArgs& a,
                            hipStream_t s) {
+    // the page table is staged in LDS: larger ones go to launch_remap instead
+    if (a.pt_in && (int64_t)a.N * a.P > kFusedRemapEntries) return hipErrorInvalidValue;
     const dim3 grid((unsigned)R), block(kThreads);
     if (!from_partials) {
         k_finalize<SMCSD_F32, false><<<grid, block, 0, s>>>(a);
