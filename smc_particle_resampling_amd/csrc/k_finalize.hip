@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
             PairPart v[kPartRegs];
             load_parts(part, a.S, v);
             // the position's block of partials starts at a multiple of 32 floats
-            const float4* tp = reinterpret_cast<const float4*>(a.tvp + u * a.S * kWaves);
+            const float4* tp = a.tv ? reinterpret_cast<const float4*>(a.tvp + u * a.S * kWaves) : nullptr;
             const int n4 = a.tv ? a.S * kWaves / 4 : 0;
             float4 tv4[kTvRegs];
 #pragma unroll
