@@ -116,8 +116,12 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
             }
         }
         // one thread per particle: its bonus token, the best (key, index) over the slices
-        // (none without noise: out_tokens then get -1 in column K); slices in batches of 8
-        for (int32_t i = tid; i < N; i += kThreads) {
+        // (none without noise: out_tokens then get -1 in column K); slices in batches of 8.
+        // When the positions leave enough threads idle, those threads take the particles, so
+        // these loads overlap the ones above.
+        const int32_t boff = N * K + N <= kThreads ? N * K : 0;
+        for (int32_t i = tid - boff; i < N; i += kThreads) {
+            if (i < 0) continue;
             if (!a.bp) {
                 s_bonus[i] = -1;
                 continue;
