@@ -159,7 +159,7 @@ typedef struct smcsd_round_args {
  *   log_w_incr_i = sum_k (a[k,x_k] - A_ik) - (b[k,x_k] - B_ik) (importance weight p/q)
  *                  + log_potential_i                         (if given)
  *   tv_ik = 1/2 sum_v |exp(a[k,v]-A_ik) - exp(b[k,v]-B_ik)|    (METASD block divergence)
- *   bonus_i = argmax_v fl32(fma(target[K,v], fl32(1/T_r), gumbel[v])), lowest v on ties
+ *   bonus_i = argmax_v (target[K,v]/T_r + gumbel[v]), lowest v on equal keys
  *   l_i = log_weights_i + log_w_incr_i, logZ = LSE_i l_i, W_i = exp(l_i - logZ),
  *   ESS = 1/sum W_i^2; resample per `mode`.
  *   Resampled: C = inclusive prefix sum of W (double), U_j = (j+u_r)/N,
@@ -168,7 +168,10 @@ typedef struct smcsd_round_args {
  *   page_table_out[j] = page_table_in[ancestors_j]; for each valid entry page of old row i
  *   with o_i = #{j : ancestors_j = i} != 1: refcount[page] += o_i - 1 (integer atomics).
  * Precision: logits widened exactly to f32, f32 accumulation over v, per-request weight
- * arithmetic and the prefix sum in f64.
+ * arithmetic and the prefix sum in f64. The bonus key is evaluated in binary32 as
+ * fl32(fma(z, fl32(1/T), G)), at most 2^-24 (|z/T| + |key|) from the exact z/T + G; where
+ * the exact top-2 keys of a row lie closer than twice that (< 1e-5 for |key| <= 64), the
+ * token may be the runner-up.
  */
 smcsd_status smcsd_round(const smcsd_round_args *args, smcsd_stream stream);
 
@@ -269,11 +272,12 @@ size_t smcsd_round_args_size(void);
  *   n_accepted_i = k* (or K if all are accepted);
  *   next_token_i = the residual draw at k*: the first v (increasing) whose inclusive prefix
  *   sum of max(p_k* - q_k*, 0) exceeds residual_uniform * sum_v max(p_k* - q_k*, 0);
- *   or, if all K are accepted, the bonus argmax_v fl32(fma(target[K,v], fl32(1/T), gumbel[v])).
+ *   or, if all K are accepted, the bonus argmax_v (target[K,v]/T + gumbel[v]) (keys in
+ *   binary32 as in smcsd_round).
  * The residual mass is the position's TV, so the pass is the TV pass of smcsd_round plus a
  * short kernel that scans one slice of the rejected row per particle.
  * Decisions are taken on f32 logits with f64 per-particle arithmetic; a residual draw whose
- * uniform lies within ~1e-4 of the residual mass from a cumulative-sum boundary may pick the
+ * uniform lies within 1e-5 of the residual mass from a cumulative-sum boundary may pick the
  * neighbouring token. Sizes, layouts, alignment and limits as for smcsd_round with TV on.
  */
 typedef struct smcsd_verify_args {
@@ -314,12 +318,15 @@ size_t smcsd_verify_args_size(void);
  * Gumbel-Top-K: k distinct tokens per row drawn without replacement from softmax(z/T) in one
  * step, as the STAND page describes for drafting (method item 2: add precomputed, cached
  * Gumbel noise to the log-probabilities and keep the indices of the k largest sums).
- *   key_v = fl32(fma(logits[row][v], fl32(1/temperature[row]), gumbel[row][v]))
+ *   key_v = logits[row][v] / temperature[row] + gumbel[row][v], evaluated in binary32 as
+ *           fl32(fma(logits[row][v], fl32(1/temperature[row]), gumbel[row][v]))
  *   out_tokens[row][0..k-1] = the k largest keys' indices, by decreasing key, equal keys by
  *   increasing index; out_keys (optional, NULL) the keys themselves.
  * rows >= 0, 1 <= k <= min(V, SMCSD_MAX_TOPK), V <= SMCSD_MAX_TV_V_* for the dtype; ld and
  * alignment as for smcsd_round (logits and gumbel 16-byte aligned, ld a multiple of 8 for
- * bf16, 4 for f32). Exact (no tolerance): both passes rank the same binary32 keys.
+ * bf16, 4 for f32). The slice and merge passes rank the same binary32 keys, so the result is
+ * the exact ranking of those keys; each is at most 2^-24 (|z/T| + |key|) from the real key,
+ * which bounds how far the order can differ from exact arithmetic in a near tie.
  */
 #define SMCSD_MAX_TOPK 64
 
@@ -338,7 +345,7 @@ size_t smcsd_topk_workspace_size(int32_t rows, int32_t V, int32_t dtype, int32_t
  * section 2) yields K + 1 tokens per particle and round without fixing when the last one is
  * drawn. Here slot j of request r takes the Gumbel-max (STAND page, method item 2, k = 1)
  * of its ancestor's bonus row with its own noise row:
- *   bonus[r][j] = argmax_v fl32(fma(target[r][a][K][v], fl32(1/T_r), gumbel[r][j][v])),
+ *   bonus[r][j] = argmax_v (target[r][a][K][v] / T_r + gumbel[r][j][v]),
  *   a = ancestors[r][j], lowest v on equal keys.
  * Run smcsd_round with gumbel = NULL first (it then skips its own bonus), then this call
  * with the round's ancestors and a fresh noise tensor.
@@ -346,7 +353,7 @@ size_t smcsd_topk_workspace_size(int32_t rows, int32_t V, int32_t dtype, int32_t
  * f32 in; bonus [R][N] out; out_tokens NULL or [R][N][K+1] whose column K receives the
  * bonus. Sizes, dtype, ld and alignment as for smcsd_round. Workspace:
  * smcsd_bonus_workspace_size bytes, 256-byte aligned. An ancestor outside [0, N) gives -1 and
- * sets SMCSD_DEVERR_ANCESTOR. Exact: the same binary32 keys as the in-pass bonus.
+ * sets SMCSD_DEVERR_ANCESTOR. Keys in binary32 as for the in-pass bonus.
  */
 smcsd_status smcsd_bonus_resampled(int32_t R, int32_t N, int32_t K, int32_t V, int64_t ld,
                                    int32_t dtype, const void *target_logits,

@@ -64,9 +64,9 @@ def lib() -> ctypes.CDLL:
                                     p, p, p, p, p, p, p, p, p, i32, i32, p, p, p, p, p, p]
             L.orc_sd_verify.restype = None
             L.orc_sd_verify.argtypes = [i32, i32, i32, i64, i64, i32, p, p, p, p, p, p, p, p,
-                                        p, p, p, p]
+                                        p, p, p, p, p]
             L.orc_gumbel_topk.restype = None
-            L.orc_gumbel_topk.argtypes = [i64, i64, i64, i32, p, p, p, i32, p, p]
+            L.orc_gumbel_topk.argtypes = [i64, i64, i64, i32, p, p, p, i32, p, p, p]
             L.orc_bonus_resampled.restype = i32
             L.orc_bonus_resampled.argtypes = [i32, i32, i32, i64, i64, i32, p, p, p, p, p, p]
             L.orc_pages_advance.restype = i32
@@ -110,7 +110,7 @@ def row_tv(zp: np.ndarray, zq: np.ndarray, T: float) -> float:
 
 
 def row_gumbel_argmax(z: np.ndarray, g: np.ndarray, T: float) -> tuple[int, float]:
-    """(argmax_v fma(z_v, 1/T, g_v) in binary32, top-2 key gap)."""
+    """(argmax_v z_v/T + g_v with keys in double, top-2 key gap)."""
     z, dt = _logits(z.reshape(-1))
     g = np.ascontiguousarray(g.reshape(-1), dtype=np.float32)
     assert g.size == z.size
@@ -211,7 +211,9 @@ def sd_verify(inputs: dict, *, V: int | None = None) -> dict:
 
     ``inputs`` as for ``round`` plus accept_uniform [R,N,K] and residual_uniform [R,N]
     float32. Returns n_accepted [R,N], next_token [R,N] (int32), acc_gap [R,N] (distance
-    of the acceptance uniforms from min(1, p/q)), and for residual draws res_lo / res_hi
+    of the acceptance uniforms from min(1, p/q)), bonus_gap [R,N] (top-2 key gap of the
+    bonus draw where the whole block was accepted, +inf elsewhere), and for residual draws
+    res_lo / res_hi
     [R,N] (distances of the target from the chosen token's cumulative-sum boundaries, as
     fractions of the residual mass) with res_below / res_above [R,N] (the neighbouring
     tokens with positive residual, -1 if none).
@@ -228,12 +230,13 @@ def sd_verify(inputs: dict, *, V: int | None = None) -> dict:
     bu = np.ascontiguousarray(inputs["residual_uniform"], dtype=np.float32)
     assert au.shape == (R, N, K) and bu.shape == (R, N)
     out = dict(n_accepted=np.zeros((R, N), np.int32), next_token=np.zeros((R, N), np.int32),
-               acc_gap=np.zeros((R, N)))
+               acc_gap=np.zeros((R, N)), bonus_gap=np.zeros((R, N)))
     res = np.zeros((R, N, 2))
     nb = np.zeros((R, N, 2), np.int32)
     lib().orc_sd_verify(R, N, K, V, ld, dt, _ptr(tgt), _ptr(dft), _ptr(tok), _ptr(temp),
                         _ptr(gum), _ptr(au), _ptr(bu), _ptr(out["n_accepted"]),
-                        _ptr(out["next_token"]), _ptr(out["acc_gap"]), _ptr(res), _ptr(nb))
+                        _ptr(out["next_token"]), _ptr(out["acc_gap"]), _ptr(res), _ptr(nb),
+                        _ptr(out["bonus_gap"]))
     out["res_lo"], out["res_hi"] = res[..., 0], res[..., 1]
     out["res_below"], out["res_above"] = nb[..., 0], nb[..., 1]
     out["res_gap"] = np.minimum(out["res_lo"], out["res_hi"])
@@ -241,10 +244,12 @@ def sd_verify(inputs: dict, *, V: int | None = None) -> dict:
 
 
 def gumbel_topk(logits: np.ndarray, temperature: np.ndarray, gumbel: np.ndarray, k: int, *,
-                V: int | None = None) -> tuple[np.ndarray, np.ndarray]:
+                V: int | None = None, gaps: bool = False):
     """Gumbel-Top-K of every row: logits [rows, ld] (float32 or bf16 bits as uint16),
     temperature [rows], gumbel [rows, ld] float32. Returns tokens [rows, k] int32 and keys
-    [rows, k] float32, in decreasing key order (equal keys by increasing index)."""
+    [rows, k] float64 (z/T + G in double), in decreasing key order (equal keys by increasing
+    index); with gaps=True also gaps [rows, k], key_j - key_(j+1) (+inf past the last token
+    of the row)."""
     z, dt = _logits(logits)
     rows, ld = z.shape
     V = ld if V is None else int(V)
@@ -254,10 +259,11 @@ def gumbel_topk(logits: np.ndarray, temperature: np.ndarray, gumbel: np.ndarray,
     g = np.ascontiguousarray(gumbel, dtype=np.float32)
     assert temp.shape == (rows,) and g.shape == (rows, ld)
     tok = np.zeros((rows, k), np.int32)
-    key = np.zeros((rows, k), np.float32)
+    key = np.zeros((rows, k), np.float64)
+    gap = np.zeros((rows, k), np.float64)
     lib().orc_gumbel_topk(rows, V, ld, dt, _ptr(z), _ptr(temp), _ptr(g), int(k), _ptr(tok),
-                          _ptr(key))
-    return tok, key
+                          _ptr(key), _ptr(gap))
+    return (tok, key, gap) if gaps else (tok, key)
 
 
 def bonus_resampled(target: np.ndarray, temperature: np.ndarray, ancestors: np.ndarray,

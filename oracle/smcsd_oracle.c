@@ -30,8 +30,9 @@
  *      inclusive prefix sum of the normalised weights, clamped to N-1.
  *   R5 ESS = 1 / sum W_i^2; mode ESS resamples iff ESS < ess_frac * N (strict).
  *   R6 bonus: drawn per original particle from its row K and inherited through the ancestor.
- *   R7 the bonus decision is taken in binary32, key_v = fma(z_v, fl(1/T), G_v) rounded once,
- *      lowest index on ties -- the precision the GPU kernel decides in.
+ *   R7 the bonus key is the real number z_v/T + G_v, evaluated here in double; an exact tie
+ *      goes to the lowest index. The gap between the best and the second-best key is returned
+ *      with every decision, so that a check can tell a clear winner from a near tie.
  *   R8 page table: [N][P] int32 per request, negative = unused; a refcount counts table
  *      entries that reference a page.
  *   R9 potential (optional): the SMC-SD page's section 5 names constrained generation and
@@ -114,16 +115,17 @@ double orc_row_tv(const void *zp, const void *zq, int dtype, int64_t V, double T
  * noise. Adding the row's normaliser to every key changes nothing, so this is argmax of
  * log p(v) + G_v, i.e. one draw from p (STAND page, method item 2: Gumbel noise added to
  * log-probabilities, top-k of the sum, noise precomputed and cached; here k = 1).
- * Decision precision per reading R7. *gap receives key(best) - key(second best).
+ * Keys in double (reading R7), lowest index on an exact tie. *gap receives
+ * key(best) - key(second best), 0 on a tie, +inf when V == 1.
  */
 int32_t orc_row_gumbel_argmax(const void *row, int dtype, const float *g, int64_t V, float T,
                               double *gap)
 {
-    float invT = 1.0f / T;
-    float k1 = -INFINITY, k2 = -INFINITY;
+    const double t = (double)T;
+    double k1 = -INFINITY, k2 = -INFINITY;
     int32_t best = 0;
     for (int64_t v = 0; v < V; ++v) {
-        float key = fmaf(elem_f32(row, dtype, v), invT, g[v]);
+        double key = elem(row, dtype, v) / t + (double)g[v];
         if (key > k1) {
             k2 = k1;
             k1 = key;
@@ -133,7 +135,7 @@ int32_t orc_row_gumbel_argmax(const void *row, int dtype, const float *g, int64_
         }
     }
     if (gap)
-        *gap = (double)k1 - (double)k2;
+        *gap = V > 1 ? k1 - k2 : INFINITY;
     return best;
 }
 
@@ -359,7 +361,7 @@ int32_t orc_round(int32_t R, int32_t N, int32_t K, int64_t V, int64_t ld, int32_
  *      increasing v with one uniform b: the first v whose inclusive prefix sum of the
  *      unnormalised residual exceeds b * sum r (clamped to the last v with r > 0);
  *   S3 if all K tokens are accepted, the next token is the bonus draw from p_K (the Gumbel-max
- *      of the round, reading R7).
+ *      of the round, reading R7); *bonus_gap then receives its top-2 key gap (+inf otherwise).
  * p and q are temperature-scaled softmaxes as in the round (R2). Outputs: *n_acc in 0..K and
  * *next the token that follows the accepted ones. *acc_gap = min over the examined positions
  * of |acc_u[k] - min(1, p/q)|. For a residual draw with target t = b sum r landing in
@@ -371,13 +373,14 @@ static void sd_verify_particle(int32_t K, int64_t V, int64_t ld, int32_t dtype,
                                const char *tgt, const char *dft, const int32_t *tok, float Tf,
                                const float *gumbel, const float *acc_u, float res_u,
                                int32_t *n_acc, int32_t *next, double *acc_gap, double *res,
-                               int32_t *nb)
+                               int32_t *nb, double *bonus_gap)
 {
     const size_t es = esize(dtype);
     const double T = (double)Tf;
     double agap = INFINITY;
     res[0] = res[1] = 1.0;
     nb[0] = nb[1] = -1;
+    *bonus_gap = INFINITY;
     for (int32_t k = 0; k < K; ++k) {
         const char *zp = tgt + (size_t)k * (size_t)ld * es;
         const char *zq = dft + (size_t)k * (size_t)ld * es;
@@ -437,19 +440,21 @@ static void sd_verify_particle(int32_t K, int64_t V, int64_t ld, int32_t dtype,
         return;
     }
     *n_acc = K;
-    *next = orc_row_gumbel_argmax(tgt + (size_t)K * (size_t)ld * es, dtype, gumbel, V, Tf, NULL);
+    *next = orc_row_gumbel_argmax(tgt + (size_t)K * (size_t)ld * es, dtype, gumbel, V, Tf,
+                                  bonus_gap);
     *acc_gap = agap;
 }
 
 /*
  * sd_verify_particle over a batch: R requests x N particles, each an independent sequence.
- * Layouts as in orc_round; acc_u [R][N][K], res_u [R][N]; outputs [R][N], res and nb [R][N][2].
+ * Layouts as in orc_round; acc_u [R][N][K], res_u [R][N]; outputs [R][N], res and nb [R][N][2],
+ * bonus_gap [R][N].
  */
 void orc_sd_verify(int32_t R, int32_t N, int32_t K, int64_t V, int64_t ld, int32_t dtype,
                    const void *target, const void *draft, const int32_t *tokens,
                    const float *temperature, const float *gumbel, const float *acc_u,
                    const float *res_u, int32_t *n_acc, int32_t *next, double *acc_gap,
-                   double *res, int32_t *nb)
+                   double *res, int32_t *nb, double *bonus_gap)
 {
     const size_t es = esize(dtype);
 #pragma omp parallel for schedule(dynamic, 1)
@@ -460,7 +465,8 @@ void orc_sd_verify(int32_t R, int32_t N, int32_t K, int64_t V, int64_t ld, int32
                            (const char *)draft + (size_t)(ri * K) * (size_t)ld * es,
                            tokens + (size_t)ri * K, temperature[r], gumbel + (size_t)ri * ld,
                            acc_u + (size_t)ri * K, res_u[ri], &n_acc[ri], &next[ri],
-                           &acc_gap[ri], res + 2 * (size_t)ri, nb + 2 * (size_t)ri);
+                           &acc_gap[ri], res + 2 * (size_t)ri, nb + 2 * (size_t)ri,
+                           &bonus_gap[ri]);
     }
 }
 
@@ -468,12 +474,13 @@ void orc_sd_verify(int32_t R, int32_t N, int32_t K, int64_t V, int64_t ld, int32
  * Gumbel-Top-K: k distinct tokens drawn without replacement from softmax(z/T) in one step,
  * as the STAND page describes for drafting (method item 2: add Gumbel noise to the
  * log-probabilities and keep the indices of the k largest sums; the noise is precomputed and
- * cached). Keys are taken in binary32 exactly as for the bonus token (reading R7),
- * key_v = fl32(fma(z_v, fl32(1/T), G_v)); the k tokens come out in decreasing key order,
- * equal keys in increasing index. out_keys may be NULL. k <= V.
+ * cached). Keys as for the bonus token (reading R7), key_v = z_v/T + G_v in double; the k
+ * tokens come out in decreasing key order, equal keys in increasing index. out_keys and
+ * out_gaps ([rows][k], may be NULL) receive the keys and, for rank j, key_j - key_(j+1), the
+ * gap to the next rank (+inf after the last token when k == V). k <= V.
  */
 typedef struct {
-    float key;
+    double key;
     int32_t idx;
 } orc_kv;
 
@@ -489,17 +496,17 @@ static int kv_order(const void *a, const void *b)
 
 void orc_gumbel_topk(int64_t rows, int64_t V, int64_t ld, int32_t dtype, const void *logits,
                      const float *temperature, const float *gumbel, int32_t k,
-                     int32_t *out_tokens, float *out_keys)
+                     int32_t *out_tokens, double *out_keys, double *out_gaps)
 {
     const size_t es = esize(dtype);
 #pragma omp parallel for schedule(dynamic, 1)
     for (int64_t r = 0; r < rows; ++r) {
         const char *z = (const char *)logits + (size_t)r * (size_t)ld * es;
         const float *g = gumbel + (size_t)r * (size_t)ld;
-        float invT = 1.0f / temperature[r];
+        const double t = (double)temperature[r];
         orc_kv *kv = malloc(sizeof(orc_kv) * (size_t)V);
         for (int64_t v = 0; v < V; ++v) {
-            kv[v].key = fmaf(elem_f32(z, dtype, v), invT, g[v]);
+            kv[v].key = elem(z, dtype, v) / t + (double)g[v];
             kv[v].idx = (int32_t)v;
         }
         qsort(kv, (size_t)V, sizeof(orc_kv), kv_order);
@@ -507,6 +514,8 @@ void orc_gumbel_topk(int64_t rows, int64_t V, int64_t ld, int32_t dtype, const v
             out_tokens[(size_t)r * k + j] = kv[j].idx;
             if (out_keys)
                 out_keys[(size_t)r * k + j] = kv[j].key;
+            if (out_gaps)
+                out_gaps[(size_t)r * k + j] = j + 1 < V ? kv[j].key - kv[j + 1].key : INFINITY;
         }
         free(kv);
     }

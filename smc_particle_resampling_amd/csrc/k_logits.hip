@@ -548,8 +548,12 @@ __device__ void pair_slice_tv(const LogitsArgs& a, uint32_t u, int s, int64_t ne
         const float4 wpv = lane < kWaves ? sh.wpart[lane] : make_float4(-INFINITY, 0.0f, -INFINITY, 0.0f);
         const float mp = readlane_f32(row_max(wpv.x), 0);
         const float mq = readlane_f32(row_max(wpv.z), 0);
-        const float sp = readlane_f32(row_sum(wpv.y * __builtin_amdgcn_exp2f((wpv.x - mp) * c)), 0);
-        const float sq = readlane_f32(row_sum(wpv.w * __builtin_amdgcn_exp2f((wpv.z - mq) * c)), 0);
+        // a wave whose share is all -inf holds (-inf, 0): it adds 0, also when the whole slice
+        // is -inf (mp = -inf would make its scale exp2(NaN))
+        const float sp = readlane_f32(
+            row_sum(wpv.x == -INFINITY ? 0.0f : wpv.y * __builtin_amdgcn_exp2f((wpv.x - mp) * c)), 0);
+        const float sq = readlane_f32(
+            row_sum(wpv.z == -INFINITY ? 0.0f : wpv.w * __builtin_amdgcn_exp2f((wpv.z - mq) * c)), 0);
         uint64_t* words = reinterpret_cast<uint64_t*>(a.pp + (size_t)u * a.S);
         if (lane == 0) {
             __hip_atomic_store(words + 2 * s, pack2(mp, sp), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -657,8 +661,12 @@ __device__ void pair_slice_stream(const LogitsArgs& a, int64_t u, int s, float4*
         const float4 wpv = lane < kWaves ? wpart[lane] : make_float4(-INFINITY, 0.0f, -INFINITY, 0.0f);
         const float mp = readlane_f32(row_max(wpv.x), 0);
         const float mq = readlane_f32(row_max(wpv.z), 0);
-        const float sp = readlane_f32(row_sum(wpv.y * __builtin_amdgcn_exp2f((wpv.x - mp) * c)), 0);
-        const float sq = readlane_f32(row_sum(wpv.w * __builtin_amdgcn_exp2f((wpv.z - mq) * c)), 0);
+        // a wave whose share is all -inf holds (-inf, 0): it adds 0, also when the whole slice
+        // is -inf (mp = -inf would make its scale exp2(NaN))
+        const float sp = readlane_f32(
+            row_sum(wpv.x == -INFINITY ? 0.0f : wpv.y * __builtin_amdgcn_exp2f((wpv.x - mp) * c)), 0);
+        const float sq = readlane_f32(
+            row_sum(wpv.z == -INFINITY ? 0.0f : wpv.w * __builtin_amdgcn_exp2f((wpv.z - mq) * c)), 0);
         if (lane == 0) a.pp[u * a.S + s] = PairPart{mp, sp, mq, sq};
     }
 }

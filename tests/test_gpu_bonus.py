@@ -4,7 +4,8 @@ C ABI) against the oracle, and of the round run without in-pass noise.
 The SMC-SD page (section 2) yields K + 1 tokens per particle and round without fixing when
 the last one is drawn; this reading draws it per new slot from the ancestor's bonus row with
 the slot's own noise row, by the Gumbel-max key of the STAND page (method item 2, k = 1).
-Both sides rank the same binary32 keys, so tokens must match bit for bit.
+Tokens are compared bit for bit wherever the oracle's top-2 gap of the exact key z/T + G is
+>= 1e-5; in a nearer tie the GPU's token must be a valid winner (tests/parity.py).
 """
 import sys
 
@@ -76,9 +77,11 @@ def test_bonus_resampled_matches_oracle(w, dev):
     o = oracle.bonus_resampled(_host(inp["target"]), _host(inp["temperature"]), _host(anc),
                                _host(noise), V=w.V)
     assert o["status"] == 0
-    bad = np.argwhere(g != o["bonus"])
-    assert bad.size == 0, "bonus mismatches at %s (gap %s)" % (bad[:5].tolist(),
-                                                              o["gap"][tuple(bad[:5].T)])
+    h = _host(inp["target"])
+    rows = h[np.arange(w.R)[:, None], _host(anc), w.K]              # ancestor's bonus row
+    st = parity.check_bonus("bonus", g, o["bonus"], o["gap"], rows, _host(noise),
+                            np.broadcast_to(_host(inp["temperature"])[:, None], g.shape), w.V)
+    _say("  bonus", st)
     ot = out_tok.cpu().numpy()
     assert np.array_equal(ot[:, :, w.K], g) and (ot[:, :, :w.K] == -5).all()
     _say("  ok")
@@ -94,7 +97,14 @@ def test_out_of_range_ancestor_is_flagged(dev):
     assert flags == smcsd.DEVERR_ANCESTOR
     o = oracle.bonus_resampled(_host(inp["target"]), _host(inp["temperature"]), _host(anc),
                                _host(inp["gumbel"]), V=w.V)
-    assert o["status"] == -1 and np.array_equal(g, o["bonus"]) and g[1, 3] == -1 and g[0, 0] == -1
+    assert o["status"] == -1 and g[1, 3] == -1 and g[0, 0] == -1
+    ok = (anc.cpu().numpy() >= 0) & (anc.cpu().numpy() < w.N)
+    h = _host(inp["target"])
+    a = np.clip(_host(anc), 0, w.N - 1)
+    rows = h[np.arange(w.R)[:, None], a, w.K]
+    T = np.broadcast_to(_host(inp["temperature"])[:, None], g.shape)
+    parity.check_bonus("bonus", g[ok], o["bonus"][ok], o["gap"][ok], rows[ok],
+                       _host(inp["gumbel"])[ok], T[ok], w.V)
 
 
 @pytest.mark.parametrize("tv", [False, True])
@@ -153,7 +163,10 @@ def test_round_then_bonus_after_resampling(mode, dev):
     assert np.array_equal(anc, ora["ancestors"])
     ob = oracle.bonus_resampled(host["target"], host["temperature"], ora["ancestors"],
                                 _host(noise), V=w.V)
-    assert np.array_equal(out["bonus"].cpu().numpy(), ob["bonus"])
+    gb = out["bonus"].cpu().numpy()
+    rows = host["target"][np.arange(w.R)[:, None], anc, w.K]
+    parity.check_bonus("bonus", gb, ob["bonus"], ob["gap"], rows, _host(noise),
+                       np.broadcast_to(host["temperature"][:, None], gb.shape), w.V)
     drafted = host["tokens"][np.arange(w.R)[:, None], anc]          # [R, N, K]
-    want = np.concatenate([drafted, ob["bonus"][:, :, None]], axis=2)
+    want = np.concatenate([drafted, gb[:, :, None]], axis=2)
     assert np.array_equal(out["out_tokens"].cpu().numpy(), want)

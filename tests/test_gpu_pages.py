@@ -291,8 +291,12 @@ def test_multi_round_driver(mode, rounds, seed, token_rows, dev):
         anc = out["ancestors"].cpu().numpy()
         assert np.array_equal(anc, ora["ancestors"])
         assert np.array_equal(out["resampled"].cpu().numpy(), ora["resampled"])
-        assert np.array_equal(out["bonus"].cpu().numpy(), ora["bonus"])
-        parity._close("log_weights", g_lw.cpu().numpy(), ora["log_weights"], parity.REL, floor=True)
+        gb = out["bonus"].cpu().numpy()
+        parity.check_bonus("bonus", gb, ora["bonus"], ora["bonus_gap"], host["target"][:, :, w.K],
+                           host["gumbel"], np.broadcast_to(host["temperature"][:, None], gb.shape),
+                           w.V)
+        parity._close("log_weights", g_lw.cpu().numpy(), ora["log_weights"], parity.REL,
+                      2 * parity.abs_lw(w.K))
         assert np.array_equal(remapped.cpu().numpy(), ora["page_table"])
         resampled_rounds += int(ora["resampled"].sum())
 

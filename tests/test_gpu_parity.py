@@ -2,10 +2,9 @@
 inputs, element by element, to the bar in tests/parity.py.
 
 Sizes: every workload scaled down so the oracle finishes in seconds while still spanning
-several slices per row and a ragged last chunk; the full-size workloads, with the oracle
-on sampled requests where a full oracle round would take minutes; and the edge cases
-(V = 1, V not a multiple of 8, N = 1, N at its maximum, K = 1, empty batch, p == q,
-every resample mode, out-of-range ids).
+several slices per row and a ragged last chunk; every workload at full size, every request
+compared; and the edge cases (V = 1, V not a multiple of 8, N = 1, N at its maximum, K = 1,
+empty batch, p == q, every resample mode, masked vocabulary ranges, out-of-range ids).
 """
 import math
 import sys
@@ -161,6 +160,26 @@ def test_all_negative_logits(tv, dev):
 
 
 @pytest.mark.parametrize("tv", [True, False])
+def test_masked_vocabulary_range(tv, dev):
+    # the first half of every target and draft row is -inf (a masked range covering whole
+    # slices): those slices add nothing, and nothing becomes NaN; drafted tokens lie in the
+    # unmasked half
+    w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="masked", R=2, N=4, K=3, V=40000, ctx=64,
+                                               tv=tv)
+
+    def mask(inp):
+        inp["target"][..., : w.V // 2] = float("-inf")
+        inp["draft"][..., : w.V // 2] = float("-inf")
+        g = torch.Generator(device=dev)
+        g.manual_seed(3)
+        inp["tokens"].copy_(torch.randint(w.V // 2, w.V, inp["tokens"].shape, generator=g,
+                                          device=dev, dtype=torch.int32))
+
+    _, _, _, gpu = run_and_compare(w, dev, seed=12, modify=mask)
+    assert np.all(np.isfinite(gpu["log_w_incr"])) and np.all(gpu["bonus"] >= w.V // 2)
+
+
+@pytest.mark.parametrize("tv", [True, False])
 def test_row_max_at_every_chunk_position(tv, dev):
     # a +200 spike (its exp overflows unless the slice max sees it) at each of the 8 element
     # positions of a 16-byte chunk, in different rows, plus one at the row's last element
@@ -192,10 +211,11 @@ def test_full_size_workloads(name, dev):
     run_and_compare(W[name], dev, seed=0)
 
 
-@pytest.mark.parametrize("name,requests", [("r64-n32-k8-v128256-bf16-tv", [0, 37, 63]),
-                                           ("r32-n32-k8-v256000-bf16-tv-mixT", [0, 13, 31])])
-def test_full_size_sampled_requests(name, requests, dev):
-    _, _, ora, gpu = run_and_compare(W[name], dev, seed=0, requests=requests)
+@pytest.mark.parametrize("name", ["r64-n32-k8-v128256-bf16-tv", "r32-n32-k8-v256000-bf16-tv-mixT"])
+def test_full_size_tv_workloads(name, dev):
+    """Every request of the two TV workloads at full size, in the launch configuration the
+    benchmark times (persistent grid over all row pairs, every temperature switch)."""
+    _, _, ora, gpu = run_and_compare(W[name], dev, seed=0)
     assert gpu["tv"].min() >= 0 and gpu["tv"].max() <= 1
 
 
@@ -258,6 +278,36 @@ def test_smcsd_resample(N, mode, dev):
         assert np.array_equal(d["ancestors"][r].cpu().numpy()[safe], ref["ancestors"][safe])
         np.testing.assert_allclose(d["log_weights"][r].cpu().numpy(), ref["log_weights"],
                                    rtol=1e-6, atol=1e-6)
+
+
+@pytest.mark.parametrize("frac,resampled", [(0.25, 0), (0.25 + 2.0 ** -20, 1)])
+def test_smcsd_resample_ess_exactly_at_threshold(frac, resampled, dev):
+    """N = 8, two particles at log weight 0 and six at -1e4: W = (1/2, 1/2, 0, ...) exactly and
+    ESS = 2 exactly. With ess_frac = 0.25 the threshold is 2 and the strict ESS < 2 keeps the
+    weights; a threshold a hair above 2 resamples (each survivor duplicated 4 times)."""
+    R, N = 3, 8
+    lw = torch.full((R, N), -1e4)
+    lw[:, 2] = 0.0
+    lw[:, 5] = 0.0
+    prev = torch.full((R, N), -math.log(N))
+    u = torch.tensor([0.0, 0.3, 0.999])
+    d = dict(log_w_incr=lw.to(dev), log_weights=prev.clone().to(dev), uniform=u.to(dev),
+             log_norm=torch.empty(R, device=dev), ess=torch.empty(R, device=dev),
+             resampled=torch.empty(R, dtype=torch.int32, device=dev),
+             ancestors=torch.empty(R, N, dtype=torch.int32, device=dev))
+    smcsd.smcsd_resample(**d, mode="ess", ess_frac=frac)
+    torch.cuda.synchronize()
+    assert torch.all(d["ess"].cpu() == 2.0)
+    assert torch.all(d["resampled"].cpu() == resampled)
+    for r in range(R):
+        ref = oracle.resample_request(lw[r].double().numpy(), prev[r].double().numpy(),
+                                      float(u[r]), "ess", frac)
+        assert ref["ess"] == 2.0 and ref["resampled"] == resampled
+        assert np.array_equal(d["ancestors"][r].cpu().numpy(), ref["ancestors"])
+        np.testing.assert_allclose(d["log_weights"][r].cpu().numpy(), ref["log_weights"],
+                                   rtol=1e-6, atol=1e-6)
+    if resampled:
+        assert np.array_equal(d["ancestors"][0].cpu().numpy(), [2] * 4 + [5] * 4)
 
 
 @pytest.mark.parametrize("N,ctx", [(16, 1024), (128, 1024), (32, 3200), (128, 4096), (100, 1600),

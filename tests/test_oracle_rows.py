@@ -156,6 +156,23 @@ def test_gumbel_noise_sign_and_temperature():
     assert oracle.row_gumbel_argmax(z, g, 0.25)[0] == 1
 
 
+def test_gumbel_keys_are_exact_not_binary32():
+    # key = z/T + G as a real number. z = 1 at T = 3 gives 1/3; token 1 has no logit and noise
+    # fl32(1/3) = 1/3 + 9.93e-9. Exactly, token 1 is larger by 9.93e-9; a binary32 key
+    # fma(z, fl32(1/T), G) would make the two equal (and pick token 0 by the tie rule).
+    g1 = np.float32(1.0) / np.float32(3.0)
+    z = np.array([1.0, 0.0], np.float32)
+    g = np.array([0.0, g1], np.float32)
+    idx, gap = oracle.row_gumbel_argmax(z, g, 3.0)
+    assert idx == 1
+    assert gap == pytest.approx(float(g1) - 1.0 / 3.0, rel=1e-6) and 9e-9 < gap < 1.1e-8
+    # the gap is the distance to the runner-up, +inf with one token
+    assert oracle.row_gumbel_argmax(np.array([4.0, 1.0, 2.5], np.float32),
+                                    np.zeros(3, np.float32), 0.5)[1] == pytest.approx(3.0)
+    assert oracle.row_gumbel_argmax(np.array([4.0], np.float32), np.zeros(1, np.float32),
+                                    1.0)[1] == float("inf")
+
+
 def test_gumbel_max_draws_follow_target_softmax():
     # The bonus token is a draw from p = softmax(z/T): chi-square over many noise rows.
     rng = np.random.default_rng(7)

@@ -16,18 +16,40 @@ import oracle
 
 
 def test_zero_noise_is_sorted_keys():
+    # With G = 0 the key is z/T and T > 0, so the k tokens are numpy's stable descending order
+    # of z whatever T is, and their keys are z/T.
     rng = np.random.default_rng(0)
     rows, V, k = 40, 257, 17
     z = rng.normal(0, 2, (rows, V)).astype(np.float32)
     z[:, 10:20] = z[:, 10:11]                       # ties on purpose
     T = rng.choice([0.6, 1.0, 1.7], rows).astype(np.float32)
-    tok, key = oracle.gumbel_topk(z, T, np.zeros_like(z), k)
-    invT = (np.float32(1.0) / T).astype(np.float32)
-    keys = (z.astype(np.float64) * invT[:, None].astype(np.float64)).astype(np.float32)
+    tok, key, gap = oracle.gumbel_topk(z, T, np.zeros_like(z), k, gaps=True)
     for r in range(rows):
-        order = np.lexsort((np.arange(V), -keys[r].astype(np.float64)))[:k]
+        order = np.lexsort((np.arange(V), -z[r]))[:k]
         assert np.array_equal(tok[r], order)
-        assert np.array_equal(key[r], keys[r][order])
+        np.testing.assert_allclose(key[r], z[r][order].astype(np.float64) / float(T[r]),
+                                   rtol=1e-15, atol=0)
+        nxt = np.lexsort((np.arange(V), -z[r]))[k]
+        np.testing.assert_allclose(gap[r][-1], (float(z[r][order[-1]]) - float(z[r][nxt])) / float(T[r]),
+                                   rtol=1e-12, atol=1e-15)
+
+
+def test_gaps_are_the_distance_to_the_next_rank():
+    rng = np.random.default_rng(4)
+    rows, V = 20, 50
+    z = rng.normal(0, 1, (rows, V)).astype(np.float32)
+    g = rng.gumbel(size=(rows, V)).astype(np.float32)
+    T = np.full(rows, 0.7, np.float32)
+    tok, key, gap = oracle.gumbel_topk(z, T, g, V, gaps=True)   # the whole row: k == V
+    assert np.array_equal(gap[:, :-1], key[:, :-1] - key[:, 1:])
+    assert np.all(np.isinf(gap[:, -1]))
+    assert np.all(gap >= 0)
+    for r in range(rows):
+        assert sorted(tok[r].tolist()) == list(range(V))
+    # the first rank's gap is the bonus draw's top-2 gap
+    for r in range(rows):
+        idx, g2 = oracle.row_gumbel_argmax(z[r], g[r], 0.7)
+        assert idx == tok[r, 0] and g2 == gap[r, 0]
 
 
 def test_k1_is_gumbel_max():
