@@ -48,7 +48,8 @@ typedef enum smcsd_status {
     SMCSD_ERR_ARG = 1,         /* null, out-of-range or inconsistent argument */
     SMCSD_ERR_UNSUPPORTED = 2, /* valid request beyond this build's limits (see below) */
     SMCSD_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than smcsd_workspace_size() */
-    SMCSD_ERR_DEVICE = 4       /* a HIP launch or runtime call failed */
+    SMCSD_ERR_DEVICE = 4,      /* a HIP launch or runtime call failed */
+    SMCSD_ERR_SCRATCH = 5      /* smcsd_round_noalloc: more than SMCSD_NOALLOC_SCRATCH_BYTES */
 } smcsd_status;
 
 typedef enum smcsd_dtype { SMCSD_F32 = 0, SMCSD_BF16 = 1 } smcsd_dtype;
@@ -174,6 +175,24 @@ typedef struct smcsd_round_args {
  * token may be the runner-up.
  */
 smcsd_status smcsd_round(const smcsd_round_args *args, smcsd_stream stream);
+
+/*
+ * smcsd_round for callers that cannot allocate device memory: code under HIP graph capture,
+ * tight serving loops, harnesses that forbid hipMalloc. Same arguments, definitions and
+ * results (bit for bit) as smcsd_round, except that args->workspace must be NULL and
+ * args->workspace_bytes 0: the workspace is a static device buffer inside the library,
+ * SMCSD_NOALLOC_SCRATCH_BYTES on every GPU the library runs on, held until the process ends.
+ * A request whose smcsd_workspace_size() exceeds that returns SMCSD_ERR_SCRATCH (validated
+ * on the host, before anything is enqueued). The first call on a device looks up that
+ * device's copy of the buffer (with the device current); no call allocates or frees memory.
+ * Every call on one GPU uses the same buffer, and it keeps the last call's contents: nothing
+ * in it needs to start at zero, because each round re-initialises what it reads (the TV
+ * exchange slots by a fill kernel on the stream). Calls that overlap in time on one GPU
+ * (different streams or host threads) race on the buffer; the caller must order them.
+ */
+#define SMCSD_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+smcsd_status smcsd_round_noalloc(const smcsd_round_args *args, smcsd_stream stream);
 
 /*
  * Normalise, ESS, resample decision and systematic resampling alone, from given per-particle

@@ -75,7 +75,9 @@ static bool overlap(const void* a, size_t na, const void* b, size_t nb) {
     return x < y + nb && y < x + na;
 }
 
-static smcsd_status check_round(const smcsd_round_args* a, Plan* plan) {
+// Validates a round's arguments and makes its plan. The workspace fields are checked too
+// unless the caller brings its own buffer (check_workspace false). No HIP call.
+smcsd_status check_round(const smcsd_round_args* a, Plan* plan, bool check_workspace) {
     if (!a) return SMCSD_ERR_ARG;
     if (a->R < 0 || a->N < 1 || a->K < 1 || a->V < 1 || a->reserved0 != 0) return SMCSD_ERR_ARG;
     if (a->dtype != SMCSD_F32 && a->dtype != SMCSD_BF16) return SMCSD_ERR_ARG;
@@ -101,8 +103,10 @@ static smcsd_status check_round(const smcsd_round_args* a, Plan* plan) {
     }
     if (!make_plan(a->R, a->N, a->K, a->V, a->ld, a->dtype, a->tv != nullptr, plan))
         return SMCSD_ERR_UNSUPPORTED;
-    if (!a->workspace || a->workspace_bytes < plan->bytes) return SMCSD_ERR_WORKSPACE;
-    if (reinterpret_cast<uintptr_t>(a->workspace) & 255u) return SMCSD_ERR_WORKSPACE;
+    if (check_workspace) {
+        if (!a->workspace || a->workspace_bytes < plan->bytes) return SMCSD_ERR_WORKSPACE;
+        if (reinterpret_cast<uintptr_t>(a->workspace) & 255u) return SMCSD_ERR_WORKSPACE;
+    }
     if (!a->gumbel) {                       // the logits pass reads no bonus row
         plan->bonus_rows = 0;
         plan->total_wgs = plan->pair_wgs;
@@ -217,6 +221,7 @@ const char* smcsd_status_string(smcsd_status s) {
     case SMCSD_ERR_UNSUPPORTED: return "unsupported size";
     case SMCSD_ERR_WORKSPACE: return "workspace missing, too small or misaligned";
     case SMCSD_ERR_DEVICE: return "HIP launch or runtime error";
+    case SMCSD_ERR_SCRATCH: return "request needs more than the library's static scratch buffer";
     }
     return "unknown status";
 }
@@ -232,11 +237,17 @@ size_t smcsd_workspace_size(int32_t R, int32_t N, int32_t K, int32_t V, int32_t 
 
 smcsd_status smcsd_round(const smcsd_round_args* args, smcsd_stream stream) {
     Plan plan;
-    const smcsd_status st = check_round(args, &plan);
+    const smcsd_status st = check_round(args, &plan, true);
     if (st != SMCSD_OK || args->R == 0) return st;
-    const smcsd_round_args& a = *args;
-    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
-    char* ws = static_cast<char*>(a.workspace);
+    return enqueue_round(*args, plan, static_cast<char*>(args->workspace),
+                         reinterpret_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"
+
+namespace smcsd {
+
+smcsd_status enqueue_round(const smcsd_round_args& a, const Plan& plan, char* ws, hipStream_t s) {
 
     LogitsArgs la{};
     la.target = a.target_logits;
@@ -332,6 +343,10 @@ smcsd_status smcsd_round(const smcsd_round_args* args, smcsd_stream stream) {
     }
     return SMCSD_OK;
 }
+
+}  // namespace smcsd
+
+extern "C" {
 
 smcsd_status smcsd_resample(int32_t R, int32_t N, const float* log_w_incr, float* log_weights,
                             const float* uniform, int32_t mode, float ess_frac,

@@ -58,6 +58,12 @@ struct BonusPart {
 bool make_plan(int32_t R, int32_t N, int32_t K, int32_t V, int64_t ld, int32_t dtype, bool tv,
                Plan* p);
 
+// smcsd_round in two steps: host validation (no HIP call; the workspace fields are skipped
+// when check_workspace is false), then the launch sequence with its workspace at ws
+// (plan.bytes bytes, 256-byte aligned). R must be > 0 for enqueue_round.
+smcsd_status check_round(const smcsd_round_args* a, Plan* plan, bool check_workspace);
+smcsd_status enqueue_round(const smcsd_round_args& a, const Plan& plan, char* ws, hipStream_t s);
+
 // Arguments of the logits pass, passed by value.
 struct LogitsArgs {
     const void* target;

@@ -19,7 +19,8 @@ if not os.path.exists(_LIB_PATH):
                       "`python -m smc_particle_resampling_amd.build`" % _LIB_PATH)
 _lib = ctypes.CDLL(_LIB_PATH)
 
-OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE = 0, 1, 2, 3, 4
+OK, ERR_ARG, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_DEVICE, ERR_SCRATCH = 0, 1, 2, 3, 4, 5
+NOALLOC_SCRATCH_BYTES = 16 << 20
 F32, BF16 = 0, 1
 RESAMPLE_ALWAYS, RESAMPLE_ESS, RESAMPLE_NEVER = 0, 1, 2
 MODES = {"always": RESAMPLE_ALWAYS, "ess": RESAMPLE_ESS, "never": RESAMPLE_NEVER}
@@ -58,6 +59,8 @@ class VerifyArgs(ctypes.Structure):
 
 _lib.smcsd_round.restype = _i32
 _lib.smcsd_round.argtypes = [ctypes.POINTER(RoundArgs), _p]
+_lib.smcsd_round_noalloc.restype = _i32
+_lib.smcsd_round_noalloc.argtypes = [ctypes.POINTER(RoundArgs), _p]
 _lib.smcsd_resample.restype = _i32
 _lib.smcsd_resample.argtypes = [_i32, _i32, _p, _p, _p, _i32, _f32, _p, _p, _p, _p, _p]
 _lib.smcsd_remap_pages.restype = _i32
@@ -162,14 +165,33 @@ def _stream(device, stream):
     return torch.cuda.current_stream(device).cuda_stream
 
 
-def smcsd_round(*, target_logits, draft_logits, draft_tokens, temperature, gumbel, uniform,
+def smcsd_round(*, workspace, stream=None, **kw) -> None:
+    """Enqueue one SMC-SD round (smcsd_round). Shapes: target [R,N,K+1,ld], draft
+    [R,N,K,ld] (both float32 or bfloat16), draft_tokens [R,N,K] int32, temperature [R],
+    gumbel [R,N,ld], uniform [R], per-request/per-particle outputs as in include/smcsd.h;
+    workspace a uint8 device tensor of at least smcsd_workspace_size() bytes."""
+    a, dev = _round_args(workspace=workspace, **kw)
+    st = _lib.smcsd_round(ctypes.byref(a), _stream(dev, stream))
+    if st != OK:
+        raise SmcsdError(st, "smcsd_round")
+
+
+def smcsd_round_noalloc(*, stream=None, **kw) -> None:
+    """smcsd_round without a workspace argument (smcsd_round_noalloc): the library's static
+    per-GPU scratch buffer serves as the workspace, and the call allocates nothing. Same
+    arguments as smcsd_round except ``workspace``."""
+    a, dev = _round_args(workspace=None, **kw)
+    st = _lib.smcsd_round_noalloc(ctypes.byref(a), _stream(dev, stream))
+    if st != OK:
+        raise SmcsdError(st, "smcsd_round_noalloc")
+
+
+def _round_args(*, target_logits, draft_logits, draft_tokens, temperature, gumbel, uniform,
                 log_weights, log_w_incr, log_norm, ess, resampled, ancestors, bonus,
                 workspace, out_tokens=None, tv=None, page_table_in=None, page_table_out=None,
                 refcount=None, error_flags=None, log_potential=None, V: int | None = None,
-                mode="always", ess_frac: float = 0.5, timing_events=None, stream=None) -> None:
-    """Enqueue one SMC-SD round (smcsd_round). Shapes: target [R,N,K+1,ld], draft
-    [R,N,K,ld] (both float32 or bfloat16), draft_tokens [R,N,K] int32, temperature [R],
-    gumbel [R,N,ld], uniform [R], per-request/per-particle outputs as in include/smcsd.h."""
+                mode="always", ess_frac: float = 0.5, timing_events=None):
+    """The smcsd_round_args struct of a round, after checking every tensor."""
     dev = target_logits.device
     if target_logits.dtype not in (torch.float32, torch.bfloat16):
         raise ValueError("logits must be float32 or bfloat16")
@@ -194,7 +216,8 @@ def smcsd_round(*, target_logits, draft_logits, draft_tokens, temperature, gumbe
     _check(ancestors, "ancestors", i32, (R, N), dev)
     if bonus is not None or gumbel is not None:
         _check(bonus, "bonus", i32, (R, N), dev)
-    _check(workspace, "workspace", torch.uint8, None, dev)
+    if workspace is not None:
+        _check(workspace, "workspace", torch.uint8, None, dev)
     if out_tokens is not None:
         _check(out_tokens, "out_tokens", i32, (R, N, K + 1), dev)
     if tv is not None:
@@ -225,12 +248,10 @@ def smcsd_round(*, target_logits, draft_logits, draft_tokens, temperature, gumbe
     a.page_table_in, a.page_table_out = _ptr(page_table_in), _ptr(page_table_out)
     a.refcount, a.error_flags = _ptr(refcount), _ptr(error_flags)
     a.log_potential = _ptr(log_potential)
-    a.workspace, a.workspace_bytes = _ptr(workspace), workspace.numel()
+    a.workspace, a.workspace_bytes = _ptr(workspace), (0 if workspace is None else workspace.numel())
     if timing_events is not None:
         a.timing_begin, a.timing_end = timing_events
-    st = _lib.smcsd_round(ctypes.byref(a), _stream(dev, stream))
-    if st != OK:
-        raise SmcsdError(st, "smcsd_round")
+    return a, dev
 
 
 def smcsd_sd_verify(*, target_logits, draft_logits, draft_tokens, temperature, gumbel,

@@ -30,7 +30,7 @@ def test_every_declared_symbol_is_exported():
             "smcsd_bench_copy", "smcsd_sd_verify", "smcsd_verify_workspace_size",
             "smcsd_verify_args_size", "smcsd_gumbel_topk", "smcsd_topk_workspace_size",
             "smcsd_pages_advance", "smcsd_pages_workspace_size", "smcsd_bonus_resampled",
-            "smcsd_bonus_workspace_size"} <= names
+            "smcsd_bonus_workspace_size", "smcsd_round_noalloc"} <= names
     lib = ctypes.CDLL(S.library_path())
     for n in sorted(names):
         assert hasattr(lib, n), n
@@ -45,7 +45,7 @@ def test_struct_layout_matches():
 
 
 def test_status_strings():
-    for st in range(5):
+    for st in range(6):
         assert S.smcsd_status_string(st) not in ("", "unknown status")
     assert S.smcsd_status_string(99) == "unknown status"
 
@@ -117,6 +117,32 @@ def test_round_validation_ess_and_pages():
 def test_empty_batch_is_a_no_op():
     assert _round(_args(R=0)) == S.OK
     assert _round(_args(R=0, target_logits=None)) == S.OK
+
+
+def test_noalloc_validation():
+    """smcsd_round_noalloc validates on the host like smcsd_round, refuses a workspace of the
+    caller's, and refuses a request larger than its static scratch buffer, all before any
+    HIP call."""
+    lib = S.raw_library()
+
+    def call(a):
+        return lib.smcsd_round_noalloc(ctypes.byref(a), None)
+
+    hdr = open(os.path.join(ROOT, "include", "smcsd.h")).read()
+    m = re.search(r"SMCSD_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", hdr)
+    assert int(m.group(1)) << int(m.group(2)) == S.NOALLOC_SCRATCH_BYTES
+    none = dict(workspace=None, workspace_bytes=0)
+    assert call(_args()) == S.ERR_ARG                                   # a workspace given
+    assert call(_args(workspace=None)) == S.ERR_ARG                     # ... or its size
+    assert call(_args(N=0, **none)) == S.ERR_ARG
+    assert call(_args(V=1048576 + 8, ld=1048576 + 8, **none)) == S.ERR_UNSUPPORTED
+    assert call(_args(R=0, **none)) == S.OK
+    big = dict(R=512, N=32, K=8, V=128256, ld=128256)
+    need = S.smcsd_workspace_size(512, 32, 8, 128256, S.BF16, True)
+    assert need > S.NOALLOC_SCRATCH_BYTES
+    assert call(_args(**big, **none)) == S.ERR_SCRATCH
+    assert S.smcsd_workspace_size(64, 32, 8, 128256, S.BF16, True) <= S.NOALLOC_SCRATCH_BYTES
+    assert S.smcsd_workspace_size(32, 32, 8, 256000, S.BF16, True) <= S.NOALLOC_SCRATCH_BYTES
 
 
 def test_resample_and_remap_validation():
