@@ -15,7 +15,9 @@
 // k) or one slice of one bonus row plus its noise row. Each lane loads its CPL chunks of both
 // rows with 16-byte non-temporal buffer loads. Chunks outside the slice and elements >= V
 // become -inf, which adds nothing to any max, sum, TV or argmax, so the arithmetic has no
-// per-element branch.
+// per-element branch. (The TV pass avoids even that where it can: when every slice fills all
+// its chunk groups but the last and V is a multiple of the chunk width, a lane past the slice
+// end re-reads an inside chunk and its exponentials are shifted by -inf.)
 //   phase 1: the maximum m of z over a share of the slice, then e = exp2((z - m) * log2e/T)
 //            and its sum, for p and q. TV off: the share is the slice (one workgroup max).
 //            TV on: each wave's own share, so nothing waits between loads and exponentials.
@@ -398,6 +400,13 @@ struct SliceMask {
     int tail_j;            // chunk group of that chunk if this lane holds it, else -1
     uint32_t keep[4];      // per word of the tail chunk: bits kept (uniform)
 
+    // Fast path: the slice fills every chunk group but the last and holds no partial tail
+    // chunk. Then nothing is masked: a lane past the slice end in the last group re-reads the
+    // slice's last chunk (its byte offset voff_last), which leaves every maximum unchanged,
+    // and its exponentials get a shift of -inf (last_inside false), so they are 0.
+    bool last_inside;      // this lane's chunk of the last group lies inside the slice
+    int voff_last;         // byte offset of this lane's load in the last group
+
     __device__ __forceinline__ SliceMask(int c0, int c1, int V) {
         constexpr int EPC = Elem<DT>::EPC;
         const int tid = threadIdx.x;
@@ -420,6 +429,10 @@ struct SliceMask {
             const int last = c1 - 1 - c0;
             if (last % kThreads == tid) tail_j = last / kThreads;
         }
+        constexpr int kLast = (CPL - 1) * kThreads;   // first chunk of the last group
+        const bool fast = n > kLast && !has_tail;
+        last_inside = kLast + tid < n;
+        voff_last = ((fast ? min(kLast + tid, n - 1) : kLast + tid) - kLast) * 16;
     }
 
     // -inf bits are exactly the complement of the kept bits within each element, so the
@@ -457,15 +470,18 @@ __device__ __forceinline__ void pair_rows(const LogitsArgs& a, uint32_t u, int c
 }
 
 // Issue the loads of this lane's chunks of the slice that starts at `row` (c0 already
-// applied) and holds n chunks.
+// applied) and holds n chunks. voff_last is the lane's byte offset within the last chunk
+// group (SliceMask::voff_last).
 template <int CPL>
-__device__ __forceinline__ void issue_at(u32x4 (&R)[CPL], const char* row, int n) {
+__device__ __forceinline__ void issue_at(u32x4 (&R)[CPL], const char* row, int n, int voff_last) {
     const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(row), 0, n * 16,
                                                                        kRsrcWord3);
     const int voff = (int)threadIdx.x * 16;
 #pragma unroll
-    for (int j = 0; j < CPL; ++j)
+    for (int j = 0; j < CPL - 1; ++j)
         R[j] = __builtin_amdgcn_raw_buffer_load_b128(r, voff, j * kThreads * 16, kLoadNontemporal);
+    R[CPL - 1] = __builtin_amdgcn_raw_buffer_load_b128(r, voff_last, (CPL - 1) * kThreads * 16,
+                                                       kLoadNontemporal);
 }
 
 // LDS of the TV pass: the wave partials (max p, sum p, max q, sum q) of the current row pair,
@@ -484,10 +500,11 @@ struct TvLds {
 // waits between the loads and the exponentials; wave 0 combines the eight wave partials into
 // the slice partial it publishes, and in phase 2 each wave scales its terms by its own
 // f = exp2((m_wave - M_row) c). P and Q hold this slice's loads, issued one row pair earlier;
-// once they are exponentials, the loads of row pair `next` (if >= 0) go into them, in flight
-// during the exchange and phase 2. Two barriers per row pair: wave partials, exchange words.
+// as soon as a chunk group's values are exponentials, the loads of row pair `next` go into
+// that group's registers, in flight during the rest of phase 1, the exchange and phase 2.
+// Two barriers per row pair: wave partials, exchange words.
 
-template <int DT>
+template <int DT, bool kFast>
 __device__ void pair_slice_tv(const LogitsArgs& a, uint32_t u, int s, int64_t next,
                               const SliceMask<DT, kTvCPL>& mask, int c0, int n, u32x4 (&P)[kTvCPL],
                               u32x4 (&Q)[kTvCPL], TvLds& sh, uint32_t& r_lo, float& c_r) {
@@ -510,36 +527,58 @@ __device__ void pair_slice_tv(const LogitsArgs& a, uint32_t u, int s, int64_t ne
     // the row pair wait for them), lowest while polling, in between after the exchange (that
     // work delays only this slice's next publish). Without it the pass took 7% longer.
     __builtin_amdgcn_s_setprio(3);
-    mask.apply(P);
-    mask.apply(Q);
-    const float mpw = wave_share_max<DT, kTvCPL>(P);
-    const float mqw = wave_share_max<DT, kTvCPL>(Q);
+    // The padding is applied to copies, so that P and Q stay the registers the next row
+    // pair's loads land in (in-place masking made the compiler copy them back, 32 moves).
+    u32x4 Pm[kTvCPL], Qm[kTvCPL];
+#pragma unroll
+    for (int j = 0; j < kTvCPL; ++j) {
+        Pm[j] = P[j];
+        Qm[j] = Q[j];
+    }
+    if constexpr (!kFast) {
+        mask.apply(Pm);
+        mask.apply(Qm);
+    }
+    const float mpw = wave_share_max<DT, kTvCPL>(Pm);
+    const float mqw = wave_share_max<DT, kTvCPL>(Qm);
+    // The next row pair's loads go into P and Q chunk group by chunk group, each right after
+    // the group's exponentials: early, without copies of the registers they overwrite, and
+    // without a branch (with no next row pair the buffer range is empty and the loads read
+    // nothing), so the order below holds.
+    const char *zpn, *zqn;
+    pair_rows<DT>(a, next >= 0 ? (uint32_t)next : u, c0, zpn, zqn);
+    const int nn = next >= 0 ? n * 16 : 0;
+    const __amdgpu_buffer_rsrc_t rp = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(zpn), 0, nn, kRsrcWord3);
+    const __amdgpu_buffer_rsrc_t rq = __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(zqn), 0, nn, kRsrcWord3);
+    const int voff = tid * 16;
     float s0 = 0.0f, s1 = 0.0f, q0 = 0.0f, q1 = 0.0f;
     {
         const float nmp = mpw == -INFINITY ? 0.0f : -mpw * c;
         const float nmq = mqw == -INFINITY ? 0.0f : -mqw * c;
+        // fast path: the re-read chunk of a lane past the slice end contributes exp2(-inf) = 0
+        const float nmp_last = !kFast || mask.last_inside ? nmp : -INFINITY;
+        const float nmq_last = !kFast || mask.last_inside ? nmq : -INFINITY;
 #pragma unroll
         for (int j = 0; j < kTvCPL; ++j) {
+            const float np = j == kTvCPL - 1 ? nmp_last : nmp;
+            const float nq = j == kTvCPL - 1 ? nmq_last : nmq;
 #pragma unroll
             for (int e = 0; e < EPC; e += 2) {
                 const int x = j * EPC + e;
-                Ep[x] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(P[j], e), c, nmp));
-                Ep[x + 1] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(P[j], e + 1), c, nmp));
-                Eq[x] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(Q[j], e), c, nmq));
-                Eq[x + 1] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(Q[j], e + 1), c, nmq));
+                Ep[x] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(Pm[j], e), c, np));
+                Ep[x + 1] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(Pm[j], e + 1), c, np));
+                Eq[x] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(Qm[j], e), c, nq));
+                Eq[x + 1] = __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(Qm[j], e + 1), c, nq));
                 s0 += Ep[x];
                 s1 += Ep[x + 1];
                 q0 += Eq[x];
                 q1 += Eq[x + 1];
             }
+            const int vo = j == kTvCPL - 1 ? mask.voff_last : voff;
+            P[j] = __builtin_amdgcn_raw_buffer_load_b128(rp, vo, j * kThreads * 16, kLoadNontemporal);
+            Q[j] = __builtin_amdgcn_raw_buffer_load_b128(rq, vo, j * kThreads * 16, kLoadNontemporal);
+            __builtin_amdgcn_sched_barrier(0);
         }
-    }
-    __builtin_amdgcn_sched_barrier(0);
-    if (next >= 0) {
-        const char *zp, *zq;
-        pair_rows<DT>(a, (uint32_t)next, c0, zp, zq);
-        issue_at<kTvCPL>(P, zp, n);
-        issue_at<kTvCPL>(Q, zq, n);
     }
     const float spw = wave_sum(s0 + s1), sqw = wave_sum(q0 + q1);
     if (lane == 0) sh.wpart[w] = make_float4(mpw, spw, mqw, sqw);
@@ -611,8 +650,9 @@ __device__ void pair_slice_tv(const LogitsArgs& a, uint32_t u, int s, int64_t ne
     if (lane == 0) a.tvp[((size_t)u * a.S + s) * kWaves + w] = acc * scale;
 }
 
-// TV on: persistent cooperative grid, gridDim.x = C * S.
-template <int DT>
+// TV on: persistent cooperative grid, gridDim.x = C * S. kFast: every slice takes the fast
+// path of SliceMask (chosen on the host by tv_fast_path).
+template <int DT, bool kFast>
 __global__ __launch_bounds__(kThreads, 4) void k_logits_tv(LogitsArgs a) {
     __shared__ TvLds sh;
     const int s = (int)(blockIdx.x % (unsigned)a.S);
@@ -626,15 +666,15 @@ __global__ __launch_bounds__(kThreads, 4) void k_logits_tv(LogitsArgs a) {
     {
         const char *zp, *zq;
         pair_rows<DT>(a, (uint32_t)cluster, c0, zp, zq);
-        issue_at<kTvCPL>(P, zp, c1 - c0);
-        issue_at<kTvCPL>(Q, zq, c1 - c0);
+        issue_at<kTvCPL>(P, zp, c1 - c0, mask.voff_last);
+        issue_at<kTvCPL>(Q, zq, c1 - c0, mask.voff_last);
     }
     const uint32_t nk = (uint32_t)a.N * (uint32_t)a.K;
     uint32_t r_lo = (uint32_t)cluster / nk * nk;   // first row pair of the current request
     float c_r = kLog2e / load_constant(a.temperature, (uint32_t)cluster / nk);
     for (int64_t it = cluster; it < a.pairs; it += C)
-        pair_slice_tv<DT>(a, (uint32_t)it, s, it + C < a.pairs ? it + C : -1, mask, c0, c1 - c0, P,
-                          Q, sh, r_lo, c_r);
+        pair_slice_tv<DT, kFast>(a, (uint32_t)it, s, it + C < a.pairs ? it + C : -1, mask, c0,
+                                 c1 - c0, P, Q, sh, r_lo, c_r);
 }
 
 // TV off: slice partials only. Each wave shifts its exponentials by the maximum of its own
@@ -697,8 +737,16 @@ __global__ void k_fill_tv(Ctrl* ctrl, uint32_t timeout, uint32_t* words, int64_t
 
 }  // namespace
 
-// Workgroups of k_logits_tv<DT> that fit on the current device at once (cached per device).
-template <int DT>
+// Whether every slice of the plan takes SliceMask's fast path: each fills all chunk groups
+// but the last, and V is a multiple of the chunk width (no partial tail chunk).
+static bool tv_fast_path(const Plan& plan) {
+    const int32_t last = plan.chunks - (plan.S - 1) * plan.cps;   // the last slice's chunks
+    return plan.V % plan.epc == 0 && last > (kTvCPL - 1) * kThreads;
+}
+
+// Workgroups of k_logits_tv<DT, kFast> that fit on the current device at once (cached per
+// device).
+template <int DT, bool kFast>
 static int64_t coop_capacity() {
     static std::atomic<int64_t> cache[64];
     int dev = 0;
@@ -708,7 +756,7 @@ static int64_t coop_capacity() {
         if (c > 0) return c;
     }
     int per_cu = 0, cus = 0, coop = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_logits_tv<DT>),
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void*>(&k_logits_tv<DT, kFast>),
                                                      kThreads, 0) != hipSuccess)
         return 0;
     if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
@@ -728,21 +776,23 @@ hipError_t launch_tv_fill(const Plan& plan, const LogitsArgs& a, uint32_t timeou
 }
 
 // The row pairs only: the round hands the bonus rows to the Gumbel-Top-K slice kernel.
-template <int DT>
+template <int DT, bool kFast>
 static hipError_t launch_tv(const Plan& plan, const LogitsArgs& a, hipStream_t s) {
-    const int64_t cap = coop_capacity<DT>();
+    const int64_t cap = coop_capacity<DT, kFast>();
     const int64_t clusters = std::min<int64_t>(cap / plan.S, plan.pairs);
     if (clusters < 1) return hipErrorCooperativeLaunchTooLarge;
     LogitsArgs copy = a;
     void* params[] = {&copy};
-    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_logits_tv<DT>),
+    return hipLaunchCooperativeKernel(reinterpret_cast<const void*>(&k_logits_tv<DT, kFast>),
                                       dim3((unsigned)(clusters * plan.S)), dim3(kThreads), params, 0, s);
 }
 
 hipError_t launch_logits(const Plan& plan, const LogitsArgs& a, hipStream_t s) {
     if (plan.tv) {
-        return plan.dtype == SMCSD_BF16 ? launch_tv<SMCSD_BF16>(plan, a, s)
-                                        : launch_tv<SMCSD_F32>(plan, a, s);
+        const bool fast = tv_fast_path(plan);
+        if (plan.dtype == SMCSD_BF16)
+            return fast ? launch_tv<SMCSD_BF16, true>(plan, a, s) : launch_tv<SMCSD_BF16, false>(plan, a, s);
+        return fast ? launch_tv<SMCSD_F32, true>(plan, a, s) : launch_tv<SMCSD_F32, false>(plan, a, s);
     }
     const dim3 grid((unsigned)plan.total_wgs), block(kThreads);
     if (plan.dtype == SMCSD_BF16) k_logits_stream<SMCSD_BF16><<<grid, block, 0, s>>>(a);
