@@ -274,8 +274,8 @@ size_t smcsd_pages_workspace_size(int32_t R, int32_t N, int32_t P, int32_t num_p
 size_t smcsd_workspace_size(int32_t R, int32_t N, int32_t K, int32_t V, int32_t dtype,
                             int32_t tv_enabled);
 
-/* Static, human-readable name of a status code. */
-const char *smcsd_status_string(smcsd_status status);
+/* Static, human-readable name of a status code ("unknown status" for any other value). */
+const char *smcsd_status_string(int32_t status);
 
 /* sizeof(smcsd_round_args) as compiled into the library (for bindings to check layout). */
 size_t smcsd_round_args_size(void);

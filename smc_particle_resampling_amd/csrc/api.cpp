@@ -46,11 +46,12 @@ bool make_plan(int32_t R, int32_t N, int32_t K, int32_t V, int64_t ld, int32_t d
     const int32_t s0 = (q.chunks + per_slice - 1) / per_slice;
     q.cps = (q.chunks + s0 - 1) / s0;
     q.S = (q.chunks + q.cps - 1) / q.cps;   // no empty slice
-    q.pairs = (int64_t)R * N * K;
+    q.pairs = (int64_t)R * N * K;          // < 2^49: R < 2^31, N <= 2^10, K <= 2^8
     q.bonus_rows = (int64_t)R * N;
+    // grid range: (pairs + bonus rows) * S workgroups below 2^31, checked before multiplying
+    if (q.pairs + q.bonus_rows >= (int64_t)INT32_MAX / q.S) return false;
     q.pair_wgs = q.pairs * q.S;
     q.total_wgs = (q.pairs + q.bonus_rows) * q.S;
-    if (q.total_wgs >= (int64_t)INT32_MAX) return false;     // grid range
     if (tv && q.S > kMaxTvSlices) return false;               // V > 1048576 (bf16) with TV
     size_t off = 0;
     q.off_ctrl = off;
@@ -214,7 +215,7 @@ extern "C" {
 
 size_t smcsd_round_args_size(void) { return sizeof(smcsd_round_args); }
 
-const char* smcsd_status_string(smcsd_status s) {
+const char* smcsd_status_string(int32_t s) {
     switch (s) {
     case SMCSD_OK: return "ok";
     case SMCSD_ERR_ARG: return "invalid argument";
@@ -383,9 +384,9 @@ smcsd_status smcsd_remap_pages(int32_t R, int32_t N, int32_t P, const int32_t* a
     if (N > SMCSD_MAX_N) return SMCSD_ERR_UNSUPPORTED;
     if (R == 0) return SMCSD_OK;
     if (!ancestors || !page_table_in || !page_table_out || !refcount) return SMCSD_ERR_ARG;
-    const size_t tb = sizeof(int32_t) * (size_t)R * N * P;
-    if (overlap(page_table_in, tb, page_table_out, tb)) return SMCSD_ERR_ARG;
     if ((int64_t)R * (((int64_t)N * P + 2047) / 2048) >= (int64_t)INT32_MAX) return SMCSD_ERR_UNSUPPORTED;
+    const size_t tb = sizeof(int32_t) * (size_t)R * N * P;   // < 2^31 * 2048 * 4 bytes
+    if (overlap(page_table_in, tb, page_table_out, tb)) return SMCSD_ERR_ARG;
     RemapArgs ra{};
     ra.ancestors = ancestors;
     ra.pt_in = page_table_in;

@@ -1,7 +1,7 @@
 // k_bench.hip -- calibration kernels for measurement (include/smcsd_bench.h): a plain
 // streaming read (attainable HBM read bandwidth) and a plain copy of known size (turns the
 // FETCH_SIZE / WRITE_SIZE hardware counters into bytes). Not part of the round.
-#include "smcsd_internal.h"
+#include "smcsd_device.h"
 
 namespace smcsd {
 namespace {

@@ -11,7 +11,7 @@
 // table, the same workgroup then remaps its request's table rows through the ancestors
 // (pointer exchange, as k_remap does), which saves the round a launch.
 #include "remap_rows.h"
-#include "smcsd_internal.h"
+#include "smcsd_device.h"
 
 namespace smcsd {
 namespace {
@@ -27,6 +27,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
     __shared__ int32_t s_off[SMCSD_MAX_N];   // offspring counts o_i
     __shared__ double s_logZ;
     __shared__ int32_t s_rs;
+    __shared__ double s_red[2 * kWaves];       // per-wave partials of the block reductions
     __shared__ int32_t s_pt[kFusedRemapEntries];   // the request's input page table
     const int tid = threadIdx.x;
     const int64_t r = blockIdx.x;
@@ -212,35 +213,72 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
                 s_rs = rs;
             }
         }
-    } else if (tid == 0) {
-        double m = -INFINITY;
-        for (int32_t i = 0; i < N; ++i) m = fmax(m, s_l[i]);
-        double se = 0.0;
-        for (int32_t i = 0; i < N; ++i) {
-            s_c[i] = exp(s_l[i] - m);
-            se += s_c[i];
+    } else {
+        // more than 64 particles: the whole workgroup, each thread on the particles 2t and
+        // 2t + 1 (N <= 2 * kThreads); every reduction and the scan combine in one fixed
+        // order (the thread's pair, a butterfly within each wave, the waves in index order)
+        static_assert(SMCSD_MAX_N <= 2 * kThreads, "two particles a thread");
+        const int lane = tid & 63, wv = tid >> 6;
+        const int i0 = 2 * tid, i1 = 2 * tid + 1;
+        const double l0 = i0 < N ? s_l[i0] : -INFINITY;
+        const double l1 = i1 < N ? s_l[i1] : -INFINITY;
+        double m = fmax(l0, l1);
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) m = fmax(m, __shfl_xor(m, d));
+        if (lane == 0) s_red[wv] = m;
+        __syncthreads();
+        m = s_red[0];
+        for (int t = 1; t < kWaves; ++t) m = fmax(m, s_red[t]);
+        const double e0 = i0 < N ? exp(l0 - m) : 0.0;
+        const double e1 = i1 < N ? exp(l1 - m) : 0.0;
+        double se = e0 + e1;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) se += __shfl_xor(se, d);
+        __syncthreads();                       // s_red is reused
+        if (lane == 0) s_red[wv] = se;
+        __syncthreads();
+        se = s_red[0];
+        for (int t = 1; t < kWaves; ++t) se += s_red[t];
+        const double w0 = e0 / se, w1 = e1 / se;
+        double s2 = w0 * w0 + w1 * w1;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) s2 += __shfl_xor(s2, d);
+        // inclusive prefix sums: the thread's pair, a scan over the lanes, then the waves
+        const double pair = w0 + w1;
+        double acc = pair;
+#pragma unroll
+        for (int d = 1; d < 64; d <<= 1) {
+            const double o = __shfl_up(acc, d);
+            if (lane >= d) acc += o;
         }
-        double s2 = 0.0;
-        for (int32_t i = 0; i < N; ++i) {
-            s_c[i] = s_c[i] / se;
-            s2 += s_c[i] * s_c[i];
-        }
+        __syncthreads();                       // s_red is reused
+        if (lane == 0) s_red[wv] = s2;
+        if (lane == 63) s_red[kWaves + wv] = acc;   // the wave's total weight
+        __syncthreads();
+        s2 = s_red[0];
+        for (int t = 1; t < kWaves; ++t) s2 += s_red[t];
+        double base = 0.0;
+        for (int t = 0; t < wv; ++t) base += s_red[kWaves + t];
+        // C at particle 2t + 1 is base + acc; C just before particle 2t is the previous
+        // lane's value, computed by the same operations; C at 2t lies between the two (min
+        // keeps the sums non-decreasing whatever the roundings)
+        double excl = __shfl_up(acc, 1);
+        if (lane == 0) excl = 0.0;
+        const double c1 = base + acc;
+        const double c0 = fmin((base + excl) + w0, c1);
         const double logZ = m + log(se);
         const double ess = 1.0 / s2;
         const int32_t rs = a.mode == SMCSD_RESAMPLE_ALWAYS ||
                            (a.mode == SMCSD_RESAMPLE_ESS && ess < (double)a.ess_frac * (double)N);
-        if (rs) {
-            double acc = 0.0;
-            for (int32_t i = 0; i < N; ++i) {
-                acc += s_c[i];
-                s_c[i] = acc;
-            }
+        if (i0 < N) s_c[i0] = rs ? c0 : w0;
+        if (i1 < N) s_c[i1] = rs ? c1 : w1;
+        if (tid == 0) {
+            a.log_norm[r] = (float)logZ;
+            a.ess[r] = (float)ess;
+            a.resampled[r] = rs;
+            s_logZ = logZ;
+            s_rs = rs;
         }
-        a.log_norm[r] = (float)logZ;
-        a.ess[r] = (float)ess;
-        a.resampled[r] = rs;
-        s_logZ = logZ;
-        s_rs = rs;
     }
     __syncthreads();
 

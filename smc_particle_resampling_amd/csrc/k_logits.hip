@@ -45,7 +45,7 @@
 #include <algorithm>
 #include <atomic>
 
-#include "smcsd_internal.h"
+#include "smcsd_device.h"
 
 namespace smcsd {
 namespace {

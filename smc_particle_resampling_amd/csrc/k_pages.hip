@@ -32,7 +32,7 @@
 //                    of the whole page or (token-major pages) of the tail's filled rows.
 // Integer atomics commute and every pop index is fixed by the sums, so the result is the
 // same as the sequential one on every run.
-#include "smcsd_internal.h"
+#include "smcsd_device.h"
 
 namespace smcsd {
 namespace {

@@ -11,7 +11,7 @@
 // in consecutive rows of a column share one atomic. Integer atomics commute, so the
 // resulting refcounts do not depend on scheduling.
 #include "remap_rows.h"
-#include "smcsd_internal.h"
+#include "smcsd_device.h"
 
 namespace smcsd {
 namespace {

@@ -9,7 +9,7 @@
 // lane holds its keys in registers and its own best; k rounds of a block argmax over the
 // lanes' bests pick the slice's k best, and only the lane that lost its best rescans. Pass 2:
 // one workgroup per row takes the S * k candidates the same way.
-#include "smcsd_internal.h"
+#include "smcsd_device.h"
 
 namespace smcsd {
 namespace {

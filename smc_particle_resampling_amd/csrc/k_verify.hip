@@ -13,7 +13,7 @@
 // (one workgroup per request) takes the acceptance decisions and picks the slice of the
 // residual draw; the residual kernel (one workgroup per particle) scans that one slice of
 // the rejected row in increasing v to find the token.
-#include "smcsd_internal.h"
+#include "smcsd_device.h"
 
 namespace smcsd {
 namespace {

@@ -11,7 +11,7 @@
 #include <mutex>
 
 #include "smcsd.h"
-#include "smcsd_internal.h"
+#include "smcsd_device.h"
 
 namespace {
 

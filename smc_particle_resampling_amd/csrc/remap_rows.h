@@ -9,7 +9,7 @@
 // commute, so the refcounts do not depend on the order.
 #pragma once
 
-#include "smcsd_internal.h"
+#include "smcsd_device.h"
 
 namespace smcsd {
 
