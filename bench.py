@@ -35,7 +35,8 @@ PEAK_HBM_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
 KERNEL_SOURCES = ["smc_particle_resampling_amd/csrc/k_logits.hip",
                   "smc_particle_resampling_amd/csrc/k_topk.hip",
-                  "smc_particle_resampling_amd/csrc/smcsd_internal.h"]
+                  "smc_particle_resampling_amd/csrc/smcsd_internal.h",
+                  "smc_particle_resampling_amd/csrc/smcsd_device.h"]
 
 
 def kernel_source_hash() -> str:
@@ -96,9 +97,9 @@ def read_roofline(smcsd, torch, dev, gib=4):
     return best
 
 
-def stored_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter runs, if they were taken on
-    the current kernel source (else None)."""
+def stored_traffic(workload: str, kernel: str):
+    """HBM bytes per launch of one kernel from the committed rocprofv3 counter runs, if they
+    were taken on the current kernel source (else None)."""
     p = os.path.join(PROFILES, "traffic_k_logits_%s.json" % workload)
     if not os.path.exists(p):
         return None
@@ -106,7 +107,13 @@ def stored_traffic(workload: str):
         d = json.load(f)
     if d.get("kernel_source_sha256_16") != kernel_source_hash():
         return None
-    return d.get("hbm_bytes_per_launch")
+    return d.get("hbm_bytes_per_launch_by_kernel", {}).get(kernel)
+
+
+def flush_caches(buf):
+    """Overwrite a buffer larger than the L2s and the Infinity Cache together, so that the
+    next round finds none of its inputs on chip."""
+    buf.add_(1)
 
 
 def cpu_model() -> str:
@@ -210,6 +217,10 @@ def main():
     ap.add_argument("--no-read-roofline", action="store_true")
     ap.add_argument("--copy-calibration", type=int, default=0,
                     help="also run N launches of a plain 1 GiB copy (for counter scaling)")
+    ap.add_argument("--flush", action="store_true",
+                    help="write a 1 GiB buffer before every timed round (evicts the L2s and the "
+                         "Infinity Cache) and time each round alone with events around all its "
+                         "launches; value is then 1 / mean round time")
     ap.add_argument("--path", choices=("round", "sd_verify", "gumbel_topk", "driver"),
                     default="round",
                     help="round: one SMC-SD round (smcsd_round, the headline); sd_verify: "
@@ -265,7 +276,11 @@ def main():
     after = args.bonus == "after" and args.path in ("round", "driver")
     bonus_noise = synth.make_gumbel(w, 1, device=dev) if after else None
     ev = HipEvents()
-    pairs = [(ev.create(), ev.create()) for _ in range(args.steps)]
+    # per timed step: (begin, split, end) around the logits pass; split separates the row-pair
+    # kernel from the bonus-row kernel of a TV pass (else it is recorded with end)
+    pairs = [(ev.create(), ev.create(), ev.create()) for _ in range(args.steps)]
+    rounds = [(ev.create(), ev.create()) for _ in range(args.steps)] if args.flush else None
+    flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush else None
     if topk:
         tz, tT, tG = synth.topk_rows(inp)
         out = smcsd.gumbel_topk(tz, tT, tG, args.topk, V=w.V)
@@ -279,13 +294,17 @@ def main():
             smcsd.gumbel_topk(tz, tT, tG, args.topk, V=w.V, outputs=out)
             if timing is not None:
                 ev.record(timing[1], cur)
+                ev.record(timing[2], cur)
     elif verify:
         inp.update(synth.make_verify_uniforms(w.R, w.N, w.K, 0, device=dev))
         out = smcsd.run_sd_verify(inp)          # allocates the outputs once
         torch.cuda.synchronize()
 
         def step(t, timing=None):
-            smcsd.run_sd_verify(inp, outputs=out, timing_events=timing)
+            smcsd.run_sd_verify(inp, outputs=out,
+                                timing_events=None if timing is None else (timing[0], timing[2]))
+            if timing is not None:
+                ev.record(timing[1], torch.cuda.current_stream(dev).cuda_stream)
     elif driver:
         # Page pool: every particle's length grows K + 1 tokens a step; the table holds a
         # context of up to 256 tokens before the first step plus what the run appends, and
@@ -356,20 +375,32 @@ def main():
         step(t)
     torch.cuda.synchronize()
     print("# warmup done", file=sys.stderr, flush=True)
+    cur_stream = torch.cuda.current_stream(dev).cuda_stream
     t0 = time.perf_counter()
     for t in range(args.steps):
+        if args.flush:
+            flush_caches(flush_buf)
+            ev.record(rounds[t][0], cur_stream)
         step(args.warmup + t, timing=pairs[t])
+        if args.flush:
+            ev.record(rounds[t][1], cur_stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
     flags = int(out["error_flags"].item())
     if flags:
         raise SystemExit("device error flags %d" % flags)
-    kms = [ev.elapsed_ms(a, b) for a, b in pairs]
-    for a, b in pairs:
-        ev.destroy(a)
-        ev.destroy(b)
+    kms = [ev.elapsed_ms(a, e) for a, _, e in pairs]
+    first_ms = [ev.elapsed_ms(a, sp) for a, sp, _ in pairs]
+    second_ms = [ev.elapsed_ms(sp, e) for _, sp, e in pairs]
+    for trio in pairs:
+        for x in trio:
+            ev.destroy(x)
     k_mean_ms = sum(kms) / len(kms)
-    ms_per_step = elapsed * 1e3 / args.steps
+    if args.flush:
+        rms = [ev.elapsed_ms(a, b) for a, b in rounds]
+        ms_per_step = sum(rms) / len(rms)
+    else:
+        ms_per_step = elapsed * 1e3 / args.steps
     alg = w.algorithmic_bytes()
     logits_bytes = alg["target"] + alg["draft"] + alg["noise"]
     if after:       # the timed pass reads the row pairs only; the bonus is drawn afterwards
@@ -377,9 +408,24 @@ def main():
     if topk:        # one logits row and one noise row per particle
         e = 2 if w.dtype == "bf16" else 4
         logits_bytes = w.R * w.N * w.V * (e + 4)
-    achieved = logits_bytes / (k_mean_ms * 1e-3) / 1e9
-    print("# %s %.3f ms, logits kernel %.3f ms (min %.3f max %.3f)" % (
-        args.path, ms_per_step, k_mean_ms, min(kms), max(kms)), file=sys.stderr, flush=True)
+    # The dominant kernel: with TV on and the bonus drawn in the pass, the row-pair kernel
+    # (k_logits_tv, timed begin..split) reads every drafted position's target and draft row;
+    # otherwise one kernel is the whole pass.
+    split = w.tv and not after and args.path in ("round", "driver")
+    if split:
+        dom_bytes = alg["target"] * w.K // (w.K + 1) + alg["draft"]
+        dom_ms = sum(first_ms) / len(first_ms)
+        dom_kernel = "k_logits_tv"
+    else:
+        dom_bytes, dom_ms = logits_bytes, k_mean_ms
+        dom_kernel = ("k_topk_slice+k_topk_merge" if topk else
+                      "k_logits_tv+k_topk_slice (bonus rows)" if verify else
+                      "k_logits_tv" if w.tv else "k_logits_stream")
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    pass_achieved = logits_bytes / (k_mean_ms * 1e-3) / 1e9
+    print("# %s %.3f ms, logits pass %.3f ms (min %.3f max %.3f), %s %.3f ms" % (
+        args.path, ms_per_step, k_mean_ms, min(kms), max(kms), dom_kernel, dom_ms),
+        file=sys.stderr, flush=True)
 
     lifecycle = None
     if driver:
@@ -439,7 +485,7 @@ def main():
         table_bytes = alg["table"]
     line = {
         "metric": metric,
-        "value": args.steps / elapsed,
+        "value": (1e3 / ms_per_step) if args.flush else args.steps / elapsed,
         "unit": unit,
         "n_gpus": 1,
         "steps": args.steps,
@@ -467,18 +513,23 @@ def main():
                                                           synth.WORKLOADS[name].V)
                                    if args.vocab_shards > 1 else None),
                    "bonus": (args.bonus if args.path in ("round", "driver") else None),
+                   "timing": ("each round alone (events around all its launches) after a 1 GiB "
+                              "write that evicts the L2s and the Infinity Cache" if args.flush
+                              else "rounds back to back, wall clock over the timed steps"),
                    "round_GBps": (logits_bytes + table_bytes) / (ms_per_step * 1e-3) / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
-                     "traffic": (None if (topk or after or args.vocab_shards > 1)
-                                 else stored_traffic(name)),
-                     "kernel": ("k_topk_slice+k_topk_merge" if topk else
-                                "k_logits_tv" if after and w.tv else
-                                "k_logits_tv+k_topk_slice (bonus rows)" if w.tv else
-                                "k_logits_stream"),
-                     "kernel_ms": k_mean_ms,
-                     "algorithmic_bytes_per_launch": logits_bytes,
-                     "attainable_read_GBps": rr},
+                     "traffic": (None if (topk or verify or after or args.vocab_shards > 1)
+                                 else stored_traffic(name, dom_kernel)),
+                     "kernel": dom_kernel,
+                     "kernel_ms": dom_ms,
+                     "algorithmic_bytes_per_launch": dom_bytes,
+                     "attainable_read_GBps": rr,
+                     "pass": {"kernels": ("k_logits_tv+k_topk_slice (bonus rows)" if split
+                                          else dom_kernel),
+                              "ms": k_mean_ms, "bytes": logits_bytes, "GBps": pass_achieved,
+                              "frac": pass_achieved / PEAK_HBM_GBPS,
+                              "bonus_rows_ms": (sum(second_ms) / len(second_ms)) if split else None}},
         "cpu_baseline": cpu,
     }
     if driver:

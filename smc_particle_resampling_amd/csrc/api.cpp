@@ -148,7 +148,8 @@ static smcsd_status check_verify(const smcsd_verify_args* a, Plan* plan) {
 // A persistent grid's share of the bonus rows ran slower than this ordinary grid.
 static_assert(kTvCPL == kTopkCPL, "bonus slices of the TV plan are Gumbel-Top-K slices");
 
-static hipError_t launch_logits_pass(const Plan& plan, const LogitsArgs& la, hipStream_t s) {
+static hipError_t launch_logits_pass(const Plan& plan, const LogitsArgs& la, hipStream_t s,
+                                     smcsd_event split = nullptr) {
     if (!plan.tv) return launch_logits(plan, la, s);
     Plan pairs = plan;
     pairs.bonus_rows = 0;
@@ -157,6 +158,7 @@ static hipError_t launch_logits_pass(const Plan& plan, const LogitsArgs& la, hip
     lp.total_wgs = la.pair_wgs;
     hipError_t e = launch_logits(pairs, lp, s);
     if (e != hipSuccess || plan.bonus_rows == 0) return e;
+    if (split && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(split), s)) != hipSuccess) return e;
     TopkArgs t{};
     t.logits = la.target;
     t.temperature = la.temperature;
@@ -281,8 +283,11 @@ smcsd_status enqueue_round(const smcsd_round_args& a, const Plan& plan, char* ws
     }
     if (a.timing_begin && hipEventRecord(reinterpret_cast<hipEvent_t>(a.timing_begin), s) != hipSuccess)
         return SMCSD_ERR_DEVICE;
-    e = launch_logits_pass(plan, la, s);
+    e = launch_logits_pass(plan, la, s, a.timing_split);
     if (e != hipSuccess) return SMCSD_ERR_DEVICE;
+    if (a.timing_split && !(plan.tv && plan.bonus_rows > 0) &&
+        hipEventRecord(reinterpret_cast<hipEvent_t>(a.timing_split), s) != hipSuccess)
+        return SMCSD_ERR_DEVICE;
     if (a.timing_end && hipEventRecord(reinterpret_cast<hipEvent_t>(a.timing_end), s) != hipSuccess)
         return SMCSD_ERR_DEVICE;
 

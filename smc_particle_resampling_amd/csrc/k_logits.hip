@@ -717,12 +717,15 @@ __global__ __launch_bounds__(kThreads) void k_logits_stream(LogitsArgs a) {
     __shared__ float red[kWaves];
     __shared__ int32_t redi[kWaves];
     __shared__ float4 wpart[kWaves];
+    // the bonus slices (a logits row and its noise row, 1.5 times a row pair's bytes) are
+    // dispatched first, so that the grid's tail holds the lighter row-pair slices
     const int64_t t = blockIdx.x;
-    if (t < a.pair_wgs) {
-        pair_slice_stream<DT>(a, t / a.S, (int)(t % a.S), wpart);
+    const int64_t bonus_wgs = a.total_wgs - a.pair_wgs;
+    if (t < bonus_wgs) {
+        bonus_slice<DT, kStreamCPL>(a, t / a.S, (int)(t % a.S), red, redi);
     } else if (t < a.total_wgs) {
-        const int64_t tb = t - a.pair_wgs;
-        bonus_slice<DT, kStreamCPL>(a, tb / a.S, (int)(tb % a.S), red, redi);
+        const int64_t tp = t - bonus_wgs;
+        pair_slice_stream<DT>(a, tp / a.S, (int)(tp % a.S), wpart);
     }
 }
 

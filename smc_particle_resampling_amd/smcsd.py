@@ -41,7 +41,7 @@ class RoundArgs(ctypes.Structure):
         ("log_norm", _p), ("ess", _p), ("resampled", _p), ("ancestors", _p), ("bonus", _p),
         ("out_tokens", _p), ("tv", _p), ("page_table_in", _p), ("page_table_out", _p),
         ("refcount", _p), ("error_flags", _p), ("workspace", _p), ("workspace_bytes", _sz),
-        ("timing_begin", _p), ("timing_end", _p), ("log_potential", _p),
+        ("timing_begin", _p), ("timing_end", _p), ("log_potential", _p), ("timing_split", _p),
     ]
 
 
@@ -250,7 +250,12 @@ def _round_args(*, target_logits, draft_logits, draft_tokens, temperature, gumbe
     a.log_potential = _ptr(log_potential)
     a.workspace, a.workspace_bytes = _ptr(workspace), (0 if workspace is None else workspace.numel())
     if timing_events is not None:
-        a.timing_begin, a.timing_end = timing_events
+        # (begin, end) around the logits pass, or (begin, split, end): split also separates
+        # the row-pair kernel from the bonus-row kernel of a TV pass
+        if len(timing_events) == 3:
+            a.timing_begin, a.timing_split, a.timing_end = timing_events
+        else:
+            a.timing_begin, a.timing_end = timing_events
     return a, dev
 
 

@@ -26,7 +26,7 @@ def test_stored_traffic_needs_the_same_kernel_sources(monkeypatch):
     if not os.path.exists(path):
         pytest.skip("no traffic record")
     monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0000000000000000")
-    assert bench.stored_traffic(wl) is None
+    assert bench.stored_traffic(wl, "k_logits_tv") is None
 
 
 def test_kernel_source_hash_is_stable():
