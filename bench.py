@@ -311,7 +311,7 @@ def main():
         # the free list starts with enough pages for every append even if nothing is
         # released.
         ps = 16
-        total = args.warmup + args.steps
+        total = args.warmup + 2 * args.steps      # the timed pass and the event pass
         grow = -(-(total * (w.K + 1)) // ps) + 1       # columns the run appends, at most
         P = 16 + grow
         pool = synth.make_page_pool(w.R, w.N, P, ps, 0, steps=total * (w.K + 1),
@@ -348,7 +348,7 @@ def main():
             inp["page_table"] = tables[t % 2]
             smcsd.run_round(inp, mode=w.mode, ess_frac=w.ess_frac, tv=w.tv, outputs=out,
                             timing_events=timing, bonus_noise=bonus_noise)
-            lt = life[t - args.warmup] if timing is not None else None
+            lt = life[t - args.warmup - args.steps] if timing is not None else None
             if lt:
                 ev.record(lt[0], cur)
             smcsd.smcsd_pages_advance(len_before=lens[t], len_after=lens[t + 1],
@@ -359,7 +359,7 @@ def main():
                                       error_flags=out["error_flags"])
             if lt:
                 ev.record(lt[1], cur)
-    else:
+    elif after:
         torch.cuda.synchronize()
         out = smcsd.alloc_outputs(w.R, w.N, w.K, dev, tv=w.tv, V=w.V,
                                   dtype=smcsd.BF16 if w.dtype == "bf16" else smcsd.F32)
@@ -370,22 +370,52 @@ def main():
             inp["page_table"] = tables[t % 2]
             smcsd.run_round(inp, mode=w.mode, ess_frac=w.ess_frac, tv=w.tv, outputs=out,
                             timing_events=timing, bonus_noise=bonus_noise)
+    else:
+        # The round's arguments are marshalled once per page-table parity (the tables swap
+        # every round, as a caller's pointer exchange would); each step enqueues a whole
+        # round, so no per-call Python work sits between the GPU's rounds.
+        torch.cuda.synchronize()
+        out = smcsd.alloc_outputs(w.R, w.N, w.K, dev, tv=w.tv, V=w.V,
+                                  dtype=smcsd.BF16 if w.dtype == "bf16" else smcsd.F32)
+        tables = [inp["page_table"], torch.empty_like(inp["page_table"])]
+        calls = [smcsd.RoundCall(
+            target_logits=inp["target"], draft_logits=inp["draft"], draft_tokens=inp["tokens"],
+            temperature=inp["temperature"], gumbel=inp["gumbel"], uniform=inp["uniform"],
+            log_weights=inp["log_weights"], log_w_incr=out["log_w_incr"],
+            log_norm=out["log_norm"], ess=out["ess"], resampled=out["resampled"],
+            ancestors=out["ancestors"], bonus=out["bonus"], out_tokens=out["out_tokens"],
+            tv=out["tv"], page_table_in=tables[p], page_table_out=tables[1 - p],
+            refcount=inp["refcount"], error_flags=out["error_flags"], workspace=out["workspace"],
+            V=w.V, mode=w.mode, ess_frac=w.ess_frac) for p in (0, 1)]
+
+        def step(t, timing=None):
+            calls[t % 2].launch(timing_events=timing)
 
     for t in range(args.warmup):
         step(t)
     torch.cuda.synchronize()
     print("# warmup done", file=sys.stderr, flush=True)
     cur_stream = torch.cuda.current_stream(dev).cuda_stream
+    # Timed steps: whole rounds back to back (or, with --flush, each after the cache flush,
+    # timed by events around all of its launches). No event sits inside a round here: each
+    # costs a few microseconds of queue time, which a small round would pay several times.
     t0 = time.perf_counter()
     for t in range(args.steps):
         if args.flush:
             flush_caches(flush_buf)
             ev.record(rounds[t][0], cur_stream)
-        step(args.warmup + t, timing=pairs[t])
+        step(args.warmup + t)
         if args.flush:
             ev.record(rounds[t][1], cur_stream)
     torch.cuda.synchronize()
     elapsed = time.perf_counter() - t0
+    # Kernel times: the same number of rounds again, with HIP events recorded by the library
+    # on the round's stream around the logits pass and between its two kernels.
+    for t in range(args.steps):
+        if args.flush:
+            flush_caches(flush_buf)
+        step(args.warmup + args.steps + t, timing=pairs[t])
+    torch.cuda.synchronize()
     flags = int(out["error_flags"].item())
     if flags:
         raise SystemExit("device error flags %d" % flags)
@@ -515,7 +545,8 @@ def main():
                    "bonus": (args.bonus if args.path in ("round", "driver") else None),
                    "timing": ("each round alone (events around all its launches) after a 1 GiB "
                               "write that evicts the L2s and the Infinity Cache" if args.flush
-                              else "rounds back to back, wall clock over the timed steps"),
+                              else "rounds back to back, wall clock over the timed steps") +
+                             "; kernel times from events in a second pass of as many rounds",
                    "round_GBps": (logits_bytes + table_bytes) / (ms_per_step * 1e-3) / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,
