@@ -507,7 +507,8 @@ struct TvLds {
 template <int DT, bool kFast>
 __device__ void pair_slice_tv(const LogitsArgs& a, uint32_t u, int s, int64_t next,
                               const SliceMask<DT, kTvCPL>& mask, int c0, int n, u32x4 (&P)[kTvCPL],
-                              u32x4 (&Q)[kTvCPL], TvLds& sh, uint32_t& r_lo, float& c_r) {
+                              u32x4 (&Q)[kTvCPL], TvLds& sh, uint32_t& r_lo, float& c_r,
+                              float& early_mp, float& early_mq) {
     constexpr int NE = kTvCPL * Elem<DT>::EPC;
     constexpr int EPC = Elem<DT>::EPC;
     const int tid = threadIdx.x;
@@ -539,8 +540,11 @@ __device__ void pair_slice_tv(const LogitsArgs& a, uint32_t u, int s, int64_t ne
         mask.apply(Pm);
         mask.apply(Qm);
     }
-    const float mpw = wave_share_max<DT, kTvCPL>(Pm);
-    const float mqw = wave_share_max<DT, kTvCPL>(Qm);
+    // the wave maxima, unless this wave took them while it waited for the previous row
+    // pair's exchange (early_mp is NaN when it did not)
+    const bool have_early = kFast && early_mp == early_mp;
+    const float mpw = have_early ? early_mp : wave_share_max<DT, kTvCPL>(Pm);
+    const float mqw = have_early ? early_mq : wave_share_max<DT, kTvCPL>(Qm);
     // The next row pair's loads go into P and Q chunk group by chunk group, each right after
     // the group's exponentials: early, without copies of the registers they overwrite, and
     // without a branch (with no next row pair the buffer range is empty and the loads read
@@ -620,6 +624,16 @@ __device__ void pair_slice_tv(const LogitsArgs& a, uint32_t u, int s, int64_t ne
         }
         if (lane == 0) sh.norm = make_float4(Mp, Sp, Mq, Sq);
     }
+    // Waves 1..7 would only wait here while wave 0 takes the exchange: they take the next
+    // row pair's wave maxima now (its loads are in P and Q), which moves 2 x 29 of their
+    // instructions per row pair off the path to the next publish. Wave 0 keeps its own in
+    // phase 1: taken here they would delay the exchange barrier for everyone (measured
+    // slower). With the mask-free slices only (masking would need copies held until then).
+    early_mp = early_mq = __builtin_nanf("");
+    if (kFast && tid >= 64 && next >= 0) {
+        early_mp = wave_share_max<DT, kTvCPL>(P);
+        early_mq = wave_share_max<DT, kTvCPL>(Q);
+    }
     __syncthreads();
     __builtin_amdgcn_s_setprio(1);
     const float4 nrm = sh.norm;
@@ -672,9 +686,10 @@ __global__ __launch_bounds__(kThreads, 4) void k_logits_tv(LogitsArgs a) {
     const uint32_t nk = (uint32_t)a.N * (uint32_t)a.K;
     uint32_t r_lo = (uint32_t)cluster / nk * nk;   // first row pair of the current request
     float c_r = kLog2e / load_constant(a.temperature, (uint32_t)cluster / nk);
+    float early_mp = __builtin_nanf(""), early_mq = __builtin_nanf("");
     for (int64_t it = cluster; it < a.pairs; it += C)
         pair_slice_tv<DT, kFast>(a, (uint32_t)it, s, it + C < a.pairs ? it + C : -1, mask, c0,
-                                 c1 - c0, P, Q, sh, r_lo, c_r);
+                                 c1 - c0, P, Q, sh, r_lo, c_r, early_mp, early_mq);
 }
 
 // TV off: slice partials only. Each wave shifts its exponentials by the maximum of its own
