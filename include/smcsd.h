@@ -151,9 +151,10 @@ typedef struct smcsd_round_args {
                                     section 5). -inf removes a particle; at least one particle
                                     per request must stay finite. NULL = phi = 1. */
     smcsd_event timing_split;    /* optional: with TV on and the bonus drawn in the pass,
-                                    recorded between the row-pair kernel and the bonus-row
-                                    kernel (timing_begin..timing_split then brackets the
-                                    row pairs alone); otherwise recorded with timing_end */
+                                    recorded between the bonus-row kernel, which runs first,
+                                    and the row-pair kernel (timing_split..timing_end then
+                                    brackets the row pairs alone); otherwise recorded with
+                                    timing_end */
 } smcsd_round_args;
 
 /*

@@ -59,7 +59,7 @@ bool make_plan(int32_t R, int32_t N, int32_t K, int32_t V, int64_t ld, int32_t d
     q.off_pp = off;
     off = align256(off + sizeof(PairPart) * (size_t)q.pair_wgs);
     q.off_tvp = off;
-    off = align256(off + (tv ? sizeof(float) * (size_t)q.pair_wgs * kWaves : 0));
+    off = align256(off + (tv ? sizeof(float) * (size_t)q.pair_wgs : 0));   // per (pair, slice)
     q.off_bp = off;
     off = align256(off + sizeof(BonusPart) * (size_t)(q.bonus_rows * q.S));
     q.off_terms = off;
@@ -148,17 +148,36 @@ static smcsd_status check_verify(const smcsd_verify_args* a, Plan* plan) {
 // A persistent grid's share of the bonus rows ran slower than this ordinary grid.
 static_assert(kTvCPL == kTopkCPL, "bonus slices of the TV plan are Gumbel-Top-K slices");
 
+static hipError_t record(smcsd_event ev, hipStream_t s) {
+    return ev ? hipEventRecord(reinterpret_cast<hipEvent_t>(ev), s) : hipSuccess;
+}
+
+// The logits pass of a round, bracketed by the optional timing events (split: see
+// smcsd_round_args). TV off: one kernel. TV on: the bonus rows first, in the Gumbel-Top-K
+// slice kernel, which also resets the control word and the exchange words of the row-pair
+// kernel that follows (a fill kernel does that when there are no bonus rows), then the row
+// pairs. Kernels, not memset nodes, so the sequence can be captured in a graph.
 static hipError_t launch_logits_pass(const Plan& plan, const LogitsArgs& la, hipStream_t s,
-                                     smcsd_event split = nullptr) {
-    if (!plan.tv) return launch_logits(plan, la, s);
+                                     smcsd_event begin, smcsd_event split, smcsd_event end) {
+    hipError_t e = hipSuccess;
+    if (!plan.tv) {
+        if ((e = record(begin, s)) != hipSuccess || (e = launch_logits(plan, la, s)) != hipSuccess ||
+            (e = record(split, s)) != hipSuccess)
+            return e;
+        return record(end, s);
+    }
     Plan pairs = plan;
     pairs.bonus_rows = 0;
     pairs.total_wgs = plan.pair_wgs;
     LogitsArgs lp = la;
     lp.total_wgs = la.pair_wgs;
-    hipError_t e = launch_logits(pairs, lp, s);
-    if (e != hipSuccess || plan.bonus_rows == 0) return e;
-    if (split && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(split), s)) != hipSuccess) return e;
+    const uint32_t timeout = exchange_timeout_ticks();
+    if (plan.bonus_rows == 0) {
+        if ((e = launch_tv_fill(plan, la, timeout, s)) != hipSuccess || (e = record(begin, s)) != hipSuccess ||
+            (e = launch_logits(pairs, lp, s)) != hipSuccess || (e = record(split, s)) != hipSuccess)
+            return e;
+        return record(end, s);
+    }
     TopkArgs t{};
     t.logits = la.target;
     t.temperature = la.temperature;
@@ -174,19 +193,14 @@ static hipError_t launch_logits_pass(const Plan& plan, const LogitsArgs& la, hip
     t.cps = plan.cps;
     t.N = la.N;
     t.K = la.K;
-    return launch_topk_slices(plan.bonus_rows, plan.dtype, t, s);
-}
-
-// The TV pass of the round over the given logits: exchange slots filled, then the pass,
-// bracketed by the optional timing events.
-static hipError_t run_tv_pass(const Plan& plan, const LogitsArgs& la, smcsd_event begin,
-                              smcsd_event end, hipStream_t s) {
-    hipError_t e = launch_tv_fill(plan, la, exchange_timeout_ticks(), s);
-    if (e != hipSuccess) return e;
-    if (begin && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(begin), s)) != hipSuccess) return e;
-    if ((e = launch_logits_pass(plan, la, s)) != hipSuccess) return e;
-    if (end && (e = hipEventRecord(reinterpret_cast<hipEvent_t>(end), s)) != hipSuccess) return e;
-    return hipSuccess;
+    t.ctrl = la.ctrl;
+    t.fill_words = reinterpret_cast<uint32_t*>(la.pp);
+    t.fill_n = plan.pair_wgs * (int64_t)(sizeof(PairPart) / 4);
+    t.timeout = timeout;
+    if ((e = record(begin, s)) != hipSuccess || (e = launch_topk_slices(plan.bonus_rows, plan.dtype, t, s)) != hipSuccess ||
+        (e = record(split, s)) != hipSuccess || (e = launch_logits(pairs, lp, s)) != hipSuccess)
+        return e;
+    return record(end, s);
 }
 
 // Slices of a Gumbel-Top-K row: as the TV pass (512 lanes x 4 chunks at most per slice).
@@ -273,23 +287,8 @@ smcsd_status enqueue_round(const smcsd_round_args& a, const Plan& plan, char* ws
     la.S = plan.S;
     la.cps = plan.cps;
 
-    hipError_t e = hipSuccess;
-    if (plan.tv) {
-        // the control word starts with abort 0 and the wait limit, every exchange word at the
-        // all-ones "empty" pattern (a fill kernel, not memset nodes, so the sequence can be
-        // captured in a graph)
-        e = launch_tv_fill(plan, la, exchange_timeout_ticks(), s);
-        if (e != hipSuccess) return SMCSD_ERR_DEVICE;
-    }
-    if (a.timing_begin && hipEventRecord(reinterpret_cast<hipEvent_t>(a.timing_begin), s) != hipSuccess)
-        return SMCSD_ERR_DEVICE;
-    e = launch_logits_pass(plan, la, s, a.timing_split);
+    hipError_t e = launch_logits_pass(plan, la, s, a.timing_begin, a.timing_split, a.timing_end);
     if (e != hipSuccess) return SMCSD_ERR_DEVICE;
-    if (a.timing_split && !(plan.tv && plan.bonus_rows > 0) &&
-        hipEventRecord(reinterpret_cast<hipEvent_t>(a.timing_split), s) != hipSuccess)
-        return SMCSD_ERR_DEVICE;
-    if (a.timing_end && hipEventRecord(reinterpret_cast<hipEvent_t>(a.timing_end), s) != hipSuccess)
-        return SMCSD_ERR_DEVICE;
 
     FinalizeArgs fa{};
     fa.target = a.target_logits;
@@ -565,7 +564,7 @@ smcsd_status smcsd_sd_verify(const smcsd_verify_args* args, smcsd_stream stream)
     la.chunks = plan.chunks;
     la.S = plan.S;
     la.cps = plan.cps;
-    if (run_tv_pass(plan, la, a.timing_begin, a.timing_end, s) != hipSuccess)
+    if (launch_logits_pass(plan, la, s, a.timing_begin, nullptr, a.timing_end) != hipSuccess)
         return SMCSD_ERR_DEVICE;
 
     VerifyArgs va{};

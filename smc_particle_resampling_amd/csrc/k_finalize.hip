@@ -10,6 +10,12 @@
 // U_j == C_i therefore resolves the same way on every run. When the round carries a page
 // table, the same workgroup then remaps its request's table rows through the ancestors
 // (pointer exchange, as k_remap does), which saves the round a launch.
+//
+// Two kernels. k_finalize_small takes the common case (at most one position a thread and
+// at most 64 particles) with everything of the request in LDS: it runs once per round on
+// one workgroup per request, so its time is latency, and it keeps the chain of dependent
+// steps and the instructions it executes few. k_finalize takes every other size, and the
+// resampling of given increments (smcsd_resample).
 #include "remap_rows.h"
 #include "smcsd_device.h"
 
@@ -17,6 +23,128 @@ namespace smcsd {
 namespace {
 
 constexpr float kLog2e = 1.44269504088896340736f;
+
+constexpr int kTvRegs = 16;   // per-slice TV partials of a position held in registers
+
+// The loads of one position (token, its S slice parts, the first kTvRegs of its per-slice
+// sums of |p - q|), issued together; nothing here waits for them.
+struct PositionLoads {
+    int32_t x;
+    PairPart v[kPartRegs];
+    float tvs[kTvRegs];
+};
+
+__device__ __forceinline__ void issue_position(const FinalizeArgs& a, int64_t u, PositionLoads& L) {
+    L.x = a.tokens[u];
+    load_parts(a.pp + u * a.S, a.S, L.v);
+    if (a.tv) {
+        const float* tp = a.tvp + u * a.S;
+#pragma unroll
+        for (int t = 0; t < kTvRegs; ++t)
+            if (t < a.S) L.tvs[t] = tp[t];
+    }
+}
+
+// The position's log p(x) - log q(x) = (zp[x] - Mp)/T - log Sp - ((zq[x] - Mq)/T - log Sq),
+// 0 with an error flag when the token is out of range; and, with TV, its total-variation
+// distance, written to a.tv (partials summed in order).
+template <int DT>
+__device__ __forceinline__ double position_term(const FinalizeArgs& a, int64_t ri, int64_t u, int32_t k,
+                                                const PositionLoads& L, float c, double invT) {
+    float Mp, Mq;
+    double Sp, Sq;
+    pair_norms_from(a.pp + u * a.S, L.v, a.S, c, Mp, Mq, Sp, Sq);
+    double term = 0.0;
+    if (L.x < 0 || L.x >= a.V) {
+        flag_error(a.error_flags, SMCSD_DEVERR_TOKEN);
+    } else {
+        const double zp = logit_at<DT>(a.target, ri * (a.K + 1) + k, a.ld, L.x);
+        const double zq = logit_at<DT>(a.draft, u, a.ld, L.x);
+        term = ((zp - (double)Mp) - (zq - (double)Mq)) * invT - (log(Sp) - log(Sq));
+    }
+    if (a.tv) {
+        const float* tp = a.tvp + u * a.S;
+        double t2 = 0.0;
+#pragma unroll
+        for (int t = 0; t < kTvRegs; ++t)
+            if (t < a.S) t2 += (double)L.tvs[t];
+        for (int t0 = kTvRegs; t0 < a.S; t0 += 8) {
+            float w[8];
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+                if (t0 + b < a.S) w[b] = tp[t0 + b];
+#pragma unroll
+            for (int b = 0; b < 8; ++b)
+                if (t0 + b < a.S) t2 += (double)w[b];
+        }
+        a.tv[u] = (float)fmin(fmax(0.5 * t2, 0.0), 1.0);
+    }
+    return term;
+}
+
+// Particle ri's bonus token: the best (key, index) over its S slices, slices in batches of
+// 8 (-1 without noise: out_tokens then get -1 in column K). Written to a.bonus too.
+__device__ __forceinline__ int32_t bonus_of(const FinalizeArgs& a, int64_t ri) {
+    if (!a.bp) return -1;
+    const BonusPart* bpart = a.bp + ri * a.S;
+    float best = -INFINITY;
+    int32_t besti = INT32_MAX;
+    for (int t0 = 0; t0 < a.S; t0 += 8) {
+        BonusPart w[8];
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+            if (t0 + b < a.S) w[b] = bpart[t0 + b];
+#pragma unroll
+        for (int b = 0; b < 8; ++b)
+            if (t0 + b < a.S && (t0 + b == 0 || better(w[b].key, w[b].idx, best, besti))) {
+                best = w[b].key;
+                besti = w[b].idx;
+            }
+    }
+    if (besti < 0 || besti >= a.V) besti = 0;   // only if every key was NaN
+    a.bonus[ri] = besti;
+    return besti;
+}
+
+// Up to 64 particles, one wave, lane i = particle i (l_i in s_l): DPP reductions (every lane
+// ends with the same bits) and an inclusive prefix scan of the weights, all in double
+// precision. Writes C_i (resampling) or W_i to s_c and the request's outputs.
+__device__ __forceinline__ void weights_wave(const FinalizeArgs& a, int64_t r, int32_t N, const double* s_l,
+                                             double* s_c, double* s_logZ, int32_t* s_rs) {
+    const int i = threadIdx.x;
+    const double l = i < N ? s_l[i] : -INFINITY;
+    const double m = wave_max_f64(l);
+    const double e = i < N ? exp(l - m) : 0.0;
+    const double se = wave_sum_f64(e);
+    const double w = e / se;
+    const double s2 = wave_sum_f64(w * w);
+    const double logZ = m + log(se);
+    const double ess = 1.0 / s2;
+    const int32_t rs = a.mode == SMCSD_RESAMPLE_ALWAYS ||
+                       (a.mode == SMCSD_RESAMPLE_ESS && ess < (double)a.ess_frac * (double)N);
+    const double acc = wave_scan_f64(w);
+    if (i < N) s_c[i] = rs ? acc : w;
+    if (i == 0) {
+        a.log_norm[r] = (float)logZ;
+        a.ess[r] = (float)ess;
+        a.resampled[r] = rs;
+        *s_logZ = logZ;
+        *s_rs = rs;
+    }
+}
+
+// Systematic resampling: slot j's ancestor min{i : U_j < C_i}, U_j = (j + u) / N, the last
+// index standing in for "none" (clamp to N - 1).
+__device__ __forceinline__ int32_t ancestor_of(int32_t j, double u, int32_t N, const double* s_c) {
+    const double U = ((double)j + u) / (double)N;
+    int32_t lo = 0, hi = N - 1;
+    while (lo < hi) {
+        const int32_t mid = (lo + hi) >> 1;
+        if (U < s_c[mid]) hi = mid;
+        else lo = mid + 1;
+    }
+    return lo;
+}
 
 template <int DT, bool FROM_PARTIALS>
 __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
@@ -32,6 +160,8 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
     const int tid = threadIdx.x;
     const int64_t r = blockIdx.x;
     const int32_t N = a.N, K = a.K;
+    // The request's uniform, loaded now: nothing of the round writes it.
+    const double u_r = (double)a.uniform[r];
 
     // The input page table does not depend on this round's ancestors, so its loads (16 a
     // thread at most; launch_finalize takes no larger table) are issued first; they arrive
@@ -57,57 +187,13 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
         // The token, the S slice parts and (with TV) the first 16 float4 of the position's
         // S * kWaves partials are all loaded before any of them is used, so a thread waits
         // for memory a few times rather than once per load. Every sum keeps its order.
-        constexpr int kTvRegs = 16;
         for (int32_t ik = tid; ik < N * K; ik += kThreads) {
             const int32_t i = ik / K, k = ik - i * K;
             const int64_t ri = r * N + i;
             const int64_t u = ri * K + k;
-            const int32_t x = a.tokens[u];
-            const PairPart* part = a.pp + u * a.S;
-            PairPart v[kPartRegs];
-            load_parts(part, a.S, v);
-            // the position's block of partials starts at a multiple of 32 floats
-            const float4* tp = a.tv ? reinterpret_cast<const float4*>(a.tvp + u * a.S * kWaves) : nullptr;
-            const int n4 = a.tv ? a.S * kWaves / 4 : 0;
-            float4 tv4[kTvRegs];
-#pragma unroll
-            for (int t = 0; t < kTvRegs; ++t)
-                if (t < n4) tv4[t] = tp[t];
-            float Mp, Mq;
-            double Sp, Sq;
-            pair_norms_from(part, v, a.S, c, Mp, Mq, Sp, Sq);
-            double term = 0.0;
-            if (x < 0 || x >= a.V) {
-                flag_error(a.error_flags, SMCSD_DEVERR_TOKEN);
-            } else {
-                // (zp[x] - Mp)/T - log Sp  -  ((zq[x] - Mq)/T - log Sq)
-                const double zp = logit_at<DT>(a.target, ri * (K + 1) + k, a.ld, x);
-                const double zq = logit_at<DT>(a.draft, u, a.ld, x);
-                term = ((zp - (double)Mp) - (zq - (double)Mq)) * invT - (log(Sp) - log(Sq));
-            }
-            a.terms[u] = term;
-            if (a.tv) {
-                double t2 = 0.0;
-                auto add4 = [&](const float4& f) {
-                    t2 += (double)f.x;
-                    t2 += (double)f.y;
-                    t2 += (double)f.z;
-                    t2 += (double)f.w;
-                };
-#pragma unroll
-                for (int t = 0; t < kTvRegs; ++t)
-                    if (t < n4) add4(tv4[t]);
-                for (int t0 = kTvRegs; t0 < n4; t0 += 8) {
-                    float4 w[8];
-#pragma unroll
-                    for (int b = 0; b < 8; ++b)
-                        if (t0 + b < n4) w[b] = tp[t0 + b];
-#pragma unroll
-                    for (int b = 0; b < 8; ++b)
-                        if (t0 + b < n4) add4(w[b]);
-                }
-                a.tv[u] = (float)fmin(fmax(0.5 * t2, 0.0), 1.0);
-            }
+            PositionLoads L;
+            issue_position(a, u, L);
+            a.terms[u] = position_term<DT>(a, ri, u, k, L, c, invT);
         }
         if (staged) {
 #pragma unroll
@@ -116,36 +202,13 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
                 if (e < NP) s_pt[e] = ptv[b];
             }
         }
-        // one thread per particle: its bonus token, the best (key, index) over the slices
-        // (none without noise: out_tokens then get -1 in column K); slices in batches of 8.
-        // When the positions leave enough threads idle, those threads take the particles, so
-        // these loads overlap the ones above.
-        const int32_t boff = N * K + N <= kThreads ? N * K : 0;
-        for (int32_t i = tid - boff; i < N; i += kThreads) {
-            if (i < 0) continue;
-            if (!a.bp) {
-                s_bonus[i] = -1;
-                continue;
-            }
-            const BonusPart* bpart = a.bp + (r * N + i) * a.S;
-            float best = -INFINITY;
-            int32_t besti = INT32_MAX;
-            for (int t0 = 0; t0 < a.S; t0 += 8) {
-                BonusPart w[8];
-#pragma unroll
-                for (int b = 0; b < 8; ++b)
-                    if (t0 + b < a.S) w[b] = bpart[t0 + b];
-#pragma unroll
-                for (int b = 0; b < 8; ++b)
-                    if (t0 + b < a.S && (t0 + b == 0 || better(w[b].key, w[b].idx, best, besti))) {
-                        best = w[b].key;
-                        besti = w[b].idx;
-                    }
-            }
-            if (besti < 0 || besti >= a.V) besti = 0;   // only if every key was NaN
-            a.bonus[r * N + i] = besti;
-            s_bonus[i] = besti;
-        }
+        // one thread per particle: its bonus token. When the positions leave enough threads
+        // idle, the waves after theirs take the particles, so these loads overlap the ones
+        // above (a wave of their own issues them at once).
+        const int32_t pos_end = (N * K + 63) / 64 * 64;
+        const int32_t boff = pos_end + N <= kThreads ? pos_end : 0;
+        for (int32_t i = tid - boff; i < N; i += kThreads)
+            if (i >= 0) s_bonus[i] = bonus_of(a, r * N + i);
         __syncthreads();   // terms written above are read by other threads below
         for (int32_t i = tid; i < N; i += kThreads) {
             const int64_t ri = r * N + i;
@@ -178,41 +241,7 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
     __syncthreads();
 
     if (N <= 64) {
-        // one wave, lane i = particle i: butterfly reductions (every lane ends with the same
-        // bits) and an inclusive prefix scan of the weights, all in double precision
-        if (tid < 64) {
-            const int i = tid;
-            const double l = i < N ? s_l[i] : -INFINITY;
-            double m = l;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) m = fmax(m, __shfl_xor(m, d));
-            const double e = i < N ? exp(l - m) : 0.0;
-            double se = e;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) se += __shfl_xor(se, d);
-            const double w = e / se;
-            double s2 = w * w;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) s2 += __shfl_xor(s2, d);
-            const double logZ = m + log(se);
-            const double ess = 1.0 / s2;
-            const int32_t rs = a.mode == SMCSD_RESAMPLE_ALWAYS ||
-                               (a.mode == SMCSD_RESAMPLE_ESS && ess < (double)a.ess_frac * (double)N);
-            double acc = w;
-#pragma unroll
-            for (int d = 1; d < 64; d <<= 1) {
-                const double o = __shfl_up(acc, d);
-                if (i >= d) acc += o;
-            }
-            if (i < N) s_c[i] = rs ? acc : w;
-            if (i == 0) {
-                a.log_norm[r] = (float)logZ;
-                a.ess[r] = (float)ess;
-                a.resampled[r] = rs;
-                s_logZ = logZ;
-                s_rs = rs;
-            }
-        }
+        if (tid < 64) weights_wave(a, r, N, s_l, s_c, &s_logZ, &s_rs);
     } else {
         // more than 64 particles: the whole workgroup, each thread on the particles 2t and
         // 2t + 1 (N <= 2 * kThreads); every reduction and the scan combine in one fixed
@@ -284,20 +313,8 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
 
     const int32_t rs = s_rs;
     const double logZ = s_logZ;
-    const double u = (double)a.uniform[r];
     for (int32_t j = tid; j < N; j += kThreads) {
-        int32_t anc = j;
-        if (rs) {
-            // min{i : U_j < C_i}, the last index standing in for "none" (clamp to N-1)
-            const double U = ((double)j + u) / (double)N;
-            int32_t lo = 0, hi = N - 1;
-            while (lo < hi) {
-                const int32_t mid = (lo + hi) >> 1;
-                if (U < s_c[mid]) hi = mid;
-                else lo = mid + 1;
-            }
-            anc = lo;
-        }
+        const int32_t anc = rs ? ancestor_of(j, u_r, N, s_c) : j;
         a.ancestors[r * N + j] = anc;
         s_anc[j] = anc;
         if (a.pt_in) atomicAdd(&s_off[anc], 1);
@@ -334,6 +351,97 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
     }
 }
 
+// The common case, at most one position a thread (N * K <= kThreads) and at most 64
+// particles, as one short kernel with every value of the request in LDS. Same results as
+// k_finalize. Every load that depends on no other load (the uniform, the page table, the
+// previous log-weights, each position's token, slice parts and TV partials, the bonus
+// parts) is issued before the first wait; the gather of the two logits at the token is the
+// only dependent one. A kernel's instruction cache is cold when it starts, so the code that
+// runs is kept short: this kernel is mostly latency.
+template <int DT>
+__global__ __launch_bounds__(kThreads) void k_finalize_small(FinalizeArgs a) {
+    constexpr int kMaxN = 64;
+    constexpr int kPtRegs = kFusedRemapEntries / kThreads;
+    __shared__ double s_term[kThreads];    // the positions' log-ratios
+    __shared__ int32_t s_tok[kThreads];    // the drafted tokens
+    __shared__ double s_l[kMaxN];          // l_i = log_weights_i + log_w_incr_i
+    __shared__ double s_c[kMaxN];          // W_i, then C_i
+    __shared__ int32_t s_bonus[kMaxN];
+    __shared__ int32_t s_anc[kMaxN];
+    __shared__ int32_t s_off[kMaxN];       // offspring counts o_i
+    __shared__ int32_t s_pt[kFusedRemapEntries];   // the request's input page table
+    __shared__ int16_t s_dl[kFusedRemapEntries];   // refcount change of the run ending at each entry
+    __shared__ double s_logZ;
+    __shared__ int32_t s_rs;
+    const int tid = threadIdx.x;
+    const int64_t r = blockIdx.x;
+    const int32_t N = a.N, K = a.K, NK = N * K;
+    const double u_r = (double)a.uniform[r];
+    const float T = a.temperature[r];
+    const int32_t NP = a.pt_in ? N * a.P : 0;
+    double lw_prev = 0.0, lpot = 0.0;
+    if (tid < N) {
+        lw_prev = (double)a.log_weights[r * N + tid];
+        if (a.log_potential) lpot = (double)a.log_potential[r * N + tid];
+    }
+    // thread tid < NK: position (i, k); the particles' bonus parts go to the waves after the
+    // positions' when they fit (a wave of their own issues its loads at once), else to the
+    // position threads after their position. The page table, needed last, is loaded after
+    // the positions' values, so that those come first.
+    const int32_t pos_end = (NK + 63) / 64 * 64;
+    const int32_t boff = pos_end + N <= kThreads ? pos_end : 0;
+    PositionLoads L;
+    const int32_t i = tid < NK ? tid / K : 0, k = tid - i * K;
+    const int64_t ri = r * N + i, u = ri * K + k;
+    if (tid < NK) issue_position(a, u, L);
+    int32_t ptv[kPtRegs];
+#pragma unroll
+    for (int b = 0; b < kPtRegs; ++b) {
+        const int32_t e = b * kThreads + tid;
+        if (e < NP) ptv[b] = a.pt_in[r * NP + e];
+    }
+    if (tid < NK) {
+        s_term[tid] = position_term<DT>(a, ri, u, k, L, kLog2e / T, 1.0 / (double)T);
+        s_tok[tid] = L.x;
+    }
+    if (tid >= boff && tid < boff + N) s_bonus[tid - boff] = bonus_of(a, r * N + (tid - boff));
+#pragma unroll
+    for (int b = 0; b < kPtRegs; ++b) {
+        const int32_t e = b * kThreads + tid;
+        if (e < NP) s_pt[e] = ptv[b];
+    }
+    if (tid < N) s_off[tid] = 0;
+    __syncthreads();
+    if (tid < N) {
+        double lw = 0.0;
+        for (int32_t k = 0; k < K; ++k) lw += s_term[tid * K + k];
+        if (a.log_potential) lw += lpot;
+        a.log_w_incr[r * N + tid] = (float)lw;
+        s_l[tid] = lw_prev + lw;
+    }
+    __syncthreads();
+    if (tid < 64) weights_wave(a, r, N, s_l, s_c, &s_logZ, &s_rs);
+    __syncthreads();
+    if (tid < N) {
+        const int32_t j = tid;
+        const int32_t anc = s_rs ? ancestor_of(j, u_r, N, s_c) : j;
+        a.ancestors[r * N + j] = anc;
+        s_anc[j] = anc;
+        if (NP > 0) atomicAdd(&s_off[anc], 1);
+        a.log_weights[r * N + j] = s_rs ? (float)(-log((double)N)) : (float)(s_l[j] - s_logZ);
+        if (a.out_tokens) {
+            int32_t* dst = a.out_tokens + (r * N + j) * (K + 1);
+            for (int32_t k = 0; k < K; ++k) dst[k] = s_tok[anc * K + k];
+            dst[K] = s_bonus[anc];
+        }
+    }
+    if (NP > 0) {
+        __syncthreads();
+        remap_request_lds<kPtRegs>(s_pt, s_dl, a.pt_out + r * NP, s_anc, s_off, N, a.P, a.refcount,
+                                   a.num_pages, a.error_flags);
+    }
+}
+
 }  // namespace
 
 hipError_t launch_finalize(int32_t R, bool from_partials, int32_t dtype, const FinalizeArgs& a,
@@ -341,7 +449,10 @@ hipError_t launch_finalize(int32_t R, bool from_partials, int32_t dtype, const F
     // the page table is staged in LDS: larger ones go to launch_remap instead
     if (a.pt_in && (int64_t)a.N * a.P > kFusedRemapEntries) return hipErrorInvalidValue;
     const dim3 grid((unsigned)R), block(kThreads);
-    if (!from_partials) {
+    if (from_partials && a.N <= 64 && a.N * a.K <= kThreads) {
+        if (dtype == SMCSD_BF16) k_finalize_small<SMCSD_BF16><<<grid, block, 0, s>>>(a);
+        else k_finalize_small<SMCSD_F32><<<grid, block, 0, s>>>(a);
+    } else if (!from_partials) {
         k_finalize<SMCSD_F32, false><<<grid, block, 0, s>>>(a);
     } else if (dtype == SMCSD_BF16) {
         k_finalize<SMCSD_BF16, true><<<grid, block, 0, s>>>(a);

@@ -120,6 +120,14 @@ __global__ __launch_bounds__(kThreads, 8) void k_topk_slice(TopkArgs a) {
         trow = r;
         lrow = (int64_t)src * (a.K + 1) + a.K;
     }
+    if constexpr (MODE == kTopkBonusRows) {
+        if (a.fill_words) {
+            if (blockIdx.x == 0 && tid == 0) *a.ctrl = Ctrl{0u, a.timeout};
+            for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < a.fill_n;
+                 i += (int64_t)gridDim.x * kThreads)
+                a.fill_words[i] = ~0u;
+        }
+    }
     const char* zrow = static_cast<const char*>(a.logits) + (size_t)(lrow * a.ld) * ESZ;
     const float* grow = a.gumbel + (size_t)row * a.ld;
     const float invT = __fdiv_rn(1.0f, a.temperature[trow]);

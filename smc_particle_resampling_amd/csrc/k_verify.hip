@@ -50,7 +50,7 @@ __global__ __launch_bounds__(kThreads) void k_verify_decide(VerifyArgs a) {
         a.terms[u] = term;
         if (a.tv) {
             double t2 = 0.0;
-            for (int t = 0; t < a.S * kWaves; ++t) t2 += (double)a.tvp[u * a.S * kWaves + t];
+            for (int t = 0; t < a.S; ++t) t2 += (double)a.tvp[u * a.S + t];
             a.tv[u] = (float)fmin(fmax(0.5 * t2, 0.0), 1.0);
         }
     }
@@ -87,8 +87,7 @@ __global__ __launch_bounds__(kThreads) void k_verify_decide(VerifyArgs a) {
             pair_norms(part, a.S, c, Mp, Mq, Sp, Sq);
             // residual mass of slice t: (sum|p - q| + P_t - Q_t) / 2, never below 0
             auto slice_res = [&](int t) {
-                double d = 0.0;
-                for (int w = 0; w < kWaves; ++w) d += (double)a.tvp[(u * a.S + t) * kWaves + w];
+                const double d = (double)a.tvp[u * a.S + t];
                 const double P = (double)part[t].sp * (double)__builtin_amdgcn_exp2f((part[t].mp - Mp) * c) / Sp;
                 const double Q = (double)part[t].sq * (double)__builtin_amdgcn_exp2f((part[t].mq - Mq) * c) / Sq;
                 return fmax(0.5 * (d + P - Q), 0.0);

@@ -129,4 +129,77 @@ __device__ __forceinline__ void remap_columns_runs(const int32_t* in, int32_t* o
     }
 }
 
+// The same remap for a whole request of at most 64 particles held in LDS (in: its N * P
+// entries, at most kPer * blockDim.x), one workgroup, with every refcount atomic in flight
+// at once. The table copy; then one thread per column walks its rows and writes, for every
+// entry, the net change of the run that ends there (0 where no run ends, the run names no
+// page, or the change is 0) into dl; after a barrier every thread adds the
+// changes of its kPer entries, one atomic each, and checks the results only once all of them
+// are issued. A change fits in 16 bits: at most 64 rows, each o_j - 1 in [-1, 63]. Same
+// refcounts and checks as remap_columns_runs.
+template <int kPer>
+__device__ __forceinline__ void remap_request_lds(const int32_t* in, int16_t* dl, int32_t* out,
+                                                  const int32_t* anc, const int32_t* off, int32_t N,
+                                                  int32_t P, int32_t* refcount, int32_t num_pages,
+                                                  int32_t* error_flags) {
+    const int32_t NP = N * P;
+    const int32_t tid = (int32_t)threadIdx.x, nt = (int32_t)blockDim.x;
+    if (nt % P == 0) {
+        // a thread keeps one column
+        const int32_t col = tid % P, dj = nt / P;
+#pragma unroll 4
+        for (int32_t j = tid / P; j < N; j += dj) {
+            const int32_t src = anc[j];
+            out[j * P + col] = src >= 0 ? in[src * P + col] : -1;
+        }
+    } else {
+        int32_t j = tid / P;
+        int32_t col = tid - j * P;
+        const int32_t dj = nt / P, dc = nt - dj * P;
+        while (j < N) {
+            const int32_t src = anc[j];
+            out[j * P + col] = src >= 0 ? in[src * P + col] : -1;
+            step_entry(j, col, dj, dc, P);
+        }
+    }
+    // The walk has no branch but the loop's: with at most two waves a SIMD nothing hides a
+    // branch's cost. Row j >= 1 closes the run that row j - 1 ended, if the page changes.
+    // Lane l holds o_l - 1 (N <= 64), read per row with readlane.
+    const int32_t lane = tid & 63;
+    const int32_t offv = lane < N ? off[lane] - 1 : 0;
+    bool bad = false;
+    for (int32_t c = tid; c < P; c += nt) {
+        int32_t run_page = in[c], run_delta = __builtin_amdgcn_readlane(offv, 0);
+        bool run_moves = run_delta != 0;
+#pragma unroll 4
+        for (int32_t j = 1; j <= N; ++j) {
+            const int32_t jc = min(j, N - 1);
+            const int32_t pgr = in[jc * P + c];          // always in range; row N is past the end
+            const int32_t pg = j < N ? pgr : -1;
+            const int32_t od = j < N ? __builtin_amdgcn_readlane(offv, jc) : 0;
+            const bool changed = j == N || pg != run_page;
+            const bool counts = changed && run_page >= 0 && run_moves;
+            bad = bad || (counts && run_page >= num_pages);
+            dl[(j - 1) * P + c] = (int16_t)(counts && run_page < num_pages ? run_delta : 0);
+            run_delta = (changed ? 0 : run_delta) + od;
+            run_moves = (!changed && run_moves) || od != 0;
+            run_page = pg;
+        }
+    }
+    __syncthreads();
+    int32_t old[kPer], d[kPer];
+#pragma unroll
+    for (int b = 0; b < kPer; ++b) {
+        const int32_t e = b * nt + tid;
+        d[b] = e < NP ? (int32_t)dl[e] : 0;
+        old[b] = 0;
+        if (d[b] != 0) old[b] = atomicAdd(&refcount[in[e]], d[b]);
+    }
+    bool neg = false;
+#pragma unroll
+    for (int b = 0; b < kPer; ++b) neg = neg || (d[b] != 0 && old[b] + d[b] < 0);
+    if (bad) flag_error(error_flags, SMCSD_DEVERR_PAGE);
+    if (neg) flag_error(error_flags, SMCSD_DEVERR_REFCOUNT);
+}
+
 }  // namespace smcsd

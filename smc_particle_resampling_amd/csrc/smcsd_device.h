@@ -75,6 +75,55 @@ __device__ __forceinline__ float wave_sum(float v) {
     return ((readlane_f32(v, 0) + readlane_f32(v, 16)) + readlane_f32(v, 32)) + readlane_f32(v, 48);
 }
 
+// The same reductions in double precision, each DPP step moving the two 32-bit halves.
+// Row masks: kRows selects the 16-lane rows the step writes; the others receive 0.
+constexpr int kDppRowShr1 = 0x111, kDppRowShr2 = 0x112, kDppRowShr4 = 0x114, kDppRowShr8 = 0x118;
+constexpr int kDppRowBcast15 = 0x142;   // lane 15 of each row to the whole next row
+constexpr int kDppRowBcast31 = 0x143;   // lane 31 to rows 2 and 3
+
+template <int kCtrl, int kRows = 0xF>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)b, kCtrl, kRows, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(b >> 32), kCtrl, kRows, 0xF, true);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+__device__ __forceinline__ double readlane_f64(double v, int lane) {
+    const uint64_t b = __builtin_bit_cast(uint64_t, v);
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)b, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(b >> 32), lane);
+    return __builtin_bit_cast(double, ((uint64_t)hi << 32) | lo);
+}
+// Whole-wave max and sum of doubles (every lane active), uniform and bit-identical from run
+// to run, in the order of wave_max and wave_sum.
+__device__ __forceinline__ double wave_max_f64(double v) {
+    v = fmax(v, dpp_f64<kDppXor1>(v));
+    v = fmax(v, dpp_f64<kDppXor2>(v));
+    v = fmax(v, dpp_f64<kDppRowHalfMirror>(v));
+    v = fmax(v, dpp_f64<kDppRowMirror>(v));
+    return fmax(fmax(readlane_f64(v, 0), readlane_f64(v, 16)), fmax(readlane_f64(v, 32), readlane_f64(v, 48)));
+}
+__device__ __forceinline__ double wave_sum_f64(double v) {
+    v += dpp_f64<kDppXor1>(v);
+    v += dpp_f64<kDppXor2>(v);
+    v += dpp_f64<kDppRowHalfMirror>(v);
+    v += dpp_f64<kDppRowMirror>(v);
+    return ((readlane_f64(v, 0) + readlane_f64(v, 16)) + readlane_f64(v, 32)) + readlane_f64(v, 48);
+}
+// Inclusive prefix sum over the 64 lanes (every lane active): a scan within each row (lane k
+// adds lane k - d for d = 1, 2, 4, 8; lanes with k < d add 0), then row 1 and row 3 add the
+// totals of rows 0 and 2, then rows 2 and 3 add lane 31 (the total of rows 0 and 1). A fixed
+// order, so the sums are bit-identical from run to run.
+__device__ __forceinline__ double wave_scan_f64(double v) {
+    v += dpp_f64<kDppRowShr1>(v);
+    v += dpp_f64<kDppRowShr2>(v);
+    v += dpp_f64<kDppRowShr4>(v);
+    v += dpp_f64<kDppRowShr8>(v);
+    v += dpp_f64<kDppRowBcast15, 0xA>(v);
+    v += dpp_f64<kDppRowBcast31, 0xC>(v);
+    return v;
+}
+
 // One logit of a row, widened exactly to double.
 template <int DT>
 __device__ __forceinline__ double logit_at(const void* base, int64_t row, int64_t ld, int32_t v) {

@@ -74,7 +74,7 @@ struct LogitsArgs {
     const float* gumbel;
     Ctrl* ctrl;
     PairPart* pp;
-    float* tvp;
+    float* tvp;               // [pairs][S] each slice's share of sum |p - q| (TV)
     BonusPart* bp;
     int32_t* error_flags;
     int64_t ld;
@@ -176,6 +176,13 @@ struct TopkArgs {
     int64_t ld;
     int32_t V, k, chunks, S, cps;
     int32_t N, K;
+    // kTopkBonusRows ahead of a TV pass: the pass's control word ({0, timeout} to *ctrl) and
+    // its fill_n exchange words (all ones) are written here, which saves the pass a launch.
+    // fill_words nullptr: nothing is written.
+    Ctrl* ctrl;
+    uint32_t* fill_words;
+    int64_t fill_n;
+    uint32_t timeout;
 };
 
 // Page lifecycle between rounds. Workspace: a header (free count before and after release,
