@@ -33,16 +33,20 @@ sys.path.insert(0, ROOT)
 
 PEAK_HBM_GBPS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-KERNEL_SOURCES = ["smc_particle_resampling_amd/csrc/k_logits.hip",
-                  "smc_particle_resampling_amd/csrc/k_topk.hip",
-                  "smc_particle_resampling_amd/csrc/smcsd_internal.h",
-                  "smc_particle_resampling_amd/csrc/smcsd_device.h"]
+# The sources each measured kernel is built from: stored counter results (HBM traffic) are
+# reported only while these still hash to the value recorded with them.
+KERNEL_SOURCES = {
+    "k_logits_tv": ["k_logits_tv.hip", "logits_common.h", "smcsd_device.h", "smcsd_internal.h"],
+    "k_logits_stream": ["k_logits_stream.hip", "logits_common.h", "smcsd_device.h",
+                        "smcsd_internal.h"],
+    "k_topk_slice": ["k_topk.hip", "smcsd_device.h", "smcsd_internal.h"],
+}
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(kernel: str) -> str:
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, p), "rb") as f:
+    for p in KERNEL_SOURCES[kernel]:
+        with open(os.path.join(ROOT, "smc_particle_resampling_amd", "csrc", p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -105,7 +109,10 @@ def stored_traffic(workload: str, kernel: str):
         return None
     with open(p) as f:
         d = json.load(f)
-    if d.get("kernel_source_sha256_16") != kernel_source_hash():
+    if kernel not in KERNEL_SOURCES:
+        return None
+    hashes = d.get("kernel_source_sha256_16")
+    if not isinstance(hashes, dict) or hashes.get(kernel) != kernel_source_hash(kernel):
         return None
     return d.get("hbm_bytes_per_launch_by_kernel", {}).get(kernel)
 

@@ -161,7 +161,7 @@ static hipError_t launch_logits_pass(const Plan& plan, const LogitsArgs& la, hip
                                      smcsd_event begin, smcsd_event split, smcsd_event end) {
     hipError_t e = hipSuccess;
     if (!plan.tv) {
-        if ((e = record(begin, s)) != hipSuccess || (e = launch_logits(plan, la, s)) != hipSuccess ||
+        if ((e = record(begin, s)) != hipSuccess || (e = launch_logits_stream(plan, la, s)) != hipSuccess ||
             (e = record(split, s)) != hipSuccess)
             return e;
         return record(end, s);
@@ -174,7 +174,7 @@ static hipError_t launch_logits_pass(const Plan& plan, const LogitsArgs& la, hip
     const uint32_t timeout = exchange_timeout_ticks();
     if (plan.bonus_rows == 0) {
         if ((e = launch_tv_fill(plan, la, timeout, s)) != hipSuccess || (e = record(begin, s)) != hipSuccess ||
-            (e = launch_logits(pairs, lp, s)) != hipSuccess || (e = record(split, s)) != hipSuccess)
+            (e = launch_logits_tv(pairs, lp, s)) != hipSuccess || (e = record(split, s)) != hipSuccess)
             return e;
         return record(end, s);
     }
@@ -198,7 +198,7 @@ static hipError_t launch_logits_pass(const Plan& plan, const LogitsArgs& la, hip
     t.fill_n = plan.pair_wgs * (int64_t)(sizeof(PairPart) / 4);
     t.timeout = timeout;
     if ((e = record(begin, s)) != hipSuccess || (e = launch_topk_slices(plan.bonus_rows, plan.dtype, t, s)) != hipSuccess ||
-        (e = record(split, s)) != hipSuccess || (e = launch_logits(pairs, lp, s)) != hipSuccess)
+        (e = record(split, s)) != hipSuccess || (e = launch_logits_tv(pairs, lp, s)) != hipSuccess)
         return e;
     return record(end, s);
 }

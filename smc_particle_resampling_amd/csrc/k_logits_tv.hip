@@ -1,170 +1,36 @@
-// k_logits.hip -- the logits pass of one SMC-SD round: the one kernel that touches the
-// logits, i.e. nearly every byte of the round.
-//
-// For every drafted position it reduces the target row and the draft row over the whole
-// vocabulary. It produces their temperature log-softmax normalisers, which the importance
-// weights of "Faster LLM Inference via Sequential Monte Carlo" (section 2) need, and, when
-// asked, the total-variation distance between the two distributions (the block-divergence
-// signal of the METASD page, section 2). It can also reduce every particle's bonus row with
-// its precomputed Gumbel noise to the Gumbel-max token (STAND page, method item 2): the round
-// does so here without TV, and with TV hands those rows to the Gumbel-Top-K slice kernel
-// (k = 1), which runs them faster than this grid's tail would.
-//
-// Work decomposition. A row is cut into 16-byte chunks and the chunks into S slices. One
-// 512-thread workgroup (8 wave64) handles one slice of one row pair (target row k, draft row
-// k) or one slice of one bonus row plus its noise row. Each lane loads its CPL chunks of both
-// rows with 16-byte non-temporal buffer loads. Chunks outside the slice and elements >= V
-// become -inf, which adds nothing to any max, sum, TV or argmax, so the arithmetic has no
-// per-element branch. (The TV pass avoids even that where it can: when every slice fills all
-// its chunk groups but the last and V is a multiple of the chunk width, a lane past the slice
-// end re-reads an inside chunk and its exponentials are shifted by -inf.)
-//   phase 1: the maximum m of z over a share of the slice, then e = exp2((z - m) * log2e/T)
-//            and its sum, for p and q. TV off: the share is the slice (one workgroup max).
-//            TV on: each wave's own share, so nothing waits between loads and exponentials.
-//   phase 2 (TV only): the S workgroups of the row pair swap their (m, sum) partials and
-//            combine them in one fixed order into the row's maxima M and sums S. With
+// k_logits_tv.hip -- the logits pass with TV on: normalisers and the per-position total
+// variation of every row pair in one HBM pass (the slices of a row pair swap partials).
+//   phase 1: each wave takes the maximum m of z over its own share of the slice, then
+//            e = exp2((z - m) * log2e/T) and its sum, for p and q, so nothing waits between
+//            the loads and the exponentials.
+//   phase 2: the S workgroups of the row pair swap their (m, sum) partials and combine them
+//            in one fixed order into the row's maxima M and sums S. With
 //            f = exp2((m - M) * log2e/T) (m of the wave that computed the e values) the
 //            |p - q| terms are (f_p / S_p) |e_p - rho e_q|, rho = (f_q S_p) / (f_p S_q).
 //            The e values stay in fp32 registers from phase 1, so phase 2 costs one fma and
 //            one add per element and no exponential. rho is exactly 1 when the two rows are
 //            equal, and then TV is exactly 0.
-// The finalize kernel combines slices (normalisers, weights, TV, argmax) in fixed order, so
-// every result is deterministic.
+// When every slice fills all its chunk groups but the last and V is a multiple of the chunk
+// width, nothing is masked: a lane past the slice end re-reads an inside chunk and its
+// exponentials are shifted by -inf.
 //
-// Launch shapes. Without TV, every (row, slice) is an independent workgroup of an ordinary
-// grid (8 chunks a lane). With TV, the S workgroups of a row pair must be resident together
-// to swap partials, so the pass runs as a persistent cooperative grid
-// (hipLaunchCooperativeKernel guarantees co-residency) over the row pairs only. It has C
-// clusters of S consecutive workgroups (4 chunks a lane, so the fp32 e values fit in
-// registers), and each cluster walks the row pairs c, c+C, c+2C, ... in lockstep. The loads
-// of a cluster's next row pair are issued while the current one is exchanged and finished.
-// The round's bonus rows run before it, as an ordinary grid of the Gumbel-Top-K slice kernel,
-// which also resets this kernel's control word and exchange words.
-// A wall-clock limit bounds every wait. A workgroup that times out raises
-// SMCSD_DEVERR_EXCHANGE and an abort flag, every later wait returns at once, and the kernel
-// always drains.
+// Launch shape. The S workgroups of a row pair must be resident together to swap partials,
+// so the pass runs as a persistent cooperative grid (hipLaunchCooperativeKernel guarantees
+// co-residency) over the row pairs only. It has C clusters of S consecutive workgroups (4
+// chunks a lane, so the fp32 e values fit in registers), and each cluster walks the row
+// pairs c, c+C, c+2C, ... in lockstep. The loads of a cluster's next row pair are issued
+// while the current one is exchanged and finished. The round's bonus rows run before it, as
+// an ordinary grid of the Gumbel-Top-K slice kernel, which also resets this kernel's control
+// word and exchange words. A wall-clock limit bounds every wait. A workgroup that times out
+// raises SMCSD_DEVERR_EXCHANGE and an abort flag, every later wait returns at once, and the
+// kernel always drains.
 #include <algorithm>
 #include <atomic>
 
-#include "smcsd_device.h"
+#include "logits_common.h"
 
 namespace smcsd {
 namespace {
-
-constexpr float kLog2e = 1.44269504088896340736f;
-
-template <int DT>
-struct Elem {
-    static constexpr int EPC = DT == SMCSD_F32 ? 4 : 8;              // elements per chunk
-    static constexpr size_t ESZ = DT == SMCSD_F32 ? 4 : 2;           // bytes per element
-    static constexpr uint32_t kNegInf = DT == SMCSD_F32 ? 0xFF800000u : 0xFF80FF80u;
-};
-
-// A per-request value that no kernel of the round writes (the temperatures), read through
-// the scalar cache. A plain load would be a vector load, and waiting for it would also wait
-// for every logits load issued before it.
-__device__ __forceinline__ float load_constant(const float* p, int64_t i) {
-    return ((const __attribute__((address_space(4))) float*)p)[i];
-}
-
-__device__ __forceinline__ u32x4 load_chunk(const char* row, int64_t chunk) {
-    return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row) + chunk);
-}
-
-// A chunk whose elements >= nv are replaced by -inf (nv < EPC: the row's tail chunk).
-template <int DT>
-__device__ __forceinline__ u32x4 mask_tail(u32x4 c, int nv) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-        if constexpr (DT == SMCSD_F32) {
-            if (w >= nv) c[w] = 0xFF800000u;
-        } else {
-            if (2 * w >= nv) c[w] = 0xFF80FF80u;
-            else if (2 * w + 1 >= nv) c[w] = (c[w] & 0x0000FFFFu) | 0xFF800000u;
-        }
-    }
-    return c;
-}
-
-// Slice loads go through a buffer resource that covers exactly the slice [c0, c1) of a row:
-// one scalar base, one lane offset (16 * lane) shared by every load, the chunk group in the
-// scalar offset, and the hardware range check returning zeros past the slice end (no
-// memory access there). Word 3 is the gfx9-family raw-buffer setting (32-bit data format,
-// no swizzle); cache policy 2 marks the loads non-temporal.
-constexpr int kRsrcWord3 = 0x00020000;
-constexpr int kLoadNontemporal = 2;
-
-// Issue the loads of the CPL chunks this lane owns in slice [c0, c1) of a row (chunk
-// c0 + j * kThreads + lane). They may still be in flight on return.
-template <int CPL>
-__device__ __forceinline__ void issue_slice(u32x4 (&R)[CPL], const char* row, int c0, int c1) {
-    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<char*>(row) + (size_t)c0 * 16, 0, (c1 - c0) * 16, kRsrcWord3);
-    const int voff = (int)threadIdx.x * 16;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j)
-        R[j] = __builtin_amdgcn_raw_buffer_load_b128(r, voff, j * kThreads * 16, kLoadNontemporal);
-}
-
-// After the loads: chunks past the slice end and elements >= V (only in the row's last
-// chunk, when V is not a multiple of EPC) become -inf. The branches are uniform.
-template <int DT, int CPL>
-__device__ __forceinline__ void mask_slice(u32x4 (&R)[CPL], int c0, int c1, int V) {
-    constexpr int EPC = Elem<DT>::EPC;
-    const int tid = threadIdx.x;
-    const int n = c1 - c0;
-    const uint32_t ni = Elem<DT>::kNegInf;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j)
-        if ((j + 1) * kThreads > n && j * kThreads + tid >= n) R[j] = u32x4{ni, ni, ni, ni};
-    if ((int64_t)c1 * EPC > V) {
-        const int last = c1 - 1 - c0;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j)
-            if (j * kThreads + tid == last) R[j] = mask_tail<DT>(R[j], V - (c1 - 1) * EPC);
-    }
-}
-
-typedef short i16x2 __attribute__((ext_vector_type(2)));
-
-// sum over the slice of exp2(z * c - m * c)
-template <int DT, int CPL>
-__device__ __forceinline__ float slice_sumexp(const u32x4 (&R)[CPL], float c, float nmc) {
-    float s0 = 0.0f, s1 = 0.0f;
-#pragma unroll
-    for (int j = 0; j < CPL; ++j) {
-#pragma unroll
-        for (int e = 0; e < Elem<DT>::EPC; e += 2) {
-            s0 += __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(R[j], e), c, nmc));
-            s1 += __builtin_amdgcn_exp2f(fmaf(chunk_elem<DT>(R[j], e + 1), c, nmc));
-        }
-    }
-    return s0 + s1;
-}
-
-struct PairLoc {
-    int64_t r;
-    const char* zp;
-    const char* zq;
-    int c0, c1;
-};
-
-template <int DT>
-__device__ __forceinline__ PairLoc pair_location(const LogitsArgs& a, int64_t u, int s) {
-    constexpr size_t ESZ = Elem<DT>::ESZ;
-    const int64_t nk = (int64_t)a.N * a.K;
-    const int64_t r = u / nk;
-    const int64_t ik = u - r * nk;
-    const int64_t i = ik / a.K;
-    const int64_t k = ik - i * a.K;
-    PairLoc L;
-    L.r = r;
-    L.zp = static_cast<const char*>(a.target) + (size_t)(((r * a.N + i) * (a.K + 1) + k) * a.ld) * ESZ;
-    L.zq = static_cast<const char*>(a.draft) + (size_t)(((r * a.N + i) * a.K + k) * a.ld) * ESZ;
-    L.c0 = s * a.cps;
-    L.c1 = min(L.c0 + a.cps, a.chunks);
-    return L;
-}
 
 // Slice exchange of the TV pass. Every (row pair, slice) partial is two 64-bit words, (max,
 // sum) of the target row and of the draft row. Before the launch, every word holds kEmpty,
@@ -211,181 +77,6 @@ __device__ bool poll_slices(const uint64_t* words, int nwords, Ctrl* ctrl, int32
         if (lane + 64 < nwords) lds[lane + 64] = v1;
     }
     return done;
-}
-
-// Every lane of each 16-lane row ends with the row's best (key, index), as in row_max.
-__device__ __forceinline__ void argmax_step(float& k, int32_t& i, float ok, int32_t oi) {
-    if (better(ok, oi, k, i)) {
-        k = ok;
-        i = oi;
-    }
-}
-__device__ __forceinline__ void row_argmax(float& k, int32_t& i) {
-    argmax_step(k, i, dpp_f32<kDppXor1>(k), dpp_i32<kDppXor1>(i));
-    argmax_step(k, i, dpp_f32<kDppXor2>(k), dpp_i32<kDppXor2>(i));
-    argmax_step(k, i, dpp_f32<kDppRowHalfMirror>(k), dpp_i32<kDppRowHalfMirror>(i));
-    argmax_step(k, i, dpp_f32<kDppRowMirror>(k), dpp_i32<kDppRowMirror>(i));
-}
-
-// Bonus rows. A workgroup handles slice s of a bonus row two chunks per lane at a time (a
-// "piece"). key = z/T + G with one
-// rounding; -inf for positions outside the slice or >= V. A lane visits its indices in
-// increasing order, so the strict comparison keeps the lowest index among equal keys.
-struct BonusRow {
-    const char* zrow;
-    const char* grow;
-    float invT;
-    int c0, c1;
-};
-
-template <int DT>
-__device__ __forceinline__ BonusRow bonus_row(const LogitsArgs& a, int64_t b, int s) {
-    constexpr size_t ESZ = Elem<DT>::ESZ;
-    BonusRow B;
-    B.zrow = static_cast<const char*>(a.target) + (size_t)((b * (a.K + 1) + a.K) * a.ld) * ESZ;
-    B.grow = reinterpret_cast<const char*>(a.gumbel + (size_t)b * a.ld);
-    B.invT = __fdiv_rn(1.0f, load_constant(a.temperature, b / a.N));
-    B.c0 = s * a.cps;
-    B.c1 = min(B.c0 + a.cps, a.chunks);
-    return B;
-}
-
-// Chunk groups j0 and j0 + 1 of this lane (two chunks keep the noise, twice the bytes of
-// the logits, from piling up in registers).
-template <int DT>
-__device__ __forceinline__ void bonus_piece(const LogitsArgs& a, const BonusRow& B, int j0,
-                                            float& best, int32_t& besti) {
-    constexpr int EPC = Elem<DT>::EPC;
-    const int tid = threadIdx.x;
-    u32x4 Z[2];
-    u32x4 g[2][EPC / 4];
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        const int ch = B.c0 + (j0 + jj) * kThreads + tid;
-        const uint32_t ni = Elem<DT>::kNegInf;
-        Z[jj] = u32x4{ni, ni, ni, ni};
-#pragma unroll
-        for (int h = 0; h < EPC / 4; ++h) g[jj][h] = u32x4{0u, 0u, 0u, 0u};
-        if (ch < B.c1) {
-            Z[jj] = load_chunk(B.zrow, ch);
-#pragma unroll
-            for (int h = 0; h < EPC / 4; ++h) g[jj][h] = load_chunk(B.grow, (int64_t)ch * (EPC / 4) + h);
-            const int nv = a.V - ch * EPC;
-            if (nv < EPC) Z[jj] = mask_tail<DT>(Z[jj], nv);
-        }
-    }
-#pragma unroll
-    for (int jj = 0; jj < 2; ++jj) {
-        const int ch = B.c0 + (j0 + jj) * kThreads + tid;
-#pragma unroll
-        for (int e = 0; e < EPC; ++e) {
-            const float key = fmaf(chunk_elem<DT>(Z[jj], e), B.invT, __uint_as_float(g[jj][e >> 2][e & 3]));
-            const bool win = key > best;
-            best = win ? key : best;
-            besti = win ? ch * EPC + e : besti;
-        }
-    }
-}
-
-// Block argmax of the lanes' (key, index) and its store. (key, index) with the lower index
-// winning ties is a total order, so the result does not depend on the order of the steps.
-__device__ void bonus_finish(const LogitsArgs& a, int64_t b, int s, float best, int32_t besti,
-                             float* red, int32_t* redi) {
-    const int tid = threadIdx.x;
-    row_argmax(best, besti);
-    float k = readlane_f32(best, 0);
-    int32_t i = __builtin_amdgcn_readlane(besti, 0);
-#pragma unroll
-    for (int r = 16; r < 64; r += 16) {
-        const float ok = readlane_f32(best, r);
-        const int32_t oi = __builtin_amdgcn_readlane(besti, r);
-        if (better(ok, oi, k, i)) {
-            k = ok;
-            i = oi;
-        }
-    }
-    const int w = tid >> 6;
-    if ((tid & 63) == 0) {
-        red[w] = k;
-        redi[w] = i;
-    }
-    __syncthreads();
-    if (tid == 0) {
-        for (int t = 1; t < kWaves; ++t)
-            if (better(red[t], redi[t], k, i)) {
-                k = red[t];
-                i = redi[t];
-            }
-        a.bp[b * a.S + s] = BonusPart{k, i};
-    }
-    __syncthreads();   // red / redi are reused by the next call
-}
-
-template <int DT, int CPL>
-__device__ void bonus_slice(const LogitsArgs& a, int64_t b, int s, float* red, int32_t* redi) {
-    const BonusRow B = bonus_row<DT>(a, b, s);
-    float best = -INFINITY;
-    int32_t besti = INT32_MAX;
-#pragma unroll 1
-    for (int j0 = 0; j0 < CPL; j0 += 2) bonus_piece<DT>(a, B, j0, best, besti);
-    bonus_finish(a, b, s, best, besti, red, redi);
-}
-
-// Wave-wide integer max / min by DPP row steps, then the four row results.
-__device__ __forceinline__ int32_t wave_max_i32(int32_t v) {
-    v = max(v, dpp_i32<kDppXor1>(v));
-    v = max(v, dpp_i32<kDppXor2>(v));
-    v = max(v, dpp_i32<kDppRowHalfMirror>(v));
-    v = max(v, dpp_i32<kDppRowMirror>(v));
-    return max(max(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-               max(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
-}
-__device__ __forceinline__ int32_t wave_min_i32(int32_t v) {
-    v = min(v, dpp_i32<kDppXor1>(v));
-    v = min(v, dpp_i32<kDppXor2>(v));
-    v = min(v, dpp_i32<kDppRowHalfMirror>(v));
-    v = min(v, dpp_i32<kDppRowMirror>(v));
-    return min(min(__builtin_amdgcn_readlane(v, 0), __builtin_amdgcn_readlane(v, 16)),
-               min(__builtin_amdgcn_readlane(v, 32), __builtin_amdgcn_readlane(v, 48)));
-}
-
-// Maximum of this wave's share of a slice (wave-uniform). bf16: the packed int16 max alone
-// decides whenever the wave holds a non-negative value (those order like their int16 bits
-// and beat every negative); only a wave whose share is entirely negative takes the int16
-// min as well (negative values order in reverse). -inf padding (int16 -128) never wins
-// either way while a finite value is present.
-template <int DT, int CPL>
-__device__ __forceinline__ float wave_share_max(const u32x4 (&R)[CPL]) {
-    if constexpr (DT == SMCSD_F32) {
-        float m = -INFINITY;
-#pragma unroll
-        for (int j = 0; j < CPL; ++j)
-#pragma unroll
-            for (int w = 0; w < 4; w += 2)
-                m = fmaxf(m, fmaxf(__uint_as_float(R[j][w]), __uint_as_float(R[j][w + 1])));
-        return wave_max(m);
-    } else {
-        i16x2 mx = {(short)-32768, (short)-32768};
-#pragma unroll
-        for (int j = 0; j < CPL; ++j)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t word = R[j][w];
-                mx = __builtin_elementwise_max(mx, __builtin_bit_cast(i16x2, word));
-            }
-        const int32_t hi = wave_max_i32(mx[0] > mx[1] ? mx[0] : mx[1]);
-        if (hi >= 0) return __uint_as_float((uint32_t)hi << 16);
-        i16x2 mn = {(short)32767, (short)32767};
-#pragma unroll
-        for (int j = 0; j < CPL; ++j)
-#pragma unroll
-            for (int w = 0; w < 4; ++w) {
-                const uint32_t word = R[j][w];
-                mn = __builtin_elementwise_min(mn, __builtin_bit_cast(i16x2, word));
-            }
-        const int32_t lo = wave_min_i32(mn[0] < mn[1] ? mn[0] : mn[1]);
-        return __uint_as_float(((uint32_t)lo & 0xFFFFu) << 16);
-    }
 }
 
 // The -inf padding of one workgroup's slice, fixed for the whole persistent loop (every row
@@ -713,58 +404,6 @@ __global__ __launch_bounds__(kThreads, 4) void k_logits_tv(LogitsArgs a) {
     if (threadIdx.x < 64) store_slice_tv(a, sh, (uint32_t)(it - C), s);
 }
 
-// TV off: slice partials only. Each wave shifts its exponentials by the maximum of its own
-// share (no barrier between the loads and the exponentials); wave 0 combines the eight wave
-// partials into the slice partial after the one barrier.
-template <int DT>
-__device__ void pair_slice_stream(const LogitsArgs& a, int64_t u, int s, float4* wpart) {
-    const PairLoc L = pair_location<DT>(a, u, s);
-    const float c = kLog2e / load_constant(a.temperature, L.r);   // exp(z/T) = exp2(z * c)
-    const int lane = threadIdx.x & 63;
-    u32x4 P[kStreamCPL], Q[kStreamCPL];
-    issue_slice<kStreamCPL>(P, L.zp, L.c0, L.c1);
-    issue_slice<kStreamCPL>(Q, L.zq, L.c0, L.c1);
-    mask_slice<DT, kStreamCPL>(P, L.c0, L.c1, a.V);
-    mask_slice<DT, kStreamCPL>(Q, L.c0, L.c1, a.V);
-    const float mpw = wave_share_max<DT, kStreamCPL>(P);
-    const float mqw = wave_share_max<DT, kStreamCPL>(Q);
-    // a wave whose share is all padding has maximum -inf: shift 0, so its terms are 0
-    const float spw = wave_sum(slice_sumexp<DT, kStreamCPL>(P, c, mpw == -INFINITY ? 0.0f : -mpw * c));
-    const float sqw = wave_sum(slice_sumexp<DT, kStreamCPL>(Q, c, mqw == -INFINITY ? 0.0f : -mqw * c));
-    if (lane == 0) wpart[threadIdx.x >> 6] = make_float4(mpw, spw, mqw, sqw);
-    __syncthreads();
-    if (threadIdx.x < 64) {
-        const float4 wpv = lane < kWaves ? wpart[lane] : make_float4(-INFINITY, 0.0f, -INFINITY, 0.0f);
-        const float mp = readlane_f32(row_max(wpv.x), 0);
-        const float mq = readlane_f32(row_max(wpv.z), 0);
-        // a wave whose share is all -inf holds (-inf, 0): it adds 0, also when the whole slice
-        // is -inf (mp = -inf would make its scale exp2(NaN))
-        const float sp = readlane_f32(
-            row_sum(wpv.x == -INFINITY ? 0.0f : wpv.y * __builtin_amdgcn_exp2f((wpv.x - mp) * c)), 0);
-        const float sq = readlane_f32(
-            row_sum(wpv.z == -INFINITY ? 0.0f : wpv.w * __builtin_amdgcn_exp2f((wpv.z - mq) * c)), 0);
-        if (lane == 0) a.pp[u * a.S + s] = PairPart{mp, sp, mq, sq};
-    }
-}
-
-// TV off: one workgroup per (row, slice).
-template <int DT>
-__global__ __launch_bounds__(kThreads) void k_logits_stream(LogitsArgs a) {
-    __shared__ float red[kWaves];
-    __shared__ int32_t redi[kWaves];
-    __shared__ float4 wpart[kWaves];
-    // the bonus slices (a logits row and its noise row, 1.5 times a row pair's bytes) are
-    // dispatched first, so that the grid's tail holds the lighter row-pair slices
-    const int64_t t = blockIdx.x;
-    const int64_t bonus_wgs = a.total_wgs - a.pair_wgs;
-    if (t < bonus_wgs) {
-        bonus_slice<DT, kStreamCPL>(a, t / a.S, (int)(t % a.S), red, redi);
-    } else if (t < a.total_wgs) {
-        const int64_t tp = t - bonus_wgs;
-        pair_slice_stream<DT>(a, tp / a.S, (int)(tp % a.S), wpart);
-    }
-}
-
 // Before a TV pass without bonus rows: the control word (abort flag 0, the wait limit) and
 // every exchange word at the all-ones "empty" pattern, in one launch.
 __global__ void k_fill_tv(Ctrl* ctrl, uint32_t timeout, uint32_t* words, int64_t n) {
@@ -826,17 +465,11 @@ static hipError_t launch_tv(const Plan& plan, const LogitsArgs& a, hipStream_t s
                                       dim3((unsigned)(clusters * plan.S)), dim3(kThreads), params, 0, s);
 }
 
-hipError_t launch_logits(const Plan& plan, const LogitsArgs& a, hipStream_t s) {
-    if (plan.tv) {
-        const bool fast = tv_fast_path(plan);
-        if (plan.dtype == SMCSD_BF16)
-            return fast ? launch_tv<SMCSD_BF16, true>(plan, a, s) : launch_tv<SMCSD_BF16, false>(plan, a, s);
-        return fast ? launch_tv<SMCSD_F32, true>(plan, a, s) : launch_tv<SMCSD_F32, false>(plan, a, s);
-    }
-    const dim3 grid((unsigned)plan.total_wgs), block(kThreads);
-    if (plan.dtype == SMCSD_BF16) k_logits_stream<SMCSD_BF16><<<grid, block, 0, s>>>(a);
-    else k_logits_stream<SMCSD_F32><<<grid, block, 0, s>>>(a);
-    return hipGetLastError();
+hipError_t launch_logits_tv(const Plan& plan, const LogitsArgs& a, hipStream_t s) {
+    const bool fast = tv_fast_path(plan);
+    if (plan.dtype == SMCSD_BF16)
+        return fast ? launch_tv<SMCSD_BF16, true>(plan, a, s) : launch_tv<SMCSD_BF16, false>(plan, a, s);
+    return fast ? launch_tv<SMCSD_F32, true>(plan, a, s) : launch_tv<SMCSD_F32, false>(plan, a, s);
 }
 
 }  // namespace smcsd

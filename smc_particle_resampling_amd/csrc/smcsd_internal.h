@@ -235,7 +235,10 @@ struct RemapArgs {
 
 // Host launchers (defined next to their kernels). Return hipSuccess or the launch error.
 // Ctrl of a TV pass: abort 0 and the wait limit (one small kernel, graph-capturable).
-hipError_t launch_logits(const Plan& plan, const LogitsArgs& a, hipStream_t s);
+// The logits pass: TV on (row pairs only, persistent cooperative grid) or TV off (row pairs
+// and bonus rows, one workgroup per (row, slice)).
+hipError_t launch_logits_tv(const Plan& plan, const LogitsArgs& a, hipStream_t s);
+hipError_t launch_logits_stream(const Plan& plan, const LogitsArgs& a, hipStream_t s);
 hipError_t launch_tv_fill(const Plan& plan, const LogitsArgs& a, uint32_t timeout, hipStream_t s);
 hipError_t launch_finalize(int32_t R, bool from_partials, int32_t dtype, const FinalizeArgs& a,
                            hipStream_t s);

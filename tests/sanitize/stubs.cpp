@@ -15,7 +15,8 @@ hipError_t stub() {
     return hipErrorNotSupported;
 }
 }  // namespace
-hipError_t launch_logits(const Plan&, const LogitsArgs&, hipStream_t) { return stub(); }
+hipError_t launch_logits_tv(const Plan&, const LogitsArgs&, hipStream_t) { return stub(); }
+hipError_t launch_logits_stream(const Plan&, const LogitsArgs&, hipStream_t) { return stub(); }
 hipError_t launch_tv_fill(const Plan&, const LogitsArgs&, uint32_t, hipStream_t) { return stub(); }
 hipError_t launch_finalize(int32_t, bool, int32_t, const FinalizeArgs&, hipStream_t) { return stub(); }
 hipError_t launch_remap(int32_t, const RemapArgs&, hipStream_t) { return stub(); }

@@ -25,13 +25,15 @@ def test_stored_traffic_needs_the_same_kernel_sources(monkeypatch):
     path = os.path.join(bench.PROFILES, "traffic_k_logits_%s.json" % wl)
     if not os.path.exists(path):
         pytest.skip("no traffic record")
-    monkeypatch.setattr(bench, "kernel_source_hash", lambda: "0000000000000000")
+    monkeypatch.setattr(bench, "kernel_source_hash", lambda kernel: "0000000000000000")
     assert bench.stored_traffic(wl, "k_logits_tv") is None
 
 
 def test_kernel_source_hash_is_stable():
-    assert bench.kernel_source_hash() == bench.kernel_source_hash()
-    assert len(bench.kernel_source_hash()) == 16
+    for k in bench.KERNEL_SOURCES:
+        assert bench.kernel_source_hash(k) == bench.kernel_source_hash(k)
+        assert len(bench.kernel_source_hash(k)) == 16
+    assert bench.kernel_source_hash("k_logits_tv") != bench.kernel_source_hash("k_logits_stream")
 
 
 @pytest.mark.parametrize("R,N,P,ps,steps,spare", [(3, 8, 6, 4, None, 40), (4, 64, 20, 8, 8, 0),
