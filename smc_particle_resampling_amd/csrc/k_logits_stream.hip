@@ -1,5 +1,5 @@
 // k_logits_stream.hip -- the logits pass with TV off: every (row, slice) is an independent
-// workgroup of an ordinary grid, 8 chunks a lane. A row-pair slice reduces the target and the
+// workgroup of an ordinary grid, 4 chunks a lane. A row-pair slice reduces the target and the
 // draft row to their slice partials (max, sum of exp2((z - m) * log2e/T)); a bonus slice
 // reduces a bonus row and its noise row to the slice's Gumbel-max (key, index). Each wave
 // shifts its exponentials by the maximum of its own share of the slice, so nothing waits

@@ -15,7 +15,7 @@ namespace smcsd {
 
 constexpr int kThreads = 512;        // workgroup size of the round's kernels (8 wave64)
 constexpr int kWaves = kThreads / 64;
-constexpr int kStreamCPL = 8;        // 16-byte chunks a lane holds per row of a slice, TV off
+constexpr int kStreamCPL = 4;        // 16-byte chunks a lane holds per row of a slice, TV off
 constexpr int kTvCPL = 4;            // ... TV on (its fp32 exponentials stay in registers)
 constexpr int kMaxTvSlices = 64;     // TV exchange: wave 0 reads the 2*S partial words
 constexpr int kFusedRemapEntries = 16 * kThreads;   // tables the finalize kernel remaps
