@@ -288,6 +288,7 @@ def main():
     pairs = [(ev.create(), ev.create(), ev.create()) for _ in range(args.steps)]
     rounds = [(ev.create(), ev.create()) for _ in range(args.steps)] if args.flush else None
     flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev) if args.flush else None
+    calls = None            # the round's marshalled calls (round path only)
     if topk:
         tz, tT, tG = synth.topk_rows(inp)
         out = smcsd.gumbel_topk(tz, tT, tG, args.topk, V=w.V)
@@ -433,6 +434,19 @@ def main():
         for x in trio:
             ev.destroy(x)
     k_mean_ms = sum(kms) / len(kms)
+    # The pass alone, `steps` times back to back between one pair of events
+    # (smcsd_bench_logits_pass): its time without an event around each launch. An event costs
+    # microseconds of queue time, which a short single-kernel pass would otherwise carry.
+    batch_ms = None
+    if calls is not None and not args.flush:
+        b0, b1 = ev.create(), ev.create()
+        ev.record(b0, cur_stream)
+        calls[0].bench_pass(args.steps)
+        ev.record(b1, cur_stream)
+        torch.cuda.synchronize()
+        batch_ms = ev.elapsed_ms(b0, b1) / args.steps
+        ev.destroy(b0)
+        ev.destroy(b1)
     if args.flush:
         rms = [ev.elapsed_ms(a, b) for a, b in rounds]
         ms_per_step = sum(rms) / len(rms)
@@ -449,6 +463,8 @@ def main():
     # (k_logits_tv, timed split..end) reads every drafted position's target and draft row;
     # otherwise one kernel is the whole pass.
     split = w.tv and not after and args.path in ("round", "driver")
+    if batch_ms is not None:
+        k_mean_ms = batch_ms
     if split:
         dom_bytes = alg["target"] * w.K // (w.K + 1) + alg["draft"]
         dom_ms = sum(second_ms) / len(second_ms)
@@ -553,7 +569,9 @@ def main():
                    "timing": ("each round alone (events around all its launches) after a 1 GiB "
                               "write that evicts the L2s and the Infinity Cache" if args.flush
                               else "rounds back to back, wall clock over the timed steps") +
-                             "; kernel times from events in a second pass of as many rounds",
+                             "; kernel times from events in a second pass of as many rounds" +
+                             ("; the pass time from the pass alone run back to back as many times "
+                              "between two events" if batch_ms is not None else ""),
                    "round_GBps": (logits_bytes + table_bytes) / (ms_per_step * 1e-3) / 1e9},
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": achieved / PEAK_HBM_GBPS,

@@ -7,6 +7,9 @@
  *  - a plain streaming read gives the attainable read bandwidth;
  *  - a plain copy of known size turns hardware byte counters (FETCH_SIZE / WRITE_SIZE) into
  *    bytes.
+ * A third runs the round's logits pass alone, many times back to back, so that its kernels
+ * can be timed without an event around each launch (an event costs microseconds of queue
+ * time, a large share of a short kernel).
  * They are not part of the round.
  */
 #ifndef SMCSD_BENCH_H
@@ -29,6 +32,15 @@ smcsd_status smcsd_bench_stream_read(const void *src, size_t bytes, uint32_t *si
 
 /* Copy `bytes` (a multiple of 16, both pointers 16-byte aligned) from src to dst. */
 smcsd_status smcsd_bench_copy(const void *src, void *dst, size_t bytes, smcsd_stream stream);
+
+/*
+ * The logits pass of smcsd_round (the kernels that read the logits; no weights,
+ * resampling, bonus choice or page remap), `repeats` >= 1 times back to back on `stream`,
+ * with the same arguments and the same checks as smcsd_round (timing events ignored). Each
+ * repeat overwrites the pass's partials in the workspace; no output of the round is written.
+ */
+smcsd_status smcsd_bench_logits_pass(const smcsd_round_args *args, int32_t repeats,
+                                     smcsd_stream stream);
 
 #ifdef __cplusplus
 }

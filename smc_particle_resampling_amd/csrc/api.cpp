@@ -264,8 +264,8 @@ smcsd_status smcsd_round(const smcsd_round_args* args, smcsd_stream stream) {
 
 namespace smcsd {
 
-smcsd_status enqueue_round(const smcsd_round_args& a, const Plan& plan, char* ws, hipStream_t s) {
-
+// The logits pass's argument block of a validated round.
+static LogitsArgs logits_args(const smcsd_round_args& a, const Plan& plan, char* ws) {
     LogitsArgs la{};
     la.target = a.target_logits;
     la.draft = a.draft_logits;
@@ -286,7 +286,11 @@ smcsd_status enqueue_round(const smcsd_round_args& a, const Plan& plan, char* ws
     la.chunks = plan.chunks;
     la.S = plan.S;
     la.cps = plan.cps;
+    return la;
+}
 
+smcsd_status enqueue_round(const smcsd_round_args& a, const Plan& plan, char* ws, hipStream_t s) {
+    const LogitsArgs la = logits_args(a, plan, ws);
     hipError_t e = launch_logits_pass(plan, la, s, a.timing_begin, a.timing_split, a.timing_end);
     if (e != hipSuccess) return SMCSD_ERR_DEVICE;
 
@@ -518,6 +522,19 @@ smcsd_status smcsd_bench_stream_read(const void* src, size_t bytes, uint32_t* si
     if (!src || !sink || grid < 1 || bytes % 16 != 0 || !aligned16(src)) return SMCSD_ERR_ARG;
     const hipError_t e = launch_bench_read(src, bytes, sink, grid, reinterpret_cast<hipStream_t>(stream));
     return e == hipSuccess ? SMCSD_OK : SMCSD_ERR_DEVICE;
+}
+
+smcsd_status smcsd_bench_logits_pass(const smcsd_round_args* args, int32_t repeats,
+                                     smcsd_stream stream) {
+    if (repeats < 1) return SMCSD_ERR_ARG;
+    Plan plan;
+    const smcsd_status st = check_round(args, &plan, true);
+    if (st != SMCSD_OK || args->R == 0) return st;
+    const LogitsArgs la = logits_args(*args, plan, static_cast<char*>(args->workspace));
+    const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    for (int32_t i = 0; i < repeats; ++i)
+        if (launch_logits_pass(plan, la, s, nullptr, nullptr, nullptr) != hipSuccess) return SMCSD_ERR_DEVICE;
+    return SMCSD_OK;
 }
 
 smcsd_status smcsd_bench_copy(const void* src, void* dst, size_t bytes, smcsd_stream stream) {

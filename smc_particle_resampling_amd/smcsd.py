@@ -95,6 +95,8 @@ _lib.smcsd_pages_workspace_size.argtypes = [_i32, _i32, _i32, _i32]
 _lib.smcsd_bench_stream_read.argtypes = [_p, _sz, _p, _i32, _p]
 _lib.smcsd_bench_copy.restype = _i32
 _lib.smcsd_bench_copy.argtypes = [_p, _p, _sz, _p]
+_lib.smcsd_bench_logits_pass.restype = _i32
+_lib.smcsd_bench_logits_pass.argtypes = [ctypes.c_void_p, _i32, _p]
 
 
 class SmcsdError(RuntimeError):
@@ -189,6 +191,16 @@ class RoundCall:
         self._ref = ctypes.byref(self._args)
         self._stream = _stream(dev, stream)
         self._fn = _lib.smcsd_round_noalloc if noalloc else _lib.smcsd_round
+
+    def bench_pass(self, repeats: int) -> None:
+        """Enqueue the round's logits pass alone, `repeats` times (smcsd_bench_logits_pass)."""
+        if self._fn is not _lib.smcsd_round:
+            raise ValueError("bench_pass needs a round with a workspace")
+        a = self._args
+        a.timing_begin = a.timing_split = a.timing_end = None
+        st = _lib.smcsd_bench_logits_pass(self._ref, int(repeats), self._stream)
+        if st != OK:
+            raise SmcsdError(st, "smcsd_bench_logits_pass")
 
     def launch(self, timing_events=None) -> None:
         a = self._args

@@ -27,7 +27,8 @@ def test_every_declared_symbol_is_exported():
     names = _declared_functions()
     assert {"smcsd_round", "smcsd_resample", "smcsd_remap_pages", "smcsd_workspace_size",
             "smcsd_status_string", "smcsd_round_args_size", "smcsd_bench_stream_read",
-            "smcsd_bench_copy", "smcsd_sd_verify", "smcsd_verify_workspace_size",
+            "smcsd_bench_copy", "smcsd_bench_logits_pass", "smcsd_sd_verify",
+            "smcsd_verify_workspace_size",
             "smcsd_verify_args_size", "smcsd_gumbel_topk", "smcsd_topk_workspace_size",
             "smcsd_pages_advance", "smcsd_pages_workspace_size", "smcsd_bonus_resampled",
             "smcsd_bonus_workspace_size", "smcsd_round_noalloc"} <= names
@@ -160,6 +161,9 @@ def test_resample_and_remap_validation():
     assert lib.smcsd_remap_pages(0, 4, 4, None, None, None, None, 10, None, None) == S.OK
     assert lib.smcsd_bench_copy(p, p, 64, None) == S.ERR_ARG
     assert lib.smcsd_bench_stream_read(p + 4, 64, p, 1, None) == S.ERR_ARG
+    assert lib.smcsd_bench_logits_pass(None, 1, None) == S.ERR_ARG
+    a = S.RoundArgs()
+    assert lib.smcsd_bench_logits_pass(ctypes.byref(a), 0, None) == S.ERR_ARG      # repeats
 
 
 def test_binding_rejects_bad_tensors_before_the_library():
