@@ -18,7 +18,6 @@
 namespace smcsd {
 namespace {
 
-constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
 template <int DT>

@@ -27,8 +27,6 @@
 namespace smcsd {
 namespace {
 
-constexpr float kLog2e = 1.44269504088896340736f;
-
 template <int DT>
 struct Elem {
     static constexpr int EPC = DT == SMCSD_F32 ? 4 : 8;              // elements per chunk

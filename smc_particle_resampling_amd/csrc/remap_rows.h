@@ -171,7 +171,6 @@ __device__ __forceinline__ void remap_request_lds(const int32_t* in, int16_t* dl
     for (int32_t c = tid; c < P; c += nt) {
         int32_t run_page = in[c], run_delta = __builtin_amdgcn_readlane(offv, 0);
         bool run_moves = run_delta != 0;
-#pragma unroll 4
         for (int32_t j = 1; j <= N; ++j) {
             const int32_t jc = min(j, N - 1);
             const int32_t pgr = in[jc * P + c];          // always in range; row N is past the end

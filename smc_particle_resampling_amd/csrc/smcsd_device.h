@@ -8,6 +8,8 @@
 namespace smcsd {
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
+constexpr float kLog2e = 1.44269504088896340736f;   // exp(x) = exp2(x * log2e)
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
 
