@@ -143,7 +143,8 @@ typedef struct smcsd_round_args {
     size_t workspace_bytes;
 
     smcsd_event timing_begin;    /* optional: recorded on `stream` right before and after */
-    smcsd_event timing_end;      /* the logits-pass kernel (for roofline timing) */
+    smcsd_event timing_end;      /* the logits pass (both of its kernels with TV on and the
+                                    bonus drawn in the pass), for roofline timing */
 
     const float *log_potential;  /* optional [R][N]: log phi_i, added to particle i's
                                     incremental log weight (the tilted target p*phi of
