@@ -64,6 +64,8 @@ bool make_plan(int32_t R, int32_t N, int32_t K, int32_t V, int64_t ld, int32_t d
     off = align256(off + sizeof(BonusPart) * (size_t)(q.bonus_rows * q.S));
     q.off_terms = off;
     off = align256(off + sizeof(double) * (size_t)q.pairs);
+    q.off_lw = off;   // the previous log-weights, for a finalize split over several workgroups
+    off = align256(off + sizeof(float) * (size_t)R * N);
     q.bytes = off;
     *p = q;
     return true;
@@ -197,6 +199,9 @@ static hipError_t launch_logits_pass(const Plan& plan, const LogitsArgs& la, hip
     t.fill_words = reinterpret_cast<uint32_t*>(la.pp);
     t.fill_n = plan.pair_wgs * (int64_t)(sizeof(PairPart) / 4);
     t.timeout = timeout;
+    t.lw_src = la.lw_src;
+    t.lw_copy = la.lw_copy;
+    t.lw_n = la.lw_n;
     if ((e = record(begin, s)) != hipSuccess || (e = launch_topk_slices(plan.bonus_rows, plan.dtype, t, s)) != hipSuccess ||
         (e = record(split, s)) != hipSuccess || (e = launch_logits_tv(pairs, lp, s)) != hipSuccess)
         return e;
@@ -289,8 +294,26 @@ static LogitsArgs logits_args(const smcsd_round_args& a, const Plan& plan, char*
     return la;
 }
 
+// Workgroups a request for the small finalize kernel: enough that each member's share of the
+// table's columns is at most kFinalizeShare entries, 1 without a table; 0 when the small
+// kernel does not take the round (the general finalize then remaps tables of at most
+// kFusedRemapEntries entries and k_remap the larger ones).
+static int32_t finalize_members(const smcsd_round_args& a) {
+    if (a.N > 64 || a.N * a.K > kThreads) return 0;
+    if (!a.page_table_in || (int64_t)a.N * a.P <= kFinalizeShare) return 1;
+    const int64_t cols = kFinalizeShare / a.N;   // >= 32 columns a member (N <= 64)
+    const int64_t m = ((int64_t)a.P + cols - 1) / cols;
+    return (int64_t)a.R * m <= INT32_MAX ? (int32_t)m : 0;   // one launch's grid
+}
+
 smcsd_status enqueue_round(const smcsd_round_args& a, const Plan& plan, char* ws, hipStream_t s) {
-    const LogitsArgs la = logits_args(a, plan, ws);
+    LogitsArgs la = logits_args(a, plan, ws);
+    const int32_t members = finalize_members(a);
+    if (members > 1) {   // the pass copies the previous log-weights for the members to read
+        la.lw_src = a.log_weights;
+        la.lw_copy = reinterpret_cast<float*>(ws + plan.off_lw);
+        la.lw_n = a.R * a.N;
+    }
     hipError_t e = launch_logits_pass(plan, la, s, a.timing_begin, a.timing_split, a.timing_end);
     if (e != hipSuccess) return SMCSD_ERR_DEVICE;
 
@@ -322,11 +345,13 @@ smcsd_status enqueue_round(const smcsd_round_args& a, const Plan& plan, char* ws
     fa.S = plan.S;
     fa.mode = a.mode;
     fa.ess_frac = a.ess_frac;
-    // Small tables are remapped by the finalize workgroup of their request, which saves a
-    // launch; larger ones (more than 16 entries a thread) keep the separate remap kernel,
-    // which spreads a request's table over several workgroups.
+    fa.members = std::max(members, 1);
+    fa.lw_in = members > 1 ? la.lw_copy : a.log_weights;
+    // The finalize remaps the table in the same launch, which saves one: the small kernel
+    // any table (split by columns over its members), the general one tables of at most 16
+    // entries a thread; larger ones there keep the separate remap kernel.
     const int64_t table_entries = (int64_t)a.N * a.P;
-    const bool fused_remap = a.page_table_in && table_entries <= kFusedRemapEntries;
+    const bool fused_remap = a.page_table_in && (members > 0 || table_entries <= kFusedRemapEntries);
     if (fused_remap) {
         fa.pt_in = a.page_table_in;
         fa.pt_out = a.page_table_out;
@@ -371,6 +396,8 @@ smcsd_status smcsd_resample(int32_t R, int32_t N, const float* log_w_incr, float
     FinalizeArgs fa{};
     fa.log_w_incr = const_cast<float*>(log_w_incr);
     fa.log_weights = log_weights;
+    fa.lw_in = log_weights;
+    fa.members = 1;
     fa.uniform = uniform;
     fa.log_norm = log_norm;
     fa.ess = ess;

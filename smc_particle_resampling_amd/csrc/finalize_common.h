@@ -87,8 +87,8 @@ __device__ __forceinline__ double position_term(const FinalizeArgs& a, int64_t r
 }
 
 // Particle ri's bonus token: the best (key, index) over its S slices, slices in batches of
-// 8 (-1 without noise: out_tokens then get -1 in column K). Written to a.bonus too.
-__device__ __forceinline__ int32_t bonus_of(const FinalizeArgs& a, int64_t ri) {
+// 8 (-1 without noise: out_tokens then get -1 in column K). Written to a.bonus too if store.
+__device__ __forceinline__ int32_t bonus_of(const FinalizeArgs& a, int64_t ri, bool store = true) {
     if (!a.bp) return -1;
     const BonusPart* bpart = a.bp + ri * a.S;
     float best = -INFINITY;
@@ -106,15 +106,15 @@ __device__ __forceinline__ int32_t bonus_of(const FinalizeArgs& a, int64_t ri) {
             }
     }
     if (besti < 0 || besti >= a.V) besti = 0;   // only if every key was NaN
-    a.bonus[ri] = besti;
+    if (store) a.bonus[ri] = besti;
     return besti;
 }
 
 // Up to 64 particles, one wave, lane i = particle i (l_i in s_l): DPP reductions (every lane
 // ends with the same bits) and an inclusive prefix scan of the weights, all in double
-// precision. Writes C_i (resampling) or W_i to s_c and the request's outputs.
+// precision. Writes C_i (resampling) or W_i to s_c and, if store, the request's outputs.
 __device__ __forceinline__ void weights_wave(const FinalizeArgs& a, int64_t r, int32_t N, const double* s_l,
-                                             double* s_c, double* s_logZ, int32_t* s_rs) {
+                                             double* s_c, double* s_logZ, int32_t* s_rs, bool store = true) {
     const int i = threadIdx.x;
     const double l = i < N ? s_l[i] : -INFINITY;
     const double m = wave_max_f64(l);
@@ -129,9 +129,11 @@ __device__ __forceinline__ void weights_wave(const FinalizeArgs& a, int64_t r, i
     const double acc = wave_scan_f64(w);
     if (i < N) s_c[i] = rs ? acc : w;
     if (i == 0) {
-        a.log_norm[r] = (float)logZ;
-        a.ess[r] = (float)ess;
-        a.resampled[r] = rs;
+        if (store) {
+            a.log_norm[r] = (float)logZ;
+            a.ess[r] = (float)ess;
+            a.resampled[r] = rs;
+        }
         *s_logZ = logZ;
         *s_rs = rs;
     }

@@ -16,6 +16,8 @@
 // one workgroup per request, so its time is latency, and it keeps the chain of dependent
 // steps and the instructions it executes few. k_finalize takes every other size, and the
 // resampling of given increments (smcsd_resample).
+#include <algorithm>
+
 #include "finalize_common.h"
 #include "remap_rows.h"
 
@@ -234,10 +236,17 @@ __global__ __launch_bounds__(kThreads) void k_finalize(FinalizeArgs a) {
 // parts) is issued before the first wait; the gather of the two logits at the token is the
 // only dependent one. A kernel's instruction cache is cold when it starts, so the code that
 // runs is kept short: this kernel is mostly latency.
+// A table of more than kFinalizeShare entries (N * P) is split by columns over a.members
+// workgroups a request (a larger share a workgroup measured slower: the remap's column walk
+// and atomics took 7 of the kernel's 16 us on 8192 entries): each member does the request's arithmetic
+// itself (the same inputs and instructions give the same bits), copies its rows j % members
+// of out_tokens and remaps its columns; member 0 alone writes the request's other outputs.
+// The previous log-weights then come from a copy (a.lw_in), since member 0 overwrites
+// log_weights while the others may still read them.
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_finalize_small(FinalizeArgs a) {
     constexpr int kMaxN = 64;
-    constexpr int kPtRegs = kFusedRemapEntries / kThreads;
+    constexpr int kPtRegs = kFinalizeShare / kThreads;
     __shared__ double s_term[kThreads];    // the positions' log-ratios
     __shared__ int32_t s_tok[kThreads];    // the drafted tokens
     __shared__ double s_l[kMaxN];          // l_i = log_weights_i + log_w_incr_i
@@ -245,19 +254,26 @@ __global__ __launch_bounds__(kThreads) void k_finalize_small(FinalizeArgs a) {
     __shared__ int32_t s_bonus[kMaxN];
     __shared__ int32_t s_anc[kMaxN];
     __shared__ int32_t s_off[kMaxN];       // offspring counts o_i
-    __shared__ int32_t s_pt[kFusedRemapEntries];   // the request's input page table
-    __shared__ int16_t s_dl[kFusedRemapEntries];   // refcount change of the run ending at each entry
+    __shared__ int32_t s_pt[kFinalizeShare];   // this member's columns of the input page table
+    __shared__ int16_t s_dl[kFinalizeShare];   // refcount change of the run ending at each entry
     __shared__ double s_logZ;
     __shared__ int32_t s_rs;
     const int tid = threadIdx.x;
-    const int64_t r = blockIdx.x;
+    const int32_t gs = a.members;
+    const int64_t r = blockIdx.x / gs;
+    const int32_t gi = (int32_t)(blockIdx.x - r * gs);
+    const bool lead = gi == 0;
     const int32_t N = a.N, K = a.K, NK = N * K;
     const double u_r = (double)a.uniform[r];
     const float T = a.temperature[r];
-    const int32_t NP = a.pt_in ? N * a.P : 0;
+    const int64_t NP = a.pt_in ? (int64_t)N * a.P : 0;   // the request's whole table
+    // this member's columns [p0, p0 + w) of it, staged as s_pt[j * w + c] (N * w entries)
+    const int32_t p0 = NP > 0 ? (int32_t)((int64_t)a.P * gi / gs) : 0;
+    const int32_t w = NP > 0 ? (int32_t)((int64_t)a.P * (gi + 1) / gs) - p0 : 0;
+    const int32_t NW = N * w;
     double lw_prev = 0.0, lpot = 0.0;
     if (tid < N) {
-        lw_prev = (double)a.log_weights[r * N + tid];
+        lw_prev = (double)a.lw_in[r * N + tid];
         if (a.log_potential) lpot = (double)a.log_potential[r * N + tid];
     }
     // thread tid < NK: position (i, k); the particles' bonus parts go to the waves after the
@@ -274,17 +290,20 @@ __global__ __launch_bounds__(kThreads) void k_finalize_small(FinalizeArgs a) {
 #pragma unroll
     for (int b = 0; b < kPtRegs; ++b) {
         const int32_t e = b * kThreads + tid;
-        if (e < NP) ptv[b] = a.pt_in[r * NP + e];
+        if (e < NW) {
+            const int32_t j = e / w;
+            ptv[b] = a.pt_in[r * NP + (int64_t)j * a.P + p0 + (e - j * w)];
+        }
     }
     if (tid < NK) {
         s_term[tid] = position_term<DT>(a, ri, u, k, L, kLog2e / T, 1.0 / (double)T);
         s_tok[tid] = L.x;
     }
-    if (tid >= boff && tid < boff + N) s_bonus[tid - boff] = bonus_of(a, r * N + (tid - boff));
+    if (tid >= boff && tid < boff + N) s_bonus[tid - boff] = bonus_of(a, r * N + (tid - boff), lead);
 #pragma unroll
     for (int b = 0; b < kPtRegs; ++b) {
         const int32_t e = b * kThreads + tid;
-        if (e < NP) s_pt[e] = ptv[b];
+        if (e < NW) s_pt[e] = ptv[b];
     }
     if (tid < N) s_off[tid] = 0;
     __syncthreads();
@@ -292,28 +311,30 @@ __global__ __launch_bounds__(kThreads) void k_finalize_small(FinalizeArgs a) {
         double lw = 0.0;
         for (int32_t k = 0; k < K; ++k) lw += s_term[tid * K + k];
         if (a.log_potential) lw += lpot;
-        a.log_w_incr[r * N + tid] = (float)lw;
+        if (lead) a.log_w_incr[r * N + tid] = (float)lw;
         s_l[tid] = lw_prev + lw;
     }
     __syncthreads();
-    if (tid < 64) weights_wave(a, r, N, s_l, s_c, &s_logZ, &s_rs);
+    if (tid < 64) weights_wave(a, r, N, s_l, s_c, &s_logZ, &s_rs, lead);
     __syncthreads();
     if (tid < N) {
         const int32_t j = tid;
         const int32_t anc = s_rs ? ancestor_of(j, u_r, N, s_c) : j;
-        a.ancestors[r * N + j] = anc;
         s_anc[j] = anc;
-        if (NP > 0) atomicAdd(&s_off[anc], 1);
-        a.log_weights[r * N + j] = s_rs ? (float)(-log((double)N)) : (float)(s_l[j] - s_logZ);
-        if (a.out_tokens) {
+        if (NW > 0) atomicAdd(&s_off[anc], 1);
+        if (lead) {
+            a.ancestors[r * N + j] = anc;
+            a.log_weights[r * N + j] = s_rs ? (float)(-log((double)N)) : (float)(s_l[j] - s_logZ);
+        }
+        if (a.out_tokens && j % gs == gi) {
             int32_t* dst = a.out_tokens + (r * N + j) * (K + 1);
             for (int32_t k = 0; k < K; ++k) dst[k] = s_tok[anc * K + k];
             dst[K] = s_bonus[anc];
         }
     }
-    if (NP > 0) {
+    if (NW > 0) {
         __syncthreads();
-        remap_request_lds<kPtRegs>(s_pt, s_dl, a.pt_out + r * NP, s_anc, s_off, N, a.P, a.refcount,
+        remap_columns_lds<kPtRegs>(s_pt, s_dl, w, a.pt_out + r * NP, a.P, p0, s_anc, s_off, N, a.refcount,
                                    a.num_pages, a.error_flags);
     }
 }
@@ -322,10 +343,15 @@ __global__ __launch_bounds__(kThreads) void k_finalize_small(FinalizeArgs a) {
 
 hipError_t launch_finalize(int32_t R, bool from_partials, int32_t dtype, const FinalizeArgs& a,
                            hipStream_t s) {
-    // the page table is staged in LDS: larger ones go to launch_remap instead
-    if (a.pt_in && (int64_t)a.N * a.P > kFusedRemapEntries) return hipErrorInvalidValue;
-    const dim3 grid((unsigned)R), block(kThreads);
-    if (from_partials && a.N <= 64 && a.N * a.K <= kThreads) {
+    const bool small = from_partials && a.N <= 64 && a.N * a.K <= kThreads;
+    // the page table is staged in LDS, a member's share of its columns at a time (k_finalize:
+    // one member); larger shares go to launch_remap instead
+    if (!small && a.members > 1) return hipErrorInvalidValue;
+    const int32_t gs = std::max(a.members, 1);
+    if (a.pt_in && (int64_t)a.N * ((a.P + gs - 1) / gs) > (small ? kFinalizeShare : kFusedRemapEntries))
+        return hipErrorInvalidValue;
+    const dim3 grid((unsigned)((int64_t)R * gs)), block(kThreads);
+    if (small) {
         if (dtype == SMCSD_BF16) k_finalize_small<SMCSD_BF16><<<grid, block, 0, s>>>(a);
         else k_finalize_small<SMCSD_F32><<<grid, block, 0, s>>>(a);
     } else if (!from_partials) {

@@ -194,6 +194,10 @@ __global__ __launch_bounds__(kThreads) void k_logits_stream(LogitsArgs a) {
     // dispatched first, so that the grid's tail holds the lighter row-pair slices
     const int64_t t = blockIdx.x;
     const int64_t bonus_wgs = a.total_wgs - a.pair_wgs;
+    // the previous log-weights, for a finalize that overwrites them while other workgroups of
+    // the request still read them (a grid-stride copy, nothing for most workgroups)
+    for (int64_t i = t * kThreads + threadIdx.x; i < a.lw_n; i += (int64_t)gridDim.x * kThreads)
+        a.lw_copy[i] = a.lw_src[i];
     if (t < bonus_wgs) {
         bonus_slice<DT, kStreamCPL>(a, t / a.S, (int)(t % a.S), red, redi);
     } else if (t < a.total_wgs) {

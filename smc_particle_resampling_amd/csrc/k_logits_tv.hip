@@ -405,9 +405,13 @@ __global__ __launch_bounds__(kThreads, 4) void k_logits_tv(LogitsArgs a) {
 }
 
 // Before a TV pass without bonus rows: the control word (abort flag 0, the wait limit) and
-// every exchange word at the all-ones "empty" pattern, in one launch.
-__global__ void k_fill_tv(Ctrl* ctrl, uint32_t timeout, uint32_t* words, int64_t n) {
+// every exchange word at the all-ones "empty" pattern, in one launch; with lw_n > 0 also the
+// copy of the previous log-weights (LogitsArgs::lw_src).
+__global__ void k_fill_tv(Ctrl* ctrl, uint32_t timeout, uint32_t* words, int64_t n, const float* lw_src,
+                          float* lw_copy, int32_t lw_n) {
     if (blockIdx.x == 0 && threadIdx.x == 0) *ctrl = Ctrl{0u, timeout};
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < lw_n; i += (int64_t)gridDim.x * blockDim.x)
+        lw_copy[i] = lw_src[i];
     for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
          i += (int64_t)gridDim.x * blockDim.x)
         words[i] = ~0u;
@@ -449,7 +453,8 @@ hipError_t launch_tv_fill(const Plan& plan, const LogitsArgs& a, uint32_t timeou
     const int64_t n = (int64_t)(plan.pair_wgs * sizeof(PairPart) / 4);
     const int64_t blocks = std::max<int64_t>(1, std::min<int64_t>((n + kThreads - 1) / kThreads, 1024));
     k_fill_tv<<<dim3((unsigned)blocks), dim3(kThreads), 0, s>>>(a.ctrl, timeout,
-                                                               reinterpret_cast<uint32_t*>(a.pp), n);
+                                                               reinterpret_cast<uint32_t*>(a.pp), n, a.lw_src,
+                                                               a.lw_copy, a.lw_n);
     return hipGetLastError();
 }
 

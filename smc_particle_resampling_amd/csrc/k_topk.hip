@@ -123,6 +123,8 @@ __global__ __launch_bounds__(kThreads, 8) void k_topk_slice(TopkArgs a) {
     if constexpr (MODE == kTopkBonusRows) {
         if (a.fill_words) {
             if (blockIdx.x == 0 && tid == 0) *a.ctrl = Ctrl{0u, a.timeout};
+            for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < a.lw_n; i += (int64_t)gridDim.x * kThreads)
+                a.lw_copy[i] = a.lw_src[i];
             for (int64_t i = (int64_t)blockIdx.x * kThreads + tid; i < a.fill_n;
                  i += (int64_t)gridDim.x * kThreads)
                 a.fill_words[i] = ~0u;

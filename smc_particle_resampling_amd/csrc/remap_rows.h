@@ -129,37 +129,39 @@ __device__ __forceinline__ void remap_columns_runs(const int32_t* in, int32_t* o
     }
 }
 
-// The same remap for a whole request of at most 64 particles held in LDS (in: its N * P
-// entries, at most kPer * blockDim.x), one workgroup, with every refcount atomic in flight
-// at once. The table copy; then one thread per column walks its rows and writes, for every
-// entry, the net change of the run that ends there (0 where no run ends, the run names no
-// page, or the change is 0) into dl; after a barrier every thread adds the
-// changes of its kPer entries, one atomic each, and checks the results only once all of them
-// are issued. A change fits in 16 bits: at most 64 rows, each o_j - 1 in [-1, 63]. Same
-// refcounts and checks as remap_columns_runs.
+// The same remap for columns [p0, p0 + w) of a request's table of P columns, with at most
+// 64 particles, held in LDS as in[j * w + c] (N * w <= kPer * blockDim.x entries), by one
+// workgroup with every refcount atomic in flight at once: the copy out to out[j * P + p0 +
+// c]; then one thread per column walks its rows and writes, for every entry, the net change
+// of the run that ends there (0 where no run ends, the run names no page, or the change is
+// 0) into dl; after a barrier every thread adds the changes of its kPer entries, one atomic
+// each, and checks the results only once all of them are issued. A change fits in 16 bits:
+// at most 64 rows, each o_j - 1 in [-1, 63]. A column's runs are those of
+// remap_columns_runs, so the refcounts and checks are the same whichever workgroup takes
+// which columns.
 template <int kPer>
-__device__ __forceinline__ void remap_request_lds(const int32_t* in, int16_t* dl, int32_t* out,
-                                                  const int32_t* anc, const int32_t* off, int32_t N,
-                                                  int32_t P, int32_t* refcount, int32_t num_pages,
-                                                  int32_t* error_flags) {
-    const int32_t NP = N * P;
+__device__ __forceinline__ void remap_columns_lds(const int32_t* in, int16_t* dl, int32_t w, int32_t* out,
+                                                  int32_t P, int32_t p0, const int32_t* anc,
+                                                  const int32_t* off, int32_t N, int32_t* refcount,
+                                                  int32_t num_pages, int32_t* error_flags) {
+    const int32_t NW = N * w;
     const int32_t tid = (int32_t)threadIdx.x, nt = (int32_t)blockDim.x;
-    if (nt % P == 0) {
+    if (nt % w == 0) {
         // a thread keeps one column
-        const int32_t col = tid % P, dj = nt / P;
+        const int32_t col = tid % w, dj = nt / w;
 #pragma unroll 4
-        for (int32_t j = tid / P; j < N; j += dj) {
+        for (int32_t j = tid / w; j < N; j += dj) {
             const int32_t src = anc[j];
-            out[j * P + col] = src >= 0 ? in[src * P + col] : -1;
+            out[(int64_t)j * P + p0 + col] = src >= 0 ? in[src * w + col] : -1;
         }
     } else {
-        int32_t j = tid / P;
-        int32_t col = tid - j * P;
-        const int32_t dj = nt / P, dc = nt - dj * P;
+        int32_t j = tid / w;
+        int32_t col = tid - j * w;
+        const int32_t dj = nt / w, dc = nt - dj * w;
         while (j < N) {
             const int32_t src = anc[j];
-            out[j * P + col] = src >= 0 ? in[src * P + col] : -1;
-            step_entry(j, col, dj, dc, P);
+            out[(int64_t)j * P + p0 + col] = src >= 0 ? in[src * w + col] : -1;
+            step_entry(j, col, dj, dc, w);
         }
     }
     // The walk has no branch but the loop's: with at most two waves a SIMD nothing hides a
@@ -168,18 +170,18 @@ __device__ __forceinline__ void remap_request_lds(const int32_t* in, int16_t* dl
     const int32_t lane = tid & 63;
     const int32_t offv = lane < N ? off[lane] - 1 : 0;
     bool bad = false;
-    for (int32_t c = tid; c < P; c += nt) {
+    for (int32_t c = tid; c < w; c += nt) {
         int32_t run_page = in[c], run_delta = __builtin_amdgcn_readlane(offv, 0);
         bool run_moves = run_delta != 0;
         for (int32_t j = 1; j <= N; ++j) {
             const int32_t jc = min(j, N - 1);
-            const int32_t pgr = in[jc * P + c];          // always in range; row N is past the end
+            const int32_t pgr = in[jc * w + c];          // always in range; row N is past the end
             const int32_t pg = j < N ? pgr : -1;
             const int32_t od = j < N ? __builtin_amdgcn_readlane(offv, jc) : 0;
             const bool changed = j == N || pg != run_page;
             const bool counts = changed && run_page >= 0 && run_moves;
             bad = bad || (counts && run_page >= num_pages);
-            dl[(j - 1) * P + c] = (int16_t)(counts && run_page < num_pages ? run_delta : 0);
+            dl[(j - 1) * w + c] = (int16_t)(counts && run_page < num_pages ? run_delta : 0);
             run_delta = (changed ? 0 : run_delta) + od;
             run_moves = (!changed && run_moves) || od != 0;
             run_page = pg;
@@ -190,7 +192,7 @@ __device__ __forceinline__ void remap_request_lds(const int32_t* in, int16_t* dl
 #pragma unroll
     for (int b = 0; b < kPer; ++b) {
         const int32_t e = b * nt + tid;
-        d[b] = e < NP ? (int32_t)dl[e] : 0;
+        d[b] = e < NW ? (int32_t)dl[e] : 0;
         old[b] = 0;
         if (d[b] != 0) old[b] = atomicAdd(&refcount[in[e]], d[b]);
     }

@@ -18,7 +18,8 @@ constexpr int kWaves = kThreads / 64;
 constexpr int kStreamCPL = 4;        // 16-byte chunks a lane holds per row of a slice, TV off
 constexpr int kTvCPL = 4;            // ... TV on (its fp32 exponentials stay in registers)
 constexpr int kMaxTvSlices = 64;     // TV exchange: wave 0 reads the 2*S partial words
-constexpr int kFusedRemapEntries = 16 * kThreads;   // tables the finalize kernel remaps
+constexpr int kFusedRemapEntries = 16 * kThreads;   // tables the general finalize kernel remaps
+constexpr int kFinalizeShare = 4 * kThreads;        // table entries a small-finalize workgroup remaps
 
 // How one logits row is cut into 16-byte chunks and the chunks into slices, one workgroup
 // per slice. Every slice is non-empty and every chunk has at least one element < V.
@@ -36,7 +37,7 @@ struct Plan {
     int64_t total_wgs = 0;   // (pairs + bonus_rows) * S
     bool tv = false;
     // workspace offsets in bytes
-    size_t off_ctrl = 0, off_pp = 0, off_tvp = 0, off_bp = 0, off_terms = 0, bytes = 0;
+    size_t off_ctrl = 0, off_pp = 0, off_tvp = 0, off_bp = 0, off_terms = 0, off_lw = 0, bytes = 0;
 };
 
 // Control block at the start of the workspace (zeroed before each TV launch).
@@ -81,6 +82,10 @@ struct LogitsArgs {
     int64_t pairs, pair_wgs, total_wgs;
     int32_t N, K, V;
     int32_t chunks, S, cps;
+    // the previous log-weights copied into the workspace by the pass (lw_n > 0: R * N of them)
+    const float* lw_src;
+    float* lw_copy;
+    int32_t lw_n;
 };
 
 // The TV exchange wait limit: 4e8 ticks (4 s, ~10^4 times the longest expected wait), or
@@ -101,6 +106,9 @@ struct FinalizeArgs {
     const float* log_potential;  // optional [R][N], added to the increment (from partials)
     float* log_w_incr;        // out (from partials) or in
     float* log_weights;       // in/out
+    // the log-weights before the round: log_weights itself, or (members > 1) a copy the
+    // logits pass made, since one member overwrites log_weights while others may still read
+    const float* lw_in;
     const float* uniform;
     float* log_norm;
     float* ess;
@@ -119,6 +127,9 @@ struct FinalizeArgs {
     int32_t N, K, V, S;
     int32_t mode;
     float ess_frac;
+    // k_finalize_small: workgroups per request (request b / members, member b % members), each
+    // remapping its share of the table's columns; 1 otherwise
+    int32_t members;
 };
 
 // Speculative-decoding verification: the residual draw one particle still needs after the
@@ -183,6 +194,11 @@ struct TopkArgs {
     uint32_t* fill_words;
     int64_t fill_n;
     uint32_t timeout;
+    // kTopkBonusRows ahead of a pass: lw_n > 0 copies the previous log-weights as the pass
+    // would (LogitsArgs::lw_src)
+    const float* lw_src;
+    float* lw_copy;
+    int32_t lw_n;
 };
 
 // Page lifecycle between rounds. Workspace: a header (free count before and after release,

@@ -311,16 +311,20 @@ def test_smcsd_resample_ess_exactly_at_threshold(frac, resampled, dev):
 
 
 @pytest.mark.parametrize("N,ctx", [(16, 1024), (128, 1024), (32, 3200), (128, 4096), (100, 1600),
-                                   (16, 9600), (8, 16384), (1, 131072)])
+                                   (16, 9600), (8, 16384), (1, 131072), (24, 14000), (64, 2608),
+                                   (8, 65536), (1, 262144)])
 def test_round_remap_with_repeated_pages(N, ctx, dev):
     # Page ids repeated across rows in any order and across columns, some columns one page for
     # every row. The round's remap (one atomic per run of equal pages in a column up to 64
     # particles, one per entry above) must still give every page the sum over its entries.
-    # Tables of up to 8192 entries a request are remapped by the finalize kernel from LDS
-    # (N * P = 1024 with P dividing the workgroup, 6400 with P = 200 not dividing it, 8192
-    # with 128 particles, 8192 with P = 1024 and P = 8192, more columns than threads), larger
-    # ones by the remap kernel over several workgroups (32768 entries by rows, 10000 by rows
-    # with a stride that is no multiple of P = 100, 9600 by column groups of 120).
+    # Up to 64 particles the small finalize kernel remaps the table from LDS, in one workgroup
+    # a request up to 2048 entries (N * P = 1024), else split by columns over several
+    # workgroups a request: 6400 entries over 4 of 50 columns, 9600 over 5 of 120, 8192 over
+    # 4 of 256, N = 1 and P = 8192 over 4 of 2048, 21000 over 11 of 79-80, 10432 over 6 of
+    # 27-28, 32768 over 16 of 256, N = 1 and P = 16384 over 8. Above 64 particles the general
+    # finalize kernel remaps up to 8192 entries (128 particles) and the remap kernel larger
+    # ones over several workgroups (10000 by rows with a stride that is no multiple of
+    # P = 100, 32768).
     w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="repeated-pages", R=3, N=N, K=2, V=3000,
                                                ctx=ctx)
 
