@@ -6,90 +6,133 @@
 // (a total order, so the selection is exact and deterministic).
 //
 // Pass 1: one 512-thread workgroup per (row, slice), 4 chunks a lane as in the TV pass. Each
-// lane holds its keys in registers and its own best; k rounds of a block argmax over the
-// lanes' bests pick the slice's k best, and only the lane that lost its best rescans. Pass 2:
-// one workgroup per row takes the S * k candidates the same way.
+// lane holds its keys in registers, the best of each chunk group and its own best; k rounds
+// of a block argmax over the lanes' bests pick the slice's k best, and only the lane that
+// lost its best rescans, and only the group it lost it from. Pass 2: one wave per row takes
+// the S * k candidates of its row by k rounds of a wave argmax (one workgroup per row, by
+// block rounds, when they exceed 8 a lane).
+//
+// Both passes rank a (key, index) pair as one 64-bit word whose unsigned order is the
+// ranking: the key's bits mapped to an order-preserving unsigned value (both zeros as +0) in
+// the high half, the complement of the index in the low half, so that one 64-bit compare
+// decides a step. Pass 1 ranks by the index within its slice (chunk group, lane, element),
+// which orders as the index in the row does.
 #include "smcsd_device.h"
 
 namespace smcsd {
 namespace {
 
-__device__ __forceinline__ void argmax_step(float& k, int32_t& i, float ok, int32_t oi) {
-    if (better(ok, oi, k, i)) {
-        k = ok;
-        i = oi;
-    }
+__device__ __forceinline__ uint64_t rank_word(float k, int32_t i) {
+    uint32_t b = __float_as_uint(k);
+    b = (b << 1) == 0u ? 0u : b;   // -0 ranks as +0
+    b = (b & 0x80000000u) ? ~b : (b | 0x80000000u);
+    return ((uint64_t)b << 32) | (uint32_t)~(uint32_t)i;
+}
+__device__ __forceinline__ float rank_key(uint64_t w) {
+    const uint32_t b = (uint32_t)(w >> 32);
+    return __uint_as_float((b & 0x80000000u) ? (b & 0x7fffffffu) : ~b);
+}
+__device__ __forceinline__ int32_t rank_idx(uint64_t w) { return (int32_t)~(uint32_t)w; }
+// The word of an absent entry (key -inf, index INT32_MAX); every present entry ranks above
+// it, and 0 ranks below everything.
+constexpr uint64_t kAbsentWord = (uint64_t(0x007fffffu) << 32) | 0x80000000u;
+
+template <int kCtrl>
+__device__ __forceinline__ uint64_t dpp_u64(uint64_t v) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, kCtrl, 0xF, 0xF, true);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), kCtrl, 0xF, 0xF, true);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t readlane_u64(uint64_t v, int lane) {
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)v, lane);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), lane);
+    return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t max_u64(uint64_t x, uint64_t y) { return x > y ? x : y; }
+
+// The wave's largest word (every lane active), uniform.
+__device__ __forceinline__ uint64_t wave_best(uint64_t w) {
+    w = max_u64(w, dpp_u64<kDppXor1>(w));
+    w = max_u64(w, dpp_u64<kDppXor2>(w));
+    w = max_u64(w, dpp_u64<kDppRowHalfMirror>(w));
+    w = max_u64(w, dpp_u64<kDppRowMirror>(w));
+    return max_u64(max_u64(readlane_u64(w, 0), readlane_u64(w, 16)),
+                   max_u64(readlane_u64(w, 32), readlane_u64(w, 48)));
 }
 
-// Block argmax of every lane's (key, index); all threads get the winner. lds holds 2 *
-// kWaves entries per buffer; callers alternate buffers between rounds, so one barrier per
-// round suffices.
-__device__ __forceinline__ void block_argmax(float& k, int32_t& i, float* lk, int32_t* li) {
-    argmax_step(k, i, dpp_f32<kDppXor1>(k), dpp_i32<kDppXor1>(i));
-    argmax_step(k, i, dpp_f32<kDppXor2>(k), dpp_i32<kDppXor2>(i));
-    argmax_step(k, i, dpp_f32<kDppRowHalfMirror>(k), dpp_i32<kDppRowHalfMirror>(i));
-    argmax_step(k, i, dpp_f32<kDppRowMirror>(k), dpp_i32<kDppRowMirror>(i));
-    float bk = readlane_f32(k, 0);
-    int32_t bi = __builtin_amdgcn_readlane(i, 0);
-#pragma unroll
-    for (int r = 16; r < 64; r += 16)
-        argmax_step(bk, bi, readlane_f32(k, r), __builtin_amdgcn_readlane(i, r));
-    const int w = threadIdx.x >> 6;
-    if ((threadIdx.x & 63) == 0) {
-        lk[w] = bk;
-        li[w] = bi;
-    }
-    __syncthreads();
-    bk = lk[0];
-    bi = li[0];
-    for (int t = 1; t < kWaves; ++t) argmax_step(bk, bi, lk[t], li[t]);
-    k = bk;
-    i = bi;
-}
-
-// The lane's best among n (key, index) pairs held in registers.
+// k rounds of a wave argmax over n words a lane (0 = no entry); round it leaves its winner
+// in lane it's res (lanes it < k; k <= 64). A lane drops a present winner it holds and takes
+// its next best; absent entries are never dropped, so once only they remain every further
+// round returns kAbsentWord.
 template <int n>
-__device__ __forceinline__ void lane_best(const float (&key)[n], const int32_t (&idx)[n], float& bk,
-                                          int32_t& bi) {
-    bk = -INFINITY;
-    bi = INT32_MAX;
+__device__ __forceinline__ uint64_t wave_select(uint64_t (&c)[n], int k) {
+    const int lane = threadIdx.x & 63;
+    uint64_t lb = c[0];
 #pragma unroll
-    for (int e = 0; e < n; ++e) argmax_step(bk, bi, key[e], idx[e]);
-}
-
-// k rounds of selection over keys held in registers; writes the winners to out (k entries).
-template <int n>
-__device__ __forceinline__ void select_k(float (&key)[n], int32_t (&idx)[n], int k,
-                                         BonusPart* out, float* lk, int32_t* li) {
-    float bk;
-    int32_t bi;
-    lane_best<n>(key, idx, bk, bi);
+    for (int e = 1; e < n; ++e) lb = max_u64(lb, c[e]);
+    uint64_t res = kAbsentWord;
     for (int it = 0; it < k; ++it) {
-        float wk = bk;
-        int32_t wi = bi;
-        const int buf = (it & 1) * kWaves;
-        block_argmax(wk, wi, lk + buf, li + buf);
-        if (threadIdx.x == 0) out[it] = BonusPart{wk, wk == -INFINITY ? INT32_MAX : wi};
-        if (bi == wi && bk != -INFINITY) {
-            // this lane held the winner: drop it and rescan
+        const uint64_t best = wave_best(lb);
+        if (lane == it) res = best;
+        if (it + 1 < k && lb == best && best != kAbsentWord) {
 #pragma unroll
-            for (int e = 0; e < n; ++e)
-                if (idx[e] == wi) key[e] = -INFINITY;
-            lane_best<n>(key, idx, bk, bi);
+            for (int e = 0; e < n; ++e) c[e] = c[e] == best ? 0 : c[e];
+            lb = c[0];
+#pragma unroll
+            for (int e = 1; e < n; ++e) lb = max_u64(lb, c[e]);
         }
     }
+    return res;
 }
 
-// The lane's best position among n keys whose indices increase with the position: the first
-// position holding the maximum (-1 if every key is -inf).
-template <int n>
-__device__ __forceinline__ int lane_best_pos(const float (&key)[n], float& bk) {
-    float m = key[0];
+// The block's largest word (all threads, every lane active); lw holds kWaves words. Callers
+// alternate two buffers between rounds, so one barrier per round suffices.
+__device__ __forceinline__ uint64_t block_best(uint64_t w, uint64_t* lw) {
+    w = wave_best(w);
+    if ((threadIdx.x & 63) == 0) lw[threadIdx.x >> 6] = w;
+    __syncthreads();
+    uint64_t b = lw[0];
 #pragma unroll
-    for (int e = 1; e < n; ++e) m = fmaxf(m, key[e]);
+    for (int t = 1; t < kWaves; ++t) b = max_u64(b, lw[t]);
+    return b;
+}
+
+// Best of chunk group j of a lane's keys (EPC keys from j * EPC): its maximum, and the first
+// position holding it in bits 4j..4j+3 of gp.
+template <int DT>
+__device__ __forceinline__ void group_best(const float (&key)[kTopkCPL * (DT == SMCSD_F32 ? 4 : 8)], int j,
+                                           float& gk, uint32_t& gp) {
+    constexpr int EPC = DT == SMCSD_F32 ? 4 : 8;
+    float m = key[j * EPC];
+#pragma unroll
+    for (int e = 1; e < EPC; ++e) m = fmaxf(m, key[j * EPC + e]);
+    uint32_t p = 0;
+#pragma unroll
+    for (int e = EPC - 1; e >= 0; --e) p = key[j * EPC + e] == m ? (uint32_t)e : p;
+    gk = m;
+    gp = (gp & ~(0xfu << (4 * j))) | (p << (4 * j));
+}
+
+// Drops key e of group j (sets it to -inf) and takes the group's best again.
+template <int DT>
+__device__ __forceinline__ void drop_in_group(float (&key)[kTopkCPL * (DT == SMCSD_F32 ? 4 : 8)], int j, int e,
+                                              float& gk, uint32_t& gp) {
+    constexpr int EPC = DT == SMCSD_F32 ? 4 : 8;
+#pragma unroll
+    for (int x = 0; x < EPC; ++x) key[j * EPC + x] = x == e ? -INFINITY : key[j * EPC + x];
+    group_best<DT>(key, j, gk, gp);
+}
+
+// The lane's best position from its groups' bests (groups in increasing index order): the
+// first group holding the maximum; -1 if every key is -inf.
+template <int EPC>
+__device__ __forceinline__ int lane_best_of_groups(const float (&gk)[kTopkCPL], uint32_t gp, float& bk) {
+    float m = gk[0];
+#pragma unroll
+    for (int j = 1; j < kTopkCPL; ++j) m = fmaxf(m, gk[j]);
     int pos = -1;
 #pragma unroll
-    for (int e = n - 1; e >= 0; --e) pos = key[e] == m ? e : pos;
+    for (int j = kTopkCPL - 1; j >= 0; --j) pos = gk[j] == m ? j * EPC + (int)((gp >> (4 * j)) & 0xfu) : pos;
     bk = m;
     return m == -INFINITY ? -1 : pos;
 }
@@ -102,8 +145,7 @@ __global__ __launch_bounds__(kThreads, 8) void k_topk_slice(TopkArgs a) {
     constexpr int EPC = DT == SMCSD_F32 ? 4 : 8;
     constexpr size_t ESZ = DT == SMCSD_F32 ? 4 : 2;
     constexpr int n = kTopkCPL * EPC;
-    __shared__ float lk[2 * kWaves];
-    __shared__ int32_t li[2 * kWaves];
+    __shared__ uint64_t cw[2 * kWaves];
     const uint32_t row32 = blockIdx.x / (unsigned)a.S;   // rows * S < 2^31
     const int64_t row = row32;
     const int s = (int)(blockIdx.x % (unsigned)a.S);
@@ -157,35 +199,78 @@ __global__ __launch_bounds__(kThreads, 8) void k_topk_slice(TopkArgs a) {
                                   : -INFINITY;
         }
     }
-    // k rounds: block argmax of the lanes' bests; the winning lane drops that key and finds
-    // its next best. A lane's keys are in increasing index order (chunk group, then element).
-    BonusPart* out = a.cand + (row * a.S + s) * a.k;
-    float bk;
-    int pos = lane_best_pos<n>(key, bk);
-    auto index_of = [&](int p) {
-        return p < 0 ? INT32_MAX : (c0 + (p / EPC) * kThreads + tid) * EPC + p % EPC;
-    };
-    for (int it = 0; it < a.k; ++it) {
-        float wk = bk;
-        int32_t wi = index_of(pos);
-        const int32_t mine = wi;
-        const int buf = (it & 1) * kWaves;
-        block_argmax(wk, wi, lk + buf, li + buf);
-        if (tid == 0) out[it] = BonusPart{wk, wk == -INFINITY ? INT32_MAX : wi};
-        if (pos >= 0 && mine == wi) {
+    // k rounds of a block argmax over the lanes' bests (as rank words); the winning lane drops
+    // that key and finds its next best. A lane's keys are in increasing index order (chunk
+    // group, then element), so its first maximum is its best; it keeps each group's best, and
+    // a drop rescans only the dropped key's group.
+    float gk[kTopkCPL];
+    uint32_t gp = 0;
 #pragma unroll
-            for (int e = 0; e < n; ++e) key[e] = e == pos ? -INFINITY : key[e];
-            pos = lane_best_pos<n>(key, bk);
+    for (int j = 0; j < kTopkCPL; ++j) group_best<DT>(key, j, gk[j], gp);
+    float bk;
+    int pos = lane_best_of_groups<EPC>(gk, gp, bk);
+    for (int it = 0; it < a.k; ++it) {
+        // ranked by the index within the slice, (group, lane, element) in that order
+        const uint64_t mine =
+            pos < 0 ? kAbsentWord : rank_word(bk, (pos / EPC) * (kThreads * EPC) + tid * EPC + pos % EPC);
+        const uint64_t best = block_best(mine, cw + (it & 1) * kWaves);
+        if (tid == 0) {
+            const float rk = rank_key(best);
+            a.cand[(row * a.S + s) * a.k + it] =
+                BonusPart{rk, rk == -INFINITY ? INT32_MAX : c0 * EPC + rank_idx(best)};
+        }
+        if (it + 1 < a.k && pos >= 0 && mine == best) {
+            const int g = pos / EPC, e = pos % EPC;
+#pragma unroll
+            for (int j = 0; j < kTopkCPL; ++j)
+                if (j == g) drop_in_group<DT>(key, j, e, gk[j], gp);
+            pos = lane_best_of_groups<EPC>(gk, gp, bk);
         }
     }
 }
 
+// Pass 2 with one wave a row, for S * k <= 512 candidates (8 a lane).
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void k_topk_merge_wave(TopkArgs a, int64_t rows) {
+    constexpr int n = kWaves * kMaxTopk / 64;
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * kWaves + (threadIdx.x >> 6);
+    if (row >= rows) return;
+    if constexpr (MODE == kTopkResampled) {
+        const int32_t x = a.ancestors[row];
+        if (x < 0 || x >= a.N) {
+            if (lane == 0) {
+                flag_error(a.error_flags, SMCSD_DEVERR_ANCESTOR);
+                a.out_tokens[row] = -1;
+                if (a.slot_tokens) a.slot_tokens[row * (a.K + 1) + a.K] = -1;
+            }
+            return;
+        }
+    }
+    const int m = a.S * a.k;
+    const BonusPart* cr = a.cand + row * m;
+    uint64_t c[n];
+#pragma unroll
+    for (int e = 0; e < n; ++e) {
+        const int t = e * 64 + lane;
+        c[e] = t < m ? rank_word(cr[t].key, cr[t].idx) : 0;
+    }
+    const uint64_t res = wave_select<n>(c, a.k);
+    const float rk = rank_key(res);
+    const int32_t ri = rk == -INFINITY ? INT32_MAX : rank_idx(res);
+    if (lane < a.k) {
+        a.out_tokens[row * a.k + lane] = ri;
+        if (a.out_keys) a.out_keys[row * a.k + lane] = rk;
+    }
+    if (a.slot_tokens && lane == 0) a.slot_tokens[row * (a.K + 1) + a.K] = ri;
+}
+
+// Pass 2 with one workgroup a row, for more than 512 candidates (at most 8 a lane).
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void k_topk_merge(TopkArgs a) {
-    constexpr int n = kMaxTopk * kMaxTopkSlices / kThreads;   // 8 candidates a lane at most
-    __shared__ float lk[2 * kWaves];
-    __shared__ int32_t li[2 * kWaves];
-    __shared__ BonusPart res[kMaxTopk];
+    constexpr int n = kMaxTopk * kMaxTopkSlices / kThreads;
+    __shared__ uint64_t cw[2 * kWaves];
+    __shared__ uint64_t res[kMaxTopk];
     const int64_t row = blockIdx.x;
     const int tid = threadIdx.x;
     if constexpr (MODE == kTopkResampled) {
@@ -200,22 +285,35 @@ __global__ __launch_bounds__(kThreads) void k_topk_merge(TopkArgs a) {
         }
     }
     const int m = a.S * a.k;
-    const BonusPart* c = a.cand + row * m;
-    float key[n];
-    int32_t idx[n];
+    const BonusPart* cr = a.cand + row * m;
+    uint64_t c[n];
 #pragma unroll
     for (int e = 0; e < n; ++e) {
         const int t = e * kThreads + tid;
-        key[e] = t < m ? c[t].key : -INFINITY;
-        idx[e] = t < m ? c[t].idx : INT32_MAX;
+        c[e] = t < m ? rank_word(cr[t].key, cr[t].idx) : 0;
     }
-    select_k<n>(key, idx, a.k, res, lk, li);
+    uint64_t lb = c[0];
+#pragma unroll
+    for (int e = 1; e < n; ++e) lb = max_u64(lb, c[e]);
+    for (int it = 0; it < a.k; ++it) {
+        const uint64_t best = block_best(lb, cw + (it & 1) * kWaves);
+        if (tid == 0) res[it] = best;
+        if (it + 1 < a.k && lb == best && best != kAbsentWord) {
+#pragma unroll
+            for (int e = 0; e < n; ++e) c[e] = c[e] == best ? 0 : c[e];
+            lb = c[0];
+#pragma unroll
+            for (int e = 1; e < n; ++e) lb = max_u64(lb, c[e]);
+        }
+    }
     __syncthreads();
     for (int j = tid; j < a.k; j += kThreads) {
-        a.out_tokens[row * a.k + j] = res[j].idx;
-        if (a.out_keys) a.out_keys[row * a.k + j] = res[j].key;
+        const float rk = rank_key(res[j]);
+        const int32_t ri = rk == -INFINITY ? INT32_MAX : rank_idx(res[j]);
+        a.out_tokens[row * a.k + j] = ri;
+        if (a.out_keys) a.out_keys[row * a.k + j] = rk;
+        if (a.slot_tokens && j == 0) a.slot_tokens[row * (a.K + 1) + a.K] = ri;
     }
-    if (a.slot_tokens && tid == 0) a.slot_tokens[row * (a.K + 1) + a.K] = res[0].idx;
 }
 
 }  // namespace
@@ -233,8 +331,15 @@ hipError_t launch_topk(int64_t rows, int32_t dtype, const TopkArgs& a, hipStream
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    if (a.row_mode == kTopkResampled) k_topk_merge<kTopkResampled><<<dim3((unsigned)rows), block, 0, s>>>(a);
-    else k_topk_merge<kTopkRows><<<dim3((unsigned)rows), block, 0, s>>>(a);
+    if ((int64_t)a.S * a.k <= kWaves * kMaxTopk) {
+        const dim3 g2((unsigned)((rows + kWaves - 1) / kWaves));
+        if (a.row_mode == kTopkResampled) k_topk_merge_wave<kTopkResampled><<<g2, block, 0, s>>>(a, rows);
+        else k_topk_merge_wave<kTopkRows><<<g2, block, 0, s>>>(a, rows);
+    } else if (a.row_mode == kTopkResampled) {
+        k_topk_merge<kTopkResampled><<<dim3((unsigned)rows), block, 0, s>>>(a);
+    } else {
+        k_topk_merge<kTopkRows><<<dim3((unsigned)rows), block, 0, s>>>(a);
+    }
     return hipGetLastError();
 }
 
