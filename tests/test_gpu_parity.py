@@ -100,6 +100,25 @@ def test_log_potential(mode, tv, dev):
         assert all(not (set(gpu["ancestors"][r].tolist()) & dead[r]) for r in range(w.R))
 
 
+@pytest.mark.parametrize("mode", ["never", "ess", "always"])
+def test_potential_with_split_table(mode, dev):
+    """A table of 32 x 256 entries a request, split by columns over four finalize workgroups
+    a request, each redoing the weights from the previous log-weights (carried over in
+    "never" and "ess"), with a log potential that removes particles."""
+    w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="potential-split", R=3, V=20000, ctx=4096,
+                                                mode=mode, ess_frac=0.7)
+    assert w.N * w.P > 2048
+
+    def add(inp):
+        inp["log_potential"] = synth.make_log_potential(w.R, w.N, 11, dev)
+        g = torch.Generator(device=dev)
+        g.manual_seed(13)
+        x = torch.randn(w.R, w.N, generator=g, device=dev)
+        inp["log_weights"].copy_(torch.log_softmax(x, dim=1))   # unequal previous weights
+
+    run_and_compare(w, dev, seed=12, modify=add)
+
+
 @pytest.mark.parametrize("N,K", [(1, 1), (1, 4), (3, 1), (1024, 2), (40, 17), (2, 256)])
 def test_particle_and_position_extremes(N, K, dev):
     w = W["r64-n32-k8-v128256-bf16-tv"].scaled(name="extreme", R=2, N=N, K=K, V=3000, ctx=64)
