@@ -18,7 +18,19 @@
 namespace smcsd {
 namespace {
 
-constexpr float kLn2 = 0.69314718055994530942f;
+// 1 - 2^t for t <= 0, without cancellation as t -> 0. For t >= -1 it is -(e^x - 1) at
+// x = t ln 2 by the Taylor series of e^x - 1 through x^9, written in t (coefficients
+// ln2^n / n!; the truncation is below 1e-8 relative there, and Horner's rounding keeps the
+// result within about 2 ulp); below -1 it is 1 - 2^t directly, which is then at least 0.5.
+__device__ __forceinline__ float one_minus_exp2(float t) {
+    constexpr float c[9] = {0.69314718f,    0.24022651f,    0.055504110f,
+                            0.0096181286f,  0.0013333558f,  1.5403530e-4f,
+                            1.5252734e-5f,  1.3215487e-6f,  1.0178086e-7f};
+    float p = c[8];
+#pragma unroll
+    for (int n = 7; n >= 0; --n) p = fmaf(t, p, c[n]);
+    return t >= -1.0f ? -t * p : 1.0f - __builtin_amdgcn_exp2f(t);
+}
 
 template <int DT>
 __global__ __launch_bounds__(kThreads) void k_verify_decide(VerifyArgs a) {
@@ -169,7 +181,7 @@ __global__ __launch_bounds__(kThreads) void k_residual(VerifyArgs a) {
                     const float lp2 = chunk_elem<DT>(P, e) * c - job.lp;
                     const float lq2 = chunk_elem<DT>(Q, e) * c - job.lq;
                     if (lp2 > lq2) {
-                        rv[e] = __builtin_amdgcn_exp2f(lp2) * -expm1f((lq2 - lp2) * kLn2);
+                        rv[e] = __builtin_amdgcn_exp2f(lp2) * one_minus_exp2(lq2 - lp2);
                         if (rv[e] > 0.0f) last = v;
                     }
                 }
