@@ -46,7 +46,7 @@ typedef struct ihipEvent_t *smcsd_event;
 typedef enum smcsd_status {
     SMCSD_OK = 0,
     SMCSD_ERR_ARG = 1,         /* null, out-of-range or inconsistent argument */
-    SMCSD_ERR_UNSUPPORTED = 2, /* valid request beyond this build's limits (see below) */
+    SMCSD_ERR_UNSUPPORTED = 2, /* valid request beyond the library's limits (see below) */
     SMCSD_ERR_WORKSPACE = 3,   /* workspace NULL or smaller than smcsd_workspace_size() */
     SMCSD_ERR_DEVICE = 4,      /* a HIP launch or runtime call failed */
     SMCSD_ERR_SCRATCH = 5      /* smcsd_round_noalloc: more than SMCSD_NOALLOC_SCRATCH_BYTES */
