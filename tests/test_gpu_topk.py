@@ -77,10 +77,12 @@ def test_topk_k_values(k, dev):
 @pytest.mark.parametrize("V,dtype,k", [(1, "bf16", 1), (9, "bf16", 9), (7, "f32", 3),
                                        (64, "bf16", 64), (5001, "bf16", 13), (16385, "f32", 8),
                                        (1048569, "bf16", 8), (524288, "f32", 5),
-                                       (1048569, "bf16", 64), (300000, "f32", 40)])
+                                       (1048569, "bf16", 64), (300000, "f32", 40),
+                                       (933888, "bf16", 9)])
 def test_topk_ragged_and_maximal(V, dtype, k, dev):
     # V = 1048569 bf16 is 64 slices: k = 8 gives 512 candidates a row (the most the one-wave
-    # merge takes), k = 64 the most of all (4096); 300000 f32 is 37 slices, k = 40 1480
+    # merge takes), k = 64 the most of all (4096); 300000 f32 is 37 slices, k = 40 1480;
+    # 933888 bf16 is 57 slices, k = 9 513 (one past the one-wave merge)
     w = W["r16-n16-k4-v128256-bf16"].scaled(name="topk-ragged", R=2, N=3, V=V, dtype=dtype, ctx=64)
     inp = synth.make_inputs(w, 2, device=dev, pages=False)
     z, T, G = synth.topk_rows(inp)
